@@ -1,0 +1,195 @@
+"""CPU oracle for MiniMax Sparse Attention — TEST INFRASTRUCTURE ONLY.
+
+ctypes front end of ``msa_oracle.c``: a plain fp64 statement of the method
+(index scoring, causal block max-pool, top-k, sparse softmax attention; plus
+textbook dense causal attention for invariants). Only the tests, the smoke
+check and the benchmark's CPU-baseline leg may import this package; the GPU
+library never does, and the two share no code.
+
+Arrays are numpy, row-major:
+  q_idx [B,T,G,dI] (uint16 bf16 bits or uint8 E4M3FN bits), k_idx [B,N,dI],
+  q [B,T,H,d] uint16, k_cache / v_cache [B,G,N,d] uint16,
+  kv_lens [B] int32, q_start [B] int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "msa_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+BF16, E4M3 = 0, 1
+
+
+def build(force: bool = True, source: str = SOURCE, out: str = LIBRARY) -> str:
+    """Compiles the oracle with gcc (-O2, fp64, no fast-math)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread",
+                               "-I", _HERE, source, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("groups", ctypes.c_int32), ("heads_per_group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_double), ("index_dtype", ctypes.c_int32)]
+
+
+@dataclass
+class Config:
+    """Shapes of one MSA layer (names follow the pages' sparse_attention_config)."""
+    groups: int = 4              # G = KV heads = index heads (sparse_num_index_heads)
+    heads_per_group: int = 8     # R
+    head_dim: int = 128          # d
+    index_dim: int = 128         # d_I (sparse_index_dim)
+    block_size: int = 128        # S (sparse_block_size)
+    topk: int = 16               # K (sparse_topk_blocks)
+    softmax_scale: float = 0.0   # <= 0: 1/sqrt(d)
+    index_dtype: int = BF16
+
+    def c(self) -> _Cfg:
+        return _Cfg(self.groups, self.heads_per_group, self.head_dim, self.index_dim,
+                    self.block_size, self.topk, float(self.softmax_scale), self.index_dtype)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class Oracle:
+    """One loaded build of the oracle library (the tests also load variants)."""
+
+    def __init__(self, path: str | None = None):
+        path = path or LIBRARY
+        if path == LIBRARY and not os.path.exists(path):
+            build(force=False)
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, P = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER
+        cfgp = P(_Cfg)
+        lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_index_topk_row.argtypes = [cfgp, vp, vp, i64, vp, vp]
+        lib.oracle_sparse_attn_row.argtypes = [cfgp, vp, vp, vp, i64, i64, vp, vp, vp]
+        lib.oracle_dense_causal_row.argtypes = [cfgp, vp, vp, vp, i64, i64, vp, vp]
+        lib.oracle_index_topk_rows.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, i64, vp, vp,
+                                               i32, vp, vp]
+        lib.oracle_sparse_attn_rows.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, vp, i64, vp, vp,
+                                                vp, i32, vp, vp]
+        lib.oracle_dense_causal_rows.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, vp, i64, vp, vp,
+                                                 i32, vp, vp]
+        for f in (lib.oracle_index_topk_row, lib.oracle_sparse_attn_row,
+                  lib.oracle_dense_causal_row, lib.oracle_index_topk_rows,
+                  lib.oracle_sparse_attn_rows, lib.oracle_dense_causal_rows):
+            f.restype = ctypes.c_int
+        self.lib = lib
+
+    # -- element decoders -------------------------------------------------
+    def bf16_value(self, bits: int) -> float:
+        return self.lib.oracle_bf16_value(bits)
+
+    def e4m3_value(self, bits: int) -> float:
+        return self.lib.oracle_e4m3_value(bits)
+
+    # -- batched, row-listed calls ---------------------------------------
+    @staticmethod
+    def _rows(rows, B, T):
+        if rows is None:
+            bb, ii = np.meshgrid(np.arange(B, dtype=np.int32), np.arange(T, dtype=np.int32),
+                                 indexing="ij")
+            return bb.reshape(-1).copy(), ii.reshape(-1).copy()
+        rows = np.asarray(rows, dtype=np.int32).reshape(-1, 2)
+        return np.ascontiguousarray(rows[:, 0]), np.ascontiguousarray(rows[:, 1])
+
+    def index_topk(self, cfg: Config, q_idx, k_idx, kv_lens, q_start, rows=None, threads=None):
+        """sel [n,G,K] int32 and pooled scores [n,G,K] float64 for the listed (b, i) rows."""
+        q_idx = np.ascontiguousarray(q_idx)
+        k_idx = np.ascontiguousarray(k_idx)
+        B, T = q_idx.shape[0], q_idx.shape[1]
+        n_stride = k_idx.shape[1]
+        rb, ri = self._rows(rows, B, T)
+        n = rb.size
+        sel = np.empty((n, cfg.groups, cfg.topk), np.int32)
+        scores = np.empty((n, cfg.groups, cfg.topk), np.float64)
+        c = cfg.c()
+        rc = self.lib.oracle_index_topk_rows(
+            ctypes.byref(c), T, n_stride, _ptr(q_idx), _ptr(k_idx), _ptr(_c(kv_lens, np.int32)),
+            _ptr(_c(q_start, np.int32)), n, _ptr(rb), _ptr(ri), threads or _threads(),
+            _ptr(sel), _ptr(scores))
+        if rc:
+            raise ValueError("oracle_index_topk_rows rejected its arguments")
+        return sel, scores
+
+    def sparse_attn(self, cfg: Config, q, k_cache, v_cache, kv_lens, q_start, sel, rows=None,
+                    threads=None):
+        """out [n,H,d] float64 and lse [n,H] float64; sel is [n,G,K] for the listed rows."""
+        q = _c(q, np.uint16)
+        k_cache = _c(k_cache, np.uint16)
+        v_cache = _c(v_cache, np.uint16)
+        B, T = q.shape[0], q.shape[1]
+        n_stride = k_cache.shape[2]
+        rb, ri = self._rows(rows, B, T)
+        n = rb.size
+        sel = _c(sel, np.int32).reshape(n, cfg.groups, cfg.topk)
+        H = cfg.groups * cfg.heads_per_group
+        out = np.empty((n, H, cfg.head_dim), np.float64)
+        lse = np.empty((n, H), np.float64)
+        c = cfg.c()
+        rc = self.lib.oracle_sparse_attn_rows(
+            ctypes.byref(c), T, n_stride, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(_c(kv_lens, np.int32)), _ptr(_c(q_start, np.int32)), n, _ptr(rb), _ptr(ri),
+            _ptr(sel), threads or _threads(), _ptr(out), _ptr(lse))
+        if rc:
+            raise ValueError("oracle_sparse_attn_rows rejected its arguments")
+        return out, lse
+
+    def dense_causal(self, cfg: Config, q, k_cache, v_cache, kv_lens, q_start, rows=None,
+                     threads=None):
+        """Dense causal GQA attention: out [n,H,d], lse [n,H] (float64)."""
+        q = _c(q, np.uint16)
+        k_cache = _c(k_cache, np.uint16)
+        v_cache = _c(v_cache, np.uint16)
+        B, T = q.shape[0], q.shape[1]
+        n_stride = k_cache.shape[2]
+        rb, ri = self._rows(rows, B, T)
+        n = rb.size
+        H = cfg.groups * cfg.heads_per_group
+        out = np.empty((n, H, cfg.head_dim), np.float64)
+        lse = np.empty((n, H), np.float64)
+        c = cfg.c()
+        rc = self.lib.oracle_dense_causal_rows(
+            ctypes.byref(c), T, n_stride, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(_c(kv_lens, np.int32)), _ptr(_c(q_start, np.int32)), n, _ptr(rb), _ptr(ri),
+            threads or _threads(), _ptr(out), _ptr(lse))
+        if rc:
+            raise ValueError("oracle_dense_causal_rows rejected its arguments")
+        return out, lse
+
+
+def _threads() -> int:
+    return max(1, min(os.cpu_count() or 1, 64))
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from this directory's source."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,378 @@
+"""Pins for the CPU oracle: checks against facts fixed outside the oracle.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with the hand-worked example, with brute force, with textbook dense
+attention written independently in numpy, with a closed form, or with an
+invariant of the method. ``test_oracle.py`` runs them on the real oracle;
+``test_oracle_mutants.py`` plants mistakes in copies of the oracle's source
+and checks that some pin catches each one.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+from oracle import BF16, E4M3, Config
+from msa_synth import float_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers (independent of the oracle)
+
+def bf16(x) -> np.ndarray:
+    return float_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def e4m3_int(v: int) -> int:
+    """E4M3FN code of a small integer, by search over the OCP format's value table."""
+    for code in range(256):
+        s = -1.0 if code & 0x80 else 1.0
+        e, m = (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            continue
+        val = s * (m / 8.0) * 2.0 ** -6 if e == 0 else s * (1 + m / 8.0) * 2.0 ** (e - 7)
+        if val == v and not (v == 0 and code & 0x80):
+            return code
+    raise ValueError(v)
+
+
+def tiny_problem(rng, L, G, R, d, dI, S, K, B=1, T=None, q_start=None, kv_lens=None,
+                 index_dtype=BF16, lo=-2, hi=2):
+    """Random integer-valued index inputs and small-integer attention inputs."""
+    T = L if T is None else T
+    cfg = Config(groups=G, heads_per_group=R, head_dim=d, index_dim=dI, block_size=S, topk=K,
+                 index_dtype=index_dtype)
+    qi = rng.integers(lo, hi + 1, size=(B, T, G, dI))
+    ki = rng.integers(lo, hi + 1, size=(B, L, dI))
+    q = rng.standard_normal((B, T, G * R, d)).astype(np.float32)
+    k = rng.standard_normal((B, G, L, d)).astype(np.float32)
+    v = rng.standard_normal((B, G, L, d)).astype(np.float32)
+    if index_dtype == E4M3:
+        enc = np.vectorize(e4m3_int)
+        qi_b, ki_b = enc(qi).astype(np.uint8), enc(ki).astype(np.uint8)
+    else:
+        qi_b, ki_b = bf16(qi), bf16(ki)
+    kv_lens = np.full(B, L, np.int32) if kv_lens is None else np.asarray(kv_lens, np.int32)
+    q_start = (kv_lens - T).astype(np.int32) if q_start is None else np.asarray(q_start, np.int32)
+    return dict(cfg=cfg, qi=qi, ki=ki, qi_b=qi_b, ki_b=ki_b, q_b=bf16(q), k_b=bf16(k),
+                v_b=bf16(v), kv_lens=kv_lens, q_start=q_start)
+
+
+def as_f(bits) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(
+        np.float64)
+
+
+def numpy_masked_attention(q, k, v, allowed, tau):
+    """Textbook softmax(tau * q k^T + mask) v for one head; allowed is a bool key mask."""
+    z = tau * (k @ q)
+    z = np.where(allowed, z, -np.inf)
+    m = z.max()
+    w = np.exp(z - m)
+    w = w / w.sum()
+    return w @ v, m + math.log(np.exp(z - m).sum())
+
+
+def brute_force_topk(s_row, p, S, K):
+    """Block choice by enumerating all subsets; the best subset has the largest
+    multiset of (pooled score, -block) keys."""
+    nv = p // S + 1
+    pooled = [max(s_row[b * S: min(b * S + S, p + 1)]) for b in range(nv)]
+    keys = [(pooled[b], -b) for b in range(nv)]
+    best = None
+    for subset in itertools.combinations(range(nv), min(K, nv)):
+        ks = sorted((keys[b] for b in subset), reverse=True)
+        if best is None or ks > best[0]:
+            best = (ks, subset)
+    chosen = sorted(best[1], key=lambda b: keys[b], reverse=True)
+    return chosen + [-1] * (K - len(chosen))
+
+
+def load_hand_example():
+    with open(os.path.join(GOLDEN, "hand_example_L8.json")) as f:
+        return json.load(f)
+
+
+def hand_inputs(topk=2, q_start=0, kv_len=8, T=None):
+    g = load_hand_example()
+    L = g["config"]["L"]
+    T = kv_len - q_start if T is None else T
+    cfg = Config(groups=1, heads_per_group=2, head_dim=1, index_dim=1, block_size=2, topk=topk,
+                 softmax_scale=1.0)
+    qi = np.array(g["q_idx"], np.float32)[q_start:q_start + T].reshape(1, T, 1, 1)
+    ki = np.array(g["k_idx"], np.float32).reshape(1, L, 1)
+    q = np.zeros((1, T, 2, 1), np.float32)
+    q[:, :, 0, 0] = 1.0
+    kk = (np.arange(L) % 2).astype(np.float32).reshape(1, 1, L, 1)
+    vv = np.arange(L, dtype=np.float32).reshape(1, 1, L, 1)
+    return cfg, bf16(qi), bf16(ki), bf16(q), bf16(kk), bf16(vv), np.array([kv_len], np.int32), \
+        np.array([q_start], np.int32)
+
+
+# ---------------------------------------------------------------------------
+# pins
+
+def pin_decoders(orc):
+    """bf16 and OCP E4M3FN decoding against values fixed by the formats."""
+    assert orc.bf16_value(0x3F80) == 1.0
+    assert orc.bf16_value(0xC000) == -2.0
+    assert orc.bf16_value(0x3F81) == 1.0 + 2.0 ** -7
+    assert orc.bf16_value(0x4080) == 4.0
+    for code, val in ((0x38, 1.0), (0x40, 2.0), (0x44, 3.0), (0x48, 4.0), (0xB8, -1.0),
+                      (0xC8, -4.0), (0x7E, 448.0), (0x01, 2.0 ** -9), (0x08, 2.0 ** -6),
+                      (0x00, 0.0), (0x3C, 1.5)):
+        assert orc.e4m3_value(code) == val, hex(code)
+    assert math.isnan(orc.e4m3_value(0x7F))
+
+
+def pin_hand_example_selection(orc):
+    """Selection and pooled scores equal the hand-worked example, row by row."""
+    g = load_hand_example()
+    cfg, qi, ki, *_ , kv, qs = hand_inputs()
+    sel, sc = orc.index_topk(cfg, qi, ki, kv, qs)
+    assert sel[:, 0, :].tolist() == g["sel_topk2"], sel[:, 0, :].tolist()
+    for t in range(8):
+        pooled = g["pooled"][t]
+        want = [pooled[b] if b >= 0 else -math.inf for b in g["sel_topk2"][t]]
+        assert sc[t, 0, :].tolist() == want, (t, sc[t, 0, :].tolist(), want)
+    cfg4, qi, ki, *_ , kv, qs = hand_inputs(topk=4)
+    sel4, _ = orc.index_topk(cfg4, qi, ki, kv, qs)
+    assert sel4[7, 0, :].tolist() == g["sel_topk4_row7"]
+
+
+def pin_hand_example_attention(orc):
+    """Attention outputs equal the example's closed forms (uniform and softmax heads)."""
+    g = load_hand_example()
+    e = math.e
+    sig = e / (1 + e)
+    closed_out = [0, sig, 1, 1 + sig, 1 + sig, 3 + sig, 1 + sig, 1 + sig]
+    closed_lse = [0, math.log(1 + e), math.log(2 + e)] + [math.log(2 + 2 * e)] * 5
+    cfg, qi, ki, q, k, v, kv, qs = hand_inputs()
+    sel, _ = orc.index_topk(cfg, qi, ki, kv, qs)
+    out, lse = orc.sparse_attn(cfg, q, k, v, kv, qs, sel)
+    for t in range(8):
+        assert abs(out[t, 0, 0] - closed_out[t]) < 1e-12, (t, out[t, 0, 0])
+        assert abs(out[t, 0, 0] - g["out_head0_softmax"][t]) < 1e-9
+        assert abs(lse[t, 0] - closed_lse[t]) < 1e-12, (t, lse[t, 0])
+        assert abs(lse[t, 0] - g["lse_head0_softmax"][t]) < 1e-9
+        assert abs(out[t, 1, 0] - g["out_head1_uniform"][t]) < 1e-12, (t, out[t, 1, 0])
+        assert abs(out[t, 1, 0] - float(np.mean(g["attended_keys"][t]))) < 1e-12
+
+
+def pin_hand_example_variants(orc):
+    """K >= #blocks is dense causal (uniform head = t/2); decode and chunked calls
+    give the same rows; a negative-zero index query ties like +0."""
+    cfg4, qi, ki, q, k, v, kv, qs = hand_inputs(topk=4)
+    sel, _ = orc.index_topk(cfg4, qi, ki, kv, qs)
+    out, _ = orc.sparse_attn(cfg4, q, k, v, kv, qs, sel)
+    for t in range(8):
+        assert abs(out[t, 1, 0] - t / 2.0) < 1e-12
+    cfg, qi, ki, q, k, v, kv, qs = hand_inputs()
+    full_sel, _ = orc.index_topk(cfg, qi, ki, kv, qs)
+    full_out, full_lse = orc.sparse_attn(cfg, q, k, v, kv, qs, full_sel)
+    # decode of the last token
+    _, qi1, ki1, q1, k1, v1, kv1, qs1 = hand_inputs(q_start=7)
+    s1, _ = orc.index_topk(cfg, qi1, ki1, kv1, qs1)
+    assert s1[0].tolist() == full_sel[7].tolist()
+    o1, l1 = orc.sparse_attn(cfg, q1, k1, v1, kv1, qs1, s1)
+    assert np.array_equal(o1[0], full_out[7]) and np.array_equal(l1[0], full_lse[7])
+    # chunk [4, 8) against the full cache
+    _, qi4, ki4, q4, k4, v4, kv4, qs4 = hand_inputs(q_start=4)
+    s4, _ = orc.index_topk(cfg, qi4, ki4, kv4, qs4)
+    assert s4.tolist() == full_sel[4:].tolist()
+    # -0.0 as the index query of row 6 (bits 0x8000)
+    qi_neg = qi.copy()
+    qi_neg[0, 6, 0, 0] = 0x8000
+    sn, scn = orc.index_topk(cfg, qi_neg, ki, kv, qs)
+    assert sn[6, 0].tolist() == [0, 1]
+
+
+def pin_brute_force_selection(orc, cases=60, seed=1):
+    """Oracle selection equals exhaustive subset search on tiny random inputs."""
+    rng = np.random.default_rng(seed)
+    for case in range(cases):
+        L = int(rng.integers(1, 17))
+        S = int(rng.choice([1, 2, 4]))
+        K = int(rng.integers(1, 6))
+        G = int(rng.integers(1, 3))
+        dI = int(rng.integers(1, 3))
+        pr = tiny_problem(rng, L, G, 1, 1, dI, S, K, index_dtype=int(case % 2))
+        sel, sc = orc.index_topk(pr["cfg"], pr["qi_b"], pr["ki_b"], pr["kv_lens"],
+                                 pr["q_start"])
+        for t in range(L):
+            for g in range(G):
+                s_row = [sum(int(pr["qi"][0, t, g, c]) * int(pr["ki"][0, j, c])
+                             for c in range(dI)) for j in range(t + 1)]
+                want = brute_force_topk(s_row, t, S, K)
+                assert sel[t, g].tolist() == want, (case, t, g, sel[t, g].tolist(), want)
+                for kk, b in enumerate(want):
+                    if b >= 0:
+                        assert sc[t, g, kk] == max(s_row[b * S: min(b * S + S, t + 1)])
+
+
+def pin_token_level_and_single_block(orc, seed=2):
+    """S = 1 is token-level top-k (stable sort of scores); S >= L gives one block."""
+    rng = np.random.default_rng(seed)
+    L, K = 12, 5
+    pr = tiny_problem(rng, L, 1, 1, 1, 2, 1, K)
+    sel, _ = orc.index_topk(pr["cfg"], pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
+    for t in range(L):
+        s = (pr["ki"][0, :t + 1] @ pr["qi"][0, t, 0]).astype(np.int64)
+        order = sorted(range(t + 1), key=lambda j: (-s[j], j))[:K]
+        assert sel[t, 0].tolist() == order + [-1] * (K - len(order))
+    pr = tiny_problem(rng, L, 1, 1, 1, 2, 16, 3)
+    sel, _ = orc.index_topk(pr["cfg"], pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
+    assert (sel[:, 0, 0] == 0).all() and (sel[:, 0, 1:] == -1).all()
+
+
+def pin_selection_invariants(orc, seed=3):
+    """Positive integer scaling of q_I keeps sel; permuting keys inside a block that
+    lies wholly in the past keeps sel; bf16 and E4M3 storage select alike."""
+    rng = np.random.default_rng(seed)
+    L, S, K = 64, 8, 3
+    pr = tiny_problem(rng, L, 2, 1, 1, 4, S, K)
+    cfg = pr["cfg"]
+    sel, _ = orc.index_topk(cfg, pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
+    sel3, _ = orc.index_topk(cfg, bf16(3 * pr["qi"]), pr["ki_b"], pr["kv_lens"], pr["q_start"])
+    assert np.array_equal(sel, sel3)
+    ki_perm = pr["ki"].copy()
+    ki_perm[0, 8:16] = ki_perm[0, 8:16][rng.permutation(8)]
+    selp, _ = orc.index_topk(cfg, pr["qi_b"], bf16(ki_perm), pr["kv_lens"], pr["q_start"])
+    assert np.array_equal(sel[16:], selp[16:])
+    enc = np.vectorize(e4m3_int)
+    cfg8 = Config(**{**cfg.__dict__, "index_dtype": E4M3})
+    sel8, _ = orc.index_topk(cfg8, enc(pr["qi"]).astype(np.uint8),
+                             enc(pr["ki"]).astype(np.uint8), pr["kv_lens"], pr["q_start"])
+    assert np.array_equal(sel, sel8)
+
+
+def pin_sparse_vs_numpy(orc, cases=12, seed=4):
+    """Sparse attention equals an independent numpy masked-softmax attention over
+    the keys of the chosen blocks; with K >= #blocks it equals dense causal."""
+    rng = np.random.default_rng(seed)
+    for case in range(cases):
+        L = int(rng.integers(2, 40))
+        S = int(rng.choice([1, 2, 4, 8]))
+        G, R, d = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 9))
+        K = int(rng.integers(1, 5)) if case % 3 else (L + S - 1) // S
+        pr = tiny_problem(rng, L, G, R, d, 2, S, K)
+        cfg = pr["cfg"]
+        sel, _ = orc.index_topk(cfg, pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
+        out, lse = orc.sparse_attn(cfg, pr["q_b"], pr["k_b"], pr["v_b"], pr["kv_lens"],
+                                   pr["q_start"], sel)
+        dout, dlse = orc.dense_causal(cfg, pr["q_b"], pr["k_b"], pr["v_b"], pr["kv_lens"],
+                                      pr["q_start"])
+        q, k, v = as_f(pr["q_b"]), as_f(pr["k_b"]), as_f(pr["v_b"])
+        tau = 1.0 / math.sqrt(d)
+        for t in range(L):
+            for h in range(G * R):
+                g = h // R
+                blocks = set(int(b) for b in sel[t, g] if b >= 0)
+                allowed = np.array([(j <= t) and (j // S in blocks) for j in range(L)])
+                o_ref, l_ref = numpy_masked_attention(q[0, t, h], k[0, g], v[0, g], allowed, tau)
+                assert np.allclose(out[t, h], o_ref, rtol=0, atol=1e-12), (case, t, h)
+                assert abs(lse[t, h] - l_ref) < 1e-12
+                causal = np.arange(L) <= t
+                o_d, l_d = numpy_masked_attention(q[0, t, h], k[0, g], v[0, g], causal, tau)
+                assert np.allclose(dout[t, h], o_d, rtol=0, atol=1e-12)
+                assert abs(dlse[t, h] - l_d) < 1e-12
+                if K * S >= L:
+                    assert np.allclose(out[t, h], dout[t, h], rtol=0, atol=1e-12)
+
+
+def pin_attention_invariants(orc, seed=5):
+    """Constant V gives that constant; q = 0 gives the mean of V over the chosen
+    keys; splitting the chosen blocks in two and merging by log-sum-exp gives the
+    full result; decode equals the last prefill row."""
+    rng = np.random.default_rng(seed)
+    L, G, R, d, S, K = 48, 2, 2, 8, 4, 4
+    pr = tiny_problem(rng, L, G, R, d, 3, S, K)
+    cfg = pr["cfg"]
+    sel, _ = orc.index_topk(cfg, pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
+    vc = np.full_like(pr["v_b"], bf16(np.float32(1.75)))
+    out, _ = orc.sparse_attn(cfg, pr["q_b"], pr["k_b"], vc, pr["kv_lens"], pr["q_start"], sel)
+    assert np.allclose(out, 1.75, rtol=0, atol=1e-12)
+    q0 = np.zeros_like(pr["q_b"])
+    out0, _ = orc.sparse_attn(cfg, q0, pr["k_b"], pr["v_b"], pr["kv_lens"], pr["q_start"], sel)
+    v = as_f(pr["v_b"])
+    for t in range(L):
+        for h in range(G * R):
+            g = h // R
+            keys = [j for j in range(t + 1) if j // S in set(sel[t, g].tolist())]
+            assert np.allclose(out0[t, h], v[0, g, keys].mean(axis=0), rtol=0, atol=1e-12)
+    out, lse = orc.sparse_attn(cfg, pr["q_b"], pr["k_b"], pr["v_b"], pr["kv_lens"],
+                               pr["q_start"], sel)
+    half = K // 2
+    sa = sel.copy()
+    sa[:, :, half:] = -1
+    sb = sel.copy()
+    sb[:, :, :half] = -1
+    oa, la = orc.sparse_attn(cfg, pr["q_b"], pr["k_b"], pr["v_b"], pr["kv_lens"], pr["q_start"], sa)
+    ob, lb = orc.sparse_attn(cfg, pr["q_b"], pr["k_b"], pr["v_b"], pr["kv_lens"], pr["q_start"], sb)
+    for t in range(L):
+        for h in range(G * R):
+            parts = [(la[t, h], oa[t, h]), (lb[t, h], ob[t, h])]
+            parts = [pp for pp in parts if np.isfinite(pp[0])]
+            m = max(pp[0] for pp in parts)
+            ws = [math.exp(pp[0] - m) for pp in parts]
+            merged = sum(w * pp[1] for w, pp in zip(ws, parts)) / sum(ws)
+            assert np.allclose(merged, out[t, h], rtol=0, atol=1e-12), (t, h)
+            assert abs(m + math.log(sum(ws)) - lse[t, h]) < 1e-12
+    # decode: one query at position L-1 against the same caches
+    qd = pr["q_b"][:, L - 1:L]
+    qid = pr["qi_b"][:, L - 1:L]
+    qs = np.array([L - 1], np.int32)
+    sd, _ = orc.index_topk(cfg, qid, pr["ki_b"], pr["kv_lens"], qs)
+    assert np.array_equal(sd[0], sel[L - 1])
+    od, ld = orc.sparse_attn(cfg, qd, pr["k_b"], pr["v_b"], pr["kv_lens"], qs, sd)
+    assert np.array_equal(od[0], out[L - 1]) and np.array_equal(ld[0], lse[L - 1])
+
+
+def pin_mixed_lengths_and_stride(orc, seed=6):
+    """Rows of a batch with per-sequence lengths inside a larger cache stride equal the
+    same rows computed alone with a tight cache (keys past kv_len are never read)."""
+    rng = np.random.default_rng(seed)
+    G, R, d, dI, S, K = 2, 2, 4, 2, 4, 3
+    lens = [37, 20, 64]
+    Nmax = 64
+    pr = tiny_problem(rng, Nmax, G, R, d, dI, S, K, B=3, T=1, kv_lens=lens)
+    cfg = pr["cfg"]
+    # garbage beyond each kv_len must not matter
+    ki_b, k_b, v_b = pr["ki_b"].copy(), pr["k_b"].copy(), pr["v_b"].copy()
+    for b, n in enumerate(lens):
+        ki_b[b, n:] = bf16(np.float32(4.0))
+        k_b[b, :, n:] = bf16(np.float32(9.0))
+        v_b[b, :, n:] = bf16(np.float32(-9.0))
+    sel, _ = orc.index_topk(cfg, pr["qi_b"], ki_b, pr["kv_lens"], pr["q_start"])
+    out, lse = orc.sparse_attn(cfg, pr["q_b"], k_b, v_b, pr["kv_lens"], pr["q_start"], sel)
+    for b, n in enumerate(lens):
+        s1, _ = orc.index_topk(cfg, pr["qi_b"][b:b + 1], pr["ki_b"][b:b + 1, :n],
+                               np.array([n], np.int32), np.array([n - 1], np.int32))
+        assert np.array_equal(s1[0], sel[b])
+        o1, l1 = orc.sparse_attn(cfg, pr["q_b"][b:b + 1], pr["k_b"][b:b + 1, :, :n],
+                                 pr["v_b"][b:b + 1, :, :n], np.array([n], np.int32),
+                                 np.array([n - 1], np.int32), s1)
+        assert np.allclose(o1[0], out[b], rtol=0, atol=1e-12)
+
+
+ALL_PINS = [pin_decoders, pin_hand_example_selection, pin_hand_example_attention,
+            pin_hand_example_variants, pin_brute_force_selection,
+            pin_token_level_and_single_block, pin_selection_invariants, pin_sparse_vs_numpy,
+            pin_attention_invariants, pin_mixed_lengths_and_stride]
+
+
+def run_all(orc):
+    """Runs every pin; returns {pin name: error text} for the pins that failed."""
+    failures = {}
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as exc:  # a mutant may also crash or reject its inputs
+            failures[pin.__name__] = "%s: %s" % (type(exc).__name__, exc)
+    return failures
