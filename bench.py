@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""MSA hot-path benchmark on one MI355X.
+
+A step is one decode pass of the whole hot path on the batch-16, 131072-token
+workload: msa_index_topk (index scores of the new token against every cached
+index key, causal block max-pool, top-16) followed by msa_sparse_attn_decode
+(attention of all 32 query heads over their group's 16 kept blocks). Eight
+query sets are rotated so that the kept blocks change from step to step.
+
+The headline value is algorithmic HBM bytes per step / time (GB/s): every
+index key once, the kept K/V blocks once, plus the queries, outputs and
+selections. The prefill leg (131072-token prefill, 32 heads / 4 groups) is
+reported alongside in TFLOP/s against the bf16 MFMA peak. The CPU oracle is
+timed on a bounded sample of the same decode batch.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0
+METRIC = "MSA decode HBM GB/s (% peak) @128k/1M; prefill TFLOP/s (% MFMA peak)"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def pinned(torch):
+    def alloc(shape, np_dtype):
+        import numpy as np
+        tdt = {np.uint16: torch.int16, np.uint8: torch.uint8}[np.dtype(np_dtype).type]
+        return torch.empty(shape, dtype=tdt, pin_memory=True)
+    return alloc
+
+
+def to_dev(torch, t, bf16=True):
+    d = t.to("cuda", non_blocking=True)
+    return d.view(torch.bfloat16) if (bf16 and d.dtype == torch.int16) else d
+
+
+def np_view(t):
+    import numpy as np
+    a = t.numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one decode step (every index key once, kept blocks once)."""
+    k_idx = w.B * w.Nmax * 128 * (1 if w.index_fp8 else 2)
+    kept = 0
+    for n in w.kv_lens:  # workload lengths are whole blocks, so each kept block is 128 keys
+        kept += w.G * min(w.topk, (n - 1) // 128 + 1) * 128 * 128 * 2 * 2
+    small = w.B * (w.H * 128 * 2 * 2 + w.G * 128 * (1 if w.index_fp8 else 2) + w.G * w.topk * 4)
+    return k_idx + kept + small, k_idx
+
+
+def run_decode(torch, msa, w, steps, warmup, nsets=8):
+    import numpy as np
+    from msa_synth import workloads as wl
+    t0 = time.time()
+    alloc = pinned(torch)
+    kh, vh, kih = wl.gen_caches(w, alloc=alloc)
+    sets = [wl.gen_queries(w, set_id=s, alloc=alloc) for s in range(nsets)]
+    log("decode inputs generated in %.1fs" % (time.time() - t0))
+    k, v = to_dev(torch, kh), to_dev(torch, vh)
+    ki = to_dev(torch, kih, bf16=not w.index_fp8)
+    qs = [(to_dev(torch, q), to_dev(torch, qi, bf16=not w.index_fp8)) for q, qi in sets]
+    kv = torch.tensor(w.kv_lens, dtype=torch.int32, device="cuda")
+    cfg = msa.Config(num_kv_groups=w.G, heads_per_group=w.R, topk=w.topk,
+                     index_dtype=msa.FP8_E4M3 if w.index_fp8 else msa.BF16)
+    ws_i = torch.empty(max(msa.workspace_size(cfg, w.B, 1, w.Nmax, msa.WS_INDEX_TOPK), 256),
+                       dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(max(msa.workspace_size(cfg, w.B, 1, w.Nmax, msa.WS_SPARSE_DECODE), 256),
+                       dtype=torch.uint8, device="cuda")
+    sel = torch.empty((w.B, 1, w.G, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, 1, w.H, 128), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(s, ev=None):
+        q, qi = qs[s % nsets]
+        if ev is not None:
+            ev[0].record()
+        msa.index_topk(cfg, qi, ki, kv, None, sel=sel, workspace=ws_i)
+        if ev is not None:
+            ev[1].record()
+        msa.sparse_attn_decode(cfg, q, k, v, kv, sel, out=out, workspace=ws_d)
+        if ev is not None:
+            ev[2].record()
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(steps):
+        step(warmup + s, evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(end)
+    idx_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    att_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    host = dict(k=np_view(kh), v=np_view(vh), ki=np_view(kih), q=np_view(sets[0][0]),
+                qi=np_view(sets[0][1]))
+    return dict(ms_per_step=ms_total / steps, wall_s=wall, idx_ms=idx_ms, att_ms=att_ms,
+                host=host, sel0=None)
+
+
+def cpu_baseline_decode(w, host, budget_rows=None):
+    """The oracle (as written, untuned) on the first query set of the decode batch."""
+    import numpy as np
+    import oracle
+    orc = oracle.default()
+    ocfg = oracle.Config(groups=w.G, heads_per_group=w.R, topk=w.topk,
+                         index_dtype=oracle.E4M3 if w.index_fp8 else oracle.BF16)
+    rows = w.B if budget_rows is None else min(budget_rows, w.B)
+    threads = max(1, min(os.cpu_count() or 1, 16, rows))
+    kv = np.array(w.kv_lens[:rows], np.int32)
+    qs = kv - 1
+    sl = slice(0, rows)
+    t0 = time.perf_counter()
+    sel, _ = orc.index_topk(ocfg, host["qi"][sl], host["ki"][sl], kv, qs, threads=threads)
+    orc.sparse_attn(ocfg, host["q"][sl], host["k"][sl], host["v"][sl], kv, qs, sel,
+                    threads=threads)
+    dt = time.perf_counter() - t0
+    sub = w.__class__(**{**w.__dict__, "B": rows, "kv_lens": list(w.kv_lens[:rows])})
+    nbytes, _ = decode_bytes(sub)
+    return dict(value=round(nbytes / dt / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                sample="%d of %d decode rows (all 4 groups, 32 heads, %d-token contexts): "
+                       "index top-k + sparse attention, %.2f s wall" %
+                       (rows, w.B, w.Nmax, dt))
+
+
+def run_prefill(torch, msa, w, steps=2, warmup=1):
+    import numpy as np
+    from msa_synth import workloads as wl
+    t0 = time.time()
+    alloc = pinned(torch)
+    kh, vh, kih = wl.gen_caches(w, alloc=alloc)
+    qh, qih = wl.gen_queries(w, alloc=alloc)
+    log("prefill inputs generated in %.1fs" % (time.time() - t0))
+    k, v, ki = to_dev(torch, kh), to_dev(torch, vh), to_dev(torch, kih, bf16=not w.index_fp8)
+    q, qi = to_dev(torch, qh), to_dev(torch, qih, bf16=not w.index_fp8)
+    del kh, vh, kih, qh, qih
+    kv = torch.tensor(w.kv_lens, dtype=torch.int32, device="cuda")
+    qs = torch.tensor(w.q_start, dtype=torch.int32, device="cuda")
+    cfg = msa.Config(num_kv_groups=w.G, heads_per_group=w.R, topk=w.topk,
+                     index_dtype=msa.FP8_E4M3 if w.index_fp8 else msa.BF16)
+    ws_i = torch.empty(msa.workspace_size(cfg, w.B, w.T, w.Nmax, msa.WS_INDEX_TOPK),
+                       dtype=torch.uint8, device="cuda")
+    sel = torch.empty((w.B, w.T, w.G, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.T, w.H, 128), dtype=torch.bfloat16, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    idx_ms, att_ms = [], []
+    for s in range(warmup + steps):
+        ev[0].record()
+        msa.index_topk(cfg, qi, ki, kv, qs, sel=sel, workspace=ws_i)
+        ev[1].record()
+        msa.sparse_attn_prefill(cfg, q, k, v, kv, sel, q_start=qs, out=out)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if s >= warmup:
+            idx_ms.append(ev[0].elapsed_time(ev[1]))
+            att_ms.append(ev[1].elapsed_time(ev[2]))
+    # Algorithmic flops: index = 2*dI*G per (row, key <= p); sparse = 4*d per
+    # (row, head, attended key), counted exactly from the selection.
+    L = w.T
+    f_idx = 2.0 * 128 * w.G * L * (L + 1) / 2
+    pos = torch.arange(L, device="cuda", dtype=torch.int64).view(1, L, 1, 1) + w.q_start[0]
+    s64 = sel.to(torch.int64)
+    valid = (s64 >= 0) & (s64 * 128 <= pos)
+    keys = torch.clamp(pos - s64 * 128 + 1, max=128) * valid
+    n_keys = float(keys.sum().item())
+    f_att = 4.0 * 128 * w.R * n_keys
+    ti, ta = min(idx_ms), min(att_ms)
+    res = dict(workload=w.name, index_ms=round(ti, 3), sparse_ms=round(ta, 3),
+               index_tflops=round(f_idx / ti / 1e9, 2), sparse_tflops=round(f_att / ta / 1e9, 2),
+               index_flops=f_idx, sparse_flops=f_att,
+               index_frac_bf16_peak=round(f_idx / ti / 1e9 / BF16_PEAK_TFLOPS, 4),
+               sparse_frac_bf16_peak=round(f_att / ta / 1e9 / BF16_PEAK_TFLOPS, 4),
+               total_tflops=round((f_idx + f_att) / (ti + ta) / 1e9, 2))
+    del q, qi, k, v, ki, sel, out, ws_i
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this MSA build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_30_amd as msa
+    from msa_synth import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    msa.load()
+
+    w = wl.workload(2)
+    res = run_decode(torch, msa, w, args.steps, args.warmup)
+    nbytes, kidx_bytes = decode_bytes(w)
+    value = nbytes / (res["ms_per_step"] * 1e-3) / 1e9
+    # Dominant kernel: the index scan (streams every index key once).
+    idx_bytes = kidx_bytes + w.B * w.G * 128 * 2 + w.B * w.G * w.topk * 4
+    achieved = idx_bytes / (res["idx_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "context": w.Nmax, "kv_groups": w.G,
+                   "heads_per_group": w.R, "head_dim": 128, "index_dim": 128, "block": 128,
+                   "topk": w.topk, "index_dtype": "bf16", "parallelism": "none (1 GPU)"},
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": nbytes,
+        "calls_ms": {"msa_index_topk": round(res["idx_ms"], 5),
+                     "msa_sparse_attn_decode": round(res["att_ms"], 5)},
+        "roofline": {"bound": "hbm", "kernel": "msa_index_topk (decode index scan + top-k)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(w, res["host"])
+    res.pop("host")
+    if not args.no_prefill:
+        line["prefill"] = run_prefill(torch, msa, wl.workload(3))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

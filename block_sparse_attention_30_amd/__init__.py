@@ -1,0 +1,255 @@
+"""Python binding of libmsa (MiniMax Sparse Attention on gfx950).
+
+Argument marshalling only: every step of the method runs in the HIP kernels
+of libmsa.so, called through its C ABI (include/msa.h) with ctypes. PyTorch
+supplies device memory and the current HIP stream. There is no CPU fallback:
+if libmsa.so is missing or a call fails, an exception is raised.
+
+Names follow the pages' sparse_attention_config (sparse_index_dim,
+sparse_num_index_heads, sparse_topk_blocks, sparse_block_size).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = ["Config", "MsaError", "index_topk", "sparse_attn_prefill", "sparse_attn_decode",
+           "workspace_size", "library_path", "load", "BF16", "FP8_E4M3",
+           "WS_INDEX_TOPK", "WS_SPARSE_PREFILL", "WS_SPARSE_DECODE"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmsa.so")
+
+BF16, FP8_E4M3 = 0, 1
+WS_INDEX_TOPK, WS_SPARSE_PREFILL, WS_SPARSE_DECODE = 0, 1, 2
+_STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARG", 2: "MSA_ERR_UNSUPPORTED",
+           3: "MSA_ERR_WORKSPACE", 4: "MSA_ERR_HIP"}
+
+
+class MsaError(RuntimeError):
+    """A libmsa call returned a non-zero msa_status."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__("%s: %s" % (_STATUS.get(status, status), detail))
+
+
+class _CConfig(ctypes.Structure):
+    _fields_ = [("num_kv_groups", ctypes.c_int32), ("heads_per_group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("index_dtype", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Config:
+    """One MSA layer's shapes (msa_config)."""
+    num_kv_groups: int = 4        # G = KV heads = sparse_num_index_heads
+    heads_per_group: int = 8      # R
+    head_dim: int = 128           # d
+    index_dim: int = 128          # sparse_index_dim
+    block_size: int = 128         # sparse_block_size
+    topk: int = 16                # sparse_topk_blocks
+    softmax_scale: float = 0.0    # 0: 1/sqrt(head_dim)
+    index_dtype: int = BF16
+
+    @property
+    def num_heads(self) -> int:
+        return self.num_kv_groups * self.heads_per_group
+
+    def _c(self) -> _CConfig:
+        return _CConfig(self.num_kv_groups, self.heads_per_group, self.head_dim, self.index_dim,
+                        self.block_size, self.topk, float(self.softmax_scale), self.index_dtype)
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Loads libmsa.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libmsa.so is not built; run block_sparse_attention_30_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(_CConfig)
+    lib.msa_index_topk.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_prefill.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, sz, vp]
+    lib.msa_sparse_attn_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in (lib.msa_index_topk, lib.msa_sparse_attn_prefill, lib.msa_sparse_attn_decode):
+        f.restype = ctypes.c_int
+    lib.msa_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
+    lib.msa_workspace_size.restype = sz
+    lib.msa_status_string.argtypes = [ctypes.c_int]
+    lib.msa_status_string.restype = ctypes.c_char_p
+    lib.msa_last_error.argtypes = []
+    lib.msa_last_error.restype = ctypes.c_char_p
+    lib.msa_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MsaError(status, load().msa_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtypes, ndim, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU (libmsa has no CPU path)" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions, has %d" % (name, ndim, t.dim()))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+_INDEX_DTYPES = {BF16: (torch.bfloat16,), FP8_E4M3: (torch.float8_e4m3fn, torch.uint8)}
+
+
+def workspace_size(cfg: Config, B: int, T: int, Nmax: int, which: int) -> int:
+    n = load().msa_workspace_size(ctypes.byref(cfg._c()), B, T, Nmax, which)
+    if n == ctypes.c_size_t(-1).value:
+        raise MsaError(1, load().msa_last_error().decode(errors="replace") or "invalid config")
+    return int(n)
+
+
+def _workspace(cfg, B, T, Nmax, which, device, workspace):
+    need = workspace_size(cfg, B, T, Nmax, which)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _lens(t, name, B, device):
+    _need(t, name, (torch.int32,), 1, device)
+    if t.shape[0] != B:
+        raise ValueError("%s must have B = %d entries" % (name, B))
+
+
+def index_topk(cfg: Config, q_idx, k_idx, kv_lens, q_start=None, sel=None, sel_scores=None,
+               want_scores: bool = False, workspace=None):
+    """Index branch: sel [B,T,G,K] int32 (and pooled scores [B,T,G,K] fp32).
+
+    q_idx [B,T,G,dI] and k_idx [B,Nmax,dI] are bf16 (or float8_e4m3fn / uint8
+    E4M3FN bits when cfg.index_dtype == FP8_E4M3); kv_lens [B] int32;
+    q_start [B] int32 or None (then q_start = kv_lens - T).
+    """
+    dev = q_idx.device
+    _need(q_idx, "q_idx", _INDEX_DTYPES[cfg.index_dtype], 4)
+    _need(k_idx, "k_idx", _INDEX_DTYPES[cfg.index_dtype], 3, dev)
+    B, T, G, dI = q_idx.shape
+    Nmax = k_idx.shape[1]
+    if G != cfg.num_kv_groups or dI != cfg.index_dim or k_idx.shape[0] != B or \
+            k_idx.shape[2] != cfg.index_dim:
+        raise ValueError("q_idx/k_idx shapes do not match the config")
+    _lens(kv_lens, "kv_lens", B, dev)
+    if q_start is not None:
+        _lens(q_start, "q_start", B, dev)
+    if sel is None:
+        sel = torch.empty((B, T, G, cfg.topk), dtype=torch.int32, device=dev)
+    _need(sel, "sel", (torch.int32,), 4, dev)
+    if tuple(sel.shape) != (B, T, G, cfg.topk):
+        raise ValueError("sel must be [B,T,G,K]")
+    if want_scores and sel_scores is None:
+        sel_scores = torch.empty((B, T, G, cfg.topk), dtype=torch.float32, device=dev)
+    if sel_scores is not None:
+        _need(sel_scores, "sel_scores", (torch.float32,), 4, dev)
+        if sel_scores.shape != sel.shape:
+            raise ValueError("sel_scores must be [B,T,G,K]")
+    ws, nws = _workspace(cfg, B, T, Nmax, WS_INDEX_TOPK, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(load().msa_index_topk(ctypes.byref(cfg._c()), B, T, Nmax, _ptr(q_idx),
+                                     _ptr(k_idx), _ptr(kv_lens), _ptr(q_start), _ptr(sel),
+                                     _ptr(sel_scores), _ptr(ws), nws, _stream(dev)))
+    return (sel, sel_scores) if (want_scores or sel_scores is not None) else sel
+
+
+def _sparse_checks(cfg, q, k_cache, v_cache, kv_lens, sel, T_expected=None):
+    dev = q.device
+    _need(q, "q", (torch.bfloat16,), 4)
+    _need(k_cache, "k_cache", (torch.bfloat16,), 4, dev)
+    _need(v_cache, "v_cache", (torch.bfloat16,), 4, dev)
+    B, T, H, d = q.shape
+    if T_expected is not None and T != T_expected:
+        raise ValueError("q must have T = %d" % T_expected)
+    if H != cfg.num_heads or d != cfg.head_dim:
+        raise ValueError("q must be [B,T,G*R,d]")
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or \
+            k_cache.shape[1] != cfg.num_kv_groups or k_cache.shape[3] != cfg.head_dim:
+        raise ValueError("k_cache / v_cache must both be [B,G,Nmax,d]")
+    _lens(kv_lens, "kv_lens", B, dev)
+    _need(sel, "sel", (torch.int32,), 4, dev)
+    if tuple(sel.shape) != (B, T, cfg.num_kv_groups, cfg.topk):
+        raise ValueError("sel must be [B,T,G,K]")
+    return dev, B, T, k_cache.shape[2]
+
+
+def _outputs(cfg, dev, B, T, out, lse, want_lse):
+    if out is None:
+        out = torch.empty((B, T, cfg.num_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", (torch.bfloat16,), 4, dev)
+    if tuple(out.shape) != (B, T, cfg.num_heads, cfg.head_dim):
+        raise ValueError("out must be [B,T,H,d]")
+    if want_lse and lse is None:
+        lse = torch.empty((B, T, cfg.num_heads), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), 3, dev)
+        if tuple(lse.shape) != (B, T, cfg.num_heads):
+            raise ValueError("lse must be [B,T,H]")
+    return out, lse
+
+
+def sparse_attn_prefill(cfg: Config, q, k_cache, v_cache, kv_lens, sel, q_start=None, out=None,
+                        lse=None, want_lse: bool = False, workspace=None):
+    """Sparse branch for T rows per sequence: out [B,T,H,d] bf16 (and lse [B,T,H])."""
+    dev, B, T, Nmax = _sparse_checks(cfg, q, k_cache, v_cache, kv_lens, sel)
+    if q_start is not None:
+        _lens(q_start, "q_start", B, dev)
+    out, lse = _outputs(cfg, dev, B, T, out, lse, want_lse)
+    ws, nws = _workspace(cfg, B, T, Nmax, WS_SPARSE_PREFILL, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(load().msa_sparse_attn_prefill(
+            ctypes.byref(cfg._c()), B, T, Nmax, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(kv_lens), _ptr(q_start), _ptr(sel), _ptr(out), _ptr(lse), _ptr(ws), nws,
+            _stream(dev)))
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def sparse_attn_decode(cfg: Config, q, k_cache, v_cache, kv_lens, sel, out=None, lse=None,
+                       want_lse: bool = False, workspace=None):
+    """Sparse branch for one new token per sequence (q [B,1,H,d], position kv_lens-1)."""
+    dev, B, T, Nmax = _sparse_checks(cfg, q, k_cache, v_cache, kv_lens, sel, T_expected=1)
+    out, lse = _outputs(cfg, dev, B, 1, out, lse, want_lse)
+    ws, nws = _workspace(cfg, B, 1, Nmax, WS_SPARSE_DECODE, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(load().msa_sparse_attn_decode(
+            ctypes.byref(cfg._c()), B, Nmax, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(kv_lens), _ptr(sel), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream(dev)))
+    return (out, lse) if (want_lse or lse is not None) else out

@@ -1,0 +1,172 @@
+// Host-only part of libmsa: argument validation, workspace layout, status
+// strings. Holds no HIP calls, so every error path can be exercised on a
+// machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "msa_internal.h"
+
+namespace msa {
+
+static thread_local char g_err[512] = "";
+
+msa_status fail(msa_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+msa_status check_config(const msa_config *c) {
+    if (!c) return fail(MSA_ERR_INVALID_ARG, "cfg is NULL");
+    if (c->num_kv_groups < 1) return fail(MSA_ERR_INVALID_ARG, "num_kv_groups must be >= 1");
+    if (c->heads_per_group < 1) return fail(MSA_ERR_INVALID_ARG, "heads_per_group must be >= 1");
+    if (c->head_dim < 1 || c->index_dim < 1 || c->block_size < 1 || c->topk < 1)
+        return fail(MSA_ERR_INVALID_ARG, "head_dim, index_dim, block_size and topk must be >= 1");
+    if (!(c->softmax_scale >= 0.0f) || isinf(c->softmax_scale))
+        return fail(MSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    if (c->index_dtype != MSA_BF16 && c->index_dtype != MSA_FP8_E4M3)
+        return fail(MSA_ERR_INVALID_ARG, "index_dtype %d is not a msa_dtype", c->index_dtype);
+    if (c->head_dim != kHeadDim)
+        return fail(MSA_ERR_UNSUPPORTED, "head_dim %d unsupported (need 128)", c->head_dim);
+    if (c->index_dim != kIndexDim)
+        return fail(MSA_ERR_UNSUPPORTED, "index_dim %d unsupported (need 128)", c->index_dim);
+    if (c->block_size != kBlock)
+        return fail(MSA_ERR_UNSUPPORTED, "block_size %d unsupported (need 128)", c->block_size);
+    if (c->topk > kMaxTopk)
+        return fail(MSA_ERR_UNSUPPORTED, "topk %d unsupported (need 1..32)", c->topk);
+    if (c->heads_per_group > kMaxHeadsPerGroup)
+        return fail(MSA_ERR_UNSUPPORTED, "heads_per_group %d unsupported (need 1..16)",
+                    c->heads_per_group);
+    if ((int64_t)c->num_kv_groups * c->heads_per_group > 4096)
+        return fail(MSA_ERR_UNSUPPORTED, "more than 4096 query heads");
+    return MSA_OK;
+}
+
+static msa_status check_dims(int32_t B, int32_t T, int32_t Nmax) {
+    if (B < 0 || T < 0) return fail(MSA_ERR_INVALID_ARG, "B and T must be >= 0");
+    if (B > 65535) return fail(MSA_ERR_UNSUPPORTED, "B = %d exceeds 65535", B);
+    if (B > 0 && T > 0 && Nmax < 1) return fail(MSA_ERR_INVALID_ARG, "Nmax must be >= 1");
+    if (Nmax < 0) return fail(MSA_ERR_INVALID_ARG, "Nmax must be >= 0");
+    return MSA_OK;
+}
+
+IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) {
+    IndexWs w{};
+    w.nb_max = ((int64_t)Nmax + kBlock - 1) / kBlock;
+    w.pooled_off = 0;
+    w.pooled_bytes = (size_t)B * (size_t)T * (size_t)cfg->num_kv_groups * (size_t)w.nb_max * 4;
+    w.total = round_up(w.pooled_bytes, kWsAlign);
+    return w;
+}
+
+SparseWs sparse_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, int32_t which) {
+    (void)Nmax;
+    SparseWs w{};
+    w.nsplit = (which == MSA_WS_SPARSE_DECODE) ? cfg->topk : 1;
+    if (w.nsplit > 1) {
+        size_t units = (size_t)B * T * cfg->num_kv_groups * w.nsplit * cfg->heads_per_group;
+        w.part_o_off = 0;
+        w.part_o_bytes = units * kHeadDim * 4;
+        w.part_ml_off = round_up(w.part_o_bytes, kWsAlign);
+        w.part_ml_bytes = units * 2 * 4;
+        w.total = round_up(w.part_ml_off + w.part_ml_bytes, kWsAlign);
+    }
+    return w;
+}
+
+static msa_status check_ws(const void *ws, size_t have, size_t need) {
+    if (need == 0) return MSA_OK;
+    if (!ws) return fail(MSA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+    if (!aligned(ws, kWsAlign)) return fail(MSA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (have < need)
+        return fail(MSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+    return MSA_OK;
+}
+
+msa_status check_index_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                            const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                            const int32_t *q_start, const int32_t *sel, const float *sel_scores,
+                            const void *workspace, size_t ws_bytes) {
+    msa_status s = check_config(cfg);
+    if (s != MSA_OK) return s;
+    if ((s = check_dims(B, T, Nmax)) != MSA_OK) return s;
+    if (B == 0 || T == 0) return MSA_OK;
+    if ((int64_t)B * T * cfg->num_kv_groups > ((int64_t)1 << 31) - 1)
+        return fail(MSA_ERR_UNSUPPORTED, "B*T*G exceeds 2^31-1 rows");
+    if (!q_idx || !k_idx || !kv_lens || !sel)
+        return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx, kv_lens and sel must not be NULL");
+    if (!aligned(q_idx, 16) || !aligned(k_idx, 16))
+        return fail(MSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+    if (!aligned(kv_lens, 4) || (q_start && !aligned(q_start, 4)) || !aligned(sel, 4) ||
+        (sel_scores && !aligned(sel_scores, 4)))
+        return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
+    return check_ws(workspace, ws_bytes, index_ws(cfg, B, T, Nmax).total);
+}
+
+msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                             const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *kv_lens, const int32_t *q_start, const int32_t *sel,
+                             const void *out, const float *lse, const void *workspace,
+                             size_t ws_bytes, int32_t which) {
+    msa_status s = check_config(cfg);
+    if (s != MSA_OK) return s;
+    if ((s = check_dims(B, T, Nmax)) != MSA_OK) return s;
+    if (B == 0 || T == 0) return MSA_OK;
+    SparseWs w = sparse_ws(cfg, B, T, Nmax, which);
+    if ((int64_t)B * T * cfg->num_kv_groups * w.nsplit > ((int64_t)1 << 31) - 1)
+        return fail(MSA_ERR_UNSUPPORTED, "too many (row, group, split) work items");
+    if (!q || !k_cache || !v_cache || !kv_lens || !sel || !out)
+        return fail(MSA_ERR_INVALID_ARG, "q, k_cache, v_cache, kv_lens, sel and out must not be NULL");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+        return fail(MSA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+    if (!aligned(kv_lens, 4) || (q_start && !aligned(q_start, 4)) || !aligned(sel, 4) ||
+        (lse && !aligned(lse, 4)))
+        return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
+    return check_ws(workspace, ws_bytes, w.total);
+}
+
+}  // namespace msa
+
+extern "C" {
+
+size_t msa_workspace_size(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                          int32_t which) {
+    if (msa::check_config(cfg) != MSA_OK || B < 0 || T < 0 || Nmax < 0) return (size_t)-1;
+    switch (which) {
+        case MSA_WS_INDEX_TOPK:
+            return msa::index_ws(cfg, B, T, Nmax).total;
+        case MSA_WS_SPARSE_PREFILL:
+        case MSA_WS_SPARSE_DECODE:
+            return msa::sparse_ws(cfg, B, which == MSA_WS_SPARSE_DECODE ? 1 : T, Nmax, which).total;
+        default:
+            msa::fail(MSA_ERR_INVALID_ARG, "unknown workspace kind %d", which);
+            return (size_t)-1;
+    }
+}
+
+const char *msa_status_string(msa_status s) {
+    switch (s) {
+        case MSA_OK: return "MSA_OK";
+        case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+        case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+        case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+        case MSA_ERR_HIP: return "MSA_ERR_HIP";
+    }
+    return "MSA_ERR_UNKNOWN";
+}
+
+const char *msa_last_error(void) { return msa::g_err; }
+
+int32_t msa_version(void) { return 100; }
+
+}  // extern "C"

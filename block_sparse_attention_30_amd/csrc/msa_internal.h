@@ -1,0 +1,49 @@
+// Private interface between the host-only validation unit (msa_host.cpp) and
+// the kernel unit (msa_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "msa.h"
+
+namespace msa {
+
+constexpr int kHeadDim = 128;
+constexpr int kIndexDim = 128;
+constexpr int kBlock = 128;
+constexpr int kMaxTopk = 32;
+constexpr int kMaxHeadsPerGroup = 16;
+constexpr int kScanMaxRows = 16;  // T*G at or below this uses the streaming index kernel
+constexpr size_t kWsAlign = 256;
+
+// Records a formatted message for msa_last_error() on this thread and returns s.
+msa_status fail(msa_status s, const char *fmt, ...);
+void clear_error();
+
+// Host-side argument checks; each returns MSA_OK or records why not.
+msa_status check_config(const msa_config *cfg);
+msa_status check_index_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                            const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                            const int32_t *q_start, const int32_t *sel, const float *sel_scores,
+                            const void *workspace, size_t ws_bytes);
+msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                             const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *kv_lens, const int32_t *q_start, const int32_t *sel,
+                             const void *out, const float *lse, const void *workspace,
+                             size_t ws_bytes, int32_t which);
+
+// Workspace layout of each call.
+struct IndexWs {
+    size_t pooled_off, pooled_bytes, total;
+    int64_t nb_max;  // ceil(Nmax / S)
+};
+IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
+
+struct SparseWs {
+    size_t part_o_off, part_o_bytes, part_ml_off, part_ml_bytes, total;
+    int32_t nsplit;  // workgroups per (row, group); 1 means no partials
+};
+SparseWs sparse_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, int32_t which);
+
+}  // namespace msa

@@ -1,0 +1,143 @@
+/*
+ * msa.h — C ABI of libmsa, a gfx950 (MI355X) implementation of MiniMax Sparse
+ * Attention (MSA).
+ *
+ * The method (web pages on MiniMax M3's sparse attention):
+ *   - cloud.tencent.com, "Something BIG Is Coming 百万token上下文提速近10倍，
+ *     MiniMax M3的稀疏注意力凭什么这么快", §二: an index branch in which one
+ *     lightweight index query per GQA group scores the KV blocks, max-pools
+ *     the scores over each block and keeps the top-k blocks; then a sparse
+ *     branch that runs full attention over only the kept blocks. §六: all
+ *     heads of one GQA group share the kept blocks.
+ *   - mlqm.cn, "如何用MiniMax-M3的稀疏注意力技术解决大模型效率瓶颈", section
+ *     核心原理: sparse_attention_config = index dim 128, 4 index heads,
+ *     top-k 16 blocks, block size 128.
+ *
+ * Definitions used by every call. Sequence b, query row i sits at position
+ * p = q_start[b] + i and may see keys j <= p (causal). For GQA group g:
+ *   score  s_j  = sum_c q_idx[b,i,g,c] * k_idx[b,j,c]            (j <= p)
+ *   pooled P_B  = max { s_j : B*S <= j <= min(B*S+S-1, p) }       (B*S <= p)
+ *   sel[b,i,g,:] = the min(K, p/S+1) blocks of largest P_B, ordered by
+ *                  (P_B descending, B ascending), then -1 padding.
+ * For each query head h of group g (h in [g*R, (g+1)*R)), with
+ *   J = { j <= p : j/S is in sel[b,i,g,:] } and tau = softmax scale:
+ *   out[b,i,h,:] = sum_{j in J} softmax_j(tau * q[b,i,h,:].K[b,g,j,:]) V[b,g,j,:]
+ *   lse[b,i,h]   = log sum_{j in J} exp(tau * q.K_j)   (natural log)
+ * A row whose J is empty gets out = 0 and lse = -inf.
+ *
+ * Layouts (row-major, contiguous, device memory; bf16 = bfloat16 bits):
+ *   q        [B, T, H, d]    bf16, H = G*R
+ *   q_idx    [B, T, G, dI]   bf16 or FP8 E4M3FN (OCP) per cfg->index_dtype
+ *   k_idx    [B, Nmax, dI]   same dtype as q_idx; one index key per token,
+ *                            shared by all groups
+ *   k_cache, v_cache [B, G, Nmax, d] bf16: each 128-token block of one group
+ *                            is one contiguous 32 KiB run
+ *   kv_lens  [B] int32       keys 0..kv_lens[b]-1 exist; kv_lens[b] <= Nmax
+ *   q_start  [B] int32 or NULL (NULL: q_start[b] = kv_lens[b] - T)
+ *   sel      [B, T, G, K] int32; sel_scores [B, T, G, K] fp32 (nullable)
+ *   out      [B, T, H, d] bf16; lse [B, T, H] fp32 (nullable)
+ *
+ * Ownership and streams: the caller owns every buffer. The library allocates
+ * nothing, keeps no state between calls and never synchronises: every call
+ * enqueues its kernels on `stream` and returns. Scratch memory comes from the
+ * caller's `workspace` (size from msa_workspace_size); it may be reused by
+ * later calls on the same stream.
+ *
+ * Errors: shapes, pointers, alignment (16 bytes for tensors, 4 for int32 and
+ * fp32 arrays, 256 for the workspace) and workspace size are checked on the
+ * host before any launch. Values that live on the device are not checked on
+ * the host: a row whose position is outside [0, min(kv_lens[b], Nmax)) is
+ * treated as empty (sel = -1, scores = -inf, out = 0, lse = -inf), and block
+ * ids in `sel` outside the row's causal range are ignored, so no kernel reads
+ * out of bounds. msa_last_error() describes the most recent failure on the
+ * calling thread.
+ *
+ * Support limits: d = dI = S = 128; 1 <= K <= 32; 1 <= R <= 16; G >= 1;
+ * B <= 65535. Results are deterministic (no floating-point atomics).
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MSA_OK = 0,
+    MSA_ERR_INVALID_ARG = 1, /* null pointer, bad shape, misalignment      */
+    MSA_ERR_UNSUPPORTED = 2, /* well-formed but outside the support limits */
+    MSA_ERR_WORKSPACE = 3,   /* workspace missing or too small             */
+    MSA_ERR_HIP = 4          /* a HIP launch or runtime call failed        */
+} msa_status;
+
+typedef enum { MSA_BF16 = 0, MSA_FP8_E4M3 = 1 } msa_dtype;
+
+/* Which call a workspace is sized for. */
+typedef enum {
+    MSA_WS_INDEX_TOPK = 0,
+    MSA_WS_SPARSE_PREFILL = 1,
+    MSA_WS_SPARSE_DECODE = 2
+} msa_ws_kind;
+
+/* Layer shapes; the names follow the pages' sparse_attention_config. */
+typedef struct {
+    int32_t num_kv_groups;   /* G: KV heads = GQA groups = index heads        */
+    int32_t heads_per_group; /* R: query heads per group                      */
+    int32_t head_dim;        /* d (must be 128)                               */
+    int32_t index_dim;       /* dI, sparse_index_dim (must be 128)            */
+    int32_t block_size;      /* S, sparse_block_size (must be 128)            */
+    int32_t topk;            /* K, sparse_topk_blocks (1..32)                 */
+    float softmax_scale;     /* tau; 0 selects 1/sqrt(d)                      */
+    int32_t index_dtype;     /* msa_dtype of q_idx and k_idx                  */
+} msa_config;
+
+/*
+ * Index branch (Tencent article §二): scores, causal block max-pool and top-k
+ * for B*T*G rows. Writes sel (and sel_scores if non-NULL: the pooled score of
+ * each kept block, -inf for padding). T small enough that T*G <= 16 uses a
+ * streaming kernel (decode); larger T uses an MFMA kernel (prefill). Chunked
+ * prefill is q_start[b] > 0 with the earlier keys already in k_idx.
+ */
+msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                          const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                          const int32_t *q_start, int32_t *sel, float *sel_scores,
+                          void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Sparse branch for T query rows per sequence (Tencent article §二 and §六):
+ * every head of group g attends over the blocks sel[b,i,g,:]. `sel` may come
+ * from msa_index_topk or from the caller (repeated ids count once).
+ */
+msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                                   const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *kv_lens, const int32_t *q_start,
+                                   const int32_t *sel, void *out, float *lse, void *workspace,
+                                   size_t ws_bytes, void *stream);
+
+/*
+ * Sparse branch for one new token per sequence (T = 1, position kv_lens[b]-1;
+ * the cache already holds that token): the kept blocks are split across
+ * workgroups and merged by log-sum-exp. Same layouts with T = 1.
+ */
+msa_status msa_sparse_attn_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                                  const void *k_cache, const void *v_cache,
+                                  const int32_t *kv_lens, const int32_t *sel, void *out,
+                                  float *lse, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes the named call needs for these shapes (0 if none); returns
+ * (size_t)-1 for an invalid configuration. For MSA_WS_SPARSE_DECODE, T is 1. */
+size_t msa_workspace_size(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                          int32_t which);
+
+const char *msa_status_string(msa_status s);
+const char *msa_last_error(void);
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

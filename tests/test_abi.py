@@ -1,0 +1,141 @@
+"""C ABI of libmsa on the CPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_30_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(msa.library_path()):
+        pytest.skip("libmsa.so not built")
+    return msa.load()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("msa_index_topk", "msa_sparse_attn_prefill", "msa_sparse_attn_decode",
+              "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", msa.library_path()], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(lib, n)  # resolvable through the dynamic loader too
+
+
+def test_status_strings_and_version(lib):
+    assert lib.msa_status_string(0) == b"MSA_OK"
+    assert lib.msa_status_string(3) == b"MSA_ERR_WORKSPACE"
+    assert lib.msa_version() >= 100
+
+
+def cfg(**kw):
+    return msa.Config(**kw)._c()
+
+
+FAKE = ctypes.c_void_p(0x100000)      # aligned, never dereferenced: calls fail before launch
+FAKE_MIS = ctypes.c_void_p(0x100002)  # misaligned
+
+
+def index_call(lib, c, B=2, T=1, N=1024, q_idx=FAKE, k_idx=FAKE, kv=FAKE, qs=None, sel=FAKE,
+               ws=FAKE, nws=0):
+    return lib.msa_index_topk(ctypes.byref(c), B, T, N, q_idx, k_idx, kv, qs, sel, None, ws,
+                              nws, None)
+
+
+def test_index_validation(lib):
+    c = cfg()
+    assert index_call(lib, c, B=0) == OK            # empty batch: nothing to do
+    assert index_call(lib, c, T=0) == OK
+    assert index_call(lib, c, q_idx=None) == INVALID
+    assert index_call(lib, c, sel=None) == INVALID
+    assert index_call(lib, c, k_idx=FAKE_MIS) == INVALID
+    assert index_call(lib, c, B=-1) == INVALID
+    assert index_call(lib, c, N=0) == INVALID
+    assert index_call(lib, c, B=70000) == UNSUPPORTED
+    assert index_call(lib, cfg(head_dim=64)) == UNSUPPORTED
+    assert index_call(lib, cfg(index_dim=64)) == UNSUPPORTED
+    assert index_call(lib, cfg(block_size=64)) == UNSUPPORTED
+    assert index_call(lib, cfg(topk=33)) == UNSUPPORTED
+    assert index_call(lib, cfg(topk=0)) == INVALID
+    assert index_call(lib, cfg(heads_per_group=17)) == UNSUPPORTED
+    assert index_call(lib, cfg(index_dtype=7)) == INVALID
+    assert index_call(lib, cfg(softmax_scale=-1.0)) == INVALID
+    assert lib.msa_index_topk(None, 1, 1, 128, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 0,
+                              None) == INVALID
+    # workspace: missing, misaligned, too small
+    need = lib.msa_workspace_size(ctypes.byref(c), 2, 1, 1024, 0)
+    assert need >= 2 * 4 * 8 * 4
+    assert index_call(lib, c, ws=None, nws=need) == WORKSPACE
+    assert index_call(lib, c, ws=ctypes.c_void_p(0x100010), nws=need) == WORKSPACE
+    assert index_call(lib, c, nws=need - 1) == WORKSPACE
+    assert b"workspace" in lib.msa_last_error()
+
+
+def test_sparse_validation(lib):
+    c = cfg()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, kv=FAKE, qs=None, sel=FAKE, out=FAKE, lse=None)
+
+    def prefill(**kw):
+        a = {**args, **kw}
+        return lib.msa_sparse_attn_prefill(ctypes.byref(kw.get("c", c)), 1, 64, 1024, a["q"],
+                                           a["k"], a["v"], a["kv"], a["qs"], a["sel"],
+                                           a["out"], a["lse"], None, 0, None)
+
+    def decode(nws=0, ws=FAKE, **kw):
+        a = {**args, **kw}
+        return lib.msa_sparse_attn_decode(ctypes.byref(c), 2, 1024, a["q"], a["k"], a["v"],
+                                          a["kv"], a["sel"], a["out"], a["lse"], ws, nws, None)
+
+    assert prefill(q=None) == INVALID
+    assert prefill(out=FAKE_MIS) == INVALID
+    assert prefill(lse=ctypes.c_void_p(0x100001)) == INVALID
+    assert prefill(c=cfg(heads_per_group=32)) == UNSUPPORTED
+    assert decode(sel=None) == INVALID
+    need = lib.msa_workspace_size(ctypes.byref(c), 2, 1, 1024, 2)
+    assert need > 0
+    assert decode(nws=need - 1) == WORKSPACE
+    assert decode(ws=None, nws=need) == WORKSPACE
+    assert lib.msa_workspace_size(ctypes.byref(c), 2, 1, 1024, 9) == ctypes.c_size_t(-1).value
+    assert lib.msa_workspace_size(None, 2, 1, 1024, 0) == ctypes.c_size_t(-1).value
+
+
+def test_workspace_sizes_follow_shapes(lib):
+    c = cfg()
+    a = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 0)
+    assert a >= 16 * 4 * 1024 * 4
+    assert lib.msa_workspace_size(ctypes.byref(c), 1, 64, 1024, 1) == 0   # prefill: none
+    d = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 2)
+    assert d >= 16 * 4 * 16 * 8 * 130 * 4
+    assert a % 256 == 0 and d % 256 == 0
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    c = msa.Config()
+    q = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        msa.index_topk(c, q, torch.zeros(1, 128, 128, dtype=torch.bfloat16),
+                       torch.ones(1, dtype=torch.int32))
