@@ -80,15 +80,25 @@ def run_decode(torch, msa, w, steps, warmup, nsets=8):
     kv = torch.tensor(w.kv_lens, dtype=torch.int32, device="cuda")
     cfg = msa.Config(num_kv_groups=w.G, heads_per_group=w.R, topk=w.topk,
                      index_dtype=msa.FP8_E4M3 if w.index_fp8 else msa.BF16)
-    ws_i = torch.empty(max(msa.workspace_size(cfg, w.B, 1, w.Nmax, msa.WS_INDEX_TOPK), 256),
-                       dtype=torch.uint8, device="cuda")
-    ws_d = torch.empty(max(msa.workspace_size(cfg, w.B, 1, w.Nmax, msa.WS_SPARSE_DECODE), 256),
-                       dtype=torch.uint8, device="cuda")
+    ws_i = msa.workspace(cfg, w.B, 1, w.Nmax, msa.WS_INDEX_TOPK)
+    ws_d = msa.workspace(cfg, w.B, 1, w.Nmax, msa.WS_SPARSE_DECODE)
     sel = torch.empty((w.B, 1, w.G, w.topk), dtype=torch.int32, device="cuda")
     out = torch.empty((w.B, 1, w.H, 128), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
 
+    ws_f = msa.workspace(cfg, w.B, 1, w.Nmax, msa.WS_DECODE)
+
     def step(s, ev=None):
+        """One decode step (msa_decode)."""
+        q, qi = qs[s % nsets]
+        if ev is not None:
+            ev[0].record()
+        msa.decode(cfg, q, qi, ki, k, v, kv, sel=sel, out=out, workspace=ws_f)
+        if ev is not None:
+            ev[1].record()
+
+    def step_two_calls(s, ev=None):
+        """The same step as msa_index_topk + msa_sparse_attn_decode."""
         q, qi = qs[s % nsets]
         if ev is not None:
             ev[0].record()
@@ -99,26 +109,29 @@ def run_decode(torch, msa, w, steps, warmup, nsets=8):
         if ev is not None:
             ev[2].record()
 
-    for s in range(warmup):
-        step(s)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    def timed(fn, nev):
+        for s in range(warmup):
+            fn(s)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for s in range(steps):
+            fn(warmup + s, evs[s])
+        end.record()
+        torch.cuda.synchronize()
+        per = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(nev - 1)]
+        return start.elapsed_time(end) / steps, per
+
+    ms_two, (idx_ms, att_ms) = timed(step_two_calls, 3)
     wall0 = time.perf_counter()
-    start.record()
-    for s in range(steps):
-        step(warmup + s, evs[s])
-    end.record()
-    torch.cuda.synchronize()
+    ms_total, (fused_ms,) = timed(step, 2)
     wall = time.perf_counter() - wall0
-    ms_total = start.elapsed_time(end)
-    idx_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    att_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     host = dict(k=np_view(kh), v=np_view(vh), ki=np_view(kih), q=np_view(sets[0][0]),
                 qi=np_view(sets[0][1]))
-    return dict(ms_per_step=ms_total / steps, wall_s=wall, idx_ms=idx_ms, att_ms=att_ms,
-                host=host, sel0=None)
+    return dict(ms_per_step=ms_total, wall_s=wall, fused_ms=fused_ms, two_call_ms=ms_two,
+                idx_ms=idx_ms, att_ms=att_ms, host=host)
 
 
 def cpu_baseline_decode(w, host, budget_rows=None):
@@ -161,8 +174,7 @@ def run_prefill(torch, msa, w, steps=2, warmup=1):
     qs = torch.tensor(w.q_start, dtype=torch.int32, device="cuda")
     cfg = msa.Config(num_kv_groups=w.G, heads_per_group=w.R, topk=w.topk,
                      index_dtype=msa.FP8_E4M3 if w.index_fp8 else msa.BF16)
-    ws_i = torch.empty(msa.workspace_size(cfg, w.B, w.T, w.Nmax, msa.WS_INDEX_TOPK),
-                       dtype=torch.uint8, device="cuda")
+    ws_i = msa.workspace(cfg, w.B, w.T, w.Nmax, msa.WS_INDEX_TOPK)
     sel = torch.empty((w.B, w.T, w.G, w.topk), dtype=torch.int32, device="cuda")
     out = torch.empty((w.B, w.T, w.H, 128), dtype=torch.bfloat16, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -206,6 +218,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the prefill leg (for profiling its kernels)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this MSA build has no multi-GPU path "
@@ -220,11 +234,15 @@ def main():
         sys.exit(1)
     msa.load()
 
+    if args.prefill_only:
+        print(json.dumps({"prefill": run_prefill(torch, msa, wl.workload(3), steps=args.steps,
+                                                 warmup=args.warmup)}), flush=True)
+        return
     w = wl.workload(2)
     res = run_decode(torch, msa, w, args.steps, args.warmup)
     nbytes, kidx_bytes = decode_bytes(w)
     value = nbytes / (res["ms_per_step"] * 1e-3) / 1e9
-    # Dominant kernel: the index scan (streams every index key once).
+    # Dominant kernel: the decode index scan (streams every index key once).
     idx_bytes = kidx_bytes + w.B * w.G * 128 * 2 + w.B * w.G * w.topk * 4
     achieved = idx_bytes / (res["idx_ms"] * 1e-3) / 1e9
     line = {
@@ -237,9 +255,11 @@ def main():
                    "topk": w.topk, "index_dtype": "bf16", "parallelism": "none (1 GPU)"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": nbytes,
-        "calls_ms": {"msa_index_topk": round(res["idx_ms"], 5),
+        "calls_ms": {"msa_decode": round(res["fused_ms"], 5),
+                     "two_call_step": round(res["two_call_ms"], 5),
+                     "msa_index_topk": round(res["idx_ms"], 5),
                      "msa_sparse_attn_decode": round(res["att_ms"], 5)},
-        "roofline": {"bound": "hbm", "kernel": "msa_index_topk (decode index scan + top-k)",
+        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel (msa_index_topk, decode)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
     }

@@ -17,14 +17,14 @@ from dataclasses import dataclass
 import torch
 
 __all__ = ["Config", "MsaError", "index_topk", "sparse_attn_prefill", "sparse_attn_decode",
-           "workspace_size", "library_path", "load", "BF16", "FP8_E4M3",
-           "WS_INDEX_TOPK", "WS_SPARSE_PREFILL", "WS_SPARSE_DECODE"]
+           "workspace_size", "workspace", "library_path", "load", "BF16", "FP8_E4M3",
+           "WS_INDEX_TOPK", "WS_SPARSE_PREFILL", "WS_SPARSE_DECODE", "WS_DECODE", "decode"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmsa.so")
 
 BF16, FP8_E4M3 = 0, 1
-WS_INDEX_TOPK, WS_SPARSE_PREFILL, WS_SPARSE_DECODE = 0, 1, 2
+WS_INDEX_TOPK, WS_SPARSE_PREFILL, WS_SPARSE_DECODE, WS_DECODE = 0, 1, 2, 3
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARG", 2: "MSA_ERR_UNSUPPORTED",
            3: "MSA_ERR_WORKSPACE", 4: "MSA_ERR_HIP"}
 
@@ -87,7 +87,9 @@ def load():
     lib.msa_sparse_attn_prefill.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                             vp, sz, vp]
     lib.msa_sparse_attn_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in (lib.msa_index_topk, lib.msa_sparse_attn_prefill, lib.msa_sparse_attn_decode):
+    lib.msa_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in (lib.msa_index_topk, lib.msa_sparse_attn_prefill, lib.msa_sparse_attn_decode,
+              lib.msa_decode):
         f.restype = ctypes.c_int
     lib.msa_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
     lib.msa_workspace_size.restype = sz
@@ -131,6 +133,13 @@ def _need(t, name, dtypes, ndim, device=None):
 _INDEX_DTYPES = {BF16: (torch.bfloat16,), FP8_E4M3: (torch.float8_e4m3fn, torch.uint8)}
 
 
+def workspace(cfg: Config, B: int, T: int, Nmax: int, which: int, device="cuda"):
+    """A zero-filled workspace for the named call; calls leave its counter block
+    zero, so it can be reused by later calls of any shape that fit in it."""
+    return torch.zeros(max(workspace_size(cfg, B, T, Nmax, which), 256), dtype=torch.uint8,
+                       device=device)
+
+
 def workspace_size(cfg: Config, B: int, T: int, Nmax: int, which: int) -> int:
     n = load().msa_workspace_size(ctypes.byref(cfg._c()), B, T, Nmax, which)
     if n == ctypes.c_size_t(-1).value:
@@ -143,7 +152,7 @@ def _workspace(cfg, B, T, Nmax, which, device, workspace):
     if workspace is None:
         if need == 0:
             return None, 0
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -253,3 +262,38 @@ def sparse_attn_decode(cfg: Config, q, k_cache, v_cache, kv_lens, sel, out=None,
             ctypes.byref(cfg._c()), B, Nmax, _ptr(q), _ptr(k_cache), _ptr(v_cache),
             _ptr(kv_lens), _ptr(sel), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream(dev)))
     return (out, lse) if (want_lse or lse is not None) else out
+
+
+def decode(cfg: Config, q, q_idx, k_idx, k_cache, v_cache, kv_lens, sel=None, sel_scores=None,
+           out=None, lse=None, want_scores: bool = False, want_lse: bool = False,
+           workspace=None):
+    """One decode step in a single launch: index top-k and sparse attention for
+    the token at position kv_lens - 1. Returns (sel, out) plus sel_scores / lse
+    when requested, as (sel, sel_scores, out, lse) in that case."""
+    dev, B, T, Nmax = _sparse_checks(cfg, q, k_cache, v_cache, kv_lens,
+                                     sel if sel is not None else torch.empty(
+                                         (q.shape[0], 1, cfg.num_kv_groups, cfg.topk),
+                                         dtype=torch.int32, device=q.device), T_expected=1)
+    _need(q_idx, "q_idx", _INDEX_DTYPES[cfg.index_dtype], 4, dev)
+    _need(k_idx, "k_idx", _INDEX_DTYPES[cfg.index_dtype], 3, dev)
+    if tuple(q_idx.shape) != (B, 1, cfg.num_kv_groups, cfg.index_dim) or \
+            tuple(k_idx.shape) != (B, Nmax, cfg.index_dim):
+        raise ValueError("q_idx must be [B,1,G,dI] and k_idx [B,Nmax,dI]")
+    if sel is None:
+        sel = torch.empty((B, 1, cfg.num_kv_groups, cfg.topk), dtype=torch.int32, device=dev)
+    if want_scores and sel_scores is None:
+        sel_scores = torch.empty(sel.shape, dtype=torch.float32, device=dev)
+    if sel_scores is not None:
+        _need(sel_scores, "sel_scores", (torch.float32,), 4, dev)
+        if sel_scores.shape != sel.shape:
+            raise ValueError("sel_scores must be [B,1,G,K]")
+    out, lse = _outputs(cfg, dev, B, 1, out, lse, want_lse)
+    ws, nws = _workspace(cfg, B, 1, Nmax, WS_DECODE, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(load().msa_decode(ctypes.byref(cfg._c()), B, Nmax, _ptr(q), _ptr(q_idx),
+                                 _ptr(k_idx), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens),
+                                 _ptr(sel), _ptr(sel_scores), _ptr(out), _ptr(lse), _ptr(ws),
+                                 nws, _stream(dev)))
+    if want_scores or want_lse or sel_scores is not None or lse is not None:
+        return sel, sel_scores, out, lse
+    return sel, out

@@ -69,18 +69,19 @@ IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) {
     return w;
 }
 
-SparseWs sparse_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, int32_t which) {
-    (void)Nmax;
-    SparseWs w{};
-    w.nsplit = (which == MSA_WS_SPARSE_DECODE) ? cfg->topk : 1;
-    if (w.nsplit > 1) {
-        size_t units = (size_t)B * T * cfg->num_kv_groups * w.nsplit * cfg->heads_per_group;
-        w.part_o_off = 0;
-        w.part_o_bytes = units * kHeadDim * 4;
-        w.part_ml_off = round_up(w.part_o_bytes, kWsAlign);
-        w.part_ml_bytes = units * 2 * 4;
-        w.total = round_up(w.part_ml_off + w.part_ml_bytes, kWsAlign);
-    }
+int32_t decode_splits(const msa_config *cfg) {
+    return (4 * cfg->topk + kDecodeChunksPerSplit - 1) / kDecodeChunksPerSplit;
+}
+
+DecodeWs decode_ws(const msa_config *cfg, int32_t B, int32_t Nmax, bool with_index) {
+    DecodeWs w{};
+    w.nb_max = ((int64_t)Nmax + kBlock - 1) / kBlock;
+    w.pooled_off = 0;
+    const size_t pooled = with_index ? index_ws(cfg, B, 1, Nmax).total : 0;
+    const size_t units = (size_t)B * cfg->num_kv_groups * decode_splits(cfg) * cfg->heads_per_group;
+    w.part_o_off = pooled;
+    w.part_ml_off = round_up(w.part_o_off + units * kHeadDim * 4, kWsAlign);
+    w.total = round_up(w.part_ml_off + units * 2 * 4, kWsAlign);
     return w;
 }
 
@@ -122,9 +123,8 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
     if (s != MSA_OK) return s;
     if ((s = check_dims(B, T, Nmax)) != MSA_OK) return s;
     if (B == 0 || T == 0) return MSA_OK;
-    SparseWs w = sparse_ws(cfg, B, T, Nmax, which);
-    if ((int64_t)B * T * cfg->num_kv_groups * w.nsplit > ((int64_t)1 << 31) - 1)
-        return fail(MSA_ERR_UNSUPPORTED, "too many (row, group, split) work items");
+    if ((int64_t)B * T * cfg->num_kv_groups * decode_splits(cfg) > ((int64_t)1 << 31) - 1)
+        return fail(MSA_ERR_UNSUPPORTED, "too many (row, group) work items");
     if (!q || !k_cache || !v_cache || !kv_lens || !sel || !out)
         return fail(MSA_ERR_INVALID_ARG, "q, k_cache, v_cache, kv_lens, sel and out must not be NULL");
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
@@ -132,7 +132,34 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
     if (!aligned(kv_lens, 4) || (q_start && !aligned(q_start, 4)) || !aligned(sel, 4) ||
         (lse && !aligned(lse, 4)))
         return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
-    return check_ws(workspace, ws_bytes, w.total);
+    if (which == MSA_WS_SPARSE_DECODE)
+        return check_ws(workspace, ws_bytes, decode_ws(cfg, B, Nmax, false).total);
+    (void)workspace;
+    (void)ws_bytes;
+    return MSA_OK;
+}
+
+msa_status check_decode_args(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                             const void *q_idx, const void *k_idx, const void *k_cache,
+                             const void *v_cache, const int32_t *kv_lens, const int32_t *sel,
+                             const float *sel_scores, const void *out, const float *lse,
+                             const void *workspace, size_t ws_bytes) {
+    msa_status s = check_config(cfg);
+    if (s != MSA_OK) return s;
+    if ((s = check_dims(B, 1, Nmax)) != MSA_OK) return s;
+    if (B == 0) return MSA_OK;
+    if ((int64_t)B * cfg->num_kv_groups > ((int64_t)1 << 31) - 1)
+        return fail(MSA_ERR_UNSUPPORTED, "too many (sequence, group) work items");
+    if (!q || !q_idx || !k_idx || !k_cache || !v_cache || !kv_lens || !sel || !out)
+        return fail(MSA_ERR_INVALID_ARG,
+                    "q, q_idx, k_idx, k_cache, v_cache, kv_lens, sel and out must not be NULL");
+    if (!aligned(q, 16) || !aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16) || !aligned(out, 16))
+        return fail(MSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (!aligned(kv_lens, 4) || !aligned(sel, 4) || (sel_scores && !aligned(sel_scores, 4)) ||
+        (lse && !aligned(lse, 4)))
+        return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
+    return check_ws(workspace, ws_bytes, decode_ws(cfg, B, Nmax, true).total);
 }
 
 }  // namespace msa
@@ -146,8 +173,11 @@ size_t msa_workspace_size(const msa_config *cfg, int32_t B, int32_t T, int32_t N
         case MSA_WS_INDEX_TOPK:
             return msa::index_ws(cfg, B, T, Nmax).total;
         case MSA_WS_SPARSE_PREFILL:
+            return 0;
         case MSA_WS_SPARSE_DECODE:
-            return msa::sparse_ws(cfg, B, which == MSA_WS_SPARSE_DECODE ? 1 : T, Nmax, which).total;
+            return msa::decode_ws(cfg, B, Nmax, false).total;
+        case MSA_WS_DECODE:
+            return msa::decode_ws(cfg, B, Nmax, true).total;
         default:
             msa::fail(MSA_ERR_INVALID_ARG, "unknown workspace kind %d", which);
             return (size_t)-1;

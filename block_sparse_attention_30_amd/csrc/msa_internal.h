@@ -17,6 +17,7 @@ constexpr int kMaxHeadsPerGroup = 16;
 constexpr int kScanMaxRows = 16;  // T*G at or below this uses the streaming index kernel
 constexpr size_t kWsAlign = 256;
 
+
 // Records a formatted message for msa_last_error() on this thread and returns s.
 msa_status fail(msa_status s, const char *fmt, ...);
 void clear_error();
@@ -33,17 +34,28 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
                              const void *out, const float *lse, const void *workspace,
                              size_t ws_bytes, int32_t which);
 
-// Workspace layout of each call.
+// Workspace layout: the index branch (and msa_decode) keeps the pooled block
+// scores of every row, [B*T*G][ceil(Nmax/S)] fp32. The sparse calls need none.
 struct IndexWs {
     size_t pooled_off, pooled_bytes, total;
     int64_t nb_max;  // ceil(Nmax / S)
 };
 IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
 
-struct SparseWs {
-    size_t part_o_off, part_o_bytes, part_ml_off, part_ml_bytes, total;
-    int32_t nsplit;  // workgroups per (row, group); 1 means no partials
+// Decode attention: split partials [B*G][nsplit][R] x (128 + 2) fp32, after
+// the pooled scores when the call also runs the index branch (msa_decode).
+constexpr int kDecodeChunksPerSplit = 8;
+int32_t decode_splits(const msa_config *cfg);
+struct DecodeWs {
+    size_t pooled_off, part_o_off, part_ml_off, total;
+    int64_t nb_max;
 };
-SparseWs sparse_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, int32_t which);
+DecodeWs decode_ws(const msa_config *cfg, int32_t B, int32_t Nmax, bool with_index);
+
+msa_status check_decode_args(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                             const void *q_idx, const void *k_idx, const void *k_cache,
+                             const void *v_cache, const int32_t *kv_lens, const int32_t *sel,
+                             const float *sel_scores, const void *out, const float *lse,
+                             const void *workspace, size_t ws_bytes);
 
 }  // namespace msa

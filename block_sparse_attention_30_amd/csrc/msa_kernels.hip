@@ -11,18 +11,25 @@
 // of the mlqm.cn guide "如何用MiniMax-M3的稀疏注意力技术解决大模型效率瓶颈", §核心原理.
 //
 // Kernels:
-//   idx_scan_kernel     decode index scores: streams k_idx once for all groups,
-//                       16x16x32 bf16 MFMA, causal block max in registers.
-//   idx_prefill_kernel  prefill index scores: 32x32x16 bf16 MFMA over a 256-row
-//                       tile with the k_idx block staged in LDS; block max-pool
-//                       in the epilogue.
-//   topk_kernel         one wavefront per row: bitonic sort of 64-bit keys
-//                       (score, inverted block id) across lanes plus ballot
-//                       compaction of candidates above the running threshold.
-//   sparse_attn_kernel  gathers the kept 128-token K/V blocks of one group,
-//                       serves all R heads of the group with 16x16x32 MFMA
-//                       (QK^T and PV) and an online fp32 softmax.
-//   combine_kernel      log-sum-exp merge of split partials (decode).
+//   idx_scan_kernel      decode index scores: streams k_idx once for all
+//                        groups through LDS, 16x16x32 bf16 MFMA, causal block
+//                        max in registers; writes pooled scores.
+//   topk_rows_kernel     one wavefront per row: bitonic sorts of 64-bit keys
+//                        (score, inverted block id) across lanes plus
+//                        compaction of candidates above a threshold.
+//   idx_prefill_kernel   prefill index scores: 32x32x16 bf16 MFMA over a
+//                        256-row tile with the k_idx block staged in LDS;
+//                        block max-pool in the epilogue.
+//   topk_kernel          (prefill) one workgroup per row.
+//   sparse_attn_kernel   (prefill) one workgroup per (row, group): gathers the
+//                        kept 128-token K/V blocks, serves all R heads of the
+//                        group with 16x16x32 MFMA (QK^T and PV) and an online
+//                        fp32 softmax.
+//   sparse_decode_kernel (decode) one 8-wave workgroup per (sequence, group,
+//                        split), one 32-token chunk per wave; optionally ranks
+//                        the row's blocks itself; waves merge in LDS into a
+//                        partial per split.
+//   combine_kernel       (decode) log-sum-exp merge of the split partials.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -37,10 +44,13 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short v4i16;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int S = msa::kBlock;
 constexpr int D = msa::kHeadDim;
 constexpr int DI = msa::kIndexDim;
+constexpr int KMAX = msa::kMaxTopk;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -65,19 +75,206 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ int clamp_kv(int kv, int Nmax) { return kv < Nmax ? kv : Nmax; }
 
+__device__ __forceinline__ bf16_t to_bf16(float v) {
+    const __bf16 h = (__bf16)v;
+    return __builtin_bit_cast(bf16_t, h);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k keys. A pooled score and its block id form one unique 64-bit key: the
+// fp32 score mapped to an order-preserving uint32 (negative zero taken as
+// zero) in the high half and 0xFFFFFFFF - block in the low half, so a larger
+// key is a better block and equal scores rank the lower block first. Key 0 is
+// "no block".
+__device__ __forceinline__ uint64_t score_key(float s, int blk) {
+    const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)blk);
+}
+
+__device__ __forceinline__ float key_score(uint64_t k) {
+    const uint32_t o = (uint32_t)(k >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ int key_block(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+    const int lo = __shfl((int)(uint32_t)v, src), hi = __shfl((int)(uint32_t)(v >> 32), src);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Value of lane (lane ^ J) for a wavefront-uniform J, without LDS traffic.
+// J = 1, 2: DPP quad permutation. J = 4, 8: DPP row shifts (row_shl:J gives
+// lane i the value of lane i+J, row_shr:J that of lane i-J, within a 16-lane
+// row), the upward one where bit J of the lane id is clear. J = 16, 32:
+// v_permlane16_swap / v_permlane32_swap of the value with itself; the first
+// result holds the partner's value in lanes whose bit J is set, the second in
+// lanes whose bit J is clear.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane32(uint32_t v, int lane) {
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+    } else if constexpr (J == 4 || J == 8) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x100 + J, 0xF, 0xF, true);
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x110 + J, 0xF, 0xF, true);
+        return (lane & J) ? dn : up;
+    } else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        static_assert(J == 32, "lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
+    const uint32_t lo = xor_lane32<J>((uint32_t)v, lane);
+    const uint32_t hi = xor_lane32<J>((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t x, int lane) {
+    const uint64_t y = xor_lane64<J>(x, lane);
+    const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
+    return keep_max ? (x > y ? x : y) : (x < y ? x : y);
+}
+
+// Bitonic sort of one key per lane across the 64-lane wavefront, descending
+// (lane 0 ends with the largest key).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
+    x = bitonic_step<2, 1>(x, lane);
+    x = bitonic_step<4, 2>(x, lane);
+    x = bitonic_step<4, 1>(x, lane);
+    x = bitonic_step<8, 4>(x, lane);
+    x = bitonic_step<8, 2>(x, lane);
+    x = bitonic_step<8, 1>(x, lane);
+    x = bitonic_step<16, 8>(x, lane);
+    x = bitonic_step<16, 4>(x, lane);
+    x = bitonic_step<16, 2>(x, lane);
+    x = bitonic_step<16, 1>(x, lane);
+    x = bitonic_step<32, 16>(x, lane);
+    x = bitonic_step<32, 8>(x, lane);
+    x = bitonic_step<32, 4>(x, lane);
+    x = bitonic_step<32, 2>(x, lane);
+    x = bitonic_step<32, 1>(x, lane);
+    x = bitonic_step<64, 32>(x, lane);
+    x = bitonic_step<64, 16>(x, lane);
+    x = bitonic_step<64, 8>(x, lane);
+    x = bitonic_step<64, 4>(x, lane);
+    x = bitonic_step<64, 2>(x, lane);
+    x = bitonic_step<64, 1>(x, lane);
+    return x;
+}
+
+// Top-K of one row by a single wavefront, K <= 32. `cand` holds the row's n
+// pooled scores; `buf` is 64 keys of this wave's LDS.
+//   Pass 1: every lane takes the best key of its strided share. The K best of
+//           those 64 lane maxima are a valid running top-K, and the K-th is a
+//           threshold below which no key can enter.
+//   Pass 2: keys above the threshold that are not their lane's maximum (those
+//           were ranked in pass 1) are appended to the LDS list; when the
+//           list is full, or at the end, the list and the current top-K are
+//           sorted together and the threshold rises.
+// On random scores pass 2 finds only a handful of keys: a row costs two
+// 64-key sorts and one read of its scores (two if n > 1024). Returns the K
+// best keys in lanes 0..K-1 (descending), 0 elsewhere.
+__device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int K, int lane,
+                                                  uint64_t *buf) {
+    constexpr int kBatch = 16;
+    const bool one_batch = n <= 64 * kBatch;  // then pass 2 reuses pass 1's registers
+    float v[kBatch];
+    auto load = [&](int base) {
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int i = base + c * 64 + lane;
+            v[c] = i < n ? cand[i] : 0.f;
+        }
+    };
+    uint64_t lmax = 0;
+    for (int base = 0; base < n; base += 64 * kBatch) {
+        load(base);
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int i = base + c * 64 + lane;
+            const uint64_t k = i < n ? score_key(v[c], i) : 0;
+            lmax = k > lmax ? k : lmax;
+        }
+    }
+    const uint64_t srt = wave_sort_desc(lmax, lane);
+    uint64_t top = lane < K ? srt : 0;
+    uint64_t thr = shfl_u64(srt, K - 1);
+    const int cap = 64 - K;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int cnt = 0;  // wavefront-uniform
+    auto merge = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the list writes have landed
+        __builtin_amdgcn_wave_barrier();
+        uint64_t x = lane < K ? top : ((lane - K) < cnt ? buf[lane - K] : 0);
+        x = wave_sort_desc(x, lane);
+        top = lane < K ? x : 0;
+        thr = shfl_u64(x, K - 1);
+        cnt = 0;
+        __builtin_amdgcn_wave_barrier();
+    };
+    for (int base = 0; base < n; base += 64 * kBatch) {
+        if (!one_batch) load(base);
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int i = base + c * 64 + lane;
+            const uint64_t kk = i < n ? score_key(v[c], i) : 0;
+            bool q = kk > thr && kk != lmax;
+            uint64_t qm = __ballot(q);
+            while (qm) {
+                if (cnt == cap) {
+                    merge();
+                    q = q && kk > thr;
+                    qm = __ballot(q);
+                    continue;
+                }
+                const int room = cap - cnt;
+                const int rank = __popcll(qm & below);
+                const bool take = q && rank < room;
+                if (take) buf[cnt + rank] = kk;
+                const int nq = __popcll(qm);
+                cnt += nq < room ? nq : room;
+                q = q && !take;
+                qm = __ballot(q);
+            }
+        }
+    }
+    if (cnt) merge();
+    return top;
+}
+
 // ---------------------------------------------------------------------------
 // Decode index scores (T*G <= 16 rows per sequence).
 //
-// MFMA D = A x B with A = index-query rows (16 rows: m = t*G + g, zero above
-// T*G) and B = k_idx^T for 16 tokens. Lane l loads 16 contiguous bytes of
-// token (l & 15) per k-chunk, so each wave reads 4 KiB of k_idx per tile.
-// Output lane l holds D[4*(l>>4) + r][l & 15]: rows 4*(l>>4)..+3 of one token.
-// A running max per row over the block's 8 tiles, then a 16-lane max,
-// gives the pooled score of the block.
+// Every index key of the sequence is streamed once and serves all T*G
+// index-query rows. Workgroup x of sequence y takes blocks_per_wg blocks;
+// each wave walks its blocks in half-block steps of 64 tokens (16 KiB): a step
+// is read with sixteen load instructions of one contiguous KiB each (four
+// token rows) and staged in the wave's own LDS region (rows padded to 272
+// bytes), while the loads of the next step are already in flight. The MFMA
+// D = A x B then takes A = index-query rows (16 rows, m = t*G + g, zero above
+// T*G) from registers and B = k_idx^T for 16 tokens from LDS; output lane l
+// holds D[4*(l>>4) + r][l & 15], i.e. rows 4*(l>>4)..+3 of one token. A
+// running per-row max over the block's tiles, then a 16-lane max, gives the
+// block's pooled score, written to pooled[b][m][block].
+constexpr int kScanRow = 272;
+constexpr int kScanStep = 64;  // tokens per staged step
+constexpr int kScanWaveLds = kScanStep * kScanRow;
+
 __global__ __launch_bounds__(256) void idx_scan_kernel(
     const bf16_t *__restrict__ q_idx, const bf16_t *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
     float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int blocks_per_wg) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * kScanWaveLds];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rows = T * G;
@@ -87,8 +284,10 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     if (p_hi < 0) return;
     const int nb = p_hi / S + 1;
     const int blk_begin = blockIdx.x * blocks_per_wg;
-    if (blk_begin >= nb) return;
     const int blk_end = min(blk_begin + blocks_per_wg, nb);
+    const int my_blocks = blk_begin + wave < blk_end ? (blk_end - blk_begin - wave + 3) / 4 : 0;
+    const int nsteps = my_blocks * (S / kScanStep);
+    if (nsteps == 0) return;
 
     const int col = lane & 15, kg = lane >> 4;
     bf16x8 a[4];
@@ -104,36 +303,89 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
         const int p = qs + m / G;
         prow[r] = (m < rows && p >= 0 && p < kv) ? p : -1;
     }
-    const bf16_t *kseq = k_idx + (size_t)b * Nmax * DI + kg * 8;
-    for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
-        const int tok0 = blk * S;
-        const bool need_mask = tok0 + S - 1 > qs;
-        float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    const unsigned char *kbytes =
+        reinterpret_cast<const unsigned char *>(k_idx + (size_t)b * Nmax * DI);
+    unsigned char *my = lds + wave * kScanWaveLds;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // Step s covers tokens [tok, tok + 64) of block blk_begin + wave + 4*(s/2).
+    auto step_tok = [&](int s) { return (blk_begin + wave + 4 * (s >> 1)) * S + (s & 1) * kScanStep; };
+    u32x4 v[16];
+    auto load_step = [&](int s) {
+        const int t0 = step_tok(s);
 #pragma unroll
-        for (int tile = 0; tile < S / 16; ++tile) {
-            const int tok = tok0 + tile * 16 + col;
-            const int tok_ld = tok < kv ? tok : kv - 1;  // stay inside the cache
-            const bf16_t *kp = kseq + (size_t)tok_ld * DI;
+        for (int i = 0; i < 16; ++i) {
+            const int tok = t0 + 4 * i + (lane >> 4);
+            v[i] = tok < kv ? ld16(kbytes + (size_t)tok * (DI * 2) + (lane & 15) * 16) : zero4;
+        }
+    };
+    load_step(0);
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int s = 0; s < nsteps; ++s) {
+        const int t0 = step_tok(s);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            *reinterpret_cast<u32x4 *>(my + (4 * i + (lane >> 4)) * kScanRow + (lane & 15) * 16) = v[i];
+        if (s + 1 < nsteps) load_step(s + 1);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS rows have landed
+        __builtin_amdgcn_wave_barrier();
+        const bool need_mask = t0 + kScanStep - 1 > qs;
+#pragma unroll
+        for (int tile = 0; tile < kScanStep / 16; ++tile) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) acc = mfma16(a[kc], ld_bf16x8(kp + kc * 32), acc);
+            for (int kc = 0; kc < 4; ++kc)
+                acc = mfma16(a[kc], as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                                        my + (tile * 16 + col) * kScanRow + kc * 64 + kg * 16)),
+                             acc);
+            const int tok = t0 + tile * 16 + col;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float s = (need_mask && tok > prow[r]) ? -INFINITY : acc[r];
-                mx[r] = fmaxf(mx[r], s);
+                const float sc = (need_mask && tok > prow[r]) ? -INFINITY : acc[r];
+                mx[r] = fmaxf(mx[r], sc);
             }
         }
+        __builtin_amdgcn_wave_barrier();
+        if (s & 1) {  // block complete
+            const int blk = t0 / S;
+            float m2[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < 4; ++r) {
+                m2[r] = mx[r];
 #pragma unroll
-            for (int off = 1; off < 16; off <<= 1) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], off));
+                for (int off = 1; off < 16; off <<= 1) m2[r] = fmaxf(m2[r], __shfl_xor(m2[r], off));
+                mx[r] = -INFINITY;
+            }
+            if (col == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (prow[r] >= blk * S)
+                        pooled[((size_t)b * rows + 4 * kg + r) * nb_max + blk] = m2[r] + 0.0f;
+            }
         }
-        if (col == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (prow[r] >= tok0)
-                    pooled[((size_t)b * rows + 4 * kg + r) * nb_max + blk] = mx[r] + 0.0f;
-        }
+    }
+}
+
+// Top-K of rows (b, t, g) from their pooled scores: one wavefront per row,
+// four rows per workgroup. Rows outside the cache get -1.
+__global__ __launch_bounds__(256) void topk_rows_kernel(
+    const float *__restrict__ pooled, int64_t nb_max, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, int B, int T, int G, int Nmax, int K,
+    int32_t *__restrict__ sel, float *__restrict__ sel_scores) {
+    __shared__ uint64_t s_buf[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+    const int rows = T * G;
+    if (row >= (int64_t)B * rows) return;
+    const int b = (int)(row / rows);
+    const int t = (int)(row % rows) / G;
+    const int kv = clamp_kv(kv_lens[b], Nmax);
+    const int qs = q_start ? q_start[b] : kv - T;
+    const int p = qs + t;
+    uint64_t top = 0;
+    if (p >= 0 && p < kv) top = wave_topk_row(pooled + row * nb_max, p / S + 1, K, lane, s_buf[wave]);
+    if (lane < K) {
+        sel[row * K + lane] = top ? key_block(top) : -1;
+        if (sel_scores) sel_scores[row * K + lane] = top ? key_score(top) : -INFINITY;
     }
 }
 
@@ -227,74 +479,31 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Top-k over the pooled scores of one row. Keys are unique 64-bit integers:
-// the fp32 score mapped to an order-preserving uint32 (negative zero taken as
-// zero) in the high half and 0xFFFFFFFF - block in the low half, so a larger
-// key is a better block and equal scores rank the lower block first. Key 0 is
-// "no block".
-__device__ __forceinline__ uint64_t score_key(float s, int blk) {
-    const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
-    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)blk);
-}
+constexpr int kTopkPerThread = 32;  // candidates per thread loaded together
 
-__device__ __forceinline__ float key_score(uint64_t k) {
-    const uint32_t o = (uint32_t)(k >> 32);
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
-__device__ __forceinline__ int key_block(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
-
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-    const int lo = __shfl((int)(uint32_t)v, src), hi = __shfl((int)(uint32_t)(v >> 32), src);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    const int lo = __shfl_xor((int)(uint32_t)v, m), hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-// Bitonic sort of one key per lane across the 64-lane wavefront, descending
-// (lane 0 ends with the largest key).
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t y = shfl_xor_u64(x, j);
-            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
-            x = keep_max ? (x > y ? x : y) : (x < y ? x : y);
-        }
-    }
-    return x;
-}
-
-// Position of the r-th (0-based) set bit of mask, or -1.
-__device__ __forceinline__ int nth_set_bit(uint64_t mask, int r) {
-    if (r < 0 || r >= __popcll(mask)) return -1;
-    int pos = 0;
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        const uint64_t low = (pos + s >= 64) ? ~0ull : ((1ull << (pos + s)) - 1ull);
-        if (__popcll(mask & low) <= r) pos += s;
-    }
-    return pos;
-}
-
-// One wavefront per row (b, t, g). Pass 1: every lane takes the best key of
-// its strided share; the K best of those 64 are a valid running top-K and the
-// K-th is a threshold below which no key can enter. Pass 2 walks the row in
-// rounds of 64 keys; keys above the threshold (rare after pass 1) are
-// compacted into lanes K..63 next to the current top-K and the 64 are sorted.
+// One workgroup (4 waves) per row (b, t, g); K <= 32.
+//   Pass 1: every thread takes the best key of its strided share of the
+//           row's n = p/S + 1 pooled scores; each wave sorts its 64 thread
+//           maxima and wave 0 merges the four top-K lists. These K keys are a
+//           valid running top-K and the K-th is a threshold below which no
+//           key can enter.
+//   Pass 2: keys above the threshold that are not their thread's maximum
+//           (those were ranked in pass 1) are appended to an LDS list; wave 0
+//           merges the list into the top-K, 64 - K keys at a time.
+// On random scores pass 2 finds only a few keys. If more than 256 keys pass
+// the threshold, wave 0 instead streams the whole row through the same
+// merge, starting from an empty list (correct for any input, just slower).
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ pooled, int64_t nb_max, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, int B, int T, int G, int Nmax, int K,
     int32_t *__restrict__ sel, float *__restrict__ sel_scores) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ uint64_t s_top[4][msa::kMaxTopk];
+    __shared__ uint64_t s_list[256];
+    __shared__ int s_cnt;
+    __shared__ uint64_t s_thr;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t row = blockIdx.x;
     const int rows = T * G;
-    if (row >= (int64_t)B * rows) return;
     const int b = (int)(row / rows);
     const int t = (int)(row % rows) / G;
     const int kv = clamp_kv(kv_lens[b], Nmax);
@@ -303,40 +512,104 @@ __global__ __launch_bounds__(256) void topk_kernel(
     int32_t *out = sel + row * K;
     float *outs = sel_scores ? sel_scores + row * K : nullptr;
     if (p < 0 || p >= kv) {
-        if (lane < K) {
-            out[lane] = -1;
-            if (outs) outs[lane] = -INFINITY;
+        if (tid < K) {
+            out[tid] = -1;
+            if (outs) outs[tid] = -INFINITY;
         }
         return;
     }
     const int n = p / S + 1;
     const float *cand = pooled + row * nb_max;
-    uint64_t lmax = 0;
-    for (int i = lane; i < n; i += 64) {
-        const uint64_t k = score_key(cand[i], i);
-        lmax = k > lmax ? k : lmax;
+
+    uint64_t tmax = 0;
+    for (int base = 0; base < n; base += 256 * kTopkPerThread) {
+        float v[kTopkPerThread];
+#pragma unroll
+        for (int c = 0; c < kTopkPerThread; ++c) {
+            const int i = base + c * 256 + tid;
+            v[c] = i < n ? cand[i] : 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < kTopkPerThread; ++c) {
+            const int i = base + c * 256 + tid;
+            const uint64_t k = i < n ? score_key(v[c], i) : 0;
+            tmax = k > tmax ? k : tmax;
+        }
     }
-    uint64_t srt = wave_sort_desc(lmax, lane);
-    uint64_t top = lane < K ? srt : 0;
-    uint64_t thr = shfl_u64(srt, K - 1);
-    const uint64_t below = (1ull << lane) - 1ull;
-    for (int base = 0; base < n; base += 64) {
-        const int i = base + lane;
-        const uint64_t kk = i < n ? score_key(cand[i], i) : 0;
-        bool q = kk > thr && kk != lmax;
-        uint64_t qm = __ballot(q);
-        while (qm) {
-            const int rank = __popcll(qm & below);
-            const bool take = q && rank < 64 - K;
-            const uint64_t tm = __ballot(take);
-            const int src = nth_set_bit(tm, lane - K);
-            const uint64_t got = shfl_u64(kk, src < 0 ? 0 : src);
-            uint64_t x = lane < K ? top : (src >= 0 ? got : 0);
+    const uint64_t srt = wave_sort_desc(tmax, lane);
+    if (lane < K) s_top[wave][lane] = srt;
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    if (wave == 0) {
+        uint64_t cur = lane < K ? s_top[0][lane] : 0;
+#pragma unroll 1
+        for (int w = 1; w < 4; ++w) {
+            uint64_t x = lane < K ? cur : (lane < 2 * K ? s_top[w][lane - K] : 0);
+            x = wave_sort_desc(x, lane);
+            cur = lane < K ? x : 0;
+        }
+        if (lane < K) s_top[0][lane] = cur;
+        if (lane == K - 1) s_thr = cur;
+    }
+    __syncthreads();
+    const uint64_t thr = s_thr;
+    for (int base = 0; base < n; base += 256 * kTopkPerThread) {
+        float v[kTopkPerThread];
+#pragma unroll
+        for (int c = 0; c < kTopkPerThread; ++c) {
+            const int i = base + c * 256 + tid;
+            v[c] = i < n ? cand[i] : 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < kTopkPerThread; ++c) {
+            const int i = base + c * 256 + tid;
+            const uint64_t k = i < n ? score_key(v[c], i) : 0;
+            if (k > thr && k != tmax) {
+                const int pos = atomicAdd(&s_cnt, 1);
+                if (pos < 256) s_list[pos] = k;
+            }
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const int cnt = s_cnt;
+    const int cap = 64 - K;
+    uint64_t top;
+    if (cnt <= 256) {
+        top = lane < K ? s_top[0][lane] : 0;
+#pragma unroll 1
+        for (int off = 0; off < cnt; off += cap) {
+            uint64_t x = lane < K ? top : (lane - K + off < cnt ? s_list[lane - K + off] : 0);
             x = wave_sort_desc(x, lane);
             top = lane < K ? x : 0;
-            thr = shfl_u64(x, K - 1);
-            q = q && !take && kk > thr;
-            qm = __ballot(q);
+        }
+    } else {
+        // Streaming fallback: rounds of 64 keys, merged whenever the round
+        // holds keys above the current K-th best.
+        top = 0;
+        uint64_t kth = 0;
+        const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll 1
+        for (int base = 0; base < n; base += 64) {
+            const int i = base + lane;
+            const uint64_t kk = i < n ? score_key(cand[i], i) : 0;
+            bool q = kk > kth;
+            uint64_t qm = __ballot(q);
+            while (qm) {
+                const int rank = __popcll(qm & below);
+                const bool take = q && rank < cap;
+                if (take) s_list[rank] = kk;
+                const int nt = __popcll(qm) < cap ? __popcll(qm) : cap;
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                __builtin_amdgcn_wave_barrier();
+                uint64_t x = lane < K ? top : (lane - K < nt ? s_list[lane - K] : 0);
+                x = wave_sort_desc(x, lane);
+                top = lane < K ? x : 0;
+                kth = shfl_u64(x, K - 1);
+                __builtin_amdgcn_wave_barrier();
+                q = q && !take && kk > kth;
+                qm = __ballot(q);
+            }
         }
     }
     if (lane < K) {
@@ -346,231 +619,386 @@ __global__ __launch_bounds__(256) void topk_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Block-sparse attention. One workgroup (4 waves) per (sequence, row, group,
-// split); split s covers kept slots [s*spl, s*spl + spl). Every kept block is
-// cut into four 32-token chunks and wave w takes chunk w of each block, so a
-// block is read once per workgroup and its K/V serve all R heads of the group.
+// Block-sparse attention (prefill and decode share the chunk step).
 //
-// Per chunk (16x16x32 bf16 MFMA):
+// A kept 128-token block is cut into four 32-token chunks. For one chunk a
+// wave computes, with 16x16x32 bf16 MFMA:
 //   S^T = K x q^T : A = 16 tokens of K (16 contiguous bytes per lane straight
-//                   from the cache), B = the group's query heads (zero above R).
-//                   Lane l holds heads (l & 15), tokens 4*(l>>4)+r.
+//                   from the cache), B = the group's query heads (zero above
+//                   R). Lane l holds heads (l & 15), tokens 4*(l>>4)+r.
 //   online softmax in the log2 domain, fp32;
 //   O  += P x V   : A = P, taken from the lane's own S^T values (two 16-token
-//                   tiles give 8 tokens), B = V read from an LDS copy of the
-//                   chunk stored transposed ([d][token]).
-// The four waves' (m, l, O) are merged in LDS; with one split the row's output
-// is written directly, otherwise an unnormalised partial and (m, l).
-constexpr int kVtStride = 36;  // bf16 per transposed V row: 32 tokens + pad (72 bytes)
+//                   tiles give 8 tokens), B = V: the chunk is staged row-major
+//                   in LDS and read back with the transposing LDS load
+//                   (ds_read_b64_tr_b16), which hands lane i of a 16-lane
+//                   group element (i % 4) of the 8-byte piece addressed by
+//                   lane 4j + i/4, for j = 0..3 - so lanes that address four
+//                   d-values of four tokens receive one d-value of each token.
+// Every K/V byte a workgroup reads serves all R heads of the group.
+constexpr int kVRow = 288;  // bytes per staged V token row: 256 + 32 pad
+constexpr int kVWave = 32 * kVRow;
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char *p) {
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// A wave's online-softmax state: running max and sum of head (lane & 15) and
+// O[head 4*(lane>>4) + r][d = dt*16 + (lane & 15)].
+struct WaveAttn {
+    float m, l;
+    f32x4 o[8];
+};
+
+__device__ __forceinline__ void wave_attn_init(WaveAttn &st) {
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// B operand of the S^T MFMA: the R query heads of one row and group.
+__device__ __forceinline__ void load_query(bf16x8 (&qf)[4], const bf16_t *q_heads, int R,
+                                           int lane) {
+    const int col = lane & 15, kg = lane >> 4;
+    const bf16_t *qp = q_heads + (size_t)(col < R ? col : 0) * D + kg * 8;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) qf[kc] = col < R ? ld_bf16x8(qp + kc * 32) : zero_bf16x8();
+}
+
+// One 32-token chunk [tok0, tok0 + 32) of a kept block; keys past p are masked.
+__device__ __forceinline__ void attend_chunk(WaveAttn &st, const bf16x8 (&qf)[4],
+                                             const bf16_t *kg_base, const bf16_t *vg_base,
+                                             int tok0, int p, float scale_log2,
+                                             unsigned char *vrows, int lane) {
+    const int col = lane & 15, kg = lane >> 4;
+    // Issue every global load of the chunk first: K in the MFMA A layout
+    // (token col of each 16-token tile), V as 16-byte row pieces.
+    u32x4 kr[2][4], vr[8];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int tok = tok0 + rt * 16 + col;
+        const bf16_t *kp = kg_base + (size_t)(tok <= p ? tok : p) * D + kg * 8;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) kr[rt][kc] = ld16(kp + kc * 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int piece = lane + 64 * i;
+        const int tok = tok0 + (piece >> 4);
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        vr[i] = tok <= p ? ld16(vg_base + (size_t)tok * D + (piece & 15) * 8) : z4;
+    }
+    f32x4 sacc[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) acc = mfma16(as_bf16x8(kr[rt][kc]), qf[kc], acc);
+        sacc[rt] = acc;
+    }
+    // V chunk into this wave's LDS rows (tokens past p were loaded as zero).
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int piece = lane + 64 * i;
+        *reinterpret_cast<u32x4 *>(vrows + (piece >> 4) * kVRow + (piece & 15) * 16) = vr[i];
+    }
+    // Online softmax (log2 domain). Lane holds head `col`, tokens 4*kg + r
+    // (tile 0) and 16 + 4*kg + r (tile 1).
+    float z[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = tok0 + rt * 16 + 4 * kg + r;
+            z[rt][r] = tok <= p ? sacc[rt][r] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, z[rt][r]);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(st.m - m_new);
+    float psum = 0.f;
+    bf16x8 pa;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pv = m_new == -INFINITY ? 0.f : exp2f(z[rt][r] - m_new);
+            psum += pv;
+            pa[rt * 4 + r] = (__bf16)pv;
+        }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    float a_row[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a_row[r] = __shfl(alpha, 4 * kg + r);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the V rows have landed
+    __builtin_amdgcn_wave_barrier();
+    // Lane (i, kg) addresses d-values dt*16 + 4*(i&3) .. +3 of tokens
+    // 4*kg + (i>>2) and 16 + 4*kg + (i>>2); the transposing read returns
+    // d = dt*16 + i of tokens 4*kg + 0..3 and 16 + 4*kg + 0..3, the same token
+    // order as the P operand.
+    const unsigned char *vlo = vrows + (4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
+    const unsigned char *vhi = vlo + 16 * kVRow;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const u32x2 lo = lds_read_tr16(vlo + dt * 32);
+        const u32x2 hi = lds_read_tr16(vhi + dt * 32);
+        const u32x4 vb = {lo[0], lo[1], hi[0], hi[1]};
+        f32x4 acc = st.o[dt];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] *= a_row[r];
+        st.o[dt] = mfma16(pa, as_bf16x8(vb), acc);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Kept blocks of a row, in slot order: ids outside the row's causal range
+// (p/S + 1 blocks) are ignored and a repeated id counts once. Thread 0 only.
+__device__ __forceinline__ int build_block_list(const int *sel_lds, int K, int p, int *blocks) {
+    int n = 0;
+    const int n_valid = p >= 0 ? p / S + 1 : 0;
+    for (int k = 0; k < K; ++k) {
+        const int blk = sel_lds[k];
+        if (blk < 0 || blk >= n_valid) continue;
+        bool dup = false;
+        for (int k2 = 0; k2 < k; ++k2) dup |= sel_lds[k2] == blk;
+        if (!dup) blocks[n++] = blk;
+    }
+    return n;
+}
+
+// Merges the NW waves' states by log-sum-exp and writes the R heads' rows of
+// out (bf16) and lse (natural log). s_m, s_l: [NW][16] fp32; s_o: [NW][16][128]
+// fp32 (may alias the V staging area: the caller has finished with it).
+template <int NW>
+__device__ __forceinline__ void merge_and_store(const WaveAttn &st, int R, float *s_m, float *s_l,
+                                                float *s_o, bf16_t *out_heads, float *lse_heads) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    if (lane < 16) {
+        s_m[wave * 16 + lane] = st.m;
+        s_l[wave * 16 + lane] = st.l;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = 4 * kg + r;
+        if (h >= R) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + h]);
+        const float mw = s_m[wave * 16 + h];
+        const float sc = mw == -INFINITY ? 0.f : exp2f(mw - M);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) s_o[(wave * 16 + h) * D + dt * 16 + col] = st.o[dt][r] * sc;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < R * D; idx += NW * 64) {
+        const int h = idx / D, dd = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + h]);
+        float Lsum = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            if (s_m[w * 16 + h] != -INFINITY) Lsum += exp2f(s_m[w * 16 + h] - M) * s_l[w * 16 + h];
+            acc += s_o[(w * 16 + h) * D + dd];
+        }
+        out_heads[(size_t)h * D + dd] = to_bf16(Lsum > 0.f ? acc / Lsum : 0.f);
+        if (lse_heads && dd == 0) lse_heads[h] = Lsum > 0.f ? M * kLn2 + logf(Lsum) : -INFINITY;
+    }
+}
+
+// Prefill: one 4-wave workgroup per (row, group); wave w takes chunk w of
+// every kept block, so a block is read once per workgroup.
+struct PrefillLds {
+    unsigned char vrows[4 * kVWave];  // V chunks; then the [4][16][128] fp32 wave outputs
+    int sel[KMAX];
+    int blocks[KMAX];
+    int nblk;
+    float m[4 * 16], l[4 * 16];
+};
 
 __global__ __launch_bounds__(256) void sparse_attn_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
     const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const int32_t *__restrict__ sel, int T, int G, int R,
-    int Nmax, int K, int spl, int nsplit, float scale_log2, bf16_t *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_ml) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[4 * D * kVtStride * 2];
-    __shared__ int s_blocks[msa::kMaxTopk];
-    __shared__ int s_nblk;
-    __shared__ float s_m[4][16], s_l[4][16];
-
+    int Nmax, int K, float scale_log2, bf16_t *__restrict__ out, float *__restrict__ lse) {
+    __shared__ PrefillLds L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t item = blockIdx.x;
-    const int split = (int)(item % nsplit);
-    const int g = (int)((item / nsplit) % G);
-    const int64_t bt = item / ((int64_t)nsplit * G);
+    const int64_t unit = blockIdx.x;  // (row, group)
+    const int g = (int)(unit % G);
+    const int64_t bt = unit / G;
     const int b = (int)(bt / T), t = (int)(bt % T);
     const int H = G * R;
     const int kv = clamp_kv(kv_lens[b], Nmax);
     const int qs = q_start ? q_start[b] : kv - T;
     const int p = qs + t;
     const bool row_ok = p >= 0 && p < kv;
-
-    if (tid == 0) {
-        int n = 0;
-        if (row_ok) {
-            const int32_t *srow = sel + (bt * G + g) * K;
-            const int n_valid = p / S + 1;
-            const int k_end = min(K, split * spl + spl);
-            for (int k = split * spl; k < k_end; ++k) {
-                const int blk = srow[k];
-                if (blk < 0 || blk >= n_valid) continue;
-                bool dup = false;
-                for (int k2 = 0; k2 < k; ++k2) dup |= srow[k2] == blk;
-                if (!dup) s_blocks[n++] = blk;
-            }
-        }
-        s_nblk = n;
-    }
+    if (tid < K) L.sel[tid] = row_ok ? sel[unit * K + tid] : -1;
     __syncthreads();
-    const int nblk = s_nblk;
-
-    const int col = lane & 15, kg = lane >> 4;
+    if (tid == 0) L.nblk = build_block_list(L.sel, K, row_ok ? p : -1, L.blocks);
+    __syncthreads();
+    const int nblk = L.nblk;
     bf16x8 qf[4];
-    {
-        const bool hv = col < R;
-        const bf16_t *qp = q + (bt * H + g * R + (hv ? col : 0)) * D + kg * 8;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) qf[kc] = hv ? ld_bf16x8(qp + kc * 32) : zero_bf16x8();
-    }
+    load_query(qf, q + (bt * H + (int64_t)g * R) * D, R, lane);
     const bf16_t *kg_base = k_cache + ((size_t)b * G + g) * Nmax * D;
     const bf16_t *vg_base = v_cache + ((size_t)b * G + g) * Nmax * D;
-    bf16_t *vt = reinterpret_cast<bf16_t *>(smem) + wave * D * kVtStride;
+    WaveAttn st;
+    wave_attn_init(st);
+    for (int c = 0; c < nblk; ++c)
+        attend_chunk(st, qf, kg_base, vg_base, L.blocks[c] * S + wave * 32, p, scale_log2,
+                     L.vrows + wave * kVWave, lane);
+    merge_and_store<4>(st, R, L.m, L.l, reinterpret_cast<float *>(L.vrows),
+                       out + (bt * H + (int64_t)g * R) * D, lse ? lse + bt * H + (int64_t)g * R : nullptr);
+}
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 o[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+// Decode: the new token of sequence b sits at position kv - 1. Group g's
+// kept blocks give 4*nblk 32-token chunks; workgroup (b, g, split) has eight
+// waves and takes chunks [8*split, 8*split + 8), one per wave, so every load
+// of the split is in flight at once. With `pooled` non-null each workgroup
+// first ranks the row itself (wave 0, from the pooled block scores; split 0
+// also writes sel / sel_scores), otherwise it reads sel. The waves merge in
+// LDS into one unnormalised partial (O, m, l) per split, which
+// combine_kernel merges by log-sum-exp.
+constexpr int kDecWaves = 8;
+constexpr int kDecChunks = kDecWaves;  // chunks per split
 
-    for (int c = 0; c < nblk; ++c) {
-        const int tok0 = s_blocks[c] * S + wave * 32;
-        // S^T for two 16-token tiles.
-        f32x4 st[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int tok = tok0 + rt * 16 + col;
-            const int tok_ld = tok <= p ? tok : p;
-            const bf16_t *kp = kg_base + (size_t)tok_ld * D + kg * 8;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) acc = mfma16(ld_bf16x8(kp + kc * 32), qf[kc], acc);
-            st[rt] = acc;
-        }
-        // Transposed V chunk into this wave's LDS region; tokens past p are zero.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int piece = lane + 64 * i;
-            const int tk = piece >> 4, cc = piece & 15;
-            const int tok = tok0 + tk;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (tok <= p) v = ld16(vg_base + (size_t)tok * D + cc * 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vt[(cc * 8 + 2 * e) * kVtStride + tk] = (bf16_t)(v[e] & 0xFFFFu);
-                vt[(cc * 8 + 2 * e + 1) * kVtStride + tk] = (bf16_t)(v[e] >> 16);
+struct DecodeLds {
+    unsigned char vrows[kDecWaves * kVWave];  // V chunks; then [8][16][128] fp32 outputs
+    uint64_t keys[64];                        // top-k list
+    int sel[KMAX];
+    int blocks[KMAX];
+    int nblk;
+    float m[kDecWaves * 16], l[kDecWaves * 16];
+};
+
+__global__ __launch_bounds__(512) void sparse_decode_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
+    const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
+    const float *__restrict__ pooled, int64_t nb_max, int32_t *__restrict__ sel,
+    float *__restrict__ sel_scores, int G, int R, int Nmax, int K, int nsplit, float scale_log2,
+    float *__restrict__ part_o, float *__restrict__ part_ml) {
+    __shared__ DecodeLds L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int split = (int)(blockIdx.x % nsplit);
+    const int64_t unit = blockIdx.x / nsplit;  // (sequence, group)
+    const int g = (int)(unit % G);
+    const int b = (int)(unit / G);
+    const int H = G * R;
+    const int kv = clamp_kv(kv_lens[b], Nmax);
+    const int p = kv - 1;
+    if (pooled) {
+        if (wave == 0) {
+            uint64_t top = 0;
+            if (p >= 0) top = wave_topk_row(pooled + unit * nb_max, p / S + 1, K, lane, L.keys);
+            if (lane < K) {
+                const int blk = top ? key_block(top) : -1;
+                L.sel[lane] = blk;
+                if (split == 0) {
+                    sel[unit * K + lane] = blk;
+                    if (sel_scores) sel_scores[unit * K + lane] = top ? key_score(top) : -INFINITY;
+                }
             }
         }
-        // Online softmax (log2 domain). Lane holds head `col`, tokens
-        // 4*kg + r (tile 0) and 16 + 4*kg + r (tile 1).
-        float z[2][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = tok0 + rt * 16 + 4 * kg + r;
-                z[rt][r] = tok <= p ? st[rt][r] * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, z[rt][r]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-        float psum = 0.f;
-        bf16x8 pa;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float pv = m_new == -INFINITY ? 0.f : exp2f(z[rt][r] - m_new);
-                psum += pv;
-                pa[rt * 4 + r] = (__bf16)pv;
-            }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        float a_row[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a_row[r] = __shfl(alpha, 4 * kg + r);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const bf16_t *vr = vt + (dt * 16 + col) * kVtStride + 4 * kg;
-            const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
-            const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
-            const u32x4 vb = {lo[0], lo[1], hi[0], hi[1]};
-            f32x4 acc = o[dt];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= a_row[r];
-            o[dt] = mfma16(pa, as_bf16x8(vb), acc);
-        }
-    }
-
-    // Merge the four waves.
-    if (lane < 16) {
-        s_m[wave][lane] = m_run;
-        s_l[wave][lane] = l_run;
+    } else if (tid < K) {
+        L.sel[tid] = p >= 0 ? sel[unit * K + tid] : -1;
     }
     __syncthreads();
-    float *s_o = reinterpret_cast<float *>(smem);  // [4][16][128] fp32, reuses the V area
+    if (tid == 0) L.nblk = build_block_list(L.sel, K, p, L.blocks);
+    __syncthreads();
+    const int c = split * kDecChunks + wave;  // this wave's chunk
+    WaveAttn st;
+    wave_attn_init(st);
+    if (c < L.nblk * 4) {
+        bf16x8 qf[4];
+        load_query(qf, q + ((int64_t)b * H + (int64_t)g * R) * D, R, lane);
+        attend_chunk(st, qf, k_cache + ((size_t)b * G + g) * Nmax * D,
+                     v_cache + ((size_t)b * G + g) * Nmax * D, L.blocks[c >> 2] * S + (c & 3) * 32,
+                     p, scale_log2, L.vrows + wave * kVWave, lane);
+    }
+    // Merge the eight waves into this split's partial.
+    float *s_o = reinterpret_cast<float *>(L.vrows);
+    const int col = lane & 15, kg = lane >> 4;
+    if (lane < 16) {
+        L.m[wave * 16 + lane] = st.m;
+        L.l[wave * 16 + lane] = st.l;
+    }
+    __syncthreads();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int h = 4 * kg + r;
+        if (h >= R) continue;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
-        const float mw = s_m[wave][h];
+        for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, L.m[w * 16 + h]);
+        const float mw = L.m[wave * 16 + h];
         const float sc = mw == -INFINITY ? 0.f : exp2f(mw - M);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) s_o[(wave * 16 + h) * D + dt * 16 + col] = o[dt][r] * sc;
+        for (int dt = 0; dt < 8; ++dt) s_o[(wave * 16 + h) * D + dt * 16 + col] = st.o[dt][r] * sc;
     }
     __syncthreads();
-    const int64_t unit = bt * G + g;  // (row, group)
-    for (int idx = tid; idx < R * D; idx += 256) {
+    for (int idx = tid; idx < R * D; idx += kDecWaves * 64) {
         const int h = idx / D, dd = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
-        float L = 0.f, acc = 0.f;
+        for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, L.m[w * 16 + h]);
+        float Lsum = 0.f, acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            if (s_m[w][h] != -INFINITY) L += exp2f(s_m[w][h] - M) * s_l[w][h];
+        for (int w = 0; w < kDecWaves; ++w) {
+            if (L.m[w * 16 + h] != -INFINITY) Lsum += exp2f(L.m[w * 16 + h] - M) * L.l[w * 16 + h];
             acc += s_o[(w * 16 + h) * D + dd];
         }
-        if (nsplit == 1) {
-            const float val = L > 0.f ? acc / L : 0.f;
-            __bf16 hv = (__bf16)val;
-            out[(bt * H + g * R + h) * D + dd] = __builtin_bit_cast(bf16_t, hv);
-            if (lse && dd == 0) lse[bt * H + g * R + h] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
-        } else {
-            const int64_t pu = (unit * nsplit + split) * R + h;
-            part_o[pu * D + dd] = acc;
-            if (dd == 0) {
-                part_ml[pu * 2] = M;
-                part_ml[pu * 2 + 1] = L;
-            }
+        const int64_t pu = (unit * nsplit + split) * R + h;
+        part_o[pu * D + dd] = acc;
+        if (dd == 0) {
+            part_ml[pu * 2] = M;
+            part_ml[pu * 2 + 1] = Lsum;
         }
     }
 }
 
-// Log-sum-exp merge of the nsplit partials of one (row, group).
-__global__ __launch_bounds__(256) void combine_kernel(
-    const float *__restrict__ part_o, const float *__restrict__ part_ml, int G, int R,
-    int nsplit, bf16_t *__restrict__ out, float *__restrict__ lse) {
-    const int64_t unit = blockIdx.x;  // (row, group)
-    const int g = (int)(unit % G);
-    const int64_t bt = unit / G;
-    const int H = G * R;
-    for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
-        const int h = idx / D, dd = idx % D;
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((unit * nsplit + s) * R + h) * 2]);
-        float L = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-            for (int s = 0; s < nsplit; ++s) {
-                const int64_t pu = (unit * nsplit + s) * R + h;
-                const float ms = part_ml[pu * 2];
-                if (ms == -INFINITY) continue;
-                const float w = exp2f(ms - M);
-                L += w * part_ml[pu * 2 + 1];
-                acc += w * part_o[pu * D + dd];
+// Log-sum-exp merge of the nsplit partials of one (sequence, group, head):
+// one thread per output element, every split's partial row read coalesced.
+__global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part_o,
+                                                      const float *__restrict__ part_ml, int G,
+                                                      int R, int nsplit, bf16_t *__restrict__ out,
+                                                      float *__restrict__ lse) {
+    const int64_t uh = blockIdx.x;  // (sequence * G + g) * R + h
+    const int h = (int)(uh % R);
+    const int64_t unit = uh / R;
+    const int dd = threadIdx.x;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, part_ml[((unit * nsplit + sp) * R + h) * 2]);
+    float Lsum = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+        for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+            float pv[8], pm[8], pl[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bool ok = sp0 + j < nsplit;
+                const int64_t pu = (unit * nsplit + sp0 + j) * R + h;
+                pv[j] = ok ? part_o[pu * D + dd] : 0.f;
+                pm[j] = ok ? part_ml[pu * 2] : -INFINITY;
+                pl[j] = ok ? part_ml[pu * 2 + 1] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (pm[j] == -INFINITY) continue;
+                const float w = exp2f(pm[j] - M);
+                Lsum += w * pl[j];
+                acc += w * pv[j];
             }
         }
-        const float val = L > 0.f ? acc / L : 0.f;
-        __bf16 hv = (__bf16)val;
-        out[(bt * H + g * R + h) * D + dd] = __builtin_bit_cast(bf16_t, hv);
-        if (lse && dd == 0) lse[bt * H + g * R + h] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
     }
+    // out / lse rows of (sequence, group) are contiguous over the R heads.
+    out[uh * D + dd] = to_bf16(Lsum > 0.f ? acc / Lsum : 0.f);
+    if (lse && dd == 0) lse[uh] = Lsum > 0.f ? M * kLn2 + logf(Lsum) : -INFINITY;
 }
 
 msa_status launch_status(const char *what) {
@@ -583,6 +1011,32 @@ msa_status launch_status(const char *what) {
 float scale_log2_of(const msa_config *cfg) {
     const float tau = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)cfg->head_dim);
     return tau * kLog2e;
+}
+
+// Blocks per decode-scan workgroup: about 2048 workgroups over the batch, at
+// least 4 (one per wave), a multiple of 4.
+int64_t scan_blocks_per_wg(int32_t B, int64_t nb_max) {
+    int64_t per = ((int64_t)B * nb_max + 2047) / 2048;
+    return per < 4 ? 4 : (per + 3) / 4 * 4;
+}
+
+// Pooled block scores of every row: the streaming kernel for T*G <= 16, the
+// MFMA prefill kernel otherwise.
+msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                         const bf16_t *qi, const bf16_t *ki, const int32_t *kv_lens,
+                         const int32_t *q_start, float *pooled, int64_t nb_max, hipStream_t st) {
+    const int G = cfg->num_kv_groups;
+    const int rows = T * G;
+    if (rows <= msa::kScanMaxRows) {
+        const int64_t per_wg = scan_blocks_per_wg(B, nb_max);
+        const dim3 grid((unsigned)((nb_max + per_wg - 1) / per_wg), (unsigned)B);
+        idx_scan_kernel<<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G, Nmax,
+                                              nb_max, (int)per_wg);
+        return launch_status("decode index kernel");
+    }
+    const dim3 grid((unsigned)((rows + kPfRows - 1) / kPfRows), (unsigned)B);
+    idx_prefill_kernel<<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G, Nmax, nb_max);
+    return launch_status("prefill index kernel");
 }
 
 }  // namespace
@@ -602,60 +1056,19 @@ msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t N
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const msa::IndexWs w = msa::index_ws(cfg, B, T, Nmax);
     float *pooled = reinterpret_cast<float *>(static_cast<char *>(workspace) + w.pooled_off);
+    s = launch_pooled(cfg, B, T, Nmax, static_cast<const bf16_t *>(q_idx),
+                      static_cast<const bf16_t *>(k_idx), kv_lens, q_start, pooled, w.nb_max, st);
+    if (s != MSA_OK) return s;
     const int G = cfg->num_kv_groups;
-    const int rows = T * G;
-    const bf16_t *qi = static_cast<const bf16_t *>(q_idx);
-    const bf16_t *ki = static_cast<const bf16_t *>(k_idx);
-    if (rows <= msa::kScanMaxRows) {
-        int64_t per_wg = ((int64_t)B * w.nb_max + 2047) / 2048;
-        per_wg = per_wg < 4 ? 4 : (per_wg + 3) / 4 * 4;
-        const dim3 grid((unsigned)((w.nb_max + per_wg - 1) / per_wg), (unsigned)B);
-        idx_scan_kernel<<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G, Nmax,
-                                              w.nb_max, (int)per_wg);
+    const int64_t nrows = (int64_t)B * T * G;
+    if (T * G <= msa::kScanMaxRows) {
+        topk_rows_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(
+            pooled, w.nb_max, kv_lens, q_start, B, T, G, Nmax, cfg->topk, sel, sel_scores);
     } else {
-        const dim3 grid((unsigned)((rows + kPfRows - 1) / kPfRows), (unsigned)B);
-        idx_prefill_kernel<<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G, Nmax,
-                                                 w.nb_max);
+        topk_kernel<<<(unsigned)nrows, 256, 0, st>>>(pooled, w.nb_max, kv_lens, q_start, B, T, G,
+                                                    Nmax, cfg->topk, sel, sel_scores);
     }
-    if ((s = launch_status("index scoring kernel")) != MSA_OK) return s;
-    const int64_t nrows = (int64_t)B * rows;
-    topk_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(pooled, w.nb_max, kv_lens, q_start,
-                                                            B, T, G, Nmax, cfg->topk, sel,
-                                                            sel_scores);
     return launch_status("top-k kernel");
-}
-
-static msa_status sparse_call(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
-                              const void *q, const void *k_cache, const void *v_cache,
-                              const int32_t *kv_lens, const int32_t *q_start, const int32_t *sel,
-                              void *out, float *lse, void *workspace, size_t ws_bytes,
-                              void *stream, int32_t which) {
-    msa::clear_error();
-    msa_status s = msa::check_sparse_args(cfg, B, T, Nmax, q, k_cache, v_cache, kv_lens, q_start,
-                                          sel, out, lse, workspace, ws_bytes, which);
-    if (s != MSA_OK || B == 0 || T == 0) return s;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const msa::SparseWs w = msa::sparse_ws(cfg, B, T, Nmax, which);
-    const int G = cfg->num_kv_groups, R = cfg->heads_per_group, K = cfg->topk;
-    const int nsplit = w.nsplit;
-    const int spl = (K + nsplit - 1) / nsplit;
-    float *part_o = nullptr, *part_ml = nullptr;
-    if (nsplit > 1) {
-        part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + w.part_o_off);
-        part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + w.part_ml_off);
-    }
-    const int64_t items = (int64_t)B * T * G * nsplit;
-    sparse_attn_kernel<<<(unsigned)items, 256, 0, st>>>(
-        static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k_cache),
-        static_cast<const bf16_t *>(v_cache), kv_lens, q_start, sel, T, G, R, Nmax, K, spl,
-        nsplit, scale_log2_of(cfg), static_cast<bf16_t *>(out), lse, part_o, part_ml);
-    if ((s = launch_status("sparse attention kernel")) != MSA_OK) return s;
-    if (nsplit > 1) {
-        combine_kernel<<<(unsigned)((int64_t)B * T * G), 256, 0, st>>>(
-            part_o, part_ml, G, R, nsplit, static_cast<bf16_t *>(out), lse);
-        if ((s = launch_status("combine kernel")) != MSA_OK) return s;
-    }
-    return MSA_OK;
 }
 
 msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
@@ -663,16 +1076,85 @@ msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, 
                                    const int32_t *kv_lens, const int32_t *q_start,
                                    const int32_t *sel, void *out, float *lse, void *workspace,
                                    size_t ws_bytes, void *stream) {
-    return sparse_call(cfg, B, T, Nmax, q, k_cache, v_cache, kv_lens, q_start, sel, out, lse,
-                       workspace, ws_bytes, stream, MSA_WS_SPARSE_PREFILL);
+    msa::clear_error();
+    msa_status s = msa::check_sparse_args(cfg, B, T, Nmax, q, k_cache, v_cache, kv_lens, q_start,
+                                          sel, out, lse, workspace, ws_bytes,
+                                          MSA_WS_SPARSE_PREFILL);
+    if (s != MSA_OK || B == 0 || T == 0) return s;
+    const int64_t units = (int64_t)B * T * cfg->num_kv_groups;
+    sparse_attn_kernel<<<(unsigned)units, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k_cache),
+        static_cast<const bf16_t *>(v_cache), kv_lens, q_start, sel, T, cfg->num_kv_groups,
+        cfg->heads_per_group, Nmax, cfg->topk, scale_log2_of(cfg), static_cast<bf16_t *>(out),
+        lse);
+    return launch_status("sparse attention kernel");
+}
+
+// Split partials of msa_sparse_attn_decode and msa_decode: sparse_decode_kernel
+// for every (sequence, group, split), then the merge.
+static msa_status launch_decode_attention(const msa_config *cfg, int32_t B, int32_t Nmax,
+                                          const void *q, const void *k_cache,
+                                          const void *v_cache, const int32_t *kv_lens,
+                                          const float *pooled, int64_t nb_max, int32_t *sel,
+                                          float *sel_scores, void *out, float *lse,
+                                          float *part_o, float *part_ml, hipStream_t st) {
+    const int G = cfg->num_kv_groups, R = cfg->heads_per_group, K = cfg->topk;
+    const int nsplit = msa::decode_splits(cfg);
+    const int64_t units = (int64_t)B * G;
+    sparse_decode_kernel<<<(unsigned)(units * nsplit), kDecWaves * 64, 0, st>>>(
+        static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k_cache),
+        static_cast<const bf16_t *>(v_cache), kv_lens, pooled, nb_max, sel, sel_scores, G, R, Nmax,
+        K, nsplit, scale_log2_of(cfg), part_o, part_ml);
+    msa_status s = launch_status("sparse decode kernel");
+    if (s != MSA_OK) return s;
+    combine_kernel<<<(unsigned)(units * R), D, 0, st>>>(part_o, part_ml, G, R, nsplit,
+                                                        static_cast<bf16_t *>(out), lse);
+    return launch_status("combine kernel");
 }
 
 msa_status msa_sparse_attn_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
                                   const void *k_cache, const void *v_cache,
                                   const int32_t *kv_lens, const int32_t *sel, void *out,
                                   float *lse, void *workspace, size_t ws_bytes, void *stream) {
-    return sparse_call(cfg, B, 1, Nmax, q, k_cache, v_cache, kv_lens, nullptr, sel, out, lse,
-                       workspace, ws_bytes, stream, MSA_WS_SPARSE_DECODE);
+    msa::clear_error();
+    msa_status s = msa::check_sparse_args(cfg, B, 1, Nmax, q, k_cache, v_cache, kv_lens, nullptr,
+                                          sel, out, lse, workspace, ws_bytes,
+                                          MSA_WS_SPARSE_DECODE);
+    if (s != MSA_OK || B == 0) return s;
+    const msa::DecodeWs w = msa::decode_ws(cfg, B, Nmax, false);
+    char *base = static_cast<char *>(workspace);
+    return launch_decode_attention(cfg, B, Nmax, q, k_cache, v_cache, kv_lens, nullptr, 0,
+                                   const_cast<int32_t *>(sel), nullptr, out, lse,
+                                   reinterpret_cast<float *>(base + w.part_o_off),
+                                   reinterpret_cast<float *>(base + w.part_ml_off),
+                                   reinterpret_cast<hipStream_t>(stream));
+}
+
+msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                      const void *q_idx, const void *k_idx, const void *k_cache,
+                      const void *v_cache, const int32_t *kv_lens, int32_t *sel,
+                      float *sel_scores, void *out, float *lse, void *workspace, size_t ws_bytes,
+                      void *stream) {
+    msa::clear_error();
+    msa_status s = msa::check_decode_args(cfg, B, Nmax, q, q_idx, k_idx, k_cache, v_cache,
+                                          kv_lens, sel, sel_scores, out, lse, workspace,
+                                          ws_bytes);
+    if (s != MSA_OK || B == 0) return s;
+    if (cfg->index_dtype != MSA_BF16)
+        return msa::fail(MSA_ERR_UNSUPPORTED, "FP8 index keys are not supported by this build");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const msa::DecodeWs w = msa::decode_ws(cfg, B, Nmax, true);
+    char *base = static_cast<char *>(workspace);
+    float *pooled = reinterpret_cast<float *>(base + w.pooled_off);
+    s = launch_pooled(cfg, B, 1, Nmax, static_cast<const bf16_t *>(q_idx),
+                      static_cast<const bf16_t *>(k_idx), kv_lens, nullptr, pooled, w.nb_max, st);
+    if (s != MSA_OK) return s;
+    // The attention kernel ranks each (sequence, group) row itself from the
+    // pooled scores, then attends over the kept blocks.
+    return launch_decode_attention(cfg, B, Nmax, q, k_cache, v_cache, kv_lens, pooled, w.nb_max,
+                                   sel, sel_scores, out, lse,
+                                   reinterpret_cast<float *>(base + w.part_o_off),
+                                   reinterpret_cast<float *>(base + w.part_ml_off), st);
 }
 
 }  // extern "C"

@@ -40,8 +40,10 @@
  * Ownership and streams: the caller owns every buffer. The library allocates
  * nothing, keeps no state between calls and never synchronises: every call
  * enqueues its kernels on `stream` and returns. Scratch memory comes from the
- * caller's `workspace` (size from msa_workspace_size); it may be reused by
- * later calls on the same stream.
+ * caller's `workspace` (size from msa_workspace_size; msa_sparse_attn_prefill
+ * needs none and accepts NULL): plain scratch that needs no initialisation
+ * and may be reused by any later call on the same stream. Calls that may run at the
+ * same time (other streams) must not share a workspace.
  *
  * Errors: shapes, pointers, alignment (16 bytes for tensors, 4 for int32 and
  * fp32 arrays, 256 for the workspace) and workspace size are checked on the
@@ -79,7 +81,8 @@ typedef enum { MSA_BF16 = 0, MSA_FP8_E4M3 = 1 } msa_dtype;
 typedef enum {
     MSA_WS_INDEX_TOPK = 0,
     MSA_WS_SPARSE_PREFILL = 1,
-    MSA_WS_SPARSE_DECODE = 2
+    MSA_WS_SPARSE_DECODE = 2,
+    MSA_WS_DECODE = 3
 } msa_ws_kind;
 
 /* Layer shapes; the names follow the pages' sparse_attention_config. */
@@ -127,8 +130,24 @@ msa_status msa_sparse_attn_decode(const msa_config *cfg, int32_t B, int32_t Nmax
                                   const int32_t *kv_lens, const int32_t *sel, void *out,
                                   float *lse, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * One whole decode step of the method (index branch and sparse branch, Tencent
+ * article §二 and §六): for every sequence b the new token at position
+ * kv_lens[b]-1 (already in the caches) is scored against every cached index
+ * key, its top-K blocks are written to sel (and sel_scores), and its G*R
+ * heads attend over them into out (and lse). Equivalent to msa_index_topk
+ * with T = 1 and q_start = NULL followed by msa_sparse_attn_decode, with one
+ * workspace (MSA_WS_DECODE) for both. Same layouts with T = 1.
+ */
+msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                      const void *q_idx, const void *k_idx, const void *k_cache,
+                      const void *v_cache, const int32_t *kv_lens, int32_t *sel,
+                      float *sel_scores, void *out, float *lse, void *workspace, size_t ws_bytes,
+                      void *stream);
+
 /* Workspace bytes the named call needs for these shapes (0 if none); returns
- * (size_t)-1 for an invalid configuration. For MSA_WS_SPARSE_DECODE, T is 1. */
+ * (size_t)-1 for an invalid configuration. For MSA_WS_SPARSE_DECODE and
+ * MSA_WS_DECODE, T is 1. */
 size_t msa_workspace_size(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                           int32_t which);
 

@@ -104,32 +104,47 @@ def test_sparse_validation(lib):
                                            a["k"], a["v"], a["kv"], a["qs"], a["sel"],
                                            a["out"], a["lse"], None, 0, None)
 
-    def decode(nws=0, ws=FAKE, **kw):
+    def decode(**kw):
         a = {**args, **kw}
         return lib.msa_sparse_attn_decode(ctypes.byref(c), 2, 1024, a["q"], a["k"], a["v"],
-                                          a["kv"], a["sel"], a["out"], a["lse"], ws, nws, None)
+                                          a["kv"], a["sel"], a["out"], a["lse"], None, 0, None)
 
     assert prefill(q=None) == INVALID
     assert prefill(out=FAKE_MIS) == INVALID
     assert prefill(lse=ctypes.c_void_p(0x100001)) == INVALID
     assert prefill(c=cfg(heads_per_group=32)) == UNSUPPORTED
     assert decode(sel=None) == INVALID
-    need = lib.msa_workspace_size(ctypes.byref(c), 2, 1, 1024, 2)
-    assert need > 0
-    assert decode(nws=need - 1) == WORKSPACE
-    assert decode(ws=None, nws=need) == WORKSPACE
+    assert decode(v=FAKE_MIS) == INVALID
+    assert decode() == WORKSPACE  # split partials need a workspace
     assert lib.msa_workspace_size(ctypes.byref(c), 2, 1, 1024, 9) == ctypes.c_size_t(-1).value
     assert lib.msa_workspace_size(None, 2, 1, 1024, 0) == ctypes.c_size_t(-1).value
+
+
+def test_decode_step_validation(lib):
+    c = cfg()
+
+    def call(ws=FAKE, nws=0, **kw):
+        a = dict(q=FAKE, qi=FAKE, ki=FAKE, k=FAKE, v=FAKE, kv=FAKE, sel=FAKE, out=FAKE)
+        a.update(kw)
+        return lib.msa_decode(ctypes.byref(c), 2, 1024, a["q"], a["qi"], a["ki"], a["k"], a["v"],
+                              a["kv"], a["sel"], None, a["out"], None, ws, nws, None)
+
+    need = lib.msa_workspace_size(ctypes.byref(c), 2, 1, 1024, 3)
+    assert need >= 2 * 4 * 8 * 4
+    assert call(qi=None, nws=need) == INVALID
+    assert call(ki=FAKE_MIS, nws=need) == INVALID
+    assert call(nws=need - 1) == WORKSPACE
+    assert call(ws=None, nws=need) == WORKSPACE
 
 
 def test_workspace_sizes_follow_shapes(lib):
     c = cfg()
     a = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 0)
-    assert a >= 16 * 4 * 1024 * 4
-    assert lib.msa_workspace_size(ctypes.byref(c), 1, 64, 1024, 1) == 0   # prefill: none
-    d = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 2)
-    assert d >= 16 * 4 * 16 * 8 * 130 * 4
-    assert a % 256 == 0 and d % 256 == 0
+    assert a >= 16 * 4 * 1024 * 4 and a % 256 == 0          # pooled block scores
+    assert lib.msa_workspace_size(ctypes.byref(c), 1, 64, 1024, 1) == 0   # sparse: none
+    d = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 2)  # split partials
+    assert d >= 16 * 4 * 2 * 8 * 130 * 4 and d % 256 == 0
+    assert lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 3) == a + d
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -147,3 +147,98 @@ def test_repeat_runs_are_bitwise_identical():
     b = run_gpu(pr, G, R, K, [N, 5000, 777], None, decode=True)
     for x, y in zip(a, b):
         assert np.array_equal(x, y, equal_nan=True)
+
+
+def test_workspace_reuse(orc):
+    """A workspace is plain scratch: calls that reuse one (starting as random
+    bytes) with different batches and lengths match calls with fresh ones and
+    the oracle."""
+    G, R, K, N = 4, 8, 16, 6000
+    cfg = lib_cfg(G, R, K)
+    ws_i = msa.workspace(cfg, 4, 1, N, msa.WS_INDEX_TOPK).random_(0, 256)  # garbage scratch
+    ws_d = msa.workspace(cfg, 4, 1, N, msa.WS_SPARSE_DECODE).random_(0, 256)
+    for trial, lens in enumerate([[6000, 3000, 128, 1], [5000, 5000], [1, 2, 3, 4000], [6000]]):
+        B = len(lens)
+        pr = random_problem(B, 1, N, G, R, seed=900 + trial)
+        kv = dev_i32(lens)
+        qi, ki = dev_index(pr["qi"]), dev_index(pr["ki"])
+        q, k, v = dev_bf16(pr["q"]), dev_bf16(pr["k"]), dev_bf16(pr["v"])
+        say("workspace reuse trial %d lens=%s" % (trial, lens))
+        sel = msa.index_topk(cfg, qi, ki, kv, workspace=ws_i)
+        out = msa.sparse_attn_decode(cfg, q, k, v, kv, sel, workspace=ws_d)
+        sel_f = msa.index_topk(cfg, qi, ki, kv)
+        out_f = msa.sparse_attn_decode(cfg, q, k, v, kv, sel_f)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, sel_f) and torch.equal(out, out_f)
+        lens_np = np.array(lens, np.int32)
+        osel, _ = orc.index_topk(oracle_cfg(G, R, K), pr["qi"], pr["ki"], lens_np, lens_np - 1)
+        assert np.array_equal(sel.cpu().numpy().reshape(osel.shape), osel)
+
+
+
+def run_fused_decode(pr, G, R, K, kv_lens, workspace=None):
+    cfg = lib_cfg(G, R, K)
+    kv = dev_i32(kv_lens)
+    qi, ki = dev_index(pr["qi"]), dev_index(pr["ki"])
+    q, k, v = dev_bf16(pr["q"]), dev_bf16(pr["k"]), dev_bf16(pr["v"])
+    say("msa_decode B=%d Nmax=%d G=%d R=%d K=%d" % (q.shape[0], k.shape[2], G, R, K))
+    sel, sc, out, lse = msa.decode(cfg, q, qi, ki, k, v, kv, want_scores=True, want_lse=True,
+                                   workspace=workspace)
+    torch.cuda.synchronize()
+    return (sel.cpu().numpy(), sc.cpu().numpy(), bf16_out_to_f64(out),
+            lse.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("G,R,K,lens", [(4, 8, 16, [3000, 2999, 1, 129, 2048, 128, 0, 5000]),
+                                        (1, 2, 16, [4096]), (3, 5, 7, [700, 513]),
+                                        (2, 16, 32, [4500, 4500, 17])])
+def test_decode_step_matches_oracle_and_two_calls(orc, G, R, K, lens):
+    Nmax = max(max(lens), 1)
+    pr = random_problem(len(lens), 1, Nmax, G, R, seed=1000 + G + R + K)
+    sel, sc, out, lse = run_fused_decode(pr, G, R, K, lens)
+    kv = np.array(lens, np.int32)
+    valid = kv > 0
+    ocfg = oracle_cfg(G, R, K)
+    rows = np.array([(b, 0) for b in range(len(lens)) if valid[b]], np.int32)
+    osel, osc = orc.index_topk(ocfg, pr["qi"], pr["ki"], kv, kv - 1, rows=rows)
+    assert np.array_equal(sel[valid].reshape(osel.shape), osel)
+    assert np.array_equal(sc[valid].reshape(osc.shape).astype(np.float64), osc)
+    assert (sel[~valid] == -1).all()
+    oout, olse = orc.sparse_attn(ocfg, pr["q"], pr["k"], pr["v"], kv, kv - 1, osel, rows=rows)
+    compare_out(out[valid].reshape(oout.shape), oout, "msa_decode")
+    compare_lse(lse[valid].reshape(olse.shape), olse, "msa_decode")
+    assert (out[~valid] == 0).all() and np.isneginf(lse[~valid]).all()
+    # Same bits as msa_index_topk + msa_sparse_attn_decode.
+    s2, _, o2, l2 = run_gpu(pr, G, R, K, lens, None, decode=True)
+    assert np.array_equal(s2, sel) and np.array_equal(o2, out)
+
+
+def test_decode_step_workspace_reuse(orc):
+    G, R, K, N = 4, 8, 16, 20000
+    cfg = lib_cfg(G, R, K)
+    ws = msa.workspace(cfg, 6, 1, N, msa.WS_DECODE).random_(0, 256)
+    for trial, lens in enumerate([[20000] * 6, [1, 20000, 333], [19999, 128, 129, 4000, 5, 6]]):
+        pr = random_problem(len(lens), 1, N, G, R, seed=1100 + trial)
+        sel, _, out, _ = run_fused_decode(pr, G, R, K, lens, workspace=ws)
+        sel2, _, out2, _ = run_fused_decode(pr, G, R, K, lens)
+        assert np.array_equal(sel, sel2) and np.array_equal(out, out2)
+        kv = np.array(lens, np.int32)
+        osel, _ = orc.index_topk(oracle_cfg(G, R, K), pr["qi"], pr["ki"], kv, kv - 1)
+        assert np.array_equal(sel.reshape(osel.shape), osel)
+
+
+
+def test_decode_many_small_sequences(orc):
+    """1030 sequences x 16 groups (16480 workgroups) of short, ragged rows."""
+    G, R, K, N = 16, 1, 4, 200
+    rng = np.random.default_rng(12)
+    lens = rng.integers(1, N + 1, size=1030).tolist()
+    pr = random_problem(len(lens), 1, N, G, R, seed=1200)
+    sel, sc, out, lse = run_fused_decode(pr, G, R, K, lens)
+    kv = np.array(lens, np.int32)
+    ocfg = oracle_cfg(G, R, K)
+    osel, _ = orc.index_topk(ocfg, pr["qi"], pr["ki"], kv, kv - 1)
+    assert np.array_equal(sel.reshape(osel.shape), osel)
+    oout, olse = orc.sparse_attn(ocfg, pr["q"], pr["k"], pr["v"], kv, kv - 1, osel)
+    compare_out(out.reshape(oout.shape), oout, "many sequences")
+    compare_lse(lse.reshape(olse.shape), olse, "many sequences")
