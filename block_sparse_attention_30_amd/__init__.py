@@ -61,8 +61,15 @@ class Config:
         return self.num_kv_groups * self.heads_per_group
 
     def _c(self) -> _CConfig:
-        return _CConfig(self.num_kv_groups, self.heads_per_group, self.head_dim, self.index_dim,
-                        self.block_size, self.topk, float(self.softmax_scale), self.index_dtype)
+        c = _CCONFIGS.get(self)
+        if c is None:
+            c = _CConfig(self.num_kv_groups, self.heads_per_group, self.head_dim, self.index_dim,
+                         self.block_size, self.topk, float(self.softmax_scale), self.index_dtype)
+            _CCONFIGS[self] = c
+        return c
+
+
+_CCONFIGS = {}
 
 
 _lib = None
@@ -113,6 +120,24 @@ def _ptr(t):
 
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class _on_device:
+    """Makes `dev` the current device for a call (a no-op when it already is)."""
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if self.dev.index is not None and cur != self.dev.index:
+            self.prev = cur
+            torch.cuda.set_device(self.dev.index)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
 
 
 def _need(t, name, dtypes, ndim, device=None):
@@ -193,7 +218,7 @@ def index_topk(cfg: Config, q_idx, k_idx, kv_lens, q_start=None, sel=None, sel_s
         if sel_scores.shape != sel.shape:
             raise ValueError("sel_scores must be [B,T,G,K]")
     ws, nws = _workspace(cfg, B, T, Nmax, WS_INDEX_TOPK, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         _check(load().msa_index_topk(ctypes.byref(cfg._c()), B, T, Nmax, _ptr(q_idx),
                                      _ptr(k_idx), _ptr(kv_lens), _ptr(q_start), _ptr(sel),
                                      _ptr(sel_scores), _ptr(ws), nws, _stream(dev)))
@@ -243,7 +268,7 @@ def sparse_attn_prefill(cfg: Config, q, k_cache, v_cache, kv_lens, sel, q_start=
         _lens(q_start, "q_start", B, dev)
     out, lse = _outputs(cfg, dev, B, T, out, lse, want_lse)
     ws, nws = _workspace(cfg, B, T, Nmax, WS_SPARSE_PREFILL, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         _check(load().msa_sparse_attn_prefill(
             ctypes.byref(cfg._c()), B, T, Nmax, _ptr(q), _ptr(k_cache), _ptr(v_cache),
             _ptr(kv_lens), _ptr(q_start), _ptr(sel), _ptr(out), _ptr(lse), _ptr(ws), nws,
@@ -257,7 +282,7 @@ def sparse_attn_decode(cfg: Config, q, k_cache, v_cache, kv_lens, sel, out=None,
     dev, B, T, Nmax = _sparse_checks(cfg, q, k_cache, v_cache, kv_lens, sel, T_expected=1)
     out, lse = _outputs(cfg, dev, B, 1, out, lse, want_lse)
     ws, nws = _workspace(cfg, B, 1, Nmax, WS_SPARSE_DECODE, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         _check(load().msa_sparse_attn_decode(
             ctypes.byref(cfg._c()), B, Nmax, _ptr(q), _ptr(k_cache), _ptr(v_cache),
             _ptr(kv_lens), _ptr(sel), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream(dev)))
@@ -289,7 +314,7 @@ def decode(cfg: Config, q, q_idx, k_idx, k_cache, v_cache, kv_lens, sel=None, se
             raise ValueError("sel_scores must be [B,1,G,K]")
     out, lse = _outputs(cfg, dev, B, 1, out, lse, want_lse)
     ws, nws = _workspace(cfg, B, 1, Nmax, WS_DECODE, dev, workspace)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         _check(load().msa_decode(ctypes.byref(cfg._c()), B, Nmax, _ptr(q), _ptr(q_idx),
                                  _ptr(k_idx), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens),
                                  _ptr(sel), _ptr(sel_scores), _ptr(out), _ptr(lse), _ptr(ws),

@@ -758,18 +758,22 @@ __device__ __forceinline__ void attend_chunk(WaveAttn &st, const bf16x8 (&qf)[4]
 }
 
 // Kept blocks of a row, in slot order: ids outside the row's causal range
-// (p/S + 1 blocks) are ignored and a repeated id counts once. Thread 0 only.
-__device__ __forceinline__ int build_block_list(const int *sel_lds, int K, int p, int *blocks) {
-    int n = 0;
+// (p/S + 1 blocks) are ignored and a repeated id counts once. Called by one
+// whole wavefront: lane k checks slot k against the earlier slots, then the
+// survivors are compacted by ballot. Returns the count (in every lane).
+__device__ __forceinline__ int build_block_list(const int *sel_lds, int K, int p, int *blocks,
+                                                int lane) {
     const int n_valid = p >= 0 ? p / S + 1 : 0;
-    for (int k = 0; k < K; ++k) {
-        const int blk = sel_lds[k];
-        if (blk < 0 || blk >= n_valid) continue;
-        bool dup = false;
-        for (int k2 = 0; k2 < k; ++k2) dup |= sel_lds[k2] == blk;
-        if (!dup) blocks[n++] = blk;
+    bool keep = false;
+    int blk = -1;
+    if (lane < K) {
+        blk = sel_lds[lane];
+        keep = blk >= 0 && blk < n_valid;
+        for (int k2 = 0; k2 < lane && keep; ++k2) keep = sel_lds[k2] != blk;
     }
-    return n;
+    const uint64_t m = __ballot(keep);
+    if (keep) blocks[__popcll(m & ((1ull << lane) - 1ull))] = blk;
+    return __popcll(m);
 }
 
 // Merges the NW waves' states by log-sum-exp and writes the R heads' rows of
@@ -842,7 +846,10 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     const bool row_ok = p >= 0 && p < kv;
     if (tid < K) L.sel[tid] = row_ok ? sel[unit * K + tid] : -1;
     __syncthreads();
-    if (tid == 0) L.nblk = build_block_list(L.sel, K, row_ok ? p : -1, L.blocks);
+    if (wave == 0) {
+        const int n = build_block_list(L.sel, K, row_ok ? p : -1, L.blocks, lane);
+        if (lane == 0) L.nblk = n;
+    }
     __syncthreads();
     const int nblk = L.nblk;
     bf16x8 qf[4];
@@ -910,7 +917,10 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
         L.sel[tid] = p >= 0 ? sel[unit * K + tid] : -1;
     }
     __syncthreads();
-    if (tid == 0) L.nblk = build_block_list(L.sel, K, p, L.blocks);
+    if (wave == 0) {
+        const int n = build_block_list(L.sel, K, p, L.blocks, lane);
+        if (lane == 0) L.nblk = n;
+    }
     __syncthreads();
     const int c = split * kDecChunks + wave;  // this wave's chunk
     WaveAttn st;
