@@ -126,6 +126,17 @@ def run_decode(torch, msa, w, steps, warmup, nsets=8):
         per = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(nev - 1)]
         return start.elapsed_time(end) / steps, per
 
+    nbm = -(-w.Nmax // 128)
+    pooled = torch.full((w.B, 1, w.G, nbm), float("-inf"), dtype=torch.float32, device="cuda")
+
+    def step_pool(s, ev=None):
+        """The index scan alone (msa_index_pool): the dominant kernel of a step."""
+        _, qi = qs[s % nsets]
+        msa.index_pool(cfg, qi, ki, kv, pooled=pooled)
+
+    # Back-to-back launches between two events: the average launch duration
+    # (no event packets between launches).
+    pool_ms, _ = timed(step_pool, 0)
     ms_two, (idx_ms, att_ms) = timed(step_two_calls, 3)
     ms_eager, _ = timed(step, 2)
     # Serving loops replay a captured graph per step: one graph per query set,
@@ -154,7 +165,7 @@ def run_decode(torch, msa, w, steps, warmup, nsets=8):
     host = dict(k=np_view(kh), v=np_view(vh), ki=np_view(kih), q=np_view(sets[0][0]),
                 qi=np_view(sets[0][1]))
     return dict(ms_per_step=ms_total, wall_s=wall, fused_ms=fused_ms, two_call_ms=ms_two,
-                eager_ms=ms_eager, idx_ms=idx_ms, att_ms=att_ms, host=host)
+                eager_ms=ms_eager, idx_ms=idx_ms, att_ms=att_ms, pool_ms=pool_ms, host=host)
 
 
 def cpu_baseline_decode(w, host, budget_rows=None):
@@ -234,6 +245,43 @@ def run_prefill(torch, msa, w, steps=2, warmup=1):
     return res
 
 
+def kernel_source_digest():
+    import hashlib
+    path = os.path.join(ROOT, "block_sparse_attention_30_amd", "csrc", "msa_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(torch, mib=512, reps=5):
+    """A plain device-to-device copy of known size (read and write `mib` MiB)."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return {"bytes_read": mib << 20, "bytes_written": mib << 20, "ms": round(ms, 5)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +289,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (the reference kernel for "
+                         "scaling HBM byte counters)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling its kernels)")
     args = ap.parse_args()
@@ -265,9 +316,11 @@ def main():
     res = run_decode(torch, msa, w, args.steps, args.warmup)
     nbytes, kidx_bytes = decode_bytes(w)
     value = nbytes / (res["ms_per_step"] * 1e-3) / 1e9
-    # Dominant kernel: the decode index scan (streams every index key once).
-    idx_bytes = kidx_bytes + w.B * w.G * 128 * 2 + w.B * w.G * w.topk * 4
-    achieved = idx_bytes / (res["idx_ms"] * 1e-3) / 1e9
+    # Dominant kernel: the decode index scan (streams every index key once),
+    # timed alone through msa_index_pool: k_idx + q_idx read, pooled written.
+    nbm = -(-w.Nmax // 128)
+    scan_bytes = kidx_bytes + w.B * w.G * 128 * 2 + w.B * w.G * nbm * 4
+    achieved = scan_bytes / (res["pool_ms"] * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
@@ -281,12 +334,18 @@ def main():
         "calls_ms": {"msa_decode_graph_replay": round(res["fused_ms"], 5),
                      "msa_decode_eager_step": round(res["eager_ms"], 5),
                      "two_call_step": round(res["two_call_ms"], 5),
+                     "msa_index_pool": round(res["pool_ms"], 5),
                      "msa_index_topk": round(res["idx_ms"], 5),
                      "msa_sparse_attn_decode": round(res["att_ms"], 5)},
-        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel (msa_index_topk, decode)",
+        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel (msa_index_pool)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("idx_scan_kernel", w.name),
+                     "algorithmic_bytes_per_launch": scan_bytes,
+                     "launch_ms": round(res["pool_ms"], 5)},
     }
+    if args.calibrate_copy:
+        line["copy_calibration"] = copy_calibration(torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(w, res["host"])
     res.pop("host")

@@ -91,12 +91,13 @@ def load():
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     cfgp = ctypes.POINTER(_CConfig)
     lib.msa_index_topk.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_index_pool.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.msa_sparse_attn_prefill.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                             vp, sz, vp]
     lib.msa_sparse_attn_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in (lib.msa_index_topk, lib.msa_sparse_attn_prefill, lib.msa_sparse_attn_decode,
-              lib.msa_decode):
+    for f in (lib.msa_index_topk, lib.msa_index_pool, lib.msa_sparse_attn_prefill,
+              lib.msa_sparse_attn_decode, lib.msa_decode):
         f.restype = ctypes.c_int
     lib.msa_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
     lib.msa_workspace_size.restype = sz
@@ -223,6 +224,36 @@ def index_topk(cfg: Config, q_idx, k_idx, kv_lens, q_start=None, sel=None, sel_s
                                      _ptr(k_idx), _ptr(kv_lens), _ptr(q_start), _ptr(sel),
                                      _ptr(sel_scores), _ptr(ws), nws, _stream(dev)))
     return (sel, sel_scores) if (want_scores or sel_scores is not None) else sel
+
+
+def index_pool(cfg: Config, q_idx, k_idx, kv_lens, q_start=None, pooled=None):
+    """Index scores max-pooled per block: pooled [B,T,G,ceil(Nmax/S)] fp32.
+
+    Entries past a row's position (and rows outside the cache) are left as
+    they were; a new `pooled` starts filled with -inf.
+    """
+    dev = q_idx.device
+    _need(q_idx, "q_idx", _INDEX_DTYPES[cfg.index_dtype], 4)
+    _need(k_idx, "k_idx", _INDEX_DTYPES[cfg.index_dtype], 3, dev)
+    B, T, G, dI = q_idx.shape
+    Nmax = k_idx.shape[1]
+    if G != cfg.num_kv_groups or dI != cfg.index_dim or k_idx.shape[0] != B or \
+            k_idx.shape[2] != cfg.index_dim:
+        raise ValueError("q_idx/k_idx shapes do not match the config")
+    _lens(kv_lens, "kv_lens", B, dev)
+    if q_start is not None:
+        _lens(q_start, "q_start", B, dev)
+    nbm = -(-Nmax // cfg.block_size)
+    if pooled is None:
+        pooled = torch.full((B, T, G, nbm), float("-inf"), dtype=torch.float32, device=dev)
+    _need(pooled, "pooled", (torch.float32,), 4, dev)
+    if tuple(pooled.shape) != (B, T, G, nbm):
+        raise ValueError("pooled must be [B,T,G,ceil(Nmax/S)]")
+    with _on_device(dev):
+        _check(load().msa_index_pool(ctypes.byref(cfg._c()), B, T, Nmax, _ptr(q_idx),
+                                     _ptr(k_idx), _ptr(kv_lens), _ptr(q_start), _ptr(pooled),
+                                     _stream(dev)))
+    return pooled
 
 
 def _sparse_checks(cfg, q, k_cache, v_cache, kv_lens, sel, T_expected=None):

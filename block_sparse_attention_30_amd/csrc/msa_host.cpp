@@ -114,6 +114,24 @@ msa_status check_index_args(const msa_config *cfg, int32_t B, int32_t T, int32_t
     return check_ws(workspace, ws_bytes, index_ws(cfg, B, T, Nmax).total);
 }
 
+msa_status check_pool_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                           const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                           const int32_t *q_start, const float *pooled) {
+    msa_status s = check_config(cfg);
+    if (s != MSA_OK) return s;
+    if ((s = check_dims(B, T, Nmax)) != MSA_OK) return s;
+    if (B == 0 || T == 0) return MSA_OK;
+    if ((int64_t)B * T * cfg->num_kv_groups > ((int64_t)1 << 31) - 1)
+        return fail(MSA_ERR_UNSUPPORTED, "B*T*G exceeds 2^31-1 rows");
+    if (!q_idx || !k_idx || !kv_lens || !pooled)
+        return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx, kv_lens and pooled must not be NULL");
+    if (!aligned(q_idx, 16) || !aligned(k_idx, 16))
+        return fail(MSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+    if (!aligned(kv_lens, 4) || (q_start && !aligned(q_start, 4)) || !aligned(pooled, 4))
+        return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
+    return MSA_OK;
+}
+
 msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                              const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *kv_lens, const int32_t *q_start, const int32_t *sel,

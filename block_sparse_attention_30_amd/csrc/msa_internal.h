@@ -28,6 +28,9 @@ msa_status check_index_args(const msa_config *cfg, int32_t B, int32_t T, int32_t
                             const void *q_idx, const void *k_idx, const int32_t *kv_lens,
                             const int32_t *q_start, const int32_t *sel, const float *sel_scores,
                             const void *workspace, size_t ws_bytes);
+msa_status check_pool_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                           const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                           const int32_t *q_start, const float *pooled);
 msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                              const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *kv_lens, const int32_t *q_start, const int32_t *sel,

@@ -73,6 +73,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+__device__ __forceinline__ i32x8 cat_i32x8(u32x4 lo, u32x4 hi) {
+    const i32x8 r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    return r;
+}
+
+// OCP E4M3 operands (format code 0 for A and B) with unit block scales (E8M0
+// exponent 127 = 1.0): 32 key bytes per lane, lane groups take consecutive
+// 32-byte slices of K (A and B use the same slice mapping).
+__device__ __forceinline__ f32x4 mfma16_f8(i32x8 a, i32x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ f32x16 mfma32_f8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 __device__ __forceinline__ int clamp_kv(int kv, int Nmax) { return kv < Nmax ? kv : Nmax; }
 
 __device__ __forceinline__ bf16_t to_bf16(float v) {
@@ -257,24 +276,38 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
 //
 // Every index key of the sequence is streamed once and serves all T*G
 // index-query rows. Workgroup x of sequence y takes blocks_per_wg blocks;
-// each wave walks its blocks in half-block steps of 64 tokens (16 KiB): a step
-// is read with sixteen load instructions of one contiguous KiB each (four
-// token rows) and staged in the wave's own LDS region (rows padded to 272
-// bytes), while the loads of the next step are already in flight. The MFMA
+// each wave walks its blocks in steps of 16 KiB of keys (64 bf16 or 128 fp8
+// tokens): a step is read with sixteen load instructions of one contiguous KiB
+// each and staged in the wave's own LDS region (rows padded by 16 bytes),
+// while the loads of the next step are already in flight. The MFMA
 // D = A x B then takes A = index-query rows (16 rows, m = t*G + g, zero above
 // T*G) from registers and B = k_idx^T for 16 tokens from LDS; output lane l
 // holds D[4*(l>>4) + r][l & 15], i.e. rows 4*(l>>4)..+3 of one token. A
 // running per-row max over the block's tiles, then a 16-lane max, gives the
 // block's pooled score, written to pooled[b][m][block].
-constexpr int kScanRow = 272;
-constexpr int kScanStep = 64;  // tokens per staged step
-constexpr int kScanWaveLds = kScanStep * kScanRow;
+//
+// bf16 keys use four 16x16x32 bf16 MFMAs per 16-token tile; OCP E4M3 keys one
+// 16x16x128 f8f6f4 MFMA (unit scales). Index data are small integers in
+// practice, so both sums are exact in fp32.
+template <bool F8>
+struct ScanGeom {
+    static constexpr int kRowBytes = DI * (F8 ? 1 : 2);     // one token's key
+    static constexpr int kRow = kRowBytes + 16;              // LDS row stride
+    static constexpr int kStep = F8 ? 128 : 64;              // tokens per step
+    static constexpr int kLanesPerRow = kRowBytes / 16;
+    static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+    static constexpr int kLoads = kStep / kRowsPerLoad;      // 16
+    static constexpr int kStepsPerBlock = S / kStep;
+    static constexpr int kWaveLds = kStep * kRow;
+};
 
+template <bool F8>
 __global__ __launch_bounds__(256) void idx_scan_kernel(
-    const bf16_t *__restrict__ q_idx, const bf16_t *__restrict__ k_idx,
+    const unsigned char *__restrict__ q_idx, const unsigned char *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
     float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int blocks_per_wg) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * kScanWaveLds];
+    typedef ScanGeom<F8> Geo;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * Geo::kWaveLds];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rows = T * G;
@@ -286,15 +319,24 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     const int blk_begin = blockIdx.x * blocks_per_wg;
     const int blk_end = min(blk_begin + blocks_per_wg, nb);
     const int my_blocks = blk_begin + wave < blk_end ? (blk_end - blk_begin - wave + 3) / 4 : 0;
-    const int nsteps = my_blocks * (S / kScanStep);
+    const int nsteps = my_blocks * Geo::kStepsPerBlock;
     if (nsteps == 0) return;
 
     const int col = lane & 15, kg = lane >> 4;
-    bf16x8 a[4];
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // A operand: index-query row `col`, key bytes [kg*32, kg*32+32) of every
+    // 128-byte K slice (bf16: four slices of 32 elements; fp8: one slice).
+    u32x4 a[4][2];
     {
-        const bf16_t *qp = q_idx + ((size_t)b * rows + (col < rows ? col : 0)) * DI + kg * 8;
+        const unsigned char *qp =
+            q_idx + ((size_t)b * rows + (col < rows ? col : 0)) * Geo::kRowBytes;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) a[kc] = col < rows ? ld_bf16x8(qp + kc * 32) : zero_bf16x8();
+        for (int kc = 0; kc < 4; ++kc) {
+            if (F8 && kc > 0) break;
+            const int off = F8 ? kg * 32 : kc * 64 + kg * 16;
+            a[kc][0] = col < rows ? ld16(qp + off) : zero4;
+            a[kc][1] = (F8 && col < rows) ? ld16(qp + off + 16) : zero4;
+        }
     }
     int prow[4];
 #pragma unroll
@@ -303,19 +345,21 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
         const int p = qs + m / G;
         prow[r] = (m < rows && p >= 0 && p < kv) ? p : -1;
     }
-    const unsigned char *kbytes =
-        reinterpret_cast<const unsigned char *>(k_idx + (size_t)b * Nmax * DI);
-    unsigned char *my = lds + wave * kScanWaveLds;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    // Step s covers tokens [tok, tok + 64) of block blk_begin + wave + 4*(s/2).
-    auto step_tok = [&](int s) { return (blk_begin + wave + 4 * (s >> 1)) * S + (s & 1) * kScanStep; };
-    u32x4 v[16];
+    const unsigned char *kbytes = k_idx + (size_t)b * Nmax * Geo::kRowBytes;
+    unsigned char *my = lds + wave * Geo::kWaveLds;
+    // Step s covers tokens [tok, tok + kStep) of block blk_begin + wave + 4*(s / steps per block).
+    auto step_tok = [&](int s) {
+        return (blk_begin + wave + 4 * (s / Geo::kStepsPerBlock)) * S +
+               (s % Geo::kStepsPerBlock) * Geo::kStep;
+    };
+    const int lrow = lane / Geo::kLanesPerRow, lcol = (lane % Geo::kLanesPerRow) * 16;
+    u32x4 v[Geo::kLoads];
     auto load_step = [&](int s) {
         const int t0 = step_tok(s);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tok = t0 + 4 * i + (lane >> 4);
-            v[i] = tok < kv ? ld16(kbytes + (size_t)tok * (DI * 2) + (lane & 15) * 16) : zero4;
+        for (int i = 0; i < Geo::kLoads; ++i) {
+            const int tok = t0 + Geo::kRowsPerLoad * i + lrow;
+            v[i] = tok < kv ? ld16(kbytes + (size_t)tok * Geo::kRowBytes + lcol) : zero4;
         }
     };
     load_step(0);
@@ -323,20 +367,27 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     for (int s = 0; s < nsteps; ++s) {
         const int t0 = step_tok(s);
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            *reinterpret_cast<u32x4 *>(my + (4 * i + (lane >> 4)) * kScanRow + (lane & 15) * 16) = v[i];
+        for (int i = 0; i < Geo::kLoads; ++i)
+            *reinterpret_cast<u32x4 *>(my + (Geo::kRowsPerLoad * i + lrow) * Geo::kRow + lcol) = v[i];
         if (s + 1 < nsteps) load_step(s + 1);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS rows have landed
         __builtin_amdgcn_wave_barrier();
-        const bool need_mask = t0 + kScanStep - 1 > qs;
+        const bool need_mask = t0 + Geo::kStep - 1 > qs;
 #pragma unroll
-        for (int tile = 0; tile < kScanStep / 16; ++tile) {
+        for (int tile = 0; tile < Geo::kStep / 16; ++tile) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const unsigned char *brow = my + (tile * 16 + col) * Geo::kRow;
+            if constexpr (F8) {
+                const u32x4 b0 = *reinterpret_cast<const u32x4 *>(brow + kg * 32);
+                const u32x4 b1 = *reinterpret_cast<const u32x4 *>(brow + kg * 32 + 16);
+                acc = mfma16_f8(cat_i32x8(a[0][0], a[0][1]), cat_i32x8(b0, b1), acc);
+            } else {
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-                acc = mfma16(a[kc], as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                                        my + (tile * 16 + col) * kScanRow + kc * 64 + kg * 16)),
-                             acc);
+                for (int kc = 0; kc < 4; ++kc)
+                    acc = mfma16(as_bf16x8(a[kc][0]),
+                                 as_bf16x8(*reinterpret_cast<const u32x4 *>(brow + kc * 64 + kg * 16)),
+                                 acc);
+            }
             const int tok = t0 + tile * 16 + col;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -345,7 +396,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
             }
         }
         __builtin_amdgcn_wave_barrier();
-        if (s & 1) {  // block complete
+        if (s % Geo::kStepsPerBlock == Geo::kStepsPerBlock - 1) {  // block complete
             const int blk = t0 / S;
             float m2[4];
 #pragma unroll
@@ -393,19 +444,25 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(
 // Prefill index scores. A workgroup owns 256 consecutive (query, group) rows
 // of one sequence; wave w owns rows [64w, 64w+64) as two 32-column MFMA tiles
 // whose index queries stay in registers (B operand). For each causal KV block
-// the 128 x 128 k_idx tile is staged once in LDS (rows padded to 272 bytes so
+// the 128-token k_idx tile is staged once in LDS (rows padded by 16 bytes so
 // that 16 lanes reading 16 bytes each hit distinct banks) and read as the A
 // operand by all four waves. D lane l holds column (l & 31) and rows
 // 8*(i>>2) + 4*(l>>5) + (i&3), so the block max of a column is an in-lane max
-// over the four row tiles plus one exchange with lane l^32.
+// over the four row tiles plus one exchange with lane l^32. bf16 keys use
+// 32x32x16 bf16 MFMAs (8 per row tile and column tile), OCP E4M3 keys
+// 32x32x64 f8f6f4 MFMAs with unit scales (2 per row tile and column tile).
 constexpr int kPfRows = 256;
-constexpr int kLdsRow = 272;
 
+template <bool F8>
 __global__ __launch_bounds__(256) void idx_prefill_kernel(
-    const bf16_t *__restrict__ q_idx, const bf16_t *__restrict__ k_idx,
+    const unsigned char *__restrict__ q_idx, const unsigned char *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
     float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[S * kLdsRow];
+    constexpr int kRowBytes = DI * (F8 ? 1 : 2);
+    constexpr int kRow = kRowBytes + 16;
+    constexpr int kPieces = S * kRowBytes / 16 / 256;  // 16-byte loads per thread per block
+    constexpr int kKs = F8 ? 2 : 8;                     // MFMA K steps over the index dim
+    __shared__ __attribute__((aligned(16))) unsigned char lds[S * kRow];
     const int b = blockIdx.y;
     const int rows = T * G;
     const int r0 = (gridDim.x - 1 - blockIdx.x) * kPfRows;  // longest rows first
@@ -419,7 +476,11 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
     const int nblk = p_hi / S + 1;
 
     const int j = lane & 31, half = lane >> 5;
-    bf16x8 qb[2][8];
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // B operand: query row (r0 + 64*wave + 32*ct + j); K step ks covers key
+    // bytes [ks*kKb, ks*kKb + kKb) of which this lane holds half `half`.
+    constexpr int kKb = F8 ? 64 : 32;
+    u32x4 qb[2][kKs][F8 ? 2 : 1];
     int pcol[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -427,22 +488,24 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
         const int p = qs + r / G;
         const bool ok = r < rows && p >= 0 && p < kv;
         pcol[ct] = ok ? p : -1;
-        const bf16_t *qp = q_idx + ((size_t)b * rows + (ok ? r : 0)) * DI + half * 8;
+        const unsigned char *qp = q_idx + ((size_t)b * rows + (ok ? r : 0)) * kRowBytes;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qb[ct][ks] = ok ? ld_bf16x8(qp + ks * 16) : zero_bf16x8();
+        for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+            for (int h = 0; h < (F8 ? 2 : 1); ++h)
+                qb[ct][ks][h] = ok ? ld16(qp + ks * kKb + half * (kKb / 2) + 16 * h) : zero4;
     }
-    const bf16_t *kseq = k_idx + (size_t)b * Nmax * DI;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const unsigned char *kseq = k_idx + (size_t)b * Nmax * kRowBytes;
     for (int blk = 0; blk < nblk; ++blk) {
         const int tok0 = blk * S;
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kPieces; ++i) {
             const int piece = tid + 256 * i;
-            const int tk = piece >> 4, c = piece & 15;
+            const int tk = piece / (kRowBytes / 16), c = piece % (kRowBytes / 16);
             const int tok = tok0 + tk;
-            const u32x4 v = tok < kv ? ld16(kseq + (size_t)tok * DI + c * 8) : zero4;
-            *reinterpret_cast<u32x4 *>(lds + tk * kLdsRow + c * 16) = v;
+            const u32x4 v = tok < kv ? ld16(kseq + (size_t)tok * kRowBytes + c * 16) : zero4;
+            *reinterpret_cast<u32x4 *>(lds + tk * kRow + c * 16) = v;
         }
         __syncthreads();
         const bool need_mask = tok0 + S - 1 > p_lo;
@@ -451,11 +514,18 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
         for (int rt = 0; rt < 4; ++rt) {
             f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8 a = as_bf16x8(
-                    *reinterpret_cast<const u32x4 *>(lds + (rt * 32 + j) * kLdsRow + ks * 32 + half * 16));
-                acc0 = mfma32(a, qb[0][ks], acc0);
-                acc1 = mfma32(a, qb[1][ks], acc1);
+            for (int ks = 0; ks < kKs; ++ks) {
+                const unsigned char *ap = lds + (rt * 32 + j) * kRow + ks * kKb + half * (kKb / 2);
+                if constexpr (F8) {
+                    const i32x8 a = cat_i32x8(*reinterpret_cast<const u32x4 *>(ap),
+                                              *reinterpret_cast<const u32x4 *>(ap + 16));
+                    acc0 = mfma32_f8(a, cat_i32x8(qb[0][ks][0], qb[0][ks][F8 ? 1 : 0]), acc0);
+                    acc1 = mfma32_f8(a, cat_i32x8(qb[1][ks][0], qb[1][ks][F8 ? 1 : 0]), acc1);
+                } else {
+                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap));
+                    acc0 = mfma32(a, as_bf16x8(qb[0][ks][0]), acc0);
+                    acc1 = mfma32(a, as_bf16x8(qb[1][ks][0]), acc1);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -1031,21 +1101,33 @@ int64_t scan_blocks_per_wg(int32_t B, int64_t nb_max) {
 }
 
 // Pooled block scores of every row: the streaming kernel for T*G <= 16, the
-// MFMA prefill kernel otherwise.
+// MFMA prefill kernel otherwise; bf16 or OCP E4M3 index data.
 msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
-                         const bf16_t *qi, const bf16_t *ki, const int32_t *kv_lens,
+                         const void *q_idx, const void *k_idx, const int32_t *kv_lens,
                          const int32_t *q_start, float *pooled, int64_t nb_max, hipStream_t st) {
     const int G = cfg->num_kv_groups;
     const int rows = T * G;
+    const bool f8 = cfg->index_dtype == MSA_FP8_E4M3;
+    const unsigned char *qi = static_cast<const unsigned char *>(q_idx);
+    const unsigned char *ki = static_cast<const unsigned char *>(k_idx);
     if (rows <= msa::kScanMaxRows) {
         const int64_t per_wg = scan_blocks_per_wg(B, nb_max);
         const dim3 grid((unsigned)((nb_max + per_wg - 1) / per_wg), (unsigned)B);
-        idx_scan_kernel<<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G, Nmax,
-                                              nb_max, (int)per_wg);
+        if (f8)
+            idx_scan_kernel<true><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
+                                                        Nmax, nb_max, (int)per_wg);
+        else
+            idx_scan_kernel<false><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
+                                                         Nmax, nb_max, (int)per_wg);
         return launch_status("decode index kernel");
     }
     const dim3 grid((unsigned)((rows + kPfRows - 1) / kPfRows), (unsigned)B);
-    idx_prefill_kernel<<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G, Nmax, nb_max);
+    if (f8)
+        idx_prefill_kernel<true><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
+                                                       Nmax, nb_max);
+    else
+        idx_prefill_kernel<false><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
+                                                        Nmax, nb_max);
     return launch_status("prefill index kernel");
 }
 
@@ -1061,13 +1143,10 @@ msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t N
     msa_status s = msa::check_index_args(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start, sel,
                                          sel_scores, workspace, ws_bytes);
     if (s != MSA_OK || B == 0 || T == 0) return s;
-    if (cfg->index_dtype != MSA_BF16)
-        return msa::fail(MSA_ERR_UNSUPPORTED, "FP8 index keys are not supported by this build");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const msa::IndexWs w = msa::index_ws(cfg, B, T, Nmax);
     float *pooled = reinterpret_cast<float *>(static_cast<char *>(workspace) + w.pooled_off);
-    s = launch_pooled(cfg, B, T, Nmax, static_cast<const bf16_t *>(q_idx),
-                      static_cast<const bf16_t *>(k_idx), kv_lens, q_start, pooled, w.nb_max, st);
+    s = launch_pooled(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start, pooled, w.nb_max, st);
     if (s != MSA_OK) return s;
     const int G = cfg->num_kv_groups;
     const int64_t nrows = (int64_t)B * T * G;
@@ -1079,6 +1158,17 @@ msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t N
                                                     Nmax, cfg->topk, sel, sel_scores);
     }
     return launch_status("top-k kernel");
+}
+
+msa_status msa_index_pool(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                          const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                          const int32_t *q_start, float *pooled, void *stream) {
+    msa::clear_error();
+    msa_status s =
+        msa::check_pool_args(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start, pooled);
+    if (s != MSA_OK || B == 0 || T == 0) return s;
+    return launch_pooled(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start, pooled,
+                         ((int64_t)Nmax + S - 1) / S, reinterpret_cast<hipStream_t>(stream));
 }
 
 msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
@@ -1150,14 +1240,11 @@ msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void
                                           kv_lens, sel, sel_scores, out, lse, workspace,
                                           ws_bytes);
     if (s != MSA_OK || B == 0) return s;
-    if (cfg->index_dtype != MSA_BF16)
-        return msa::fail(MSA_ERR_UNSUPPORTED, "FP8 index keys are not supported by this build");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const msa::DecodeWs w = msa::decode_ws(cfg, B, Nmax, true);
     char *base = static_cast<char *>(workspace);
     float *pooled = reinterpret_cast<float *>(base + w.pooled_off);
-    s = launch_pooled(cfg, B, 1, Nmax, static_cast<const bf16_t *>(q_idx),
-                      static_cast<const bf16_t *>(k_idx), kv_lens, nullptr, pooled, w.nb_max, st);
+    s = launch_pooled(cfg, B, 1, Nmax, q_idx, k_idx, kv_lens, nullptr, pooled, w.nb_max, st);
     if (s != MSA_OK) return s;
     // The attention kernel ranks each (sequence, group) row itself from the
     // pooled scores, then attends over the kept blocks.

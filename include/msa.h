@@ -110,6 +110,19 @@ msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t N
                           void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * First two steps of the index branch alone (Tencent article §二: index scores,
+ * then the max over each block): pooled [B, T, G, nbm] fp32, nbm =
+ * ceil(Nmax / S), with pooled[b,i,g,B'] = P_B' for every block B' <= p/S of a
+ * row inside the cache. Other entries (blocks past the row's position, rows
+ * outside the cache) are not written. Needs no workspace. Same dispatch as
+ * msa_index_topk; the returned values are exact (integer-valued index data
+ * give integer scores).
+ */
+msa_status msa_index_pool(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                          const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                          const int32_t *q_start, float *pooled, void *stream);
+
+/*
  * Sparse branch for T query rows per sequence (Tencent article §二 and §六):
  * every head of group g attends over the blocks sel[b,i,g,:]. `sel` may come
  * from msa_index_topk or from the caller (repeated ids count once).

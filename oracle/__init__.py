@@ -88,11 +88,15 @@ class Oracle:
         lib.oracle_dense_causal_row.argtypes = [cfgp, vp, vp, vp, i64, i64, vp, vp]
         lib.oracle_index_topk_rows.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, i64, vp, vp,
                                                i32, vp, vp]
+        lib.oracle_index_pool_row.argtypes = [cfgp, vp, vp, i64, vp]
+        lib.oracle_index_pool_rows.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, i64, vp, vp,
+                                               i32, i64, vp]
         lib.oracle_sparse_attn_rows.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, vp, i64, vp, vp,
                                                 vp, i32, vp, vp]
         lib.oracle_dense_causal_rows.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, vp, i64, vp, vp,
                                                  i32, vp, vp]
-        for f in (lib.oracle_index_topk_row, lib.oracle_sparse_attn_row,
+        for f in (lib.oracle_index_pool_row, lib.oracle_index_pool_rows,
+                  lib.oracle_index_topk_row, lib.oracle_sparse_attn_row,
                   lib.oracle_dense_causal_row, lib.oracle_index_topk_rows,
                   lib.oracle_sparse_attn_rows, lib.oracle_dense_causal_rows):
             f.restype = ctypes.c_int
@@ -133,6 +137,27 @@ class Oracle:
         if rc:
             raise ValueError("oracle_index_topk_rows rejected its arguments")
         return sel, scores
+
+    def index_pool(self, cfg: Config, q_idx, k_idx, kv_lens, q_start, rows=None, nb=None,
+                   threads=None):
+        """Pooled block scores [n,G,nb] float64 for the listed (b, i) rows; blocks
+        past a row's position are -inf. nb defaults to ceil(n_stride / S)."""
+        q_idx = np.ascontiguousarray(q_idx)
+        k_idx = np.ascontiguousarray(k_idx)
+        B, T = q_idx.shape[0], q_idx.shape[1]
+        n_stride = k_idx.shape[1]
+        nb = -(-n_stride // cfg.block_size) if nb is None else nb
+        rb, ri = self._rows(rows, B, T)
+        n = rb.size
+        pooled = np.empty((n, cfg.groups, nb), np.float64)
+        c = cfg.c()
+        rc = self.lib.oracle_index_pool_rows(
+            ctypes.byref(c), T, n_stride, _ptr(q_idx), _ptr(k_idx), _ptr(_c(kv_lens, np.int32)),
+            _ptr(_c(q_start, np.int32)), n, _ptr(rb), _ptr(ri), threads or _threads(), nb,
+            _ptr(pooled))
+        if rc:
+            raise ValueError("oracle_index_pool_rows rejected its arguments")
+        return pooled
 
     def sparse_attn(self, cfg: Config, q, k_cache, v_cache, kv_lens, q_start, sel, rows=None,
                     threads=None):

@@ -80,20 +80,15 @@ static int rank_cmp(const void *a, const void *b) {
     return (x->block > y->block) - (x->block < y->block);
 }
 
-/* [T] §二: index query of group g scored against every past index key,
- * max-pooled over each block, top-K blocks kept. */
-int oracle_index_topk_row(const oracle_cfg *cfg, const void *q_idx_row, const void *k_idx_seq,
-                          int64_t p, int32_t *sel, double *scores) {
-    if (check_cfg(cfg) || p < 0 || !q_idx_row || !k_idx_seq || !sel) return -1;
-    const int G = cfg->groups, dI = cfg->index_dim, S = cfg->block_size, K = cfg->topk;
+/* [T] §二, first two steps: the index query of group g scored against every
+ * past index key, then max-pooled over each block. */
+int oracle_index_pool_row(const oracle_cfg *cfg, const void *q_idx_row, const void *k_idx_seq,
+                          int64_t p, double *pooled) {
+    if (check_cfg(cfg) || p < 0 || !q_idx_row || !k_idx_seq || !pooled) return -1;
+    const int G = cfg->groups, dI = cfg->index_dim, S = cfg->block_size;
     const int64_t n_valid = p / S + 1; /* blocks holding at least one key j <= p */
     double *s = malloc(sizeof(double) * (size_t)(p + 1));
-    ranked_block *pool = malloc(sizeof(ranked_block) * (size_t)n_valid);
-    if (!s || !pool) {
-        free(s);
-        free(pool);
-        return -1;
-    }
+    if (!s) return -1;
     for (int g = 0; g < G; ++g) {
         /* Step 1: s_j = sum_c q_I[g, c] * k_I[j, c] for every j <= p. */
         for (int64_t j = 0; j <= p; ++j) {
@@ -111,10 +106,32 @@ int oracle_index_topk_row(const oracle_cfg *cfg, const void *q_idx_row, const vo
             double m = s[lo];
             for (int64_t j = lo + 1; j <= hi; ++j)
                 if (s[j] > m) m = s[j];
-            pool[beta].score = m;
+            pooled[g * n_valid + beta] = m;
+        }
+    }
+    free(s);
+    return 0;
+}
+
+/* [T] §二, third step: of the pooled scores, the top-K blocks are kept. */
+int oracle_index_topk_row(const oracle_cfg *cfg, const void *q_idx_row, const void *k_idx_seq,
+                          int64_t p, int32_t *sel, double *scores) {
+    if (check_cfg(cfg) || p < 0 || !q_idx_row || !k_idx_seq || !sel) return -1;
+    const int G = cfg->groups, S = cfg->block_size, K = cfg->topk;
+    const int64_t n_valid = p / S + 1;
+    double *pooled = malloc(sizeof(double) * (size_t)(G * n_valid));
+    ranked_block *pool = malloc(sizeof(ranked_block) * (size_t)n_valid);
+    if (!pooled || !pool || oracle_index_pool_row(cfg, q_idx_row, k_idx_seq, p, pooled)) {
+        free(pooled);
+        free(pool);
+        return -1;
+    }
+    for (int g = 0; g < G; ++g) {
+        for (int64_t beta = 0; beta < n_valid; ++beta) {
+            pool[beta].score = pooled[g * n_valid + beta];
             pool[beta].block = (int32_t)beta;
         }
-        /* Step 3: order all valid blocks, keep the first min(K, n_valid). */
+        /* Order all valid blocks, keep the first min(K, n_valid). */
         qsort(pool, (size_t)n_valid, sizeof(ranked_block), rank_cmp);
         for (int k = 0; k < K; ++k) {
             if (k < n_valid) {
@@ -126,7 +143,7 @@ int oracle_index_topk_row(const oracle_cfg *cfg, const void *q_idx_row, const vo
             }
         }
     }
-    free(s);
+    free(pooled);
     free(pool);
     return 0;
 }
@@ -236,7 +253,7 @@ int oracle_dense_causal_row(const oracle_cfg *cfg, const uint16_t *q_row, const 
 /* Row-parallel drivers: a pthread pool pulling row numbers from a counter.   */
 
 typedef struct {
-    int kind; /* 0 index, 1 sparse, 2 dense */
+    int kind; /* 0 index, 1 sparse, 2 dense, 3 pooled scores */
     const oracle_cfg *cfg;
     int32_t T;
     int64_t n_stride;
@@ -245,7 +262,8 @@ typedef struct {
     const int32_t *kv_lens, *q_start, *rows_b, *rows_i, *sel_in;
     int64_t nrows;
     int32_t *sel;
-    double *scores, *out, *lse;
+    double *scores, *out, *lse, *pooled;
+    int64_t nb_out; /* pooled: blocks stored per (row, group) */
     int64_t next; /* shared row counter */
     int failed;
 } row_work;
@@ -260,12 +278,25 @@ static int run_row(row_work *w, int64_t r) {
     if (b < 0 || i < 0 || i >= w->T) return -1;
     int64_t p = (int64_t)w->q_start[b] + i;
     if (p >= w->kv_lens[b] || w->kv_lens[b] > w->n_stride) return -1;
-    if (w->kind == 0) {
+    if (w->kind == 0 || w->kind == 3) {
         int64_t es = index_elem_size(cfg);
         const char *qrow = (const char *)w->q_idx + (((int64_t)b * w->T + i) * G * dI) * es;
         const char *kseq = (const char *)w->k_idx + ((int64_t)b * w->n_stride * dI) * es;
-        return oracle_index_topk_row(cfg, qrow, kseq, p, w->sel + r * G * K,
-                                     w->scores ? w->scores + r * G * K : NULL);
+        if (w->kind == 0)
+            return oracle_index_topk_row(cfg, qrow, kseq, p, w->sel + r * G * K,
+                                         w->scores ? w->scores + r * G * K : NULL);
+        /* pooled[r, g, beta] for beta < nb_out; blocks past p are -inf. */
+        const int64_t n_valid = p / cfg->block_size + 1;
+        if (n_valid > w->nb_out) return -1;
+        double *tmp = malloc(sizeof(double) * (size_t)(G * n_valid));
+        if (!tmp) return -1;
+        int rc = oracle_index_pool_row(cfg, qrow, kseq, p, tmp);
+        for (int g = 0; g < G; ++g)
+            for (int64_t beta = 0; beta < w->nb_out; ++beta)
+                w->pooled[(r * G + g) * w->nb_out + beta] =
+                    beta < n_valid ? tmp[g * n_valid + beta] : -INFINITY;
+        free(tmp);
+        return rc;
     }
     const uint16_t *qrow = w->q + ((int64_t)b * w->T + i) * H * d;
     const uint16_t *kseq = w->k_cache + (int64_t)b * G * w->n_stride * d;
@@ -322,6 +353,17 @@ int oracle_index_topk_rows(const oracle_cfg *cfg, int32_t T, int64_t n_stride, c
     w.kind = 0; w.cfg = cfg; w.T = T; w.n_stride = n_stride; w.q_idx = q_idx; w.k_idx = k_idx;
     w.kv_lens = kv_lens; w.q_start = q_start; w.nrows = nrows; w.rows_b = rows_b;
     w.rows_i = rows_i; w.sel = sel; w.scores = scores;
+    return run_rows(&w, nthreads);
+}
+
+int oracle_index_pool_rows(const oracle_cfg *cfg, int32_t T, int64_t n_stride, const void *q_idx,
+                           const void *k_idx, const int32_t *kv_lens, const int32_t *q_start,
+                           int64_t nrows, const int32_t *rows_b, const int32_t *rows_i,
+                           int32_t nthreads, int64_t nb_out, double *pooled) {
+    row_work w = { 0 };
+    w.kind = 3; w.cfg = cfg; w.T = T; w.n_stride = n_stride; w.q_idx = q_idx; w.k_idx = k_idx;
+    w.kv_lens = kv_lens; w.q_start = q_start; w.nrows = nrows; w.rows_b = rows_b;
+    w.rows_i = rows_i; w.nb_out = nb_out; w.pooled = pooled;
     return run_rows(&w, nthreads);
 }
 

@@ -44,6 +44,14 @@ double oracle_bf16_value(uint16_t bits);
 double oracle_e4m3_value(uint8_t bits);
 
 /*
+ * Index scores and causal block max-pool for one query row at position p:
+ * writes pooled[G * (p/S + 1)], pooled[g*(p/S+1) + beta] = max of the scores
+ * of keys beta*S .. min(beta*S+S-1, p). Same argument layouts as below.
+ */
+int oracle_index_pool_row(const oracle_cfg *cfg, const void *q_idx_row, const void *k_idx_seq,
+                          int64_t p, double *pooled);
+
+/*
  * Index branch for one query row at position p (0 <= p < N):
  *   q_idx_row : [G, d_I] elements (bf16 or e4m3 per cfg->index_dtype)
  *   k_idx_seq : [N, d_I] elements of this sequence (row j = position j)
@@ -83,6 +91,12 @@ int oracle_index_topk_rows(const oracle_cfg *cfg, int32_t T, int64_t n_stride, c
                            const void *k_idx, const int32_t *kv_lens, const int32_t *q_start,
                            int64_t nrows, const int32_t *rows_b, const int32_t *rows_i,
                            int32_t nthreads, int32_t *sel, double *scores);
+
+/* pooled [nrows, G, nb_out]: blocks past the row's position are -inf. */
+int oracle_index_pool_rows(const oracle_cfg *cfg, int32_t T, int64_t n_stride, const void *q_idx,
+                           const void *k_idx, const int32_t *kv_lens, const int32_t *q_start,
+                           int64_t nrows, const int32_t *rows_b, const int32_t *rows_i,
+                           int32_t nthreads, int64_t nb_out, double *pooled);
 
 int oracle_sparse_attn_rows(const oracle_cfg *cfg, int32_t T, int64_t n_stride, const uint16_t *q,
                             const uint16_t *k_cache, const uint16_t *v_cache,

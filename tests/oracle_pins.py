@@ -144,6 +144,10 @@ def pin_hand_example_selection(orc):
     cfg4, qi, ki, *_ , kv, qs = hand_inputs(topk=4)
     sel4, _ = orc.index_topk(cfg4, qi, ki, kv, qs)
     assert sel4[7, 0, :].tolist() == g["sel_topk4_row7"]
+    pooled = orc.index_pool(cfg, qi, ki, kv, qs)
+    for t in range(8):
+        want = g["pooled"][t] + [-math.inf] * (4 - len(g["pooled"][t]))
+        assert pooled[t, 0, :].tolist() == want, (t, pooled[t, 0, :].tolist(), want)
 
 
 def pin_hand_example_attention(orc):
@@ -205,10 +209,15 @@ def pin_brute_force_selection(orc, cases=60, seed=1):
         pr = tiny_problem(rng, L, G, 1, 1, dI, S, K, index_dtype=int(case % 2))
         sel, sc = orc.index_topk(pr["cfg"], pr["qi_b"], pr["ki_b"], pr["kv_lens"],
                                  pr["q_start"])
+        pooled = orc.index_pool(pr["cfg"], pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
         for t in range(L):
             for g in range(G):
                 s_row = [sum(int(pr["qi"][0, t, g, c]) * int(pr["ki"][0, j, c])
                              for c in range(dI)) for j in range(t + 1)]
+                nb = -(-L // S)
+                want_pool = [max(s_row[b * S: min(b * S + S, t + 1)]) if b * S <= t
+                             else -math.inf for b in range(nb)]
+                assert pooled[t, g].tolist() == want_pool, (case, t, g)
                 want = brute_force_topk(s_row, t, S, K)
                 assert sel[t, g].tolist() == want, (case, t, g, sel[t, g].tolist(), want)
                 for kk, b in enumerate(want):

@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_three_entry_points():
     names = declared_functions()
-    for n in ("msa_index_topk", "msa_sparse_attn_prefill", "msa_sparse_attn_decode",
+    for n in ("msa_index_topk", "msa_index_pool", "msa_sparse_attn_prefill",
+              "msa_sparse_attn_decode", "msa_decode",
               "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_version"):
         assert n in names
 
@@ -92,6 +93,20 @@ def test_index_validation(lib):
     assert index_call(lib, c, ws=ctypes.c_void_p(0x100010), nws=need) == WORKSPACE
     assert index_call(lib, c, nws=need - 1) == WORKSPACE
     assert b"workspace" in lib.msa_last_error()
+
+
+def test_pool_validation(lib):
+    c = cfg()
+
+    def call(B=2, T=1, N=1024, qi=FAKE, ki=FAKE, kv=FAKE, pooled=FAKE, c=c):
+        return lib.msa_index_pool(ctypes.byref(c), B, T, N, qi, ki, kv, None, pooled, None)
+
+    assert call(B=0) == OK
+    assert call(pooled=None) == INVALID
+    assert call(pooled=ctypes.c_void_p(0x100002)) == INVALID
+    assert call(ki=FAKE_MIS) == INVALID
+    assert call(N=0) == INVALID
+    assert call(c=cfg(block_size=64)) == UNSUPPORTED
 
 
 def test_sparse_validation(lib):

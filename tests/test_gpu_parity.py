@@ -176,8 +176,8 @@ def test_workspace_reuse(orc):
 
 
 
-def run_fused_decode(pr, G, R, K, kv_lens, workspace=None):
-    cfg = lib_cfg(G, R, K)
+def run_fused_decode(pr, G, R, K, kv_lens, workspace=None, fp8=False):
+    cfg = lib_cfg(G, R, K, fp8)
     kv = dev_i32(kv_lens)
     qi, ki = dev_index(pr["qi"]), dev_index(pr["ki"])
     q, k, v = dev_bf16(pr["q"]), dev_bf16(pr["k"]), dev_bf16(pr["v"])
@@ -189,16 +189,19 @@ def run_fused_decode(pr, G, R, K, kv_lens, workspace=None):
             lse.cpu().numpy().astype(np.float64))
 
 
-@pytest.mark.parametrize("G,R,K,lens", [(4, 8, 16, [3000, 2999, 1, 129, 2048, 128, 0, 5000]),
-                                        (1, 2, 16, [4096]), (3, 5, 7, [700, 513]),
-                                        (2, 16, 32, [4500, 4500, 17])])
-def test_decode_step_matches_oracle_and_two_calls(orc, G, R, K, lens):
+@pytest.mark.parametrize("G,R,K,lens,fp8", [
+    (4, 8, 16, [3000, 2999, 1, 129, 2048, 128, 0, 5000], False), (1, 2, 16, [4096], False),
+    (3, 5, 7, [700, 513], False), (2, 16, 32, [4500, 4500, 17], False),
+    (4, 8, 16, [3000, 2999, 1, 129, 2048, 128, 0, 5000], True)])
+def test_decode_step_matches_oracle_and_two_calls(orc, G, R, K, lens, fp8):
     Nmax = max(max(lens), 1)
-    pr = random_problem(len(lens), 1, Nmax, G, R, seed=1000 + G + R + K)
-    sel, sc, out, lse = run_fused_decode(pr, G, R, K, lens)
+    lim = 16 if fp8 else 4
+    pr = random_problem(len(lens), 1, Nmax, G, R, seed=1000 + G + R + K + fp8, fp8=fp8,
+                        idx_lo=-lim, idx_hi=lim)
+    sel, sc, out, lse = run_fused_decode(pr, G, R, K, lens, fp8=fp8)
     kv = np.array(lens, np.int32)
     valid = kv > 0
-    ocfg = oracle_cfg(G, R, K)
+    ocfg = oracle_cfg(G, R, K, fp8)
     rows = np.array([(b, 0) for b in range(len(lens)) if valid[b]], np.int32)
     osel, osc = orc.index_topk(ocfg, pr["qi"], pr["ki"], kv, kv - 1, rows=rows)
     assert np.array_equal(sel[valid].reshape(osel.shape), osel)
@@ -209,7 +212,7 @@ def test_decode_step_matches_oracle_and_two_calls(orc, G, R, K, lens):
     compare_lse(lse[valid].reshape(olse.shape), olse, "msa_decode")
     assert (out[~valid] == 0).all() and np.isneginf(lse[~valid]).all()
     # Same bits as msa_index_topk + msa_sparse_attn_decode.
-    s2, _, o2, l2 = run_gpu(pr, G, R, K, lens, None, decode=True)
+    s2, _, o2, l2 = run_gpu(pr, G, R, K, lens, None, decode=True, fp8=fp8)
     assert np.array_equal(s2, sel) and np.array_equal(o2, out)
 
 
@@ -242,3 +245,47 @@ def test_decode_many_small_sequences(orc):
     oout, olse = orc.sparse_attn(ocfg, pr["q"], pr["k"], pr["v"], kv, kv - 1, osel)
     compare_out(out.reshape(oout.shape), oout, "many sequences")
     compare_lse(lse.reshape(olse.shape), olse, "many sequences")
+
+
+@pytest.mark.parametrize("B,T,G,N,lens,qstart", [
+    (3, 1, 4, 9000, [9000, 4100, 1], None),          # streaming kernel, one row per group
+    (2, 4, 4, 3000, [3000, 130], None),               # streaming kernel, 16 rows
+    (2, 300, 4, 1000, [1000, 400], [700, 50]),        # MFMA kernel, chunked rows
+])
+def test_index_pool_matches_oracle(orc, B, T, G, N, lens, qstart):
+    """msa_index_pool: every pooled block score equals the oracle's exactly;
+    blocks past a row's position stay as the caller filled them (-inf)."""
+    pr = random_problem(B, T, N, G, 1, seed=1300 + T)
+    cfg = lib_cfg(G, 1, 16)
+    kv = np.asarray(lens, np.int32)
+    qs = (kv - T) if qstart is None else np.asarray(qstart, np.int32)
+    say("index_pool B=%d T=%d G=%d N=%d" % (B, T, G, N))
+    pooled = msa.index_pool(cfg, dev_index(pr["qi"]), dev_index(pr["ki"]), dev_i32(kv),
+                            None if qstart is None else dev_i32(qs))
+    torch.cuda.synchronize()
+    got = pooled.cpu().numpy().astype(np.float64).reshape(B * T, G, -1)
+    want = orc.index_pool(oracle_cfg(G, 1, 16), pr["qi"], pr["ki"], kv, qs)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), int((got != want).sum())
+
+
+@pytest.mark.parametrize("B,T,N,lens,qstart,decode", [
+    (2, 300, 1000, [1000, 400], [700, 50], False),     # MFMA kernel, chunked rows
+    (1, 1100, 4500, [4500], None, False),               # several 256-row tiles, ragged tail
+    (6, 1, 3000, [3000, 2999, 1, 129, 2048, 128], None, True),  # streaming kernel
+    (2, 4, 3000, [3000, 130], None, False),             # streaming kernel, 16 rows
+])
+def test_fp8_index_matches_oracle(orc, B, T, N, lens, qstart, decode):
+    """OCP E4M3 index queries and keys (integers in [-16, 16]): selections and
+    pooled scores bit-exact, attention within tolerance."""
+    G, R, K = 4, 8, 16
+    pr = random_problem(B, T, N, G, R, seed=1500 + T + B, fp8=True, idx_lo=-16, idx_hi=16)
+    check_all_rows(orc, pr, G, R, K, lens, qstart, decode=decode, fp8=True,
+                   what="fp8 B%d T%d" % (B, T))
+    kv = np.asarray(lens, np.int32)
+    qs = (kv - T) if qstart is None else np.asarray(qstart, np.int32)
+    pooled = msa.index_pool(lib_cfg(G, R, K, True), dev_index(pr["qi"]), dev_index(pr["ki"]),
+                            dev_i32(kv), None if qstart is None else dev_i32(qs))
+    torch.cuda.synchronize()
+    want = orc.index_pool(oracle_cfg(G, R, K, True), pr["qi"], pr["ki"], kv, qs)
+    assert np.array_equal(pooled.cpu().numpy().astype(np.float64).reshape(want.shape), want)
