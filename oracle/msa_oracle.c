@@ -55,8 +55,20 @@ double oracle_e4m3_value(uint8_t bits) {
     return sign ? -mag : mag;
 }
 
+/* The 256 E4M3 values, decoded once by oracle_e4m3_value (a lookup keeps
+ * long rows fast; the values are the decoder's own). */
+static double e4m3_table[256];
+static pthread_once_t e4m3_once = PTHREAD_ONCE_INIT;
+
+static void fill_e4m3_table(void) {
+    for (int c = 0; c < 256; ++c) e4m3_table[c] = oracle_e4m3_value((uint8_t)c);
+}
+
 static double index_elem(const oracle_cfg *cfg, const void *base, int64_t i) {
-    if (cfg->index_dtype == 1) return oracle_e4m3_value(((const uint8_t *)base)[i]);
+    if (cfg->index_dtype == 1) {
+        pthread_once(&e4m3_once, fill_e4m3_table);
+        return e4m3_table[((const uint8_t *)base)[i]];
+    }
     return oracle_bf16_value(((const uint16_t *)base)[i]);
 }
 
