@@ -337,7 +337,7 @@ def main():
                      "msa_index_pool": round(res["pool_ms"], 5),
                      "msa_index_topk": round(res["idx_ms"], 5),
                      "msa_sparse_attn_decode": round(res["att_ms"], 5)},
-        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel (msa_index_pool)",
+        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel<false> (bf16 keys, via msa_index_pool)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("idx_scan_kernel", w.name),
