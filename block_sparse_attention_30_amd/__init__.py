@@ -160,9 +160,9 @@ _INDEX_DTYPES = {BF16: (torch.bfloat16,), FP8_E4M3: (torch.float8_e4m3fn, torch.
 
 
 def workspace(cfg: Config, B: int, T: int, Nmax: int, which: int, device="cuda"):
-    """A zero-filled workspace for the named call; calls leave its counter block
-    zero, so it can be reused by later calls of any shape that fit in it."""
-    return torch.zeros(max(workspace_size(cfg, B, T, Nmax, which), 256), dtype=torch.uint8,
+    """A workspace for the named call: plain scratch (no initialisation needed),
+    reusable by later calls on the same stream whose size fits in it."""
+    return torch.empty(max(workspace_size(cfg, B, T, Nmax, which), 256), dtype=torch.uint8,
                        device=device)
 
 
@@ -178,7 +178,7 @@ def _workspace(cfg, B, T, Nmax, which, device, workspace):
     if workspace is None:
         if need == 0:
             return None, 0
-        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 

@@ -69,6 +69,44 @@ IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) {
     return w;
 }
 
+int32_t prefill_entries_per_tile(int32_t R) {
+    return kPfRounds * kPfWaves * kPfNq * (16 / R);
+}
+
+PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) {
+    PrefillWs w{};
+    const int64_t G = cfg->num_kv_groups, K = cfg->topk, R = cfg->heads_per_group;
+    w.kv_major = (int64_t)B * T * G >= kPfKvMajorMinRows;
+    if (!w.kv_major || B == 0 || T == 0) return w;
+    // Largest power of two of rows whose partials fit the budget (at least 1).
+    const size_t row_bytes = (size_t)B * G * K * R * (kHeadDim * 2 + 8);
+    int64_t rows = 1;
+    // Also keep one workgroup per (sequence, row, group) within 2^24 per pass.
+    const int64_t max_units = (int64_t)1 << 24;
+    while (rows * 2 <= T && (size_t)(rows * 2) * row_bytes <= kPfPartialBudget &&
+           rows * 2 * B * G <= max_units)
+        rows *= 2;
+    if ((size_t)T * row_bytes <= kPfPartialBudget && (int64_t)T * B * G <= max_units) rows = T;
+    w.rows = (int32_t)rows;
+    w.entries_per_tile = prefill_entries_per_tile(cfg->heads_per_group);
+    w.nb_max = ((int64_t)Nmax + kBlock - 1) / kBlock;
+    w.nlists = (int64_t)B * G * w.nb_max;
+    w.nslots = (int64_t)B * rows * G * K;
+    w.max_tiles = (w.nslots + w.entries_per_tile - 1) / w.entries_per_tile + w.nlists;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
+    w.counts_off = take((size_t)w.nlists * 4);
+    w.offsets_off = take((size_t)(w.nlists + 1) * 4);
+    w.tile_first_off = take((size_t)(w.nlists + 1) * 4);
+    w.tile_map_off = take((size_t)w.max_tiles * 4);
+    w.rank_off = take((size_t)w.nslots * 4);
+    w.list_off = take((size_t)w.nslots * 4);
+    w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 2);
+    w.part_ml_off = take((size_t)w.nslots * R * 8);
+    w.total = off;
+    return w;
+}
+
 int32_t decode_splits(const msa_config *cfg) {
     return (4 * cfg->topk + kDecodeChunksPerSplit - 1) / kDecodeChunksPerSplit;
 }
@@ -143,6 +181,13 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
     if (B == 0 || T == 0) return MSA_OK;
     if ((int64_t)B * T * cfg->num_kv_groups * decode_splits(cfg) > ((int64_t)1 << 31) - 1)
         return fail(MSA_ERR_UNSUPPORTED, "too many (row, group) work items");
+    if (which == MSA_WS_SPARSE_PREFILL) {
+        const PrefillWs pw = prefill_ws(cfg, B, T, Nmax);
+        if (pw.kv_major && (pw.nlists + 1 > ((int64_t)1 << 31) - 1 ||
+                            pw.nslots * cfg->heads_per_group > ((int64_t)1 << 31) - 1 ||
+                            pw.max_tiles >= ((int64_t)1 << 24)))
+            return fail(MSA_ERR_UNSUPPORTED, "sparse prefill lists exceed 2^31 entries");
+    }
     if (!q || !k_cache || !v_cache || !kv_lens || !sel || !out)
         return fail(MSA_ERR_INVALID_ARG, "q, k_cache, v_cache, kv_lens, sel and out must not be NULL");
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
@@ -152,9 +197,7 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
         return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
     if (which == MSA_WS_SPARSE_DECODE)
         return check_ws(workspace, ws_bytes, decode_ws(cfg, B, Nmax, false).total);
-    (void)workspace;
-    (void)ws_bytes;
-    return MSA_OK;
+    return check_ws(workspace, ws_bytes, prefill_ws(cfg, B, T, Nmax).total);
 }
 
 msa_status check_decode_args(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
@@ -191,7 +234,7 @@ size_t msa_workspace_size(const msa_config *cfg, int32_t B, int32_t T, int32_t N
         case MSA_WS_INDEX_TOPK:
             return msa::index_ws(cfg, B, T, Nmax).total;
         case MSA_WS_SPARSE_PREFILL:
-            return 0;
+            return msa::prefill_ws(cfg, B, T, Nmax).total;
         case MSA_WS_SPARSE_DECODE:
             return msa::decode_ws(cfg, B, Nmax, false).total;
         case MSA_WS_DECODE:

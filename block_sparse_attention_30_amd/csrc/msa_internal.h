@@ -38,12 +38,36 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
                              size_t ws_bytes, int32_t which);
 
 // Workspace layout: the index branch (and msa_decode) keeps the pooled block
-// scores of every row, [B*T*G][ceil(Nmax/S)] fp32. The sparse calls need none.
+// scores of every row, [B*T*G][ceil(Nmax/S)] fp32.
 struct IndexWs {
     size_t pooled_off, pooled_bytes, total;
     int64_t nb_max;  // ceil(Nmax / S)
 };
 IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
+
+// Sparse prefill. Below kPfKvMajorMinRows (B*T*G) rows the query-major kernel
+// runs (no workspace). Otherwise the KV-major path works in passes of
+// `rows` query rows of every sequence, sized so that one pass's partial
+// outputs stay within kPfPartialBudget bytes. Per pass the workspace holds the
+// per-(sequence, group, block) list sizes, offsets and tile starts, the
+// tile -> list map, the rank of every (row, group, slot) in its list, the
+// lists, and per-(row, group, slot, head) partials: O / l in bf16 [d] and
+// (m, l) as two fp32.
+constexpr int64_t kPfKvMajorMinRows = 256;
+constexpr size_t kPfPartialBudget = (size_t)5 << 30;
+constexpr int kPfWaves = 4;       // waves per attention workgroup
+constexpr int kPfNq = 2;          // 16-column query tiles per wave
+constexpr int kPfRounds = 8;      // passes of every wave over its tiles per workgroup
+int32_t prefill_entries_per_tile(int32_t R);
+struct PrefillWs {
+    bool kv_major;
+    int32_t rows;  // query rows of every sequence per pass
+    int32_t entries_per_tile;
+    int64_t nb_max, nlists, nslots, max_tiles;
+    size_t counts_off, offsets_off, tile_first_off, tile_map_off, rank_off, list_off;
+    size_t part_o_off, part_ml_off, total;
+};
+PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
 
 // Decode attention: split partials [B*G][nsplit][R] x (128 + 2) fp32, after
 // the pooled scores when the call also runs the index branch (msa_decode).

@@ -935,6 +935,345 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
                        out + (bt * H + (int64_t)g * R) * D, lse ? lse + bt * H + (int64_t)g * R : nullptr);
 }
 
+// ---------------------------------------------------------------------------
+// Sparse prefill, KV-major. The dev.to summary of the M3 design (section 二)
+// makes the KV tile the outer loop: a tile is read once and serves every query
+// that needs it; [T] §六 has all heads of a group share the kept blocks. Here
+// a kept block of one group is staged in LDS once per workgroup and every
+// (row, head) that kept it attends over it there. Per pass of `rows` query
+// rows of every sequence:
+//   pf_count_kernel   each kept (row, group, slot) takes a rank in the list of
+//                     its (sequence, group, block), from an atomic counter;
+//   pf_scan_kernel    one workgroup: list offsets, tile starts (tiles of CH
+//                     entries) and the tile -> list map;
+//   pf_scatter_kernel entry (row << 5 | slot) goes to offset + rank;
+//   pf_attn_kernel    one workgroup per tile: K and V of the block in LDS,
+//                     then R heads per entry attend over its 128 keys
+//                     (16x16x32 MFMA, the chunk step of attend_chunk with
+//                     kPfNq query tiles per wave), writing a normalised partial
+//                     (O / l in bf16, m and l in fp32) per (row, group, slot);
+//   pf_merge_kernel   one workgroup per (row, group): log-sum-exp merge of the
+//                     kept slots' partials into out and lse.
+// A slot is kept when its block id is a causal block of the row (0 <= id <=
+// p/S) and no earlier slot of the row holds the same id; list order does not
+// change any result, since every partial has its own place.
+constexpr int kKRow = 272;  // staged K row bytes: 256 + 16 pad
+constexpr int kPfWaves = msa::kPfWaves;
+constexpr int kPfNq = msa::kPfNq;
+
+__device__ __forceinline__ bool slot_kept(const int32_t *sel_row, int k, int n_valid) {
+    const int blk = sel_row[k];
+    if (blk < 0 || blk >= n_valid) return false;
+    for (int k2 = 0; k2 < k; ++k2)
+        if (sel_row[k2] == blk) return false;
+    return true;
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// Row position helper shared by the pass kernels: returns p (or -1 when the
+// row is outside the cache or past T).
+__device__ __forceinline__ int pf_row_pos(const int32_t *kv_lens, const int32_t *q_start, int b,
+                                          int t, int T, int Nmax) {
+    if (t >= T) return -1;
+    const int kv = clamp_kv(kv_lens[b], Nmax);
+    const int qs = q_start ? q_start[b] : kv - T;
+    const int p = qs + t;
+    return (p >= 0 && p < kv) ? p : -1;
+}
+
+// Thread per (sequence, row of the pass, group, slot).
+__global__ __launch_bounds__(256) void pf_count_kernel(
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, int B, int T, int G, int Nmax, int K, int t0, int rows,
+    int64_t nb_max, int32_t *__restrict__ counts, int32_t *__restrict__ rank) {
+    const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (slot >= (int64_t)B * rows * G * K) return;
+    const int k = (int)(slot % K);
+    const int64_t unit = slot / K;  // (b, tl, g)
+    const int g = (int)(unit % G);
+    const int64_t btl = unit / G;
+    const int b = (int)(btl / rows), tl = (int)(btl % rows);
+    const int t = t0 + tl;
+    const int p = pf_row_pos(kv_lens, q_start, b, t, T, Nmax);
+    int r = -1;
+    if (p >= 0) {
+        const int32_t *sr = sel + (((int64_t)b * T + t) * G + g) * K;
+        if (slot_kept(sr, k, p / S + 1))
+            r = atomicAdd(&counts[((int64_t)b * G + g) * nb_max + sr[k]], 1);
+    }
+    rank[slot] = r;
+}
+
+// One workgroup of 1024 threads: exclusive scans of the list sizes and of
+// their tile counts, and the tile -> list map.
+__global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict__ counts,
+                                                       int64_t n, int ch,
+                                                       int32_t *__restrict__ offsets,
+                                                       int32_t *__restrict__ tile_first,
+                                                       int32_t *__restrict__ tile_map) {
+    __shared__ int32_t s_e[1024], s_t[1024];
+    const int tid = threadIdx.x;
+    const int64_t per = (n + 1023) / 1024;
+    const int64_t a = min(n, (int64_t)tid * per), e = min(n, a + per);
+    int32_t se = 0, st = 0;
+    for (int64_t i = a; i < e; ++i) {
+        const int32_t c = counts[i];
+        se += c;
+        st += (c + ch - 1) / ch;
+    }
+    s_e[tid] = se;
+    s_t[tid] = st;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t ve = tid >= off ? s_e[tid - off] : 0;
+        const int32_t vt = tid >= off ? s_t[tid - off] : 0;
+        __syncthreads();
+        s_e[tid] += ve;
+        s_t[tid] += vt;
+        __syncthreads();
+    }
+    int32_t oe = s_e[tid] - se, ot = s_t[tid] - st;
+    for (int64_t i = a; i < e; ++i) {
+        const int32_t c = counts[i], nt = (c + ch - 1) / ch;
+        offsets[i] = oe;
+        tile_first[i] = ot;
+        for (int32_t j = 0; j < nt; ++j) tile_map[ot + j] = (int32_t)i;
+        oe += c;
+        ot += nt;
+    }
+    if (tid == 1023) {
+        offsets[n] = s_e[1023];
+        tile_first[n] = s_t[1023];
+    }
+}
+
+__global__ __launch_bounds__(256) void pf_scatter_kernel(
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ rank,
+    const int32_t *__restrict__ offsets, int B, int T, int G, int K, int t0, int rows,
+    int64_t nb_max, int32_t *__restrict__ list) {
+    const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (slot >= (int64_t)B * rows * G * K) return;
+    const int r = rank[slot];
+    if (r < 0) return;
+    const int k = (int)(slot % K);
+    const int64_t unit = slot / K;
+    const int g = (int)(unit % G);
+    const int64_t btl = unit / G;
+    const int b = (int)(btl / rows), tl = (int)(btl % rows);
+    const int blk = sel[(((int64_t)b * T + t0 + tl) * G + g) * K + k];
+    list[offsets[((int64_t)b * G + g) * nb_max + blk] + r] = (tl << 5) | k;
+}
+
+__global__ __launch_bounds__(256) void pf_attn_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
+    const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ tile_first, const int32_t *__restrict__ tile_map,
+    const int32_t *__restrict__ list, int64_t nlists, int T, int G, int R, int Nmax, int K,
+    int t0, int rows, int64_t nb_max, int ch, float scale_log2, bf16_t *__restrict__ part_o,
+    float2 *__restrict__ part_ml) {
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[S * kKRow];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[S * kVRow];
+    const int w = blockIdx.x;
+    if (w >= tile_first[nlists]) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    const int li = tile_map[w];
+    const int beg = offsets[li] + (w - tile_first[li]) * ch;
+    const int nent = min(beg + ch, offsets[li + 1]) - beg;
+    const int64_t bg = li / nb_max;
+    const int blk = (int)(li % nb_max);
+    const int b = (int)(bg / G), g = (int)(bg % G);
+    const int H = G * R;
+    const int kv = clamp_kv(kv_lens[b], Nmax);
+    const int qs = q_start ? q_start[b] : kv - T;
+    // Stage the block: 128 K rows and 128 V rows of 256 bytes, zero past kv.
+    {
+        const bf16_t *kb = k_cache + (bg * Nmax + (int64_t)blk * S) * D;
+        const bf16_t *vb = v_cache + (bg * Nmax + (int64_t)blk * S) * D;
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        u32x4 kr[8], vr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
+            const bool in = blk * S + tk < kv;
+            kr[i] = in ? ld16(kb + (size_t)tk * D + c * 8) : z4;
+            vr[i] = in ? ld16(vb + (size_t)tk * D + c * 8) : z4;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
+            *reinterpret_cast<u32x4 *>(k_lds + tk * kKRow + c * 16) = kr[i];
+            *reinterpret_cast<u32x4 *>(v_lds + tk * kVRow + c * 16) = vr[i];
+        }
+    }
+    __syncthreads();
+    const int et = 16 / R;  // entries per 16-column query tile
+    const int tok_base = blk * S;
+    for (int round = 0;; ++round) {
+        const int e0 = (round * kPfWaves + wave) * kPfNq * et;
+        if (e0 >= nent) break;
+        // Column `col` of query tile nq: entry e0 + nq*et + col/R, head col%R.
+        int ent[kPfNq], pcol[kPfNq];
+        bf16x8 qf[kPfNq][4];
+        WaveAttn st[kPfNq];
+#pragma unroll
+        for (int nq = 0; nq < kPfNq; ++nq) {
+            const int e = e0 + nq * et + col / R;
+            const bool ok = col < et * R && e < nent;
+            ent[nq] = ok ? list[beg + e] : -1;
+            const int tl = ok ? (ent[nq] >> 5) : 0;
+            pcol[nq] = ok ? qs + t0 + tl : -1;
+            const bf16_t *qp = q + (((int64_t)b * T + t0 + tl) * H + (int64_t)g * R + col % R) * D + kg * 8;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) qf[nq][kc] = ok ? ld_bf16x8(qp + kc * 32) : zero_bf16x8();
+            wave_attn_init(st[nq]);
+        }
+#pragma unroll 1
+        for (int c = 0; c < S / 32; ++c) {
+            f32x4 sacc[kPfNq][2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                u32x4 ka[4];
+                const unsigned char *kp = k_lds + (c * 32 + rt * 16 + col) * kKRow + kg * 16;
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) ka[kc] = *reinterpret_cast<const u32x4 *>(kp + kc * 64);
+#pragma unroll
+                for (int nq = 0; nq < kPfNq; ++nq) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kc = 0; kc < 4; ++kc) acc = mfma16(as_bf16x8(ka[kc]), qf[nq][kc], acc);
+                    sacc[nq][rt] = acc;
+                }
+            }
+            bf16x8 pa[kPfNq];
+            float a_row[kPfNq][4];
+#pragma unroll
+            for (int nq = 0; nq < kPfNq; ++nq) {
+                float z[2][4];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int tok = tok_base + c * 32 + rt * 16 + 4 * kg + r;
+                        z[rt][r] = tok <= pcol[nq] ? sacc[nq][rt][r] * scale_log2 : -INFINITY;
+                        mx = fmaxf(mx, z[rt][r]);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(st[nq].m, mx);
+                const float alpha = m_new == -INFINITY ? 1.f : exp2f(st[nq].m - m_new);
+                float psum = 0.f;
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float pv = m_new == -INFINITY ? 0.f : exp2f(z[rt][r] - m_new);
+                        psum += pv;
+                        pa[nq][rt * 4 + r] = (__bf16)pv;
+                    }
+                psum += __shfl_xor(psum, 16);
+                psum += __shfl_xor(psum, 32);
+                st[nq].l = st[nq].l * alpha + psum;
+                st[nq].m = m_new;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a_row[nq][r] = __shfl(alpha, 4 * kg + r);
+            }
+            // P x V with V read transposed from LDS (same addressing as attend_chunk).
+            const unsigned char *vlo = v_lds + (c * 32 + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
+            const unsigned char *vhi = vlo + 16 * kVRow;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const u32x2 lo = lds_read_tr16(vlo + dt * 32);
+                const u32x2 hi = lds_read_tr16(vhi + dt * 32);
+                const u32x4 vbv = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int nq = 0; nq < kPfNq; ++nq) {
+                    f32x4 acc = st[nq].o[dt];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] *= a_row[nq][r];
+                    st[nq].o[dt] = mfma16(pa[nq], as_bf16x8(vbv), acc);
+                }
+            }
+        }
+        // Partials. Lane holds O rows (query columns) 4*kg + r, d = dt*16 + col;
+        // lanes 0..15 hold m and l of column `col`.
+#pragma unroll
+        for (int nq = 0; nq < kPfNq; ++nq) {
+            if (lane < 16 && ent[nq] >= 0) {
+                const int64_t slot = (((int64_t)b * rows + (ent[nq] >> 5)) * G + g) * K + (ent[nq] & 31);
+                part_ml[slot * R + col % R] = make_float2(st[nq].m, st[nq].l);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int qc = 4 * kg + r;
+                const int e_q = __shfl(ent[nq], qc);
+                const float l_q = __shfl(st[nq].l, qc);
+                if (e_q < 0) continue;
+                const int64_t slot = (((int64_t)b * rows + (e_q >> 5)) * G + g) * K + (e_q & 31);
+                bf16_t *op = part_o + (slot * R + qc % R) * D + col;
+                const float inv = 1.f / l_q;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) op[dt * 16] = to_bf16(st[nq].o[dt][r] * inv);
+            }
+        }
+    }
+}
+
+// One workgroup per (sequence, row of the pass, group).
+__global__ __launch_bounds__(256) void pf_merge_kernel(
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, const bf16_t *__restrict__ part_o,
+    const float2 *__restrict__ part_ml, int T, int G, int R, int Nmax, int K, int t0, int rows,
+    bf16_t *__restrict__ out, float *__restrict__ lse) {
+    __shared__ int32_t s_sel[KMAX];
+    __shared__ int32_t s_keep[KMAX];
+    const int tid = threadIdx.x;
+    const int64_t unit = blockIdx.x;  // (b, tl, g)
+    const int g = (int)(unit % G);
+    const int64_t btl = unit / G;
+    const int b = (int)(btl / rows), tl = (int)(btl % rows);
+    const int t = t0 + tl;
+    if (t >= T) return;
+    const int p = pf_row_pos(kv_lens, q_start, b, t, T, Nmax);
+    if (tid < K) s_sel[tid] = p >= 0 ? sel[(((int64_t)b * T + t) * G + g) * K + tid] : -1;
+    __syncthreads();
+    if (tid < K) s_keep[tid] = p >= 0 && slot_kept(s_sel, tid, p / S + 1);
+    __syncthreads();
+    const int H = G * R;
+    const int64_t slot0 = unit * K;
+    for (int idx = tid; idx < R * (D / 4); idx += 256) {
+        const int r = idx / (D / 4), d0 = (idx % (D / 4)) * 4;
+        float M = -INFINITY;
+        for (int k = 0; k < K; ++k)
+            if (s_keep[k]) M = fmaxf(M, part_ml[(slot0 + k) * R + r].x);
+        float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < K; ++k) {
+            if (!s_keep[k]) continue;
+            const float2 ml = part_ml[(slot0 + k) * R + r];
+            const float wk = exp2f(ml.x - M) * ml.y;
+            L += wk;
+            const u32x2 ov = *reinterpret_cast<const u32x2 *>(part_o + ((slot0 + k) * R + r) * D + d0);
+            acc[0] += wk * __uint_as_float(ov[0] << 16);
+            acc[1] += wk * __uint_as_float(ov[0] & 0xFFFF0000u);
+            acc[2] += wk * __uint_as_float(ov[1] << 16);
+            acc[3] += wk * __uint_as_float(ov[1] & 0xFFFF0000u);
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        bf16_t *op = out + (((int64_t)b * T + t) * H + (int64_t)g * R + r) * D + d0;
+        const uint32_t lo = (uint32_t)to_bf16(acc[0] * inv) | ((uint32_t)to_bf16(acc[1] * inv) << 16);
+        const uint32_t hi = (uint32_t)to_bf16(acc[2] * inv) | ((uint32_t)to_bf16(acc[3] * inv) << 16);
+        *reinterpret_cast<u32x2 *>(op) = u32x2{lo, hi};
+        if (lse && d0 == 0)
+            lse[((int64_t)b * T + t) * H + (int64_t)g * R + r] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+    }
+}
+
 // Decode: the new token of sequence b sits at position kv - 1. Group g's
 // kept blocks give 4*nblk 32-token chunks; workgroup (b, g, split) has eight
 // waves and takes chunks [8*split, 8*split + 8), one per wave, so every load
@@ -1181,13 +1520,47 @@ msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, 
                                           sel, out, lse, workspace, ws_bytes,
                                           MSA_WS_SPARSE_PREFILL);
     if (s != MSA_OK || B == 0 || T == 0) return s;
-    const int64_t units = (int64_t)B * T * cfg->num_kv_groups;
-    sparse_attn_kernel<<<(unsigned)units, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
-        static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k_cache),
-        static_cast<const bf16_t *>(v_cache), kv_lens, q_start, sel, T, cfg->num_kv_groups,
-        cfg->heads_per_group, Nmax, cfg->topk, scale_log2_of(cfg), static_cast<bf16_t *>(out),
-        lse);
-    return launch_status("sparse attention kernel");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int G = cfg->num_kv_groups, R = cfg->heads_per_group, K = cfg->topk;
+    const float sl2 = scale_log2_of(cfg);
+    const bf16_t *qp = static_cast<const bf16_t *>(q);
+    const bf16_t *kp = static_cast<const bf16_t *>(k_cache);
+    const bf16_t *vp = static_cast<const bf16_t *>(v_cache);
+    bf16_t *op = static_cast<bf16_t *>(out);
+    const msa::PrefillWs w = msa::prefill_ws(cfg, B, T, Nmax);
+    if (!w.kv_major) {
+        const int64_t units = (int64_t)B * T * G;
+        sparse_attn_kernel<<<(unsigned)units, 256, 0, st>>>(qp, kp, vp, kv_lens, q_start, sel, T,
+                                                           G, R, Nmax, K, sl2, op, lse);
+        return launch_status("sparse attention kernel");
+    }
+    char *base = static_cast<char *>(workspace);
+    int32_t *counts = reinterpret_cast<int32_t *>(base + w.counts_off);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + w.offsets_off);
+    int32_t *tile_first = reinterpret_cast<int32_t *>(base + w.tile_first_off);
+    int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.tile_map_off);
+    int32_t *rank = reinterpret_cast<int32_t *>(base + w.rank_off);
+    int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
+    bf16_t *part_o = reinterpret_cast<bf16_t *>(base + w.part_o_off);
+    float2 *part_ml = reinterpret_cast<float2 *>(base + w.part_ml_off);
+    const unsigned slot_blocks = (unsigned)((w.nslots + 255) / 256);
+    for (int32_t t0 = 0; t0 < T; t0 += w.rows) {
+        fill_i32_kernel<<<(unsigned)((w.nlists + 255) / 256), 256, 0, st>>>(counts, w.nlists, 0);
+        pf_count_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
+                                                     w.rows, w.nb_max, counts, rank);
+        pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets,
+                                           tile_first, tile_map);
+        pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, rank, offsets, B, T, G, K, t0, w.rows,
+                                                       w.nb_max, list);
+        pf_attn_kernel<<<(unsigned)w.max_tiles, 256, 0, st>>>(
+            qp, kp, vp, kv_lens, q_start, offsets, tile_first, tile_map, list, w.nlists, T, G, R,
+            Nmax, K, t0, w.rows, w.nb_max, w.entries_per_tile, sl2, part_o, part_ml);
+        pf_merge_kernel<<<(unsigned)((int64_t)B * w.rows * G), 256, 0, st>>>(
+            sel, kv_lens, q_start, part_o, part_ml, T, G, R, Nmax, K, t0, w.rows, op, lse);
+        s = launch_status("sparse prefill kernels");
+        if (s != MSA_OK) return s;
+    }
+    return MSA_OK;
 }
 
 // Split partials of msa_sparse_attn_decode and msa_decode: sparse_decode_kernel

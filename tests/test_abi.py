@@ -115,7 +115,7 @@ def test_sparse_validation(lib):
 
     def prefill(**kw):
         a = {**args, **kw}
-        return lib.msa_sparse_attn_prefill(ctypes.byref(kw.get("c", c)), 1, 64, 1024, a["q"],
+        return lib.msa_sparse_attn_prefill(ctypes.byref(kw.get("c", c)), 1, 32, 1024, a["q"],
                                            a["k"], a["v"], a["kv"], a["qs"], a["sel"],
                                            a["out"], a["lse"], None, 0, None)
 
@@ -128,6 +128,9 @@ def test_sparse_validation(lib):
     assert prefill(out=FAKE_MIS) == INVALID
     assert prefill(lse=ctypes.c_void_p(0x100001)) == INVALID
     assert prefill(c=cfg(heads_per_group=32)) == UNSUPPORTED
+    # 64 rows x 4 groups takes the KV-major path, which needs a workspace.
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), 1, 64, 1024, FAKE, FAKE, FAKE, FAKE,
+                                       None, FAKE, FAKE, None, None, 0, None) == WORKSPACE
     assert decode(sel=None) == INVALID
     assert decode(v=FAKE_MIS) == INVALID
     assert decode() == WORKSPACE  # split partials need a workspace
@@ -156,7 +159,9 @@ def test_workspace_sizes_follow_shapes(lib):
     c = cfg()
     a = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 0)
     assert a >= 16 * 4 * 1024 * 4 and a % 256 == 0          # pooled block scores
-    assert lib.msa_workspace_size(ctypes.byref(c), 1, 64, 1024, 1) == 0   # sparse: none
+    assert lib.msa_workspace_size(ctypes.byref(c), 1, 63, 1024, 1) == 0   # query-major: none
+    pf = lib.msa_workspace_size(ctypes.byref(c), 1, 64, 1024, 1)           # KV-major lists
+    assert pf >= 64 * 4 * 16 * 8 * 128 * 2 and pf % 256 == 0
     d = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 2)  # split partials
     assert d >= 16 * 4 * 2 * 8 * 130 * 4 and d % 256 == 0
     assert lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 3) == a + d
