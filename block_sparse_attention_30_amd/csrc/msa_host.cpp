@@ -64,7 +64,11 @@ IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) {
     IndexWs w{};
     w.nb_max = ((int64_t)Nmax + kBlock - 1) / kBlock;
     w.pooled_off = 0;
-    w.pooled_bytes = (size_t)B * (size_t)T * (size_t)cfg->num_kv_groups * (size_t)w.nb_max * 4;
+    // Only the streaming (decode) path keeps pooled scores; the prefill kernel
+    // ranks rows in registers.
+    const bool scan = (int64_t)T * cfg->num_kv_groups <= kScanMaxRows;
+    w.pooled_bytes =
+        scan ? (size_t)B * (size_t)T * (size_t)cfg->num_kv_groups * (size_t)w.nb_max * 4 : 0;
     w.total = round_up(w.pooled_bytes, kWsAlign);
     return w;
 }

@@ -37,8 +37,9 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
                              const void *out, const float *lse, const void *workspace,
                              size_t ws_bytes, int32_t which);
 
-// Workspace layout: the index branch (and msa_decode) keeps the pooled block
-// scores of every row, [B*T*G][ceil(Nmax/S)] fp32.
+// Workspace layout: the streaming index path (T*G <= kScanMaxRows, and
+// msa_decode) keeps the pooled block scores of every row, [B*T*G][ceil(Nmax/S)]
+// fp32. The prefill index path needs none.
 struct IndexWs {
     size_t pooled_off, pooled_bytes, total;
     int64_t nb_max;  // ceil(Nmax / S)

@@ -17,14 +17,17 @@
 //   topk_rows_kernel     one wavefront per row: bitonic sorts of 64-bit keys
 //                        (score, inverted block id) across lanes plus
 //                        compaction of candidates above a threshold.
-//   idx_prefill_kernel   prefill index scores: 32x32x16 bf16 MFMA over a
-//                        256-row tile with the k_idx block staged in LDS;
-//                        block max-pool in the epilogue.
-//   topk_kernel          (prefill) one workgroup per row.
-//   sparse_attn_kernel   (prefill) one workgroup per (row, group): gathers the
-//                        kept 128-token K/V blocks, serves all R heads of the
-//                        group with 16x16x32 MFMA (QK^T and PV) and an online
-//                        fp32 softmax.
+//   idx_prefill_kernel   prefill index scores: 32x32x16 bf16 (or 32x32x64
+//                        E4M3) MFMA over a 256-row tile with the k_idx block
+//                        staged in LDS; block max-pool and a per-row running
+//                        top-K in registers in the epilogue.
+//   sparse_attn_kernel   (small prefill) one workgroup per (row, group):
+//                        gathers the kept 128-token K/V blocks, serves all R
+//                        heads of the group with 16x16x32 MFMA (QK^T and PV)
+//                        and an online fp32 softmax.
+//   pf_*_kernel          (prefill) KV-major sparse attention: per-block entry
+//                        lists, one staged block per workgroup serving every
+//                        (row, head) that kept it, log-sum-exp merge.
 //   sparse_decode_kernel (decode) one 8-wave workgroup per (sequence, group,
 //                        split), one 32-token chunk per wave; optionally ranks
 //                        the row's blocks itself; waves merge in LDS into a
@@ -453,11 +456,32 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(
 // 32x32x64 f8f6f4 MFMAs with unit scales (2 per row tile and column tile).
 constexpr int kPfRows = 256;
 
-template <bool F8>
+// Running top-KC of one row in registers, for blocks offered in ascending id
+// order: ts/tb are sorted by score, descending; a new block goes after every
+// kept block of equal score (a lower id ranks first). Branch-free: slot i
+// keeps its entry, takes the new one, or takes slot i-1's old entry.
+template <int KC>
+__device__ __forceinline__ void topk_insert(float (&ts)[KC], int (&tb)[KC], float xs, int xb) {
+#pragma unroll
+    for (int i = KC - 1; i >= 0; --i) {
+        const bool keep = ts[i] >= xs;
+        const bool prev_ge = i == 0 || ts[i > 0 ? i - 1 : 0] >= xs;
+        const float ps = i > 0 ? ts[i - 1] : xs;
+        const int pb = i > 0 ? tb[i - 1] : xb;
+        ts[i] = keep ? ts[i] : (prev_ge ? xs : ps);
+        tb[i] = keep ? tb[i] : (prev_ge ? xb : pb);
+    }
+}
+
+// KC = 0: pooled block scores are written out. KC = 16 or 32: every lane owns
+// one row, keeps its top-KC blocks in registers while the blocks stream by,
+// and writes sel / sel_scores (first K) at the end; no pooled scores.
+template <bool F8, int KC>
 __global__ __launch_bounds__(256) void idx_prefill_kernel(
     const unsigned char *__restrict__ q_idx, const unsigned char *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
-    float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max) {
+    float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int K,
+    int32_t *__restrict__ sel, float *__restrict__ sel_scores) {
     constexpr int kRowBytes = DI * (F8 ? 1 : 2);
     constexpr int kRow = kRowBytes + 16;
     constexpr int kPieces = S * kRowBytes / 16 / 256;  // 16-byte loads per thread per block
@@ -471,9 +495,9 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
     const int qs = q_start ? q_start[b] : kv - T;
     const int r_last = min(r0 + kPfRows, rows) - 1;
     const int p_hi = min(qs + r_last / G, kv - 1);
-    if (p_hi < 0) return;
+    if (KC == 0 && p_hi < 0) return;
     const int p_lo = qs + r0 / G;
-    const int nblk = p_hi / S + 1;
+    const int nblk = p_hi >= 0 ? p_hi / S + 1 : 0;
 
     const int j = lane & 31, half = lane >> 5;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -495,196 +519,110 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
             for (int h = 0; h < (F8 ? 2 : 1); ++h)
                 qb[ct][ks][h] = ok ? ld16(qp + ks * kKb + half * (kKb / 2) + 16 * h) : zero4;
     }
+    constexpr int KCS = KC > 0 ? KC : 1;
+    float ts[KCS];
+    int tb[KCS];
+#pragma unroll
+    for (int i = 0; i < KCS; ++i) {
+        ts[i] = -INFINITY;
+        tb[i] = -1;
+    }
     const unsigned char *kseq = k_idx + (size_t)b * Nmax * kRowBytes;
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int tok0 = blk * S;
-        __syncthreads();
+    // The next block's k_idx rows are loaded into registers while the current
+    // block is being used from LDS.
+    u32x4 pre[kPieces];
+    // Loads are unconditional (clamped to the last key, kv >= 1 whenever a
+    // block exists) and tokens past kv are zeroed afterwards.
+    auto load_block = [&](int blk) {
 #pragma unroll
         for (int i = 0; i < kPieces; ++i) {
             const int piece = tid + 256 * i;
             const int tk = piece / (kRowBytes / 16), c = piece % (kRowBytes / 16);
-            const int tok = tok0 + tk;
-            const u32x4 v = tok < kv ? ld16(kseq + (size_t)tok * kRowBytes + c * 16) : zero4;
-            *reinterpret_cast<u32x4 *>(lds + tk * kRow + c * 16) = v;
+            const int tok = blk * S + tk;
+            pre[i] = ld16(kseq + (size_t)min(tok, kv - 1) * kRowBytes + c * 16);
+            if (tok >= kv) pre[i] = zero4;
         }
-        __syncthreads();
+    };
+    if (nblk > 0) load_block(0);
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int tok0 = blk * S;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+        __builtin_amdgcn_s_barrier();        // ... and every other wave's
+#pragma unroll
+        for (int i = 0; i < kPieces; ++i) {
+            const int piece = tid + 256 * i;
+            const int tk = piece / (kRowBytes / 16), c = piece % (kRowBytes / 16);
+            *reinterpret_cast<u32x4 *>(lds + tk * kRow + c * 16) = pre[i];
+        }
+        if (blk + 1 < nblk) load_block(blk + 1);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block's LDS rows are written
+        __builtin_amdgcn_s_barrier();
         const bool need_mask = tok0 + S - 1 > p_lo;
         float cm0 = -INFINITY, cm1 = -INFINITY;
+        // Two row tiles at a time: four independent accumulator chains.
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            f32x16 acc0 = {}, acc1 = {};
+        for (int rp = 0; rp < 2; ++rp) {
+            f32x16 acc[2][2] = {};
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks) {
-                const unsigned char *ap = lds + (rt * 32 + j) * kRow + ks * kKb + half * (kKb / 2);
-                if constexpr (F8) {
-                    const i32x8 a = cat_i32x8(*reinterpret_cast<const u32x4 *>(ap),
-                                              *reinterpret_cast<const u32x4 *>(ap + 16));
-                    acc0 = mfma32_f8(a, cat_i32x8(qb[0][ks][0], qb[0][ks][F8 ? 1 : 0]), acc0);
-                    acc1 = mfma32_f8(a, cat_i32x8(qb[1][ks][0], qb[1][ks][F8 ? 1 : 0]), acc1);
-                } else {
-                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap));
-                    acc0 = mfma32(a, as_bf16x8(qb[0][ks][0]), acc0);
-                    acc1 = mfma32(a, as_bf16x8(qb[1][ks][0]), acc1);
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int rt = 2 * rp + h2;
+                    const unsigned char *ap = lds + (rt * 32 + j) * kRow + ks * kKb + half * (kKb / 2);
+                    if constexpr (F8) {
+                        const i32x8 a = cat_i32x8(*reinterpret_cast<const u32x4 *>(ap),
+                                                  *reinterpret_cast<const u32x4 *>(ap + 16));
+                        acc[h2][0] = mfma32_f8(a, cat_i32x8(qb[0][ks][0], qb[0][ks][F8 ? 1 : 0]), acc[h2][0]);
+                        acc[h2][1] = mfma32_f8(a, cat_i32x8(qb[1][ks][0], qb[1][ks][F8 ? 1 : 0]), acc[h2][1]);
+                    } else {
+                        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap));
+                        acc[h2][0] = mfma32(a, as_bf16x8(qb[0][ks][0]), acc[h2][0]);
+                        acc[h2][1] = mfma32(a, as_bf16x8(qb[1][ks][0]), acc[h2][1]);
+                    }
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int tok = tok0 + rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                float s0 = acc0[i], s1 = acc1[i];
-                if (need_mask) {
-                    if (tok > pcol[0]) s0 = -INFINITY;
-                    if (tok > pcol[1]) s1 = -INFINITY;
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int rt = 2 * rp + h2;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int tok = tok0 + rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    float s0 = acc[h2][0][i], s1 = acc[h2][1][i];
+                    if (need_mask) {
+                        if (tok > pcol[0]) s0 = -INFINITY;
+                        if (tok > pcol[1]) s1 = -INFINITY;
+                    }
+                    cm0 = fmaxf(cm0, s0);
+                    cm1 = fmaxf(cm1, s1);
                 }
-                cm0 = fmaxf(cm0, s0);
-                cm1 = fmaxf(cm1, s1);
             }
         }
         cm0 = fmaxf(cm0, __shfl_xor(cm0, 32));
         cm1 = fmaxf(cm1, __shfl_xor(cm1, 32));
-        const float v = half ? cm1 : cm0;
+        const float v = (half ? cm1 : cm0) + 0.0f;
         const int pc = half ? pcol[1] : pcol[0];
+        if constexpr (KC == 0) {
+            const int r = r0 + 64 * wave + 32 * half + j;
+            if (pc >= tok0) pooled[((size_t)b * rows + r) * nb_max + blk] = v;
+        } else {
+            const bool offer = pc >= tok0 && v > ts[KC - 1];
+            if (__ballot(offer)) {
+                if (offer) topk_insert<KC>(ts, tb, v, blk);
+            }
+        }
+    }
+    if constexpr (KC > 0) {
         const int r = r0 + 64 * wave + 32 * half + j;
-        if (pc >= tok0) pooled[((size_t)b * rows + r) * nb_max + blk] = v + 0.0f;
-    }
-}
-
-// ---------------------------------------------------------------------------
-constexpr int kTopkPerThread = 32;  // candidates per thread loaded together
-
-// One workgroup (4 waves) per row (b, t, g); K <= 32.
-//   Pass 1: every thread takes the best key of its strided share of the
-//           row's n = p/S + 1 pooled scores; each wave sorts its 64 thread
-//           maxima and wave 0 merges the four top-K lists. These K keys are a
-//           valid running top-K and the K-th is a threshold below which no
-//           key can enter.
-//   Pass 2: keys above the threshold that are not their thread's maximum
-//           (those were ranked in pass 1) are appended to an LDS list; wave 0
-//           merges the list into the top-K, 64 - K keys at a time.
-// On random scores pass 2 finds only a few keys. If more than 256 keys pass
-// the threshold, wave 0 instead streams the whole row through the same
-// merge, starting from an empty list (correct for any input, just slower).
-__global__ __launch_bounds__(256) void topk_kernel(
-    const float *__restrict__ pooled, int64_t nb_max, const int32_t *__restrict__ kv_lens,
-    const int32_t *__restrict__ q_start, int B, int T, int G, int Nmax, int K,
-    int32_t *__restrict__ sel, float *__restrict__ sel_scores) {
-    __shared__ uint64_t s_top[4][msa::kMaxTopk];
-    __shared__ uint64_t s_list[256];
-    __shared__ int s_cnt;
-    __shared__ uint64_t s_thr;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t row = blockIdx.x;
-    const int rows = T * G;
-    const int b = (int)(row / rows);
-    const int t = (int)(row % rows) / G;
-    const int kv = clamp_kv(kv_lens[b], Nmax);
-    const int qs = q_start ? q_start[b] : kv - T;
-    const int p = qs + t;
-    int32_t *out = sel + row * K;
-    float *outs = sel_scores ? sel_scores + row * K : nullptr;
-    if (p < 0 || p >= kv) {
-        if (tid < K) {
-            out[tid] = -1;
-            if (outs) outs[tid] = -INFINITY;
-        }
-        return;
-    }
-    const int n = p / S + 1;
-    const float *cand = pooled + row * nb_max;
-
-    uint64_t tmax = 0;
-    for (int base = 0; base < n; base += 256 * kTopkPerThread) {
-        float v[kTopkPerThread];
+        if (r < rows) {
+            const size_t o = ((size_t)b * rows + r) * K;
 #pragma unroll
-        for (int c = 0; c < kTopkPerThread; ++c) {
-            const int i = base + c * 256 + tid;
-            v[c] = i < n ? cand[i] : 0.f;
-        }
-#pragma unroll
-        for (int c = 0; c < kTopkPerThread; ++c) {
-            const int i = base + c * 256 + tid;
-            const uint64_t k = i < n ? score_key(v[c], i) : 0;
-            tmax = k > tmax ? k : tmax;
-        }
-    }
-    const uint64_t srt = wave_sort_desc(tmax, lane);
-    if (lane < K) s_top[wave][lane] = srt;
-    if (tid == 0) s_cnt = 0;
-    __syncthreads();
-    if (wave == 0) {
-        uint64_t cur = lane < K ? s_top[0][lane] : 0;
-#pragma unroll 1
-        for (int w = 1; w < 4; ++w) {
-            uint64_t x = lane < K ? cur : (lane < 2 * K ? s_top[w][lane - K] : 0);
-            x = wave_sort_desc(x, lane);
-            cur = lane < K ? x : 0;
-        }
-        if (lane < K) s_top[0][lane] = cur;
-        if (lane == K - 1) s_thr = cur;
-    }
-    __syncthreads();
-    const uint64_t thr = s_thr;
-    for (int base = 0; base < n; base += 256 * kTopkPerThread) {
-        float v[kTopkPerThread];
-#pragma unroll
-        for (int c = 0; c < kTopkPerThread; ++c) {
-            const int i = base + c * 256 + tid;
-            v[c] = i < n ? cand[i] : 0.f;
-        }
-#pragma unroll
-        for (int c = 0; c < kTopkPerThread; ++c) {
-            const int i = base + c * 256 + tid;
-            const uint64_t k = i < n ? score_key(v[c], i) : 0;
-            if (k > thr && k != tmax) {
-                const int pos = atomicAdd(&s_cnt, 1);
-                if (pos < 256) s_list[pos] = k;
+            for (int i = 0; i < KC; ++i) {
+                if (i < K) {
+                    sel[o + i] = tb[i];
+                    if (sel_scores) sel_scores[o + i] = ts[i];
+                }
             }
         }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    const int cnt = s_cnt;
-    const int cap = 64 - K;
-    uint64_t top;
-    if (cnt <= 256) {
-        top = lane < K ? s_top[0][lane] : 0;
-#pragma unroll 1
-        for (int off = 0; off < cnt; off += cap) {
-            uint64_t x = lane < K ? top : (lane - K + off < cnt ? s_list[lane - K + off] : 0);
-            x = wave_sort_desc(x, lane);
-            top = lane < K ? x : 0;
-        }
-    } else {
-        // Streaming fallback: rounds of 64 keys, merged whenever the round
-        // holds keys above the current K-th best.
-        top = 0;
-        uint64_t kth = 0;
-        const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll 1
-        for (int base = 0; base < n; base += 64) {
-            const int i = base + lane;
-            const uint64_t kk = i < n ? score_key(cand[i], i) : 0;
-            bool q = kk > kth;
-            uint64_t qm = __ballot(q);
-            while (qm) {
-                const int rank = __popcll(qm & below);
-                const bool take = q && rank < cap;
-                if (take) s_list[rank] = kk;
-                const int nt = __popcll(qm) < cap ? __popcll(qm) : cap;
-                __builtin_amdgcn_s_waitcnt(0xC07F);
-                __builtin_amdgcn_wave_barrier();
-                uint64_t x = lane < K ? top : (lane - K < nt ? s_list[lane - K] : 0);
-                x = wave_sort_desc(x, lane);
-                top = lane < K ? x : 0;
-                kth = shfl_u64(x, K - 1);
-                __builtin_amdgcn_wave_barrier();
-                q = q && !take && kk > kth;
-                qm = __ballot(q);
-            }
-        }
-    }
-    if (lane < K) {
-        out[lane] = top ? key_block(top) : -1;
-        if (outs) outs[lane] = top ? key_score(top) : -INFINITY;
     }
 }
 
@@ -1462,11 +1400,11 @@ msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nm
     }
     const dim3 grid((unsigned)((rows + kPfRows - 1) / kPfRows), (unsigned)B);
     if (f8)
-        idx_prefill_kernel<true><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
-                                                       Nmax, nb_max);
+        idx_prefill_kernel<true, 0><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
+                                                          Nmax, nb_max, 0, nullptr, nullptr);
     else
-        idx_prefill_kernel<false><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
-                                                        Nmax, nb_max);
+        idx_prefill_kernel<false, 0><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
+                                                           Nmax, nb_max, 0, nullptr, nullptr);
     return launch_status("prefill index kernel");
 }
 
@@ -1483,19 +1421,31 @@ msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t N
                                          sel_scores, workspace, ws_bytes);
     if (s != MSA_OK || B == 0 || T == 0) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int G = cfg->num_kv_groups, K = cfg->topk;
+    if (T * G > msa::kScanMaxRows) {
+        // Prefill: scores, block max and the row's top-K in one kernel.
+        const bool f8 = cfg->index_dtype == MSA_FP8_E4M3;
+        const unsigned char *qi = static_cast<const unsigned char *>(q_idx);
+        const unsigned char *ki = static_cast<const unsigned char *>(k_idx);
+        const int64_t nbm = ((int64_t)Nmax + S - 1) / S;
+        const dim3 grid((unsigned)(((int64_t)T * G + kPfRows - 1) / kPfRows), (unsigned)B);
+#define MSA_IDX_PREFILL(F8_, KC_)                                                              \
+    idx_prefill_kernel<F8_, KC_><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, nullptr, T, G, \
+                                                       Nmax, nbm, K, sel, sel_scores)
+        if (f8 && K <= 16) MSA_IDX_PREFILL(true, 16);
+        else if (f8) MSA_IDX_PREFILL(true, 32);
+        else if (K <= 16) MSA_IDX_PREFILL(false, 16);
+        else MSA_IDX_PREFILL(false, 32);
+#undef MSA_IDX_PREFILL
+        return launch_status("prefill index kernel");
+    }
     const msa::IndexWs w = msa::index_ws(cfg, B, T, Nmax);
     float *pooled = reinterpret_cast<float *>(static_cast<char *>(workspace) + w.pooled_off);
     s = launch_pooled(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start, pooled, w.nb_max, st);
     if (s != MSA_OK) return s;
-    const int G = cfg->num_kv_groups;
     const int64_t nrows = (int64_t)B * T * G;
-    if (T * G <= msa::kScanMaxRows) {
-        topk_rows_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(
-            pooled, w.nb_max, kv_lens, q_start, B, T, G, Nmax, cfg->topk, sel, sel_scores);
-    } else {
-        topk_kernel<<<(unsigned)nrows, 256, 0, st>>>(pooled, w.nb_max, kv_lens, q_start, B, T, G,
-                                                    Nmax, cfg->topk, sel, sel_scores);
-    }
+    topk_rows_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(
+        pooled, w.nb_max, kv_lens, q_start, B, T, G, Nmax, K, sel, sel_scores);
     return launch_status("top-k kernel");
 }
 
