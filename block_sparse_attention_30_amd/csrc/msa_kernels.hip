@@ -1006,7 +1006,7 @@ __global__ __launch_bounds__(256) void pf_scatter_kernel(
     list[offsets[((int64_t)b * G + g) * nb_max + blk] + r] = (tl << 5) | k;
 }
 
-__global__ __launch_bounds__(256) void pf_attn_kernel(
+__global__ __launch_bounds__(256, 2) void pf_attn_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
     const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const int32_t *__restrict__ offsets,
@@ -1052,13 +1052,12 @@ __global__ __launch_bounds__(256) void pf_attn_kernel(
     __syncthreads();
     const int et = 16 / R;  // entries per 16-column query tile
     const int tok_base = blk * S;
-    for (int round = 0;; ++round) {
-        const int e0 = (round * kPfWaves + wave) * kPfNq * et;
-        if (e0 >= nent) break;
-        // Column `col` of query tile nq: entry e0 + nq*et + col/R, head col%R.
-        int ent[kPfNq], pcol[kPfNq];
-        bf16x8 qf[kPfNq][4];
-        WaveAttn st[kPfNq];
+    // Column `col` of query tile nq in a round: entry e0 + nq*et + col/R, head
+    // col%R. The next round's entries and queries are loaded while the
+    // current round computes.
+    int ent[kPfNq], pcol[kPfNq];
+    bf16x8 qf[kPfNq][4];
+    auto load_round = [&](int e0) {
 #pragma unroll
         for (int nq = 0; nq < kPfNq; ++nq) {
             const int e = e0 + nq * et + col / R;
@@ -1066,63 +1065,88 @@ __global__ __launch_bounds__(256) void pf_attn_kernel(
             ent[nq] = ok ? list[beg + e] : -1;
             const int tl = ok ? (ent[nq] >> 5) : 0;
             pcol[nq] = ok ? qs + t0 + tl : -1;
-            const bf16_t *qp = q + (((int64_t)b * T + t0 + tl) * H + (int64_t)g * R + col % R) * D + kg * 8;
+            const bf16_t *qp =
+                q + (((int64_t)b * T + t0 + tl) * H + (int64_t)g * R + col % R) * D + kg * 8;
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) qf[nq][kc] = ok ? ld_bf16x8(qp + kc * 32) : zero_bf16x8();
-            wave_attn_init(st[nq]);
         }
-#pragma unroll 1
-        for (int c = 0; c < S / 32; ++c) {
-            f32x4 sacc[kPfNq][2];
+    };
+    const int round_step = kPfWaves * kPfNq * et;
+    int e0 = wave * kPfNq * et;
+    if (e0 < nent) load_round(e0);
+    for (; e0 < nent; e0 += round_step) {
+        // S^T for the whole block: key tile kt (16 keys) x 16 query columns;
+        // lane holds column `col`, keys kt*16 + 4*kg + r.
+        f32x4 sacc[kPfNq][8];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                u32x4 ka[4];
-                const unsigned char *kp = k_lds + (c * 32 + rt * 16 + col) * kKRow + kg * 16;
+        for (int kt = 0; kt < 8; ++kt) {
+            u32x4 ka[4];
+            const unsigned char *kp = k_lds + (kt * 16 + col) * kKRow + kg * 16;
 #pragma unroll
-                for (int kc = 0; kc < 4; ++kc) ka[kc] = *reinterpret_cast<const u32x4 *>(kp + kc * 64);
-#pragma unroll
-                for (int nq = 0; nq < kPfNq; ++nq) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kc = 0; kc < 4; ++kc) acc = mfma16(as_bf16x8(ka[kc]), qf[nq][kc], acc);
-                    sacc[nq][rt] = acc;
-                }
-            }
-            bf16x8 pa[kPfNq];
-            float a_row[kPfNq][4];
+            for (int kc = 0; kc < 4; ++kc) ka[kc] = *reinterpret_cast<const u32x4 *>(kp + kc * 64);
 #pragma unroll
             for (int nq = 0; nq < kPfNq; ++nq) {
-                float z[2][4];
-                float mx = -INFINITY;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int tok = tok_base + c * 32 + rt * 16 + 4 * kg + r;
-                        z[rt][r] = tok <= pcol[nq] ? sacc[nq][rt][r] * scale_log2 : -INFINITY;
-                        mx = fmaxf(mx, z[rt][r]);
-                    }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(st[nq].m, mx);
-                const float alpha = m_new == -INFINITY ? 1.f : exp2f(st[nq].m - m_new);
-                float psum = 0.f;
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float pv = m_new == -INFINITY ? 0.f : exp2f(z[rt][r] - m_new);
-                        psum += pv;
-                        pa[nq][rt * 4 + r] = (__bf16)pv;
-                    }
-                psum += __shfl_xor(psum, 16);
-                psum += __shfl_xor(psum, 32);
-                st[nq].l = st[nq].l * alpha + psum;
-                st[nq].m = m_new;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) a_row[nq][r] = __shfl(alpha, 4 * kg + r);
+                for (int kc = 0; kc < 4; ++kc) acc = mfma16(as_bf16x8(ka[kc]), qf[nq][kc], acc);
+                sacc[nq][kt] = acc;
             }
-            // P x V with V read transposed from LDS (same addressing as attend_chunk).
+        }
+        // The queries are no longer needed: load the next round's now.
+        int cent[kPfNq], cpcol[kPfNq];
+#pragma unroll
+        for (int nq = 0; nq < kPfNq; ++nq) {
+            cent[nq] = ent[nq];
+            cpcol[nq] = pcol[nq];
+        }
+        if (e0 + round_step < nent) load_round(e0 + round_step);
+        // Softmax over the block's 128 keys in one pass (the block is whole).
+        // Only a block that reaches past some column's position is masked.
+        bool diag = false;
+#pragma unroll
+        for (int nq = 0; nq < kPfNq; ++nq) diag |= cent[nq] >= 0 && cpcol[nq] < tok_base + S - 1;
+        diag = __ballot(diag) != 0;
+        bf16x8 pa[kPfNq][4];
+        float mrow[kPfNq], lrow[kPfNq];
+#pragma unroll
+        for (int nq = 0; nq < kPfNq; ++nq) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float z = sacc[nq][kt][r] * scale_log2;
+                    if (diag && tok_base + kt * 16 + 4 * kg + r > cpcol[nq]) z = -INFINITY;
+                    sacc[nq][kt][r] = z;
+                    mx = fmaxf(mx, z);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            float psum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pv = mx == -INFINITY ? 0.f : exp2f(sacc[nq][kt][r] - mx);
+                    psum += pv;
+                    pa[nq][kt >> 1][(kt & 1) * 4 + r] = (__bf16)pv;
+                }
+            psum += __shfl_xor(psum, 16);
+            psum += __shfl_xor(psum, 32);
+            mrow[nq] = mx;
+            lrow[nq] = psum;
+        }
+        // O^T = V^T x P^T, 32 keys per MFMA step: the V tile read transposed
+        // from LDS (same addressing as attend_chunk) is the A operand and the
+        // probabilities the B operand, so lane (col, kg) ends up with
+        // O[column col][d = dt*16 + 4*kg + r] - four consecutive d per dt.
+        f32x4 o[kPfNq][8];
+#pragma unroll
+        for (int nq = 0; nq < kPfNq; ++nq)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[nq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < S / 32; ++c) {
             const unsigned char *vlo = v_lds + (c * 32 + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
             const unsigned char *vhi = vlo + 16 * kVRow;
 #pragma unroll
@@ -1131,47 +1155,42 @@ __global__ __launch_bounds__(256) void pf_attn_kernel(
                 const u32x2 hi = lds_read_tr16(vhi + dt * 32);
                 const u32x4 vbv = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-                for (int nq = 0; nq < kPfNq; ++nq) {
-                    f32x4 acc = st[nq].o[dt];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] *= a_row[nq][r];
-                    st[nq].o[dt] = mfma16(pa[nq], as_bf16x8(vbv), acc);
-                }
+                for (int nq = 0; nq < kPfNq; ++nq) o[nq][dt] = mfma16(as_bf16x8(vbv), pa[nq][c], o[nq][dt]);
             }
         }
-        // Partials. Lane holds O rows (query columns) 4*kg + r, d = dt*16 + col;
-        // lanes 0..15 hold m and l of column `col`.
+        // Partials: m and l of column `col` are in every lane of the column.
 #pragma unroll
         for (int nq = 0; nq < kPfNq; ++nq) {
-            if (lane < 16 && ent[nq] >= 0) {
-                const int64_t slot = (((int64_t)b * rows + (ent[nq] >> 5)) * G + g) * K + (ent[nq] & 31);
-                part_ml[slot * R + col % R] = make_float2(st[nq].m, st[nq].l);
-            }
+            if (cent[nq] < 0) continue;
+            const int64_t slot = (((int64_t)b * rows + (cent[nq] >> 5)) * G + g) * K + (cent[nq] & 31);
+            if (kg == 0) part_ml[slot * R + col % R] = make_float2(mrow[nq], lrow[nq]);
+            bf16_t *op = part_o + (slot * R + col % R) * D + 4 * kg;
+            const float inv = 1.f / lrow[nq];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int qc = 4 * kg + r;
-                const int e_q = __shfl(ent[nq], qc);
-                const float l_q = __shfl(st[nq].l, qc);
-                if (e_q < 0) continue;
-                const int64_t slot = (((int64_t)b * rows + (e_q >> 5)) * G + g) * K + (e_q & 31);
-                bf16_t *op = part_o + (slot * R + qc % R) * D + col;
-                const float inv = 1.f / l_q;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) op[dt * 16] = to_bf16(st[nq].o[dt][r] * inv);
+            for (int dt = 0; dt < 8; ++dt) {
+                const uint32_t lo = (uint32_t)to_bf16(o[nq][dt][0] * inv) |
+                                    ((uint32_t)to_bf16(o[nq][dt][1] * inv) << 16);
+                const uint32_t hi = (uint32_t)to_bf16(o[nq][dt][2] * inv) |
+                                    ((uint32_t)to_bf16(o[nq][dt][3] * inv) << 16);
+                *reinterpret_cast<u32x2 *>(op + dt * 16) = u32x2{lo, hi};
             }
         }
     }
 }
 
-// One workgroup per (sequence, row of the pass, group).
+// One workgroup per (sequence, row of the pass, group): the kept slots are
+// listed once, their (m, l) staged in LDS, then every thread merges four
+// d-values of one head over the kept slots.
 __global__ __launch_bounds__(256) void pf_merge_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const bf16_t *__restrict__ part_o,
     const float2 *__restrict__ part_ml, int T, int G, int R, int Nmax, int K, int t0, int rows,
     bf16_t *__restrict__ out, float *__restrict__ lse) {
     __shared__ int32_t s_sel[KMAX];
-    __shared__ int32_t s_keep[KMAX];
-    const int tid = threadIdx.x;
+    __shared__ int32_t s_kept[KMAX];
+    __shared__ int32_t s_n;
+    __shared__ float2 s_ml[KMAX * msa::kMaxHeadsPerGroup];
+    const int tid = threadIdx.x, lane = tid & 63;
     const int64_t unit = blockIdx.x;  // (b, tl, g)
     const int g = (int)(unit % G);
     const int64_t btl = unit / G;
@@ -1181,22 +1200,30 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
     const int p = pf_row_pos(kv_lens, q_start, b, t, T, Nmax);
     if (tid < K) s_sel[tid] = p >= 0 ? sel[(((int64_t)b * T + t) * G + g) * K + tid] : -1;
     __syncthreads();
-    if (tid < K) s_keep[tid] = p >= 0 && slot_kept(s_sel, tid, p / S + 1);
+    if (tid < 64) {
+        const bool keep = lane < K && p >= 0 && slot_kept(s_sel, lane, p / S + 1);
+        const uint64_t m = __ballot(keep);
+        if (keep) s_kept[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+        if (lane == 0) s_n = __popcll(m);
+    }
+    __syncthreads();
+    const int n = s_n;
+    const int64_t slot0 = unit * K;
+    for (int i = tid; i < n * R; i += 256) s_ml[i] = part_ml[(slot0 + s_kept[i / R]) * R + i % R];
     __syncthreads();
     const int H = G * R;
-    const int64_t slot0 = unit * K;
     for (int idx = tid; idx < R * (D / 4); idx += 256) {
         const int r = idx / (D / 4), d0 = (idx % (D / 4)) * 4;
         float M = -INFINITY;
-        for (int k = 0; k < K; ++k)
-            if (s_keep[k]) M = fmaxf(M, part_ml[(slot0 + k) * R + r].x);
+        for (int i = 0; i < n; ++i) M = fmaxf(M, s_ml[i * R + r].x);
         float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < K; ++k) {
-            if (!s_keep[k]) continue;
-            const float2 ml = part_ml[(slot0 + k) * R + r];
+#pragma unroll 8
+        for (int i = 0; i < n; ++i) {
+            const float2 ml = s_ml[i * R + r];
             const float wk = exp2f(ml.x - M) * ml.y;
             L += wk;
-            const u32x2 ov = *reinterpret_cast<const u32x2 *>(part_o + ((slot0 + k) * R + r) * D + d0);
+            const u32x2 ov =
+                *reinterpret_cast<const u32x2 *>(part_o + ((slot0 + s_kept[i]) * R + r) * D + d0);
             acc[0] += wk * __uint_as_float(ov[0] << 16);
             acc[1] += wk * __uint_as_float(ov[0] & 0xFFFF0000u);
             acc[2] += wk * __uint_as_float(ov[1] << 16);
