@@ -58,7 +58,7 @@ constexpr int64_t kPfKvMajorMinRows = 256;
 constexpr size_t kPfPartialBudget = (size_t)5 << 30;
 constexpr int kPfWaves = 4;       // waves per attention workgroup
 constexpr int kPfNq = 1;          // 16-column query tiles per wave
-constexpr int kPfRounds = 8;      // passes of every wave over its tiles per workgroup
+constexpr int kPfRounds = 16;     // passes of every wave over its tiles per workgroup
 int32_t prefill_entries_per_tile(int32_t R);
 struct PrefillWs {
     bool kv_major;

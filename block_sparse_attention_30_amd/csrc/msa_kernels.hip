@@ -97,6 +97,19 @@ __device__ __forceinline__ f32x16 mfma32_f8(i32x8 a, i32x8 b, f32x16 c) {
 
 __device__ __forceinline__ int clamp_kv(int kv, int Nmax) { return kv < Nmax ? kv : Nmax; }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two fp32 values rounded to bf16 (nearest even) and packed, low half first:
+// one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 2^x with the hardware instruction (no denormal rescaling; arguments here
+// are <= 0, where that only moves results below 2^-126 to zero).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ bf16_t to_bf16(float v) {
     const __bf16 h = (__bf16)v;
     return __builtin_bit_cast(bf16_t, h);
@@ -1110,30 +1123,38 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
         float mrow[kPfNq], lrow[kPfNq];
 #pragma unroll
         for (int nq = 0; nq < kPfNq; ++nq) {
+            // Max of the raw scores (the scale is positive), then
+            // p = 2^(s*scale - m) with one fma per score.
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float z = sacc[nq][kt][r] * scale_log2;
-                    if (diag && tok_base + kt * 16 + 4 * kg + r > cpcol[nq]) z = -INFINITY;
-                    sacc[nq][kt][r] = z;
-                    mx = fmaxf(mx, z);
+                    float sv = sacc[nq][kt][r];
+                    if (diag && tok_base + kt * 16 + 4 * kg + r > cpcol[nq]) sv = -INFINITY;
+                    sacc[nq][kt][r] = sv;
+                    mx = fmaxf(mx, sv);
                 }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m2 = mx * scale_log2;
+            const float neg_m = mx == -INFINITY ? 0.f : -m2;
             float psum = 0.f;
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt)
+            for (int c = 0; c < 4; ++c) {
+                float pv[8];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float pv = mx == -INFINITY ? 0.f : exp2f(sacc[nq][kt][r] - mx);
-                    psum += pv;
-                    pa[nq][kt >> 1][(kt & 1) * 4 + r] = (__bf16)pv;
+                for (int i = 0; i < 8; ++i) {
+                    pv[i] = fast_exp2(fmaf(sacc[nq][2 * c + (i >> 2)][i & 3], scale_log2, neg_m));
+                    psum += pv[i];
                 }
+                const u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                  pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+                pa[nq][c] = as_bf16x8(pk);
+            }
             psum += __shfl_xor(psum, 16);
             psum += __shfl_xor(psum, 32);
-            mrow[nq] = mx;
+            mrow[nq] = m2;
             lrow[nq] = psum;
         }
         // O^T = V^T x P^T, 32 keys per MFMA step: the V tile read transposed
@@ -1167,13 +1188,10 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
             bf16_t *op = part_o + (slot * R + col % R) * D + 4 * kg;
             const float inv = 1.f / lrow[nq];
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const uint32_t lo = (uint32_t)to_bf16(o[nq][dt][0] * inv) |
-                                    ((uint32_t)to_bf16(o[nq][dt][1] * inv) << 16);
-                const uint32_t hi = (uint32_t)to_bf16(o[nq][dt][2] * inv) |
-                                    ((uint32_t)to_bf16(o[nq][dt][3] * inv) << 16);
-                *reinterpret_cast<u32x2 *>(op + dt * 16) = u32x2{lo, hi};
-            }
+            for (int dt = 0; dt < 8; ++dt)
+                *reinterpret_cast<u32x2 *>(op + dt * 16) =
+                    u32x2{pack_bf16x2(o[nq][dt][0] * inv, o[nq][dt][1] * inv),
+                          pack_bf16x2(o[nq][dt][2] * inv, o[nq][dt][3] * inv)};
         }
     }
 }
@@ -1220,7 +1238,7 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
 #pragma unroll 8
         for (int i = 0; i < n; ++i) {
             const float2 ml = s_ml[i * R + r];
-            const float wk = exp2f(ml.x - M) * ml.y;
+            const float wk = fast_exp2(ml.x - M) * ml.y;
             L += wk;
             const u32x2 ov =
                 *reinterpret_cast<const u32x2 *>(part_o + ((slot0 + s_kept[i]) * R + r) * D + d0);
@@ -1231,9 +1249,8 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
         }
         const float inv = L > 0.f ? 1.f / L : 0.f;
         bf16_t *op = out + (((int64_t)b * T + t) * H + (int64_t)g * R + r) * D + d0;
-        const uint32_t lo = (uint32_t)to_bf16(acc[0] * inv) | ((uint32_t)to_bf16(acc[1] * inv) << 16);
-        const uint32_t hi = (uint32_t)to_bf16(acc[2] * inv) | ((uint32_t)to_bf16(acc[3] * inv) << 16);
-        *reinterpret_cast<u32x2 *>(op) = u32x2{lo, hi};
+        *reinterpret_cast<u32x2 *>(op) =
+            u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
         if (lse && d0 == 0)
             lse[((int64_t)b * T + t) * H + (int64_t)g * R + r] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
     }
