@@ -123,7 +123,9 @@ DecodeWs decode_ws(const msa_config *cfg, int32_t B, int32_t Nmax, bool with_ind
     const size_t units = (size_t)B * cfg->num_kv_groups * decode_splits(cfg) * cfg->heads_per_group;
     w.part_o_off = pooled;
     w.part_ml_off = round_up(w.part_o_off + units * kHeadDim * 4, kWsAlign);
-    w.total = round_up(w.part_ml_off + units * 2 * 4, kWsAlign);
+    w.counters_off = round_up(w.part_ml_off + units * 2 * 4, kWsAlign);
+    const size_t counters = with_index ? (size_t)B * cfg->num_kv_groups * 4 : 0;
+    w.total = round_up(w.counters_off + counters, kWsAlign);
     return w;
 }
 

@@ -74,8 +74,10 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
 // the pooled scores when the call also runs the index branch (msa_decode).
 constexpr int kDecodeChunksPerSplit = 8;
 int32_t decode_splits(const msa_config *cfg);
+// msa_decode also keeps one arrival counter per (sequence, group), zeroed by
+// the index kernel of the same call.
 struct DecodeWs {
-    size_t pooled_off, part_o_off, part_ml_off, total;
+    size_t pooled_off, part_o_off, part_ml_off, counters_off, total;
     int64_t nb_max;
 };
 DecodeWs decode_ws(const msa_config *cfg, int32_t B, int32_t Nmax, bool with_index);

@@ -321,11 +321,16 @@ template <bool F8>
 __global__ __launch_bounds__(256) void idx_scan_kernel(
     const unsigned char *__restrict__ q_idx, const unsigned char *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
-    float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int blocks_per_wg) {
+    float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int blocks_per_wg,
+    int32_t *__restrict__ zero_counters) {
     typedef ScanGeom<F8> Geo;
     __shared__ __attribute__((aligned(16))) unsigned char lds[4 * Geo::kWaveLds];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // Zero the arrival counters the decode attention kernel of the same call
+    // uses (one per (sequence, group)); the kernel boundary orders the two.
+    if (zero_counters && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < G; i += 256) zero_counters[(int64_t)b * G + i] = 0;
     const int rows = T * G;
     const int kv = clamp_kv(kv_lens[b], Nmax);
     const int qs = q_start ? q_start[b] : kv - T;
@@ -687,29 +692,52 @@ __device__ __forceinline__ void load_query(bf16x8 (&qf)[4], const bf16_t *q_head
     for (int kc = 0; kc < 4; ++kc) qf[kc] = col < R ? ld_bf16x8(qp + kc * 32) : zero_bf16x8();
 }
 
-// One 32-token chunk [tok0, tok0 + 32) of a kept block; keys past p are masked.
-__device__ __forceinline__ void attend_chunk(WaveAttn &st, const bf16x8 (&qf)[4],
-                                             const bf16_t *kg_base, const bf16_t *vg_base,
-                                             int tok0, int p, float scale_log2,
-                                             unsigned char *vrows, int lane) {
-    const int col = lane & 15, kg = lane >> 4;
-    // Issue every global load of the chunk first: K in the MFMA A layout
-    // (token col of each 16-token tile), V as 16-byte row pieces.
+// The global loads of one 32-token chunk [tok0, tok0 + 32): K in the MFMA A
+// layout (token col of each 16-token tile), V as 16-byte row pieces; keys
+// past p are clamped (K) or zero (V).
+struct ChunkRegs {
     u32x4 kr[2][4], vr[8];
+};
+
+__device__ __forceinline__ void load_chunk(ChunkRegs &cr, const bf16_t *kg_base,
+                                           const bf16_t *vg_base, int tok0, int p, int lane) {
+    const int col = lane & 15, kg = lane >> 4;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const int tok = tok0 + rt * 16 + col;
         const bf16_t *kp = kg_base + (size_t)(tok <= p ? tok : p) * D + kg * 8;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) kr[rt][kc] = ld16(kp + kc * 32);
+        for (int kc = 0; kc < 4; ++kc) cr.kr[rt][kc] = ld16(kp + kc * 32);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int piece = lane + 64 * i;
         const int tok = tok0 + (piece >> 4);
         const u32x4 z4 = {0u, 0u, 0u, 0u};
-        vr[i] = tok <= p ? ld16(vg_base + (size_t)tok * D + (piece & 15) * 8) : z4;
+        cr.vr[i] = tok <= p ? ld16(vg_base + (size_t)tok * D + (piece & 15) * 8) : z4;
     }
+}
+
+__device__ __forceinline__ void compute_chunk(WaveAttn &st, const bf16x8 (&qf)[4],
+                                              const ChunkRegs &cr, int tok0, int p,
+                                              float scale_log2, unsigned char *vrows, int lane);
+
+// One 32-token chunk [tok0, tok0 + 32) of a kept block; keys past p are masked.
+__device__ __forceinline__ void attend_chunk(WaveAttn &st, const bf16x8 (&qf)[4],
+                                             const bf16_t *kg_base, const bf16_t *vg_base,
+                                             int tok0, int p, float scale_log2,
+                                             unsigned char *vrows, int lane) {
+    ChunkRegs cr;
+    load_chunk(cr, kg_base, vg_base, tok0, p, lane);
+    compute_chunk(st, qf, cr, tok0, p, scale_log2, vrows, lane);
+}
+
+__device__ __forceinline__ void compute_chunk(WaveAttn &st, const bf16x8 (&qf)[4],
+                                              const ChunkRegs &cr, int tok0, int p,
+                                              float scale_log2, unsigned char *vrows, int lane) {
+    const int col = lane & 15, kg = lane >> 4;
+    const auto &kr = cr.kr;
+    const auto &vr = cr.vr;
     f32x4 sacc[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -1281,7 +1309,8 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
     const float *__restrict__ pooled, int64_t nb_max, int32_t *__restrict__ sel,
     float *__restrict__ sel_scores, int G, int R, int Nmax, int K, int nsplit, float scale_log2,
-    float *__restrict__ part_o, float *__restrict__ part_ml) {
+    float *__restrict__ part_o, float *__restrict__ part_ml, int32_t *__restrict__ counters,
+    bf16_t *__restrict__ out, float *__restrict__ lse) {
     __shared__ DecodeLds L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int split = (int)(blockIdx.x % nsplit);
@@ -1356,11 +1385,58 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
             acc += s_o[(w * 16 + h) * D + dd];
         }
         const int64_t pu = (unit * nsplit + split) * R + h;
-        part_o[pu * D + dd] = acc;
-        if (dd == 0) {
-            part_ml[pu * 2] = M;
-            part_ml[pu * 2 + 1] = Lsum;
+        if (counters) {
+            // Device-scope stores: written through to memory, where the
+            // merging workgroup (possibly on another XCD) reads them.
+            __hip_atomic_store(&part_o[pu * D + dd], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (dd == 0) {
+                __hip_atomic_store(&part_ml[pu * 2], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&part_ml[pu * 2 + 1], Lsum, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            part_o[pu * D + dd] = acc;
+            if (dd == 0) {
+                part_ml[pu * 2] = M;
+                part_ml[pu * 2 + 1] = Lsum;
+            }
         }
+    }
+    if (!counters) return;
+    // The last of the nsplit workgroups of (sequence, group) to arrive merges
+    // all partials. Every thread's partial stores have completed (vmcnt(0))
+    // before the workgroup's arrival is counted; the merging workgroup reads
+    // the partials with device-scope loads, after its own arrival.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (tid == 0)
+        L.nblk = __hip_atomic_fetch_add(&counters[unit], 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+    __syncthreads();
+    if (!L.nblk) return;
+    for (int idx = tid; idx < R * D; idx += kDecWaves * 64) {
+        const int h = idx / D, dd = idx % D;
+        const int64_t pu0 = unit * nsplit * R + h;
+        float M = -INFINITY;
+        for (int sp = 0; sp < nsplit; ++sp)
+            M = fmaxf(M, __hip_atomic_load(&part_ml[(pu0 + (int64_t)sp * R) * 2], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+        float Lsum = 0.f, acc = 0.f;
+#pragma unroll 4
+        for (int sp = 0; sp < nsplit; ++sp) {
+            const int64_t pu = pu0 + (int64_t)sp * R;
+            const float pm = __hip_atomic_load(&part_ml[pu * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float pl = __hip_atomic_load(&part_ml[pu * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float pv = __hip_atomic_load(&part_o[pu * D + dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (pm != -INFINITY) {
+                const float w = exp2f(pm - M);
+                Lsum += w * pl;
+                acc += w * pv;
+            }
+        }
+        const int64_t uh = unit * R + h;
+        out[uh * D + dd] = to_bf16(Lsum > 0.f ? acc / Lsum : 0.f);
+        if (lse && dd == 0) lse[uh] = Lsum > 0.f ? M * kLn2 + logf(Lsum) : -INFINITY;
     }
 }
 
@@ -1425,7 +1501,8 @@ int64_t scan_blocks_per_wg(int32_t B, int64_t nb_max) {
 // MFMA prefill kernel otherwise; bf16 or OCP E4M3 index data.
 msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                          const void *q_idx, const void *k_idx, const int32_t *kv_lens,
-                         const int32_t *q_start, float *pooled, int64_t nb_max, hipStream_t st) {
+                         const int32_t *q_start, float *pooled, int64_t nb_max, hipStream_t st,
+                         int32_t *zero_counters = nullptr) {
     const int G = cfg->num_kv_groups;
     const int rows = T * G;
     const bool f8 = cfg->index_dtype == MSA_FP8_E4M3;
@@ -1436,10 +1513,10 @@ msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nm
         const dim3 grid((unsigned)((nb_max + per_wg - 1) / per_wg), (unsigned)B);
         if (f8)
             idx_scan_kernel<true><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
-                                                        Nmax, nb_max, (int)per_wg);
+                                                        Nmax, nb_max, (int)per_wg, zero_counters);
         else
             idx_scan_kernel<false><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
-                                                         Nmax, nb_max, (int)per_wg);
+                                                         Nmax, nb_max, (int)per_wg, zero_counters);
         return launch_status("decode index kernel");
     }
     const dim3 grid((unsigned)((rows + kPfRows - 1) / kPfRows), (unsigned)B);
@@ -1564,16 +1641,18 @@ static msa_status launch_decode_attention(const msa_config *cfg, int32_t B, int3
                                           const void *v_cache, const int32_t *kv_lens,
                                           const float *pooled, int64_t nb_max, int32_t *sel,
                                           float *sel_scores, void *out, float *lse,
-                                          float *part_o, float *part_ml, hipStream_t st) {
+                                          float *part_o, float *part_ml, hipStream_t st,
+                                          int32_t *counters = nullptr) {
     const int G = cfg->num_kv_groups, R = cfg->heads_per_group, K = cfg->topk;
     const int nsplit = msa::decode_splits(cfg);
     const int64_t units = (int64_t)B * G;
     sparse_decode_kernel<<<(unsigned)(units * nsplit), kDecWaves * 64, 0, st>>>(
         static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k_cache),
         static_cast<const bf16_t *>(v_cache), kv_lens, pooled, nb_max, sel, sel_scores, G, R, Nmax,
-        K, nsplit, scale_log2_of(cfg), part_o, part_ml);
+        K, nsplit, scale_log2_of(cfg), part_o, part_ml, counters, static_cast<bf16_t *>(out),
+        lse);
     msa_status s = launch_status("sparse decode kernel");
-    if (s != MSA_OK) return s;
+    if (s != MSA_OK || counters) return s;
     combine_kernel<<<(unsigned)(units * R), D, 0, st>>>(part_o, part_ml, G, R, nsplit,
                                                         static_cast<bf16_t *>(out), lse);
     return launch_status("combine kernel");
@@ -1611,14 +1690,17 @@ msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void
     const msa::DecodeWs w = msa::decode_ws(cfg, B, Nmax, true);
     char *base = static_cast<char *>(workspace);
     float *pooled = reinterpret_cast<float *>(base + w.pooled_off);
-    s = launch_pooled(cfg, B, 1, Nmax, q_idx, k_idx, kv_lens, nullptr, pooled, w.nb_max, st);
+    int32_t *counters = reinterpret_cast<int32_t *>(base + w.counters_off);
+    s = launch_pooled(cfg, B, 1, Nmax, q_idx, k_idx, kv_lens, nullptr, pooled, w.nb_max, st,
+                      counters);
     if (s != MSA_OK) return s;
     // The attention kernel ranks each (sequence, group) row itself from the
-    // pooled scores, then attends over the kept blocks.
+    // pooled scores, attends over the kept blocks, and the last split of each
+    // (sequence, group) merges the partials.
     return launch_decode_attention(cfg, B, Nmax, q, k_cache, v_cache, kv_lens, pooled, w.nb_max,
                                    sel, sel_scores, out, lse,
                                    reinterpret_cast<float *>(base + w.part_o_off),
-                                   reinterpret_cast<float *>(base + w.part_ml_off), st);
+                                   reinterpret_cast<float *>(base + w.part_ml_off), st, counters);
 }
 
 }  // extern "C"
