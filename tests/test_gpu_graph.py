@@ -73,4 +73,7 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for a, b in zip(got, (sel, out, sel2, out2, psel, pout)):
             assert torch.equal(a, b), rep
-        assert torch.equal(sel, sel2) and torch.equal(out, out2)
+        # msa_decode and the two-call form select the same blocks; their split
+        # partials merge in a different order.
+        assert torch.equal(sel, sel2)
+        assert (out.float() - out2.float()).abs().max().item() <= 2e-2

@@ -211,9 +211,12 @@ def test_decode_step_matches_oracle_and_two_calls(orc, G, R, K, lens, fp8):
     compare_out(out[valid].reshape(oout.shape), oout, "msa_decode")
     compare_lse(lse[valid].reshape(olse.shape), olse, "msa_decode")
     assert (out[~valid] == 0).all() and np.isneginf(lse[~valid]).all()
-    # Same bits as msa_index_topk + msa_sparse_attn_decode.
+    # The same selection as msa_index_topk + msa_sparse_attn_decode; the
+    # outputs agree to the tolerance (their split partials merge in a
+    # different order).
     s2, _, o2, l2 = run_gpu(pr, G, R, K, lens, None, decode=True, fp8=fp8)
-    assert np.array_equal(s2, sel) and np.array_equal(o2, out)
+    assert np.array_equal(s2, sel)
+    compare_out(o2[valid].reshape(oout.shape), out[valid].reshape(oout.shape), "two-call vs msa_decode")
 
 
 def test_decode_step_workspace_reuse(orc):
