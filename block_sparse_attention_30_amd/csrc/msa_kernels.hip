@@ -219,8 +219,10 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
 // On random scores pass 2 finds only a handful of keys: a row costs two
 // 64-key sorts and one read of its scores (two if n > 1024). Returns the K
 // best keys in lanes 0..K-1 (descending), 0 elsewhere.
-__device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int K, int lane,
-                                                  uint64_t *buf) {
+// n_load (>= n) entries of cand may be read: the first batch is loaded
+// before n is known to be positive, so its loads can be issued at once.
+__device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int n_load, int K,
+                                                  int lane, uint64_t *buf) {
     constexpr int kBatch = 16;
     const bool one_batch = n <= 64 * kBatch;  // then pass 2 reuses pass 1's registers
     float v[kBatch];
@@ -228,12 +230,13 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
 #pragma unroll
         for (int c = 0; c < kBatch; ++c) {
             const int i = base + c * 64 + lane;
-            v[c] = i < n ? cand[i] : 0.f;
+            v[c] = i < n_load ? cand[i] : 0.f;
         }
     };
     uint64_t lmax = 0;
+    load(0);
     for (int base = 0; base < n; base += 64 * kBatch) {
-        load(base);
+        if (base > 0) load(base);
 #pragma unroll
         for (int c = 0; c < kBatch; ++c) {
             const int i = base + c * 64 + lane;
@@ -257,6 +260,37 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
         cnt = 0;
         __builtin_amdgcn_wave_barrier();
     };
+    if (one_batch) {
+        // Usual case: every lane counts its keys above the threshold (other
+        // than its maximum, already ranked); a wave prefix sum built from
+        // five ballots of the count bits places them in the list at once.
+        int my = 0;
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int i = c * 64 + lane;
+            const uint64_t kk = i < n ? score_key(v[c], i) : 0;
+            my += (kk > thr && kk != lmax) ? 1 : 0;
+        }
+        int excl = 0, total = 0;
+#pragma unroll
+        for (int bit = 0; bit < 5; ++bit) {  // my <= 16
+            const uint64_t bm = __ballot((my >> bit) & 1);
+            excl += __popcll(bm & below) << bit;
+            total += __popcll(bm) << bit;
+        }
+        if (total <= cap) {
+            int pos = excl;
+#pragma unroll
+            for (int c = 0; c < kBatch; ++c) {
+                const int i = c * 64 + lane;
+                const uint64_t kk = i < n ? score_key(v[c], i) : 0;
+                if (kk > thr && kk != lmax) buf[pos++] = kk;
+            }
+            cnt = total;
+            if (cnt) merge();
+            return top;
+        }
+    }
     for (int base = 0; base < n; base += 64 * kBatch) {
         if (!one_batch) load(base);
 #pragma unroll
@@ -454,7 +488,8 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(
     const int qs = q_start ? q_start[b] : kv - T;
     const int p = qs + t;
     uint64_t top = 0;
-    if (p >= 0 && p < kv) top = wave_topk_row(pooled + row * nb_max, p / S + 1, K, lane, s_buf[wave]);
+    if (p >= 0 && p < kv)
+        top = wave_topk_row(pooled + row * nb_max, p / S + 1, p / S + 1, K, lane, s_buf[wave]);
     if (lane < K) {
         sel[row * K + lane] = top ? key_block(top) : -1;
         if (sel_scores) sel_scores[row * K + lane] = top ? key_score(top) : -INFINITY;
@@ -811,14 +846,16 @@ __device__ __forceinline__ void compute_chunk(WaveAttn &st, const bf16x8 (&qf)[4
 // whole wavefront: lane k checks slot k against the earlier slots, then the
 // survivors are compacted by ballot. Returns the count (in every lane).
 __device__ __forceinline__ int build_block_list(const int *sel_lds, int K, int p, int *blocks,
-                                                int lane) {
+                                                int lane, bool unique = false) {
     const int n_valid = p >= 0 ? p / S + 1 : 0;
     bool keep = false;
     int blk = -1;
     if (lane < K) {
         blk = sel_lds[lane];
         keep = blk >= 0 && blk < n_valid;
-        for (int k2 = 0; k2 < lane && keep; ++k2) keep = sel_lds[k2] != blk;
+        // unique: the list comes from this library's own top-k (no repeats).
+        if (!unique)
+            for (int k2 = 0; k2 < lane && keep; ++k2) keep = sel_lds[k2] != blk;
     }
     const uint64_t m = __ballot(keep);
     if (keep) blocks[__popcll(m & ((1ull << lane) - 1ull))] = blk;
@@ -1320,10 +1357,15 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     const int H = G * R;
     const int kv = clamp_kv(kv_lens[b], Nmax);
     const int p = kv - 1;
+    // The query does not depend on the selection: its loads overlap the ranking.
+    bf16x8 qf[4];
+    load_query(qf, q + ((int64_t)b * H + (int64_t)g * R) * D, R, lane);
     if (pooled) {
         if (wave == 0) {
-            uint64_t top = 0;
-            if (p >= 0) top = wave_topk_row(pooled + unit * nb_max, p / S + 1, K, lane, L.keys);
+            // n_load = nb_max: the row's pooled scores are loaded while kv_lens
+            // is still in flight.
+            const uint64_t top = wave_topk_row(pooled + unit * nb_max, p >= 0 ? p / S + 1 : 0,
+                                               (int)nb_max, K, lane, L.keys);
             if (lane < K) {
                 const int blk = top ? key_block(top) : -1;
                 L.sel[lane] = blk;
@@ -1338,7 +1380,7 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     }
     __syncthreads();
     if (wave == 0) {
-        const int n = build_block_list(L.sel, K, p, L.blocks, lane);
+        const int n = build_block_list(L.sel, K, p, L.blocks, lane, pooled != nullptr);
         if (lane == 0) L.nblk = n;
     }
     __syncthreads();
@@ -1346,8 +1388,6 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     WaveAttn st;
     wave_attn_init(st);
     if (c < L.nblk * 4) {
-        bf16x8 qf[4];
-        load_query(qf, q + ((int64_t)b * H + (int64_t)g * R) * D, R, lane);
         attend_chunk(st, qf, k_cache + ((size_t)b * G + g) * Nmax * D,
                      v_cache + ((size_t)b * G + g) * Nmax * D, L.blocks[c >> 2] * S + (c & 3) * 32,
                      p, scale_log2, L.vrows + wave * kVWave, lane);
@@ -1414,25 +1454,36 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
                                         __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
     __syncthreads();
     if (!L.nblk) return;
+    // One round of loads per batch of eight splits, merged online.
     for (int idx = tid; idx < R * D; idx += kDecWaves * 64) {
         const int h = idx / D, dd = idx % D;
         const int64_t pu0 = unit * nsplit * R + h;
-        float M = -INFINITY;
-        for (int sp = 0; sp < nsplit; ++sp)
-            M = fmaxf(M, __hip_atomic_load(&part_ml[(pu0 + (int64_t)sp * R) * 2], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-        float Lsum = 0.f, acc = 0.f;
-#pragma unroll 4
-        for (int sp = 0; sp < nsplit; ++sp) {
-            const int64_t pu = pu0 + (int64_t)sp * R;
-            const float pm = __hip_atomic_load(&part_ml[pu * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float pl = __hip_atomic_load(&part_ml[pu * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float pv = __hip_atomic_load(&part_o[pu * D + dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (pm != -INFINITY) {
-                const float w = exp2f(pm - M);
-                Lsum += w * pl;
-                acc += w * pv;
+        float M = -INFINITY, Lsum = 0.f, acc = 0.f;
+        for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+            float pm[8], pl[8], pv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t pu = pu0 + (int64_t)min(sp0 + j, nsplit - 1) * R;
+                pm[j] = __hip_atomic_load(&part_ml[pu * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pl[j] = __hip_atomic_load(&part_ml[pu * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pv[j] = __hip_atomic_load(&part_o[pu * D + dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (sp0 + j >= nsplit) pm[j] = -INFINITY;
             }
+            float Mb = M;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) Mb = fmaxf(Mb, pm[j]);
+            if (Mb == -INFINITY) continue;
+            const float sc = M == -INFINITY ? 0.f : exp2f(M - Mb);
+            Lsum *= sc;
+            acc *= sc;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (pm[j] == -INFINITY) continue;
+                const float w = exp2f(pm[j] - Mb);
+                Lsum += w * pl[j];
+                acc += w * pv[j];
+            }
+            M = Mb;
         }
         const int64_t uh = unit * R + h;
         out[uh * D + dd] = to_bf16(Lsum > 0.f ? acc / Lsum : 0.f);
