@@ -82,20 +82,25 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) 
     const int64_t G = cfg->num_kv_groups, K = cfg->topk, R = cfg->heads_per_group;
     w.kv_major = (int64_t)B * T * G >= kPfKvMajorMinRows;
     if (!w.kv_major || B == 0 || T == 0) return w;
-    // Largest power of two of rows whose partials fit the budget (at least 1).
-    const size_t row_bytes = (size_t)B * G * K * R * (kHeadDim * 2 + 8);
-    int64_t rows = 1;
-    // Also keep one workgroup per (sequence, row, group) within 2^24 per pass.
+    // One pass covers every group and `rows` query rows of every sequence: the
+    // largest power of two of rows (or all T) whose partials fit
+    // kPfPartialBudget, with at most 2^24 (sequence, row, group) units. (Passes
+    // of one group whose queries stay in the last-level cache were measured
+    // slower: the list build is paid per pass.)
+    const size_t part_row = (size_t)B * G * K * R * (kHeadDim * 2 + 8);
     const int64_t max_units = (int64_t)1 << 24;
-    while (rows * 2 <= T && (size_t)(rows * 2) * row_bytes <= kPfPartialBudget &&
+    int64_t rows = 1;
+    while (rows * 2 <= T && (size_t)(rows * 2) * part_row <= kPfPartialBudget &&
            rows * 2 * B * G <= max_units)
         rows *= 2;
-    if ((size_t)T * row_bytes <= kPfPartialBudget && (int64_t)T * B * G <= max_units) rows = T;
+    if ((size_t)T * part_row <= kPfPartialBudget && (int64_t)T * B * G <= max_units) rows = T;
+    const int64_t groups = G;
     w.rows = (int32_t)rows;
+    w.groups = (int32_t)groups;
     w.entries_per_tile = prefill_entries_per_tile(cfg->heads_per_group);
     w.nb_max = ((int64_t)Nmax + kBlock - 1) / kBlock;
-    w.nlists = (int64_t)B * G * w.nb_max;
-    w.nslots = (int64_t)B * rows * G * K;
+    w.nlists = (int64_t)B * groups * w.nb_max;
+    w.nslots = (int64_t)B * rows * groups * K;
     w.max_tiles = (w.nslots + w.entries_per_tile - 1) / w.entries_per_tile + w.nlists;
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };

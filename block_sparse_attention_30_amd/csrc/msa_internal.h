@@ -47,9 +47,8 @@ struct IndexWs {
 IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
 
 // Sparse prefill. Below kPfKvMajorMinRows (B*T*G) rows the query-major kernel
-// runs (no workspace). Otherwise the KV-major path works in passes of
-// `rows` query rows of every sequence, sized so that one pass's partial
-// outputs stay within kPfPartialBudget bytes. Per pass the workspace holds the
+// runs (no workspace). Otherwise the KV-major path works in passes over
+// `groups` groups and `rows` query rows of every sequence (see prefill_ws). Per pass the workspace holds the
 // per-(sequence, group, block) list sizes, offsets and tile starts, the
 // tile -> list map, the rank of every (row, group, slot) in its list, the
 // lists, and per-(row, group, slot, head) partials: O / l in bf16 [d] and
@@ -57,12 +56,13 @@ IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
 constexpr int64_t kPfKvMajorMinRows = 256;
 constexpr size_t kPfPartialBudget = (size_t)5 << 30;
 constexpr int kPfWaves = 4;       // waves per attention workgroup
-constexpr int kPfNq = 1;          // 16-column query tiles per wave
+constexpr int kPfNq = 2;          // 16-column query tiles per wave
 constexpr int kPfRounds = 16;     // passes of every wave over its tiles per workgroup
 int32_t prefill_entries_per_tile(int32_t R);
 struct PrefillWs {
     bool kv_major;
-    int32_t rows;  // query rows of every sequence per pass
+    int32_t rows;    // query rows of every sequence per pass
+    int32_t groups;  // groups per pass
     int32_t entries_per_tile;
     int64_t nb_max, nlists, nslots, max_tiles;
     size_t counts_off, offsets_off, tile_first_off, tile_map_off, rank_off, list_off;

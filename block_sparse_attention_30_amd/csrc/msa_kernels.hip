@@ -166,6 +166,17 @@ __device__ __forceinline__ uint32_t xor_lane32(uint32_t v, int lane) {
     }
 }
 
+// Max / sum of a float over the lanes l, l^16, l^32, l^48 (VALU lane swaps).
+__device__ __forceinline__ float max_xor16_32(float v, int lane) {
+    v = fmaxf(v, __uint_as_float(xor_lane32<16>(__float_as_uint(v), lane)));
+    return fmaxf(v, __uint_as_float(xor_lane32<32>(__float_as_uint(v), lane)));
+}
+
+__device__ __forceinline__ float sum_xor16_32(float v, int lane) {
+    v += __uint_as_float(xor_lane32<16>(__float_as_uint(v), lane));
+    return v + __uint_as_float(xor_lane32<32>(__float_as_uint(v), lane));
+}
+
 template <int J>
 __device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
     const uint32_t lo = xor_lane32<J>((uint32_t)v, lane);
@@ -1005,21 +1016,21 @@ __device__ __forceinline__ int pf_row_pos(const int32_t *kv_lens, const int32_t 
 __global__ __launch_bounds__(256) void pf_count_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, int B, int T, int G, int Nmax, int K, int t0, int rows,
-    int64_t nb_max, int32_t *__restrict__ counts, int32_t *__restrict__ rank) {
+    int g0, int ng, int64_t nb_max, int32_t *__restrict__ counts, int32_t *__restrict__ rank) {
     const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (slot >= (int64_t)B * rows * G * K) return;
+    if (slot >= (int64_t)B * rows * ng * K) return;
     const int k = (int)(slot % K);
-    const int64_t unit = slot / K;  // (b, tl, g)
-    const int g = (int)(unit % G);
-    const int64_t btl = unit / G;
+    const int64_t unit = slot / K;  // (b, tl, gl), group g0 + gl
+    const int gl = (int)(unit % ng);
+    const int64_t btl = unit / ng;
     const int b = (int)(btl / rows), tl = (int)(btl % rows);
     const int t = t0 + tl;
     const int p = pf_row_pos(kv_lens, q_start, b, t, T, Nmax);
     int r = -1;
     if (p >= 0) {
-        const int32_t *sr = sel + (((int64_t)b * T + t) * G + g) * K;
+        const int32_t *sr = sel + (((int64_t)b * T + t) * G + g0 + gl) * K;
         if (slot_kept(sr, k, p / S + 1))
-            r = atomicAdd(&counts[((int64_t)b * G + g) * nb_max + sr[k]], 1);
+            r = atomicAdd(&counts[((int64_t)b * ng + gl) * nb_max + sr[k]], 1);
     }
     rank[slot] = r;
 }
@@ -1069,19 +1080,19 @@ __global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict
 
 __global__ __launch_bounds__(256) void pf_scatter_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ rank,
-    const int32_t *__restrict__ offsets, int B, int T, int G, int K, int t0, int rows,
-    int64_t nb_max, int32_t *__restrict__ list) {
+    const int32_t *__restrict__ offsets, int B, int T, int G, int K, int t0, int rows, int g0,
+    int ng, int64_t nb_max, int32_t *__restrict__ list) {
     const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (slot >= (int64_t)B * rows * G * K) return;
+    if (slot >= (int64_t)B * rows * ng * K) return;
     const int r = rank[slot];
     if (r < 0) return;
     const int k = (int)(slot % K);
     const int64_t unit = slot / K;
-    const int g = (int)(unit % G);
-    const int64_t btl = unit / G;
+    const int gl = (int)(unit % ng);
+    const int64_t btl = unit / ng;
     const int b = (int)(btl / rows), tl = (int)(btl % rows);
-    const int blk = sel[(((int64_t)b * T + t0 + tl) * G + g) * K + k];
-    list[offsets[((int64_t)b * G + g) * nb_max + blk] + r] = (tl << 5) | k;
+    const int blk = sel[(((int64_t)b * T + t0 + tl) * G + g0 + gl) * K + k];
+    list[offsets[((int64_t)b * ng + gl) * nb_max + blk] + r] = (tl << 5) | k;
 }
 
 __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
@@ -1090,8 +1101,8 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
     const int32_t *__restrict__ q_start, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ tile_first, const int32_t *__restrict__ tile_map,
     const int32_t *__restrict__ list, int64_t nlists, int T, int G, int R, int Nmax, int K,
-    int t0, int rows, int64_t nb_max, int ch, float scale_log2, bf16_t *__restrict__ part_o,
-    float2 *__restrict__ part_ml) {
+    int t0, int rows, int g0, int ng, int64_t nb_max, int ch, float scale_log2,
+    bf16_t *__restrict__ part_o, float2 *__restrict__ part_ml) {
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[S * kKRow];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[S * kVRow];
     const int w = blockIdx.x;
@@ -1101,9 +1112,10 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
     const int li = tile_map[w];
     const int beg = offsets[li] + (w - tile_first[li]) * ch;
     const int nent = min(beg + ch, offsets[li + 1]) - beg;
-    const int64_t bg = li / nb_max;
+    const int64_t bgl = li / nb_max;  // (sequence, group of the pass)
     const int blk = (int)(li % nb_max);
-    const int b = (int)(bg / G), g = (int)(bg % G);
+    const int b = (int)(bgl / ng), gl = (int)(bgl % ng), g = g0 + gl;
+    const int64_t bg = (int64_t)b * G + g;
     const int H = G * R;
     const int kv = clamp_kv(kv_lens[b], Nmax);
     const int qs = q_start ? q_start[b] : kv - T;
@@ -1131,11 +1143,11 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
     const int et = 16 / R;  // entries per 16-column query tile
     const int tok_base = blk * S;
     // Column `col` of query tile nq in a round: entry e0 + nq*et + col/R, head
-    // col%R. The next round's entries and queries are loaded while the
-    // current round computes.
-    int ent[kPfNq], pcol[kPfNq];
-    bf16x8 qf[kPfNq][4];
-    auto load_round = [&](int e0) {
+    // col%R. Two register sets alternate between rounds: right after a round's
+    // score MFMAs its set is reloaded with the queries of the round after
+    // next, so those loads have about a round and a half to land.
+    auto load_round = [&](int e0, int (&ent)[kPfNq], int (&pcol)[kPfNq],
+                          bf16x8 (&qf)[kPfNq][4]) {
 #pragma unroll
         for (int nq = 0; nq < kPfNq; ++nq) {
             const int e = e0 + nq * et + col / R;
@@ -1150,14 +1162,15 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
         }
     };
     const int round_step = kPfWaves * kPfNq * et;
-    int e0 = wave * kPfNq * et;
-    if (e0 < nent) load_round(e0);
-    for (; e0 < nent; e0 += round_step) {
+    auto do_round = [&](int e0, int (&ent)[kPfNq], int (&pcol)[kPfNq], bf16x8 (&qf)[kPfNq][4]) {
         // S^T for the whole block: key tile kt (16 keys) x 16 query columns;
         // lane holds column `col`, keys kt*16 + 4*kg + r.
         f32x4 sacc[kPfNq][8];
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
+            // Keeps the scheduler from hoisting every key tile's LDS reads at
+            // once (that exhausts the registers).
+            if (kt % 2 == 0) __builtin_amdgcn_sched_barrier(0);
             u32x4 ka[4];
             const unsigned char *kp = k_lds + (kt * 16 + col) * kKRow + kg * 16;
 #pragma unroll
@@ -1170,14 +1183,14 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
                 sacc[nq][kt] = acc;
             }
         }
-        // The queries are no longer needed: load the next round's now.
+        // The queries are no longer needed: reload the set for two rounds on.
         int cent[kPfNq], cpcol[kPfNq];
 #pragma unroll
         for (int nq = 0; nq < kPfNq; ++nq) {
             cent[nq] = ent[nq];
             cpcol[nq] = pcol[nq];
         }
-        if (e0 + round_step < nent) load_round(e0 + round_step);
+        if (e0 + 2 * round_step < nent) load_round(e0 + 2 * round_step, ent, pcol, qf);
         // Softmax over the block's 128 keys in one pass (the block is whole).
         // Only a block that reaches past some column's position is masked.
         bool diag = false;
@@ -1200,8 +1213,7 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
                     sacc[nq][kt][r] = sv;
                     mx = fmaxf(mx, sv);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_xor16_32(mx, lane);
             const float m2 = mx * scale_log2;
             const float neg_m = mx == -INFINITY ? 0.f : -m2;
             float psum = 0.f;
@@ -1217,8 +1229,7 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
                                   pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
                 pa[nq][c] = as_bf16x8(pk);
             }
-            psum += __shfl_xor(psum, 16);
-            psum += __shfl_xor(psum, 32);
+            psum = sum_xor16_32(psum, lane);
             mrow[nq] = m2;
             lrow[nq] = psum;
         }
@@ -1237,6 +1248,7 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
             const unsigned char *vhi = vlo + 16 * kVRow;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
+                if (dt % 4 == 0) __builtin_amdgcn_sched_barrier(0);
                 const u32x2 lo = lds_read_tr16(vlo + dt * 32);
                 const u32x2 hi = lds_read_tr16(vhi + dt * 32);
                 const u32x4 vbv = {lo[0], lo[1], hi[0], hi[1]};
@@ -1248,7 +1260,7 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
 #pragma unroll
         for (int nq = 0; nq < kPfNq; ++nq) {
             if (cent[nq] < 0) continue;
-            const int64_t slot = (((int64_t)b * rows + (cent[nq] >> 5)) * G + g) * K + (cent[nq] & 31);
+            const int64_t slot = (((int64_t)b * rows + (cent[nq] >> 5)) * ng + gl) * K + (cent[nq] & 31);
             if (kg == 0) part_ml[slot * R + col % R] = make_float2(mrow[nq], lrow[nq]);
             bf16_t *op = part_o + (slot * R + col % R) * D + 4 * kg;
             const float inv = 1.f / lrow[nq];
@@ -1258,6 +1270,18 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
                     u32x2{pack_bf16x2(o[nq][dt][0] * inv, o[nq][dt][1] * inv),
                           pack_bf16x2(o[nq][dt][2] * inv, o[nq][dt][3] * inv)};
         }
+    };
+    int entA[kPfNq], pcolA[kPfNq], entB[kPfNq], pcolB[kPfNq];
+    bf16x8 qA[kPfNq][4], qB[kPfNq][4];
+    int e0 = wave * kPfNq * et;
+    if (e0 < nent) load_round(e0, entA, pcolA, qA);
+    if (e0 + round_step < nent) load_round(e0 + round_step, entB, pcolB, qB);
+    while (e0 < nent) {
+        do_round(e0, entA, pcolA, qA);
+        e0 += round_step;
+        if (e0 >= nent) break;
+        do_round(e0, entB, pcolB, qB);
+        e0 += round_step;
     }
 }
 
@@ -1268,15 +1292,15 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const bf16_t *__restrict__ part_o,
     const float2 *__restrict__ part_ml, int T, int G, int R, int Nmax, int K, int t0, int rows,
-    bf16_t *__restrict__ out, float *__restrict__ lse) {
+    int g0, int ng, bf16_t *__restrict__ out, float *__restrict__ lse) {
     __shared__ int32_t s_sel[KMAX];
     __shared__ int32_t s_kept[KMAX];
     __shared__ int32_t s_n;
     __shared__ float2 s_ml[KMAX * msa::kMaxHeadsPerGroup];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int64_t unit = blockIdx.x;  // (b, tl, g)
-    const int g = (int)(unit % G);
-    const int64_t btl = unit / G;
+    const int64_t unit = blockIdx.x;  // (b, tl, gl), group g0 + gl
+    const int g = g0 + (int)(unit % ng);
+    const int64_t btl = unit / ng;
     const int b = (int)(btl / rows), tl = (int)(btl % rows);
     const int t = t0 + tl;
     if (t >= T) return;
@@ -1667,19 +1691,21 @@ msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, 
     bf16_t *part_o = reinterpret_cast<bf16_t *>(base + w.part_o_off);
     float2 *part_ml = reinterpret_cast<float2 *>(base + w.part_ml_off);
     const unsigned slot_blocks = (unsigned)((w.nslots + 255) / 256);
-    for (int32_t t0 = 0; t0 < T; t0 += w.rows) {
+    for (int32_t g0 = 0; g0 < G; g0 += w.groups)
+      for (int32_t t0 = 0; t0 < T; t0 += w.rows) {
+        const int ng = w.groups;
         fill_i32_kernel<<<(unsigned)((w.nlists + 255) / 256), 256, 0, st>>>(counts, w.nlists, 0);
         pf_count_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
-                                                     w.rows, w.nb_max, counts, rank);
+                                                     w.rows, g0, ng, w.nb_max, counts, rank);
         pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets,
                                            tile_first, tile_map);
         pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, rank, offsets, B, T, G, K, t0, w.rows,
-                                                       w.nb_max, list);
+                                                       g0, ng, w.nb_max, list);
         pf_attn_kernel<<<(unsigned)w.max_tiles, 256, 0, st>>>(
             qp, kp, vp, kv_lens, q_start, offsets, tile_first, tile_map, list, w.nlists, T, G, R,
-            Nmax, K, t0, w.rows, w.nb_max, w.entries_per_tile, sl2, part_o, part_ml);
-        pf_merge_kernel<<<(unsigned)((int64_t)B * w.rows * G), 256, 0, st>>>(
-            sel, kv_lens, q_start, part_o, part_ml, T, G, R, Nmax, K, t0, w.rows, op, lse);
+            Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2, part_o, part_ml);
+        pf_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), 256, 0, st>>>(
+            sel, kv_lens, q_start, part_o, part_ml, T, G, R, Nmax, K, t0, w.rows, g0, ng, op, lse);
         s = launch_status("sparse prefill kernels");
         if (s != MSA_OK) return s;
     }
