@@ -292,3 +292,54 @@ def test_fp8_index_matches_oracle(orc, B, T, N, lens, qstart, decode):
     torch.cuda.synchronize()
     want = orc.index_pool(oracle_cfg(G, R, K, True), pr["qi"], pr["ki"], kv, qs)
     assert np.array_equal(pooled.cpu().numpy().astype(np.float64).reshape(want.shape), want)
+
+
+def test_kv_major_prefill_caller_selection_and_empty_rows(orc):
+    """The KV-major sparse prefill (>= 256 (row, group) pairs) with a caller
+    selection holding repeats, negative and out-of-range ids, and rows past
+    the cache (empty)."""
+    G, R, K, N, T = 2, 4, 8, 3000, 300
+    pr = random_problem(1, T, N, G, R, seed=1700)
+    rng = np.random.default_rng(17)
+    sel = rng.integers(-3, 26, size=(1, T, G, K)).astype(np.int32)
+    sel[0, :, :, 1] = sel[0, :, :, 0]
+    kv, qs = np.array([2900], np.int32), np.array([2650], np.int32)  # rows 250.. sit at p >= 2900
+    _, _, out, lse = run_gpu(pr, G, R, K, kv, qs, sel_override=sel)
+    assert (out[0, 250:] == 0).all() and np.isneginf(lse[0, 250:]).all()
+    rows = np.array([(0, i) for i in range(250)], np.int32)
+    oout, olse = orc.sparse_attn(oracle_cfg(G, R, K), pr["q"], pr["k"], pr["v"], kv, qs,
+                                 sel[0, :250].reshape(250, G, K), rows=rows)
+    compare_out(out[0, :250].reshape(oout.shape), oout, "kv-major caller sel")
+    compare_lse(lse[0, :250].reshape(olse.shape), olse, "kv-major caller sel")
+
+
+def test_kv_major_prefill_workspace_reuse(orc):
+    """Garbage-filled prefill workspace reused across calls of different
+    shapes gives the same bits as fresh workspaces."""
+    G, R, K, N = 4, 8, 16, 5000
+    cfg = lib_cfg(G, R, K)
+    ws = msa.workspace(cfg, 2, 400, N, msa.WS_SPARSE_PREFILL).random_(0, 256)
+    for trial, (B, T, lens, qs) in enumerate([(2, 400, [5000, 2000], [4600, 1600]),
+                                              (1, 300, [4000], [0]),
+                                              (2, 128, [5000, 129], [4872, 1])]):
+        pr = random_problem(B, T, N, G, R, seed=1800 + trial)
+        kv, qsd = dev_i32(lens), dev_i32(qs)
+        qi, ki = dev_index(pr["qi"]), dev_index(pr["ki"])
+        q, k, v = dev_bf16(pr["q"]), dev_bf16(pr["k"]), dev_bf16(pr["v"])
+        say("prefill workspace reuse trial %d B=%d T=%d" % (trial, B, T))
+        sel = msa.index_topk(cfg, qi, ki, kv, qsd)
+        out = msa.sparse_attn_prefill(cfg, q, k, v, kv, sel, q_start=qsd, workspace=ws)
+        out_f = msa.sparse_attn_prefill(cfg, q, k, v, kv, sel, q_start=qsd)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_f)
+
+
+@pytest.mark.parametrize("G,R,K,T,N,fp8", [(2, 16, 32, 300, 4500, True), (4, 16, 16, 100, 3000, False),
+                                          (1, 3, 5, 700, 2000, False), (3, 1, 32, 200, 6000, True)])
+def test_prefill_paths_more_shapes(orc, G, R, K, T, N, fp8):
+    """E4M3 with K = 32 (32-slot register top-K), R = 16 (one entry per query
+    tile), R = 3 (tiles of 5 entries), R = 1; all through the KV-major path."""
+    lim = 16 if fp8 else 4
+    pr = random_problem(2, T, N, G, R, seed=1900 + G + R + K + T, fp8=fp8, idx_lo=-lim, idx_hi=lim)
+    check_all_rows(orc, pr, G, R, K, [N, N - 300], None, fp8=fp8,
+                   what="G%d R%d K%d T%d fp8=%d" % (G, R, K, T, fp8))
