@@ -16,7 +16,10 @@ selections. The prefill leg (131072-token prefill, 32 heads / 4 groups) is
 reported alongside in TFLOP/s against the bf16 MFMA peak. The CPU oracle is
 timed on a bounded sample of the same decode batch.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
+The 1M-token prefill in 32768-row chunks with E4M3 index data is timed too
+(index TFLOP/s against the fp8 MFMA peak).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-chunked]
 """
 from __future__ import annotations
 
@@ -205,6 +208,28 @@ def cpu_baseline_decode(w, host, budget_rows=None):
                        (rows, w.B, w.Nmax, dt))
 
 
+def sparse_work(torch, w, sel, q0):
+    """Algorithmic flops of the sparse branch (4*d per (row, head, attended
+    key), counted exactly from the selection) and the irreducible bytes of
+    the KV-major schedule: each kept (row, group, slot) reads the row's R
+    query heads once and writes and reads back one partial (R x (2d + 8) B),
+    plus the output and every kept block's K and V once."""
+    L = sel.shape[1]
+    pos = torch.arange(L, device="cuda", dtype=torch.int64).view(1, L, 1, 1) + q0
+    s64 = sel.to(torch.int64)
+    valid = (s64 >= 0) & (s64 * 128 <= pos)
+    keys = torch.clamp(pos - s64 * 128 + 1, max=128) * valid
+    n_keys = float(keys.sum().item())
+    n_slots = float(valid.sum().item())
+    n_blocks = 0
+    for g in range(w.G):
+        n_blocks += int(torch.unique(s64[..., g, :][valid[..., g, :]]).numel())
+    f_att = 4.0 * 128 * w.R * n_keys
+    nbytes = (n_slots * w.R * 128 * 2 + 2 * n_slots * w.R * (128 * 2 + 8) +
+              L * w.H * 128 * 2 + n_blocks * 128 * 128 * 2 * 2)
+    return f_att, nbytes
+
+
 def run_prefill(torch, msa, w, steps=2, warmup=1):
     import numpy as np
     from msa_synth import workloads as wl
@@ -235,24 +260,76 @@ def run_prefill(torch, msa, w, steps=2, warmup=1):
         if s >= warmup:
             idx_ms.append(ev[0].elapsed_time(ev[1]))
             att_ms.append(ev[1].elapsed_time(ev[2]))
-    # Algorithmic flops: index = 2*dI*G per (row, key <= p); sparse = 4*d per
-    # (row, head, attended key), counted exactly from the selection.
     L = w.T
     f_idx = 2.0 * 128 * w.G * L * (L + 1) / 2
-    pos = torch.arange(L, device="cuda", dtype=torch.int64).view(1, L, 1, 1) + w.q_start[0]
-    s64 = sel.to(torch.int64)
-    valid = (s64 >= 0) & (s64 * 128 <= pos)
-    keys = torch.clamp(pos - s64 * 128 + 1, max=128) * valid
-    n_keys = float(keys.sum().item())
-    f_att = 4.0 * 128 * w.R * n_keys
+    f_att, kv_bytes = sparse_work(torch, w, sel, w.q_start[0])
     ti, ta = min(idx_ms), min(att_ms)
     res = dict(workload=w.name, index_ms=round(ti, 3), sparse_ms=round(ta, 3),
                index_tflops=round(f_idx / ti / 1e9, 2), sparse_tflops=round(f_att / ta / 1e9, 2),
                index_flops=f_idx, sparse_flops=f_att,
                index_frac_bf16_peak=round(f_idx / ti / 1e9 / BF16_PEAK_TFLOPS, 4),
                sparse_frac_bf16_peak=round(f_att / ta / 1e9 / BF16_PEAK_TFLOPS, 4),
+               sparse_schedule_bytes=kv_bytes,
+               sparse_schedule_gbs=round(kv_bytes / ta / 1e6, 1),
                total_tflops=round((f_idx + f_att) / (ti + ta) / 1e9, 2))
     del q, qi, k, v, ki, sel, out, ws_i
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_chunked(torch, msa, w):
+    """The 1M-token prefill in 32768-row chunks with E4M3 index data: every
+    chunk runs msa_index_topk and msa_sparse_attn_prefill over the cache of
+    the tokens before and in it. Inputs are generated once and resident in
+    HBM; one untimed pass, then one timed pass of all chunks."""
+    import numpy as np
+    from msa_synth import workloads as wl
+    t0 = time.time()
+    alloc = pinned(torch)
+    kh, vh, kih = wl.gen_caches(w, alloc=alloc)
+    qh, qih = wl.gen_queries(w, row0=0, rows=w.Nmax, alloc=alloc)
+    log("chunked-prefill inputs generated in %.1fs" % (time.time() - t0))
+    k, v, ki = to_dev(torch, kh), to_dev(torch, vh), to_dev(torch, kih, bf16=False)
+    q, qi = to_dev(torch, qh), to_dev(torch, qih, bf16=False)
+    del kh, vh, kih, qh, qih
+    qi = qi.view(torch.float8_e4m3fn)
+    ki = ki.view(torch.float8_e4m3fn)
+    C, L = w.chunk, w.Nmax
+    cfg = msa.Config(num_kv_groups=w.G, heads_per_group=w.R, topk=w.topk, index_dtype=msa.FP8_E4M3)
+    ws_p = msa.workspace(cfg, 1, C, L, msa.WS_SPARSE_PREFILL)
+    sel = torch.empty((1, C, w.G, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, C, w.H, 128), dtype=torch.bfloat16, device="cuda")
+    lens = [torch.tensor([(c + 1) * C], dtype=torch.int32, device="cuda") for c in range(L // C)]
+    starts = [torch.tensor([c * C], dtype=torch.int32, device="cuda") for c in range(L // C)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L // C)]
+    f_att = 0.0
+    for rep in range(2):
+        timed_pass = rep == 1
+        for c in range(L // C):
+            rows = slice(c * C, (c + 1) * C)
+            if timed_pass:
+                ev[c][0].record()
+            msa.index_topk(cfg, qi[:, rows], ki, lens[c], starts[c], sel=sel)
+            if timed_pass:
+                ev[c][1].record()
+            msa.sparse_attn_prefill(cfg, q[:, rows], k, v, lens[c], sel, q_start=starts[c],
+                                    out=out, workspace=ws_p)
+            if timed_pass:
+                ev[c][2].record()
+                torch.cuda.synchronize()
+                f_att += sparse_work(torch, w, sel, c * C)[0]
+        torch.cuda.synchronize()
+    ti = sum(e[0].elapsed_time(e[1]) for e in ev)
+    ta = sum(e[1].elapsed_time(e[2]) for e in ev)
+    f_idx = 2.0 * 128 * w.G * L * (L + 1) / 2
+    res = dict(workload=w.name, chunks=L // C, index_ms=round(ti, 2), sparse_ms=round(ta, 2),
+               index_tflops=round(f_idx / ti / 1e9, 2),
+               index_frac_fp8_peak=round(f_idx / ti / 1e9 / FP8_PEAK_TFLOPS, 4),
+               sparse_tflops=round(f_att / ta / 1e9, 2),
+               sparse_frac_bf16_peak=round(f_att / ta / 1e9 / BF16_PEAK_TFLOPS, 4),
+               total_tflops=round((f_idx + f_att) / (ti + ta) / 1e9, 2),
+               note="index in E4M3 (mixed precision total)")
+    del q, qi, k, v, ki, sel, out, ws_p
     torch.cuda.empty_cache()
     return res
 
@@ -304,6 +381,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (the reference kernel for "
                          "scaling HBM byte counters)")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the 1M-token chunked prefill with E4M3 index data")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling its kernels)")
     args = ap.parse_args()
@@ -321,8 +400,11 @@ def main():
     msa.load()
 
     if args.prefill_only:
-        print(json.dumps({"prefill": run_prefill(torch, msa, wl.workload(3), steps=args.steps,
-                                                 warmup=args.warmup)}), flush=True)
+        res = {"prefill": run_prefill(torch, msa, wl.workload(3), steps=args.steps,
+                                      warmup=args.warmup)}
+        if not args.no_chunked:
+            res["chunked_prefill"] = run_chunked(torch, msa, wl.workload(5))
+        print(json.dumps(res), flush=True)
         return
     w = wl.workload(2)
     res = run_decode(torch, msa, w, args.steps, args.warmup)
@@ -363,6 +445,8 @@ def main():
     res.pop("host")
     if not args.no_prefill:
         line["prefill"] = run_prefill(torch, msa, wl.workload(3))
+    if not args.no_prefill and not args.no_chunked:
+        line["chunked_prefill"] = run_chunked(torch, msa, wl.workload(5))
     print(json.dumps(line), flush=True)
 
 
