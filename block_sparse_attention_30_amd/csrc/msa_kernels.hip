@@ -31,8 +31,12 @@
 //   sparse_decode_kernel (decode) one 8-wave workgroup per (sequence, group,
 //                        split), one 32-token chunk per wave; optionally ranks
 //                        the row's blocks itself; waves merge in LDS into a
-//                        partial per split.
-//   combine_kernel       (decode) log-sum-exp merge of the split partials.
+//                        partial per split; with arrival counters (msa_decode)
+//                        the last split of a (sequence, group) merges them all.
+//   combine_kernel       (msa_sparse_attn_decode) log-sum-exp merge of the
+//                        split partials.
+//   fill_i32_kernel      zeroes the prefill list counters (no memset, so the
+//                        calls can be captured in graphs).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -621,7 +625,10 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
         if (blk + 1 < nblk) load_block(blk + 1);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block's LDS rows are written
         __builtin_amdgcn_s_barrier();
-        const bool need_mask = tok0 + S - 1 > p_lo;
+        // Only blocks that reach past the first row's position need the causal
+        // mask; the test is uniform, so the other blocks take a branch with
+        // the plain max.
+        const bool need_mask = __builtin_amdgcn_readfirstlane(tok0 + S - 1 > p_lo ? 1 : 0) != 0;
         float cm0 = -INFINITY, cm1 = -INFINITY;
         // Two row tiles at a time: four independent accumulator chains.
 #pragma unroll
@@ -645,19 +652,31 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
                     }
                 }
             }
+            // (E4M3 only: with its MFMAs twice as fast the epilogue dominates;
+            // the bf16 kernel measured faster with the if-converted form.)
+            if (F8 && !need_mask) {
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int rt = 2 * rp + h2;
+                for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int tok = tok0 + rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                    float s0 = acc[h2][0][i], s1 = acc[h2][1][i];
-                    if (need_mask) {
-                        if (tok > pcol[0]) s0 = -INFINITY;
-                        if (tok > pcol[1]) s1 = -INFINITY;
+                    for (int i = 0; i < 16; ++i) {
+                        cm0 = fmaxf(cm0, acc[h2][0][i]);
+                        cm1 = fmaxf(cm1, acc[h2][1][i]);
                     }
-                    cm0 = fmaxf(cm0, s0);
-                    cm1 = fmaxf(cm1, s1);
+            } else {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int rt = 2 * rp + h2;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int tok = tok0 + rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                        float s0 = acc[h2][0][i], s1 = acc[h2][1][i];
+                        if (need_mask) {
+                            if (tok > pcol[0]) s0 = -INFINITY;
+                            if (tok > pcol[1]) s1 = -INFINITY;
+                        }
+                        cm0 = fmaxf(cm0, s0);
+                        cm1 = fmaxf(cm1, s1);
+                    }
                 }
             }
         }
