@@ -180,7 +180,55 @@ def run_decode(torch, msa, w, steps, warmup, nsets=8):
     host = dict(k=np_view(kh), v=np_view(vh), ki=np_view(kih), q=np_view(sets[0][0]),
                 qi=np_view(sets[0][1]))
     return dict(ms_per_step=ms_total, wall_s=wall, graph_ms=ms_graph, two_call_ms=ms_two,
-                idx_ms=idx_ms, att_ms=att_ms, pool_ms=pool_ms, host=host)
+                idx_ms=idx_ms, att_ms=att_ms, pool_ms=pool_ms, host=host, k=k, v=v)
+
+
+def run_decode_fp8_index(torch, msa, w, k, v, steps, warmup, nsets=8):
+    """The same decode step with E4M3 index queries and keys (the K/V caches
+    of the bf16 run, already on the GPU): msa_decode back to back, and the
+    index scan alone through msa_index_pool."""
+    from msa_synth import workloads as wl
+    alloc = pinned(torch)
+    ki = to_dev(torch, wl.gen_index_cache(w, alloc=alloc), bf16=False).view(torch.float8_e4m3fn)
+    qs = []
+    for s in range(nsets):
+        qh, qih = wl.gen_queries(w, set_id=s, alloc=alloc)
+        qs.append((to_dev(torch, qh), to_dev(torch, qih, bf16=False).view(torch.float8_e4m3fn)))
+    kv = torch.tensor(w.kv_lens, dtype=torch.int32, device="cuda")
+    cfg = msa.Config(num_kv_groups=w.G, heads_per_group=w.R, topk=w.topk,
+                     index_dtype=msa.FP8_E4M3)
+    ws = msa.workspace(cfg, w.B, 1, w.Nmax, msa.WS_DECODE)
+    sel = torch.empty((w.B, 1, w.G, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, 1, w.H, 128), dtype=torch.bfloat16, device="cuda")
+    pooled = torch.full((w.B, 1, w.G, -(-w.Nmax // 128)), float("-inf"), dtype=torch.float32,
+                        device="cuda")
+
+    def run(fn):
+        for s in range(warmup):
+            fn(s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for s in range(steps):
+            fn(warmup + s)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms_step = run(lambda s: msa.decode(cfg, qs[s % nsets][0], qs[s % nsets][1], ki, k, v, kv,
+                                       sel=sel, out=out, workspace=ws))
+    ms_pool = run(lambda s: msa.index_pool(cfg, qs[s % nsets][1], ki, kv, pooled=pooled))
+    nbytes, kidx_bytes = decode_bytes(w)
+    scan_bytes = kidx_bytes + w.B * w.G * 128 + w.B * w.G * (-(-w.Nmax // 128)) * 4
+    del ki, qs, ws, pooled
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms_per_step": round(ms_step, 5),
+            "GB/s": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
+            "frac_hbm_peak": round(nbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": nbytes,
+            "idx_scan_kernel<true> (via msa_index_pool)": {
+                "ms": round(ms_pool, 5), "bytes": scan_bytes,
+                "GB/s": round(scan_bytes / (ms_pool * 1e-3) / 1e9, 2)}}
 
 
 def cpu_baseline_decode(w, host, budget_rows=None):
@@ -371,6 +419,41 @@ def copy_calibration(torch, mib=512, reps=5):
     return {"bytes_read": mib << 20, "bytes_written": mib << 20, "ms": round(ms, 5)}
 
 
+def read_ceiling(torch, mib=512, reps=20):
+    """The HBM read ceiling measured live: a plain streaming read of `mib` MiB
+    (16-byte loads, nothing stored) from the benchmark's probe library, best
+    of two workgroup counts, back-to-back launches between two events."""
+    import ctypes
+    path = os.path.join(ROOT, "block_sparse_attention_30_amd", "libmsa_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.msa_probe_stream_read.restype = ctypes.c_int
+    lib.msa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = mib << 20
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = 0.0
+    for wgs in (2048, 16384):
+        def launch():
+            rc = lib.msa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, wgs,
+                                           ctypes.c_void_p(sink.data_ptr()), stream)
+            if rc != 0:
+                raise RuntimeError("stream-read probe failed: %d" % rc)
+        for _ in range(3):
+            launch()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            launch()
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9)
+    del buf, sink
+    return round(best, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -438,11 +521,20 @@ def main():
                      "algorithmic_bytes_per_launch": scan_bytes,
                      "launch_ms": round(res["pool_ms"], 5)},
     }
+    ceiling = read_ceiling(torch)
+    line["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling, 4)
+    line["read_ceiling"] = {"value": ceiling, "unit": "GB/s",
+                            "what": "plain streaming read of 512 MiB (16-byte loads, best of "
+                                    "2048 and 16384 workgroups), measured in this run"}
     if args.calibrate_copy:
         line["copy_calibration"] = copy_calibration(torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(w, res["host"])
     res.pop("host")
+    line["decode_fp8_index"] = run_decode_fp8_index(torch, msa, wl.workload(2, fp8_index=True),
+                                                    res.pop("k"), res.pop("v"), args.steps,
+                                                    args.warmup)
+    torch.cuda.empty_cache()
     if not args.no_prefill:
         line["prefill"] = run_prefill(torch, msa, wl.workload(3))
     if not args.no_prefill and not args.no_chunked:

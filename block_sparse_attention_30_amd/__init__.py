@@ -96,8 +96,9 @@ def load():
                                             vp, sz, vp]
     lib.msa_sparse_attn_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_cache_append.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in (lib.msa_index_topk, lib.msa_index_pool, lib.msa_sparse_attn_prefill,
-              lib.msa_sparse_attn_decode, lib.msa_decode):
+              lib.msa_sparse_attn_decode, lib.msa_decode, lib.msa_cache_append):
         f.restype = ctypes.c_int
     lib.msa_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
     lib.msa_workspace_size.restype = sz
@@ -353,3 +354,31 @@ def decode(cfg: Config, q, q_idx, k_idx, k_cache, v_cache, kv_lens, sel=None, se
     if want_scores or want_lse or sel_scores is not None or lse is not None:
         return sel, sel_scores, out, lse
     return sel, out
+
+
+def cache_append(cfg: Config, k_new, v_new, k_idx_new, pos0, k_cache, v_cache, k_idx):
+    """Writes T new tokens per sequence into the caches, in place: row t of
+    sequence b goes to position pos0[b] + t (rows outside [0, Nmax) are
+    skipped). k_new, v_new [B,T,G,d] bf16; k_idx_new [B,T,dI] in the index
+    dtype; pos0 [B] int32; k_cache, v_cache [B,G,Nmax,d]; k_idx [B,Nmax,dI]."""
+    dev = k_cache.device
+    _need(k_new, "k_new", (torch.bfloat16,), 4, dev)
+    _need(v_new, "v_new", (torch.bfloat16,), 4, dev)
+    _need(k_idx_new, "k_idx_new", _INDEX_DTYPES[cfg.index_dtype], 3, dev)
+    _need(k_cache, "k_cache", (torch.bfloat16,), 4, dev)
+    _need(v_cache, "v_cache", (torch.bfloat16,), 4, dev)
+    _need(k_idx, "k_idx", _INDEX_DTYPES[cfg.index_dtype], 3, dev)
+    B, G, Nmax, d = k_cache.shape
+    T = k_new.shape[1]
+    if G != cfg.num_kv_groups or d != cfg.head_dim or tuple(v_cache.shape) != (B, G, Nmax, d):
+        raise ValueError("k_cache/v_cache must be [B,G,Nmax,d] for the config")
+    if tuple(k_new.shape) != (B, T, G, d) or tuple(v_new.shape) != (B, T, G, d):
+        raise ValueError("k_new/v_new must be [B,T,G,d]")
+    if tuple(k_idx.shape) != (B, Nmax, cfg.index_dim) or \
+            tuple(k_idx_new.shape) != (B, T, cfg.index_dim):
+        raise ValueError("k_idx must be [B,Nmax,dI] and k_idx_new [B,T,dI]")
+    _lens(pos0, "pos0", B, dev)
+    with _on_device(dev):
+        _check(load().msa_cache_append(ctypes.byref(cfg._c()), B, T, Nmax, _ptr(k_new),
+                                       _ptr(v_new), _ptr(k_idx_new), _ptr(pos0), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(k_idx), _stream(dev)))

@@ -1,5 +1,6 @@
 """Builds libmsa.so in-tree: the host validation unit with g++, the gfx950
-kernels with hipcc, linked into one shared library next to this file."""
+kernels with hipcc, linked into one shared library next to this file; and
+libmsa_probe.so, the benchmark's streaming-read probe."""
 from __future__ import annotations
 
 import os
@@ -11,6 +12,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libmsa.so")
+# The benchmark's streaming-read probe (measured HBM read ceiling), a
+# separate object: nothing in libmsa uses it.
+PROBE_LIBRARY = os.path.join(PKG, "libmsa_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 
@@ -46,10 +50,14 @@ def build(verbose: bool = False) -> str:
         tmp = LIBRARY + ".tmp%d" % os.getpid()
         run([_hipcc(), "-shared", "-fPIC", kern_o, host_o, "-o", tmp,
              "-Wl,-rpath,/opt/rocm/lib"])
+        probe_tmp = PROBE_LIBRARY + ".tmp%d" % os.getpid()
+        run([_hipcc()] + HIPCC_FLAGS + ["-shared", os.path.join(CSRC, "read_probe.hip"), "-o",
+                                        probe_tmp, "-Wl,-rpath,/opt/rocm/lib"])
     except subprocess.CalledProcessError as exc:
         out = exc.stdout.decode(errors="replace") if exc.stdout else ""
         raise RuntimeError("libmsa build failed:\n" + out) from exc
     os.replace(tmp, LIBRARY)
+    os.replace(probe_tmp, PROBE_LIBRARY)
     return LIBRARY
 
 

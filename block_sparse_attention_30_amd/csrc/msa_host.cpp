@@ -181,6 +181,26 @@ msa_status check_pool_args(const msa_config *cfg, int32_t B, int32_t T, int32_t 
     return MSA_OK;
 }
 
+msa_status check_append_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                             const void *k_new, const void *v_new, const void *k_idx_new,
+                             const int32_t *pos0, const void *k_cache, const void *v_cache,
+                             const void *k_idx) {
+    msa_status s = check_config(cfg);
+    if (s != MSA_OK) return s;
+    if ((s = check_dims(B, T, Nmax)) != MSA_OK) return s;
+    if (B == 0 || T == 0) return MSA_OK;
+    if ((int64_t)B * T > ((int64_t)1 << 31) - 1)
+        return fail(MSA_ERR_UNSUPPORTED, "B*T exceeds 2^31-1 rows");
+    if (!k_new || !v_new || !k_idx_new || !pos0 || !k_cache || !v_cache || !k_idx)
+        return fail(MSA_ERR_INVALID_ARG,
+                    "k_new, v_new, k_idx_new, pos0, k_cache, v_cache and k_idx must not be NULL");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_idx_new, 16) ||
+        !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_idx, 16))
+        return fail(MSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (!aligned(pos0, 4)) return fail(MSA_ERR_INVALID_ARG, "pos0 must be 4-byte aligned");
+    return MSA_OK;
+}
+
 msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                              const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *kv_lens, const int32_t *q_start, const int32_t *sel,

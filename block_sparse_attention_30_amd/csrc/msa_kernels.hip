@@ -37,6 +37,8 @@
 //                        split partials.
 //   fill_i32_kernel      zeroes the prefill list counters (no memset, so the
 //                        calls can be captured in graphs).
+//   cache_append_kernel  (msa_cache_append) copies new K, V and index-key rows
+//                        into the caches, one wavefront per (sequence, row).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -1020,6 +1022,32 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t *__restrict__ p, 
     if (i < n) p[i] = v;
 }
 
+// One wavefront per new (sequence, row): the row's G K rows and G V rows
+// (256 B each) and its index key (kib bytes) are copied 16 B per lane.
+__global__ __launch_bounds__(256) void cache_append_kernel(
+    const u32x4 *__restrict__ k_new, const u32x4 *__restrict__ v_new,
+    const unsigned char *__restrict__ ki_new, const int32_t *__restrict__ pos0, int B, int T,
+    int G, int Nmax, int kib, u32x4 *__restrict__ k_cache, u32x4 *__restrict__ v_cache,
+    unsigned char *__restrict__ k_idx) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * T + t
+    if (row >= (int64_t)B * T) return;
+    const int b = (int)(row / T), t = (int)(row % T);
+    const int64_t pos = (int64_t)pos0[b] + t;
+    if (pos < 0 || pos >= Nmax) return;
+    constexpr int kPieces = D * 2 / 16;  // 16-byte pieces per K or V row
+    for (int i = lane; i < G * kPieces; i += 64) {
+        const int g = i / kPieces, c = i % kPieces;
+        const int64_t dst = (((int64_t)b * G + g) * Nmax + pos) * kPieces + c;
+        k_cache[dst] = k_new[row * G * kPieces + i];
+        v_cache[dst] = v_new[row * G * kPieces + i];
+    }
+    const int ki_pieces = kib / 16;
+    if (lane < ki_pieces)
+        reinterpret_cast<u32x4 *>(k_idx + ((int64_t)b * Nmax + pos) * kib)[lane] =
+            reinterpret_cast<const u32x4 *>(ki_new + row * kib)[lane];
+}
+
 // Row position helper shared by the pass kernels: returns p (or -1 when the
 // row is outside the cache or past T).
 __device__ __forceinline__ int pf_row_pos(const int32_t *kv_lens, const int32_t *q_start, int b,
@@ -1771,6 +1799,25 @@ msa_status msa_sparse_attn_decode(const msa_config *cfg, int32_t B, int32_t Nmax
                                    reinterpret_cast<float *>(base + w.part_o_off),
                                    reinterpret_cast<float *>(base + w.part_ml_off),
                                    reinterpret_cast<hipStream_t>(stream));
+}
+
+msa_status msa_cache_append(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                            const void *k_new, const void *v_new, const void *k_idx_new,
+                            const int32_t *pos0, void *k_cache, void *v_cache, void *k_idx,
+                            void *stream) {
+    msa::clear_error();
+    msa_status s = msa::check_append_args(cfg, B, T, Nmax, k_new, v_new, k_idx_new, pos0,
+                                          k_cache, v_cache, k_idx);
+    if (s != MSA_OK || B == 0 || T == 0) return s;
+    const int64_t rows = (int64_t)B * T;
+    const int kib = DI * (cfg->index_dtype == MSA_FP8_E4M3 ? 1 : 2);
+    cache_append_kernel<<<(unsigned)((rows + 3) / 4), 256, 0,
+                          reinterpret_cast<hipStream_t>(stream)>>>(
+        static_cast<const u32x4 *>(k_new), static_cast<const u32x4 *>(v_new),
+        static_cast<const unsigned char *>(k_idx_new), pos0, B, T, cfg->num_kv_groups, Nmax, kib,
+        static_cast<u32x4 *>(k_cache), static_cast<u32x4 *>(v_cache),
+        static_cast<unsigned char *>(k_idx));
+    return launch_status("cache append kernel");
 }
 
 msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,

@@ -40,10 +40,11 @@
  * Ownership and streams: the caller owns every buffer. The library allocates
  * nothing, keeps no state between calls and never synchronises: every call
  * enqueues its kernels on `stream` and returns. Scratch memory comes from the
- * caller's `workspace` (size from msa_workspace_size; msa_sparse_attn_prefill
- * needs none and accepts NULL): plain scratch that needs no initialisation
- * and may be reused by any later call on the same stream. Calls that may run at the
- * same time (other streams) must not share a workspace.
+ * caller's `workspace` (size from msa_workspace_size; a call whose size is 0,
+ * such as msa_index_topk on prefill shapes, accepts NULL): plain scratch that
+ * needs no initialisation and may be reused by any later call on the same
+ * stream. Calls that may run at the same time (other streams) must not share
+ * a workspace.
  *
  * Errors: shapes, pointers, alignment (16 bytes for tensors, 4 for int32 and
  * fp32 arrays, 256 for the workspace) and workspace size are checked on the
@@ -157,6 +158,24 @@ msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void
                       const void *v_cache, const int32_t *kv_lens, int32_t *sel,
                       float *sel_scores, void *out, float *lse, void *workspace, size_t ws_bytes,
                       void *stream);
+
+/*
+ * Appends T new tokens per sequence to the caches that the calls above read
+ * (the decode step's reading of the Tencent article §二 is that the new
+ * token's K, V and index key are in the caches when it attends): for every
+ * sequence b, row t < T and group g, with pos = pos0[b] + t,
+ *   k_cache[b,g,pos,:] = k_new[b,t,g,:]    v_cache[b,g,pos,:] = v_new[b,t,g,:]
+ *   k_idx[b,pos,:]     = k_idx_new[b,t,:]
+ * Rows with pos outside [0, Nmax) are skipped (pos0 lives on the device and is
+ * not checked on the host). Layouts: k_new, v_new [B, T, G, d] bf16;
+ * k_idx_new [B, T, dI] in cfg->index_dtype; pos0 [B] int32. The bytes are
+ * copied unchanged. Needs no workspace. A caller that appends at the old
+ * length then passes kv_lens = old length + T to the calls above.
+ */
+msa_status msa_cache_append(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                            const void *k_new, const void *v_new, const void *k_idx_new,
+                            const int32_t *pos0, void *k_cache, void *v_cache, void *k_idx,
+                            void *stream);
 
 /* Workspace bytes the named call needs for these shapes (0 if none); returns
  * (size_t)-1 for an invalid configuration. For MSA_WS_SPARSE_DECODE and

@@ -47,8 +47,17 @@ class Workload:
         return self.G * self.R
 
 
-def workload(cid, mixed=False, scale=1):
-    """The named workload; `scale` > 1 divides every length (for quick tests)."""
+def workload(cid, mixed=False, scale=1, fp8_index=False):
+    """The named workload; `scale` > 1 divides every length (for quick tests);
+    `fp8_index` stores a decode workload's index data as E4M3FN (same values)."""
+    w = _workload(cid, mixed, scale)
+    if fp8_index and w.phase == "decode":
+        w.index_fp8 = True
+        w.name += "_fp8idx"
+    return w
+
+
+def _workload(cid, mixed, scale):
     if cid == 1:
         L = 4096 // scale
         return Workload(1, "prefill_L%d_G1_R2" % L, "prefill", 1, L, L, [L], [0], G=1, R=2)
@@ -93,11 +102,16 @@ def gen_caches(w: Workload, alloc=None):
     """
     k = _alloc((w.B, w.G, w.Nmax, HEAD_DIM), np.uint16, alloc)
     v = _alloc((w.B, w.G, w.Nmax, HEAD_DIM), np.uint16, alloc)
-    ki = _alloc((w.B, w.Nmax, INDEX_DIM), np.uint8 if w.index_fp8 else np.uint16, alloc)
     fill_normal_bf16(k, stream_seed(w.cid, "k_cache"))
     fill_normal_bf16(v, stream_seed(w.cid, "v_cache"))
+    return k, v, gen_index_cache(w, alloc)
+
+
+def gen_index_cache(w: Workload, alloc=None):
+    """k_idx [B,Nmax,dI] alone (bf16 or E4M3 bits), as gen_caches makes it."""
+    ki = _alloc((w.B, w.Nmax, INDEX_DIM), np.uint8 if w.index_fp8 else np.uint16, alloc)
     _fill_index(ki, stream_seed(w.cid, "k_idx"), 0, w.index_fp8)
-    return k, v, ki
+    return ki
 
 
 def gen_queries(w: Workload, row0=0, rows=None, set_id=0, alloc=None):

@@ -2,7 +2,8 @@
 
 ctypes front end of ``msa_oracle.c``: a plain fp64 statement of the method
 (index scoring, causal block max-pool, top-k, sparse softmax attention; plus
-textbook dense causal attention for invariants). Only the tests, the smoke
+textbook dense causal attention for invariants), and ``cache_append``, the
+cache write of new tokens, in plain numpy. Only the tests, the smoke
 check and the benchmark's CPU-baseline leg may import this package; the GPU
 library never does, and the two share no code.
 
@@ -203,6 +204,30 @@ class Oracle:
         if rc:
             raise ValueError("oracle_dense_causal_rows rejected its arguments")
         return out, lse
+
+
+def cache_append(k_new, v_new, k_idx_new, pos0, k_cache, v_cache, k_idx):
+    """The caches after appending T new tokens per sequence (new arrays; the
+    inputs are not modified). The decode step reads the new token's K, V and
+    index key from the caches (Tencent article, section 二: the index query
+    scores every cached key, the new one included), so each new row t of
+    sequence b is stored at position pos0[b] + t; positions outside the cache
+    [0, Nmax) are skipped. Shapes: k_new, v_new [B,T,G,d]; k_idx_new [B,T,dI];
+    k_cache, v_cache [B,G,Nmax,d]; k_idx [B,Nmax,dI]; any element dtype (the
+    bits are copied unchanged)."""
+    k_cache, v_cache, k_idx = k_cache.copy(), v_cache.copy(), k_idx.copy()
+    B, G, Nmax = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    T = k_new.shape[1]
+    for b in range(B):
+        for t in range(T):
+            pos = int(pos0[b]) + t
+            if pos < 0 or pos >= Nmax:
+                continue
+            for g in range(G):
+                k_cache[b, g, pos, :] = k_new[b, t, g, :]
+                v_cache[b, g, pos, :] = v_new[b, t, g, :]
+            k_idx[b, pos, :] = k_idx_new[b, t, :]
+    return k_cache, v_cache, k_idx
 
 
 def _threads() -> int:

@@ -370,10 +370,62 @@ def pin_mixed_lengths_and_stride(orc, seed=6):
         assert np.allclose(o1[0], out[b], rtol=0, atol=1e-12)
 
 
+def pin_cache_append(orc, seed=7):
+    """Appending the last T tokens of a cache (given as [B,T,G,d] rows) into a
+    cache that lacks them rebuilds the full cache bit for bit, and the decode
+    of the last token then equals the decode on the full cache; rows whose
+    position falls outside the cache are skipped and nothing else changes."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    G, R, d, dI, S, K = 3, 2, 4, 2, 4, 3
+    B, L, T = 2, 29, 3
+    pr = tiny_problem(rng, L, G, R, d, dI, S, K, B=B, T=1)
+    cfg = pr["cfg"]
+    full_k, full_v, full_ki = pr["k_b"], pr["v_b"], pr["ki_b"]
+    # The new rows in the call's layout, written out element by element.
+    k_new = np.zeros((B, T, G, d), np.uint16)
+    v_new = np.zeros((B, T, G, d), np.uint16)
+    ki_new = np.zeros((B, T, dI), np.uint16)
+    for b in range(B):
+        for t in range(T):
+            ki_new[b, t] = full_ki[b, L - T + t]
+            for g in range(G):
+                k_new[b, t, g] = full_k[b, g, L - T + t]
+                v_new[b, t, g] = full_v[b, g, L - T + t]
+    old_k, old_v, old_ki = full_k.copy(), full_v.copy(), full_ki.copy()
+    old_k[:, :, L - T:] = 0x7F80   # +inf bits: must all be overwritten
+    old_v[:, :, L - T:] = 0x7F80
+    old_ki[:, L - T:] = 0x7F80
+    pos0 = np.full(B, L - T, np.int32)
+    nk, nv, nki = oracle.cache_append(k_new, v_new, ki_new, pos0, old_k, old_v, old_ki)
+    assert np.array_equal(nk, full_k) and np.array_equal(nv, full_v)
+    assert np.array_equal(nki, full_ki)
+    assert np.all(old_k[:, :, L - T:] == 0x7F80)   # inputs untouched
+    kv = np.full(B, L, np.int32)
+    qs = kv - 1
+    s_full, _ = orc.index_topk(cfg, pr["qi_b"], full_ki, kv, qs)
+    s_app, _ = orc.index_topk(cfg, pr["qi_b"], nki, kv, qs)
+    assert np.array_equal(s_full, s_app)
+    o_full, l_full = orc.sparse_attn(cfg, pr["q_b"], full_k, full_v, kv, qs, s_full)
+    o_app, l_app = orc.sparse_attn(cfg, pr["q_b"], nk, nv, kv, qs, s_app)
+    assert np.array_equal(o_full, o_app) and np.array_equal(l_full, l_app)
+    # Out-of-range rows are skipped: sequence 0 starts two rows before the
+    # cache end (row 2 falls outside), sequence 1 two rows before position 0.
+    pos0 = np.array([L - 2, -2], np.int32)
+    nk, nv, nki = oracle.cache_append(k_new, v_new, ki_new, pos0, old_k, old_v, old_ki)
+    assert np.array_equal(nk[0, :, L - 2:], k_new[0, :2].transpose(1, 0, 2))
+    assert np.array_equal(nki[0, L - 2:], ki_new[0, :2])
+    assert np.array_equal(nk[1, :, 0], k_new[1, 2]) and np.array_equal(nki[1, 0], ki_new[1, 2])
+    keep = np.ones(nk.shape, bool)
+    keep[0, :, L - 2:] = False
+    keep[1, :, 0] = False
+    assert np.array_equal(nk[keep], old_k[keep]) and np.array_equal(nv[keep], old_v[keep])
+
+
 ALL_PINS = [pin_decoders, pin_hand_example_selection, pin_hand_example_attention,
             pin_hand_example_variants, pin_brute_force_selection,
             pin_token_level_and_single_block, pin_selection_invariants, pin_sparse_vs_numpy,
-            pin_attention_invariants, pin_mixed_lengths_and_stride]
+            pin_attention_invariants, pin_mixed_lengths_and_stride, pin_cache_append]
 
 
 def run_all(orc):

@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_three_entry_points():
     names = declared_functions()
     for n in ("msa_index_topk", "msa_index_pool", "msa_sparse_attn_prefill",
-              "msa_sparse_attn_decode", "msa_decode",
+              "msa_sparse_attn_decode", "msa_decode", "msa_cache_append",
               "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_version"):
         assert n in names
 
@@ -155,6 +155,29 @@ def test_decode_step_validation(lib):
     assert call(ws=None, nws=need) == WORKSPACE
 
 
+def test_cache_append_validation(lib):
+    c = cfg()
+
+    def call(B=2, T=1, N=1024, **kw):
+        a = dict(kn=FAKE, vn=FAKE, kin=FAKE, pos=FAKE, k=FAKE, v=FAKE, ki=FAKE)
+        a.update(kw)
+        return lib.msa_cache_append(ctypes.byref(c), B, T, N, a["kn"], a["vn"], a["kin"],
+                                    a["pos"], a["k"], a["v"], a["ki"], None)
+
+    assert call(B=0) == OK and call(T=0) == OK        # nothing to write
+    for name in ("kn", "vn", "kin", "pos", "k", "v", "ki"):
+        assert call(**{name: None}) == INVALID, name
+    for name in ("kn", "vn", "kin", "k", "v", "ki"):
+        assert call(**{name: FAKE_MIS}) == INVALID, name
+    assert call(pos=ctypes.c_void_p(0x100002)) == INVALID
+    assert call(B=-1) == INVALID and call(N=0) == INVALID
+    assert call(B=70000) == UNSUPPORTED
+    assert lib.msa_cache_append(ctypes.byref(cfg(head_dim=64)), 1, 1, 128, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert b"NULL" in lib.msa_last_error() or b"aligned" in lib.msa_last_error() or \
+        b"head_dim" in lib.msa_last_error()
+
+
 def test_workspace_sizes_follow_shapes(lib):
     c = cfg()
     a = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 0)
@@ -177,3 +200,19 @@ def test_python_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError, match="GPU"):
         msa.index_topk(c, q, torch.zeros(1, 128, 128, dtype=torch.bfloat16),
                        torch.ones(1, dtype=torch.int32))
+
+
+def test_read_probe_loads_and_rejects_bad_arguments():
+    """The benchmark's streaming-read probe (a separate object) loads, and its
+    argument checks run before any launch."""
+    path = os.path.join(os.path.dirname(msa.__file__), "libmsa_probe.so")
+    probe = ctypes.CDLL(path)
+    fn = probe.msa_probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    dummy = ctypes.c_void_p(0x1000)
+    assert fn(None, 1 << 20, 64, dummy, None) == -1
+    assert fn(dummy, 1 << 20, 64, None, None) == -1
+    assert fn(dummy, 1 << 20, 0, dummy, None) == -1
+    assert fn(dummy, (1 << 20) + 16, 64, dummy, None) == -1   # not a multiple of 16 * wgs

@@ -5,6 +5,7 @@ configuration the benchmark uses:
                                                  oracle);
   decode, 4 sequences x 1048576 tokens           every row, uniform lengths and
                                                  mixed {256k, 512k, 768k, 1M};
+  both decode batches with E4M3 index data       every row (uniform lengths);
   prefill, 131072 tokens (4 groups x 8 heads)    a stratified sample of 2048 rows;
   chunked prefill, 1048576 tokens in 32768-row   the first, a middle and the
   chunks, E4M3 index data                        last chunk, about 1500 sampled
@@ -82,6 +83,14 @@ def test_decode_B4_N1M_all_rows(orc):
 
 def test_decode_B4_mixed_lengths_all_rows(orc):
     check_decode_workload(orc, wl.workload(4, mixed=True))
+
+
+def test_decode_B16_N131072_fp8_index_all_rows(orc):
+    check_decode_workload(orc, wl.workload(2, fp8_index=True))
+
+
+def test_decode_B4_N1M_fp8_index_all_rows(orc):
+    check_decode_workload(orc, wl.workload(4, fp8_index=True))
 
 
 def stratified_rows(row0, T, C, n_random, seed):
