@@ -17,7 +17,14 @@ reported alongside in TFLOP/s against the bf16 MFMA peak. The CPU oracle is
 timed on a bounded sample of the same decode batch.
 
 The 1M-token prefill in 32768-row chunks with E4M3 index data is timed too
-(index TFLOP/s against the fp8 MFMA peak).
+(index TFLOP/s against the fp8 MFMA peak), and the decode step with E4M3
+index data on the same caches.
+
+Back-to-back steps re-read the same caches, so part of a working set that
+fits the 256 MB last-level cache may be served from it; each decode leg also
+reports a cold-cache time (a 1 GiB read between steps, per-step events). A
+plain streaming read of 512 MiB, timed in the same run, gives the measured HBM
+read ceiling next to the published 8 TB/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-chunked]
 """
@@ -70,6 +77,49 @@ def decode_bytes(w):
         kept += w.G * min(w.topk, (n - 1) // 128 + 1) * 128 * 128 * 2 * 2
     small = w.B * (w.H * 128 * 2 * 2 + w.G * 128 * (1 if w.index_fp8 else 2) + w.G * w.topk * 4)
     return k_idx + kept + small, k_idx
+
+
+def _probe_lib():
+    """The benchmark's streaming-read probe (libmsa_probe.so)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_30_amd", "libmsa_probe.so"))
+    lib.msa_probe_stream_read.restype = ctypes.c_int
+    lib.msa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def _stream_read(torch, lib, buf, wgs, sink):
+    import ctypes
+    rc = lib.msa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), wgs,
+                                   ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError("stream-read probe failed: %d" % rc)
+
+
+def cold_ms(torch, fn, steps, warmup, flush_cache=True):
+    """Average ms of fn(s) with the last-level cache flushed before each step:
+    a 1 GiB buffer is read between steps (reads, so no dirty lines are left to
+    write back during the step) and every step is bracketed by its own event
+    pair (the events add a few microseconds per step)."""
+    lib = _probe_lib()
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
+    for s in range(warmup):
+        fn(s)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        if flush_cache:
+            _stream_read(torch, lib, flush, 16384, sink)
+        evs[s][0].record()
+        fn(warmup + s)
+        evs[s][1].record()
+    torch.cuda.synchronize()
+    del flush, sink
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
 
 
 def run_decode(torch, msa, w, steps, warmup, nsets=8):
@@ -177,9 +227,12 @@ def run_decode(torch, msa, w, steps, warmup, nsets=8):
     wall0 = time.perf_counter()
     ms_total, _ = timed(step, 0)
     wall = time.perf_counter() - wall0
+    ms_cold = cold_ms(torch, step, steps, warmup)
+    ms_ev = cold_ms(torch, step, steps, warmup, flush_cache=False)
     host = dict(k=np_view(kh), v=np_view(vh), ki=np_view(kih), q=np_view(sets[0][0]),
                 qi=np_view(sets[0][1]))
     return dict(ms_per_step=ms_total, wall_s=wall, graph_ms=ms_graph, two_call_ms=ms_two,
+                cold_ms=ms_cold, events_ms=ms_ev,
                 idx_ms=idx_ms, att_ms=att_ms, pool_ms=pool_ms, host=host, k=k, v=v)
 
 
@@ -215,8 +268,12 @@ def run_decode_fp8_index(torch, msa, w, k, v, steps, warmup, nsets=8):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
-    ms_step = run(lambda s: msa.decode(cfg, qs[s % nsets][0], qs[s % nsets][1], ki, k, v, kv,
-                                       sel=sel, out=out, workspace=ws))
+    def step(s):
+        msa.decode(cfg, qs[s % nsets][0], qs[s % nsets][1], ki, k, v, kv, sel=sel, out=out,
+                   workspace=ws)
+
+    ms_step = run(step)
+    ms_cold = cold_ms(torch, step, steps, warmup)
     ms_pool = run(lambda s: msa.index_pool(cfg, qs[s % nsets][1], ki, kv, pooled=pooled))
     nbytes, kidx_bytes = decode_bytes(w)
     scan_bytes = kidx_bytes + w.B * w.G * 128 + w.B * w.G * (-(-w.Nmax // 128)) * 4
@@ -226,6 +283,8 @@ def run_decode_fp8_index(torch, msa, w, k, v, steps, warmup, nsets=8):
             "GB/s": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
             "frac_hbm_peak": round(nbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_step": nbytes,
+            "cold_cache_ms_per_step": round(ms_cold, 5),
+            "cold_cache_GB/s": round(nbytes / (ms_cold * 1e-3) / 1e9, 2),
             "idx_scan_kernel<true> (via msa_index_pool)": {
                 "ms": round(ms_pool, 5), "bytes": scan_bytes,
                 "GB/s": round(scan_bytes / (ms_pool * 1e-3) / 1e9, 2)}}
@@ -423,23 +482,14 @@ def read_ceiling(torch, mib=512, reps=20):
     """The HBM read ceiling measured live: a plain streaming read of `mib` MiB
     (16-byte loads, nothing stored) from the benchmark's probe library, best
     of two workgroup counts, back-to-back launches between two events."""
-    import ctypes
-    path = os.path.join(ROOT, "block_sparse_attention_30_amd", "libmsa_probe.so")
-    lib = ctypes.CDLL(path)
-    lib.msa_probe_stream_read.restype = ctypes.c_int
-    lib.msa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib = _probe_lib()
     nbytes = mib << 20
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     best = 0.0
     for wgs in (2048, 16384):
         def launch():
-            rc = lib.msa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, wgs,
-                                           ctypes.c_void_p(sink.data_ptr()), stream)
-            if rc != 0:
-                raise RuntimeError("stream-read probe failed: %d" % rc)
+            _stream_read(torch, lib, buf, wgs, sink)
         for _ in range(3):
             launch()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -513,7 +563,10 @@ def main():
                      "two_call_step": round(res["two_call_ms"], 5),
                      "msa_index_pool": round(res["pool_ms"], 5),
                      "msa_index_topk": round(res["idx_ms"], 5),
-                     "msa_sparse_attn_decode": round(res["att_ms"], 5)},
+                     "msa_sparse_attn_decode": round(res["att_ms"], 5),
+                     "msa_decode_cold_cache": round(res["cold_ms"], 5),
+                     "msa_decode_per_step_events_warm": round(res["events_ms"], 5)},
+        "cold_cache_GB/s": round(nbytes / (res["cold_ms"] * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel<false> (bf16 keys, via msa_index_pool)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
