@@ -526,6 +526,11 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(
 // 32x32x64 f8f6f4 MFMAs with unit scales (2 per row tile and column tile).
 constexpr int kPfRows = 256;
 
+template <bool V>
+struct BoolTag {
+    static constexpr bool value = V;
+};
+
 // Running top-KC of one row in registers, for blocks offered in ascending id
 // order: ts/tb are sorted by score, descending; a new block goes after every
 // kept block of equal score (a lower id ranks first). Branch-free: slot i
@@ -547,7 +552,7 @@ __device__ __forceinline__ void topk_insert(float (&ts)[KC], int (&tb)[KC], floa
 // one row, keeps its top-KC blocks in registers while the blocks stream by,
 // and writes sel / sel_scores (first K) at the end; no pooled scores.
 template <bool F8, int KC>
-__global__ __launch_bounds__(256) void idx_prefill_kernel(
+__global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     const unsigned char *__restrict__ q_idx, const unsigned char *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
     float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int K,
@@ -613,8 +618,13 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
             if (tok >= kv) pre[i] = zero4;
         }
     };
-    if (nblk > 0) load_block(0);
-    for (int blk = 0; blk < nblk; ++blk) {
+    // One block: stage it in LDS, prefetch the next, score it, then block max
+    // and top-K insertion. MASK: the block reaches past the first row's
+    // position, so keys past each row's position are masked; the blocks
+    // before that take a plain max (two separate loops, so each is compiled
+    // without the other's epilogue).
+    auto do_block = [&](auto mask_tag, int blk) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int tok0 = blk * S;
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
         __builtin_amdgcn_s_barrier();        // ... and every other wave's
@@ -627,10 +637,6 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
         if (blk + 1 < nblk) load_block(blk + 1);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block's LDS rows are written
         __builtin_amdgcn_s_barrier();
-        // Only blocks that reach past the first row's position need the causal
-        // mask; the test is uniform, so the other blocks take a branch with
-        // the plain max.
-        const bool need_mask = __builtin_amdgcn_readfirstlane(tok0 + S - 1 > p_lo ? 1 : 0) != 0;
         float cm0 = -INFINITY, cm1 = -INFINITY;
         // Two row tiles at a time: four independent accumulator chains.
 #pragma unroll
@@ -654,31 +660,19 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
                     }
                 }
             }
-            // (E4M3 only: with its MFMAs twice as fast the epilogue dominates;
-            // the bf16 kernel measured faster with the if-converted form.)
-            if (F8 && !need_mask) {
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int rt = 2 * rp + h2;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        cm0 = fmaxf(cm0, acc[h2][0][i]);
-                        cm1 = fmaxf(cm1, acc[h2][1][i]);
-                    }
-            } else {
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const int rt = 2 * rp + h2;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
+                for (int i = 0; i < 16; ++i) {
+                    float s0 = acc[h2][0][i], s1 = acc[h2][1][i];
+                    if constexpr (MASK) {
                         const int tok = tok0 + rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                        float s0 = acc[h2][0][i], s1 = acc[h2][1][i];
-                        if (need_mask) {
-                            if (tok > pcol[0]) s0 = -INFINITY;
-                            if (tok > pcol[1]) s1 = -INFINITY;
-                        }
-                        cm0 = fmaxf(cm0, s0);
-                        cm1 = fmaxf(cm1, s1);
+                        if (tok > pcol[0]) s0 = -INFINITY;
+                        if (tok > pcol[1]) s1 = -INFINITY;
                     }
+                    cm0 = fmaxf(cm0, s0);
+                    cm1 = fmaxf(cm1, s1);
                 }
             }
         }
@@ -695,7 +689,12 @@ __global__ __launch_bounds__(256) void idx_prefill_kernel(
                 if (offer) topk_insert<KC>(ts, tb, v, blk);
             }
         }
-    }
+    };
+    // Blocks [0, n_plain) end at or before the first row's position.
+    const int n_plain = p_lo >= 0 ? min((p_lo + 1) / S, nblk) : 0;
+    if (nblk > 0) load_block(0);
+    for (int blk = 0; blk < n_plain; ++blk) do_block(BoolTag<false>{}, blk);
+    for (int blk = n_plain; blk < nblk; ++blk) do_block(BoolTag<true>{}, blk);
     if constexpr (KC > 0) {
         const int r = r0 + 64 * wave + 32 * half + j;
         if (r < rows) {
