@@ -96,7 +96,11 @@ class Oracle:
                                                 vp, i32, vp, vp]
         lib.oracle_dense_causal_rows.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, vp, i64, vp, vp,
                                                  i32, vp, vp]
-        for f in (lib.oracle_index_pool_row, lib.oracle_index_pool_rows,
+        lib.oracle_index_topk_qblock.argtypes = [cfgp, vp, i32, vp, i64, i64, i64, vp, vp]
+        lib.oracle_index_topk_qblocks.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, i64, vp, vp,
+                                                  i32, vp, vp]
+        for f in (lib.oracle_index_topk_qblock, lib.oracle_index_topk_qblocks,
+                  lib.oracle_index_pool_row, lib.oracle_index_pool_rows,
                   lib.oracle_index_topk_row, lib.oracle_sparse_attn_row,
                   lib.oracle_dense_causal_row, lib.oracle_index_topk_rows,
                   lib.oracle_sparse_attn_rows, lib.oracle_dense_causal_rows):
@@ -137,6 +141,32 @@ class Oracle:
             _ptr(sel), _ptr(scores))
         if rc:
             raise ValueError("oracle_index_topk_rows rejected its arguments")
+        return sel, scores
+
+    def index_topk_qblock(self, cfg: Config, q_idx, k_idx, kv_lens, q_start, items=None,
+                          threads=None):
+        """Query-block-shared selection: sel [n,G,K] int32 and scores [n,G,K]
+        float64 for the listed (b, slot) items (default: every slot of every
+        sequence, slot = query block - q_start // S, qblock_slots(T, S) slots)."""
+        q_idx = np.ascontiguousarray(q_idx)
+        k_idx = np.ascontiguousarray(k_idx)
+        B, T = q_idx.shape[0], q_idx.shape[1]
+        n_stride = k_idx.shape[1]
+        if items is None:
+            nq = qblock_slots(T, cfg.block_size)
+            ib, isl = self._rows(None, B, nq)
+        else:
+            ib, isl = self._rows(items, B, 1 << 30)
+        n = ib.size
+        sel = np.empty((n, cfg.groups, cfg.topk), np.int32)
+        scores = np.empty((n, cfg.groups, cfg.topk), np.float64)
+        c = cfg.c()
+        rc = self.lib.oracle_index_topk_qblocks(
+            ctypes.byref(c), T, n_stride, _ptr(q_idx), _ptr(k_idx), _ptr(_c(kv_lens, np.int32)),
+            _ptr(_c(q_start, np.int32)), n, _ptr(ib), _ptr(isl), threads or _threads(),
+            _ptr(sel), _ptr(scores))
+        if rc:
+            raise ValueError("oracle_index_topk_qblocks rejected its arguments")
         return sel, scores
 
     def index_pool(self, cfg: Config, q_idx, k_idx, kv_lens, q_start, rows=None, nb=None,
@@ -204,6 +234,23 @@ class Oracle:
         if rc:
             raise ValueError("oracle_dense_causal_rows rejected its arguments")
         return out, lse
+
+
+def qblock_slots(T: int, S: int) -> int:
+    """Query blocks that T consecutive positions can touch: ceil((T-1)/S) + 1."""
+    return 0 if T <= 0 else (T - 1 + S - 1) // S + 1
+
+
+def qblock_rows_sel(sel_blk, q_start, T, S, rows=None):
+    """Per-row selections [n,G,K] from query-block selections [B,nslots,G,K]:
+    row i of sequence b takes the selection of its block, slot
+    (q_start[b] + i) // S - q_start[b] // S; rows default to every (b, i)."""
+    sel_blk = np.asarray(sel_blk)
+    q_start = np.asarray(q_start, np.int64)
+    B = sel_blk.shape[0]
+    rb, ri = Oracle._rows(rows, B, T)
+    slots = (q_start[rb] + ri) // S - q_start[rb] // S
+    return np.ascontiguousarray(sel_blk[rb, slots]).astype(np.int32)
 
 
 def cache_append(k_new, v_new, k_idx_new, pos0, k_cache, v_cache, k_idx):

@@ -17,7 +17,8 @@
  *   - the index score is the plain dot product of the group's index query
  *     with the token's index key (no scale, no activation);
  *   - one index key per token, shared by every group;
- *   - selection is per query token and per group;
+ *   - selection is per query token and per group (the query-block-shared
+ *     variant of [M] 核心原理 is oracle_index_topk_qblock, reading stated there);
  *   - causal: a row at position p pools and attends only over keys j <= p;
  *   - fewer valid blocks than K: all valid blocks are kept, then -1 padding;
  *   - no block is forced in (no sink, no local window);
@@ -160,6 +161,78 @@ int oracle_index_topk_row(const oracle_cfg *cfg, const void *q_idx_row, const vo
     return 0;
 }
 
+/* Query-block-shared selection ([M] 核心原理: the sequence is cut into
+ * 128-token blocks and each block interacts with its 16 most relevant
+ * blocks). Reading: the query block of a row at position p is p / S (the
+ * same blocks as the keys); for the rows of one query block that the call
+ * holds, a key block's score is the largest pooled score any of those rows
+ * gives it (each row pooling causally, as in oracle_index_pool_row), and the
+ * top-K of those scores, in the order of rank_cmp, is shared by every row of
+ * the block. q_idx_seq [T, G, d_I] holds this sequence's rows, row i at
+ * position q_start + i; rows at or past kv_len do not exist. `slot` counts
+ * query blocks from q_start's block. Writes sel[G*K] and scores[G*K] (-1 /
+ * -inf when the block has no row). */
+int oracle_index_topk_qblock(const oracle_cfg *cfg, const void *q_idx_seq, int32_t T,
+                             const void *k_idx_seq, int64_t q_start, int64_t kv_len,
+                             int64_t slot, int32_t *sel, double *scores) {
+    if (check_cfg(cfg) || T < 0 || q_start < 0 || slot < 0 || !q_idx_seq || !k_idx_seq || !sel)
+        return -1;
+    const int G = cfg->groups, dI = cfg->index_dim, S = cfg->block_size, K = cfg->topk;
+    const int64_t qb = q_start / S + slot;
+    const int64_t es = cfg->index_dtype == 1 ? 1 : 2;
+    /* Rows of the call in query block qb (positions below kv_len). */
+    int64_t i_lo = qb * S - q_start, i_hi = qb * S + S - 1 - q_start;
+    if (i_lo < 0) i_lo = 0;
+    if (i_hi > T - 1) i_hi = T - 1;
+    if (i_hi > kv_len - 1 - q_start) i_hi = kv_len - 1 - q_start;
+    for (int k = 0; k < G * K; ++k) {
+        sel[k] = -1;
+        if (scores) scores[k] = -INFINITY;
+    }
+    if (i_lo > i_hi) return 0;
+    const int64_t n_valid = (q_start + i_hi) / S + 1; /* = qb + 1 */
+    double *best = malloc(sizeof(double) * (size_t)(G * n_valid));
+    double *row = malloc(sizeof(double) * (size_t)(G * n_valid));
+    ranked_block *pool = malloc(sizeof(ranked_block) * (size_t)n_valid);
+    if (!best || !row || !pool) {
+        free(best);
+        free(row);
+        free(pool);
+        return -1;
+    }
+    for (int64_t k = 0; k < G * n_valid; ++k) best[k] = -INFINITY;
+    for (int64_t i = i_lo; i <= i_hi; ++i) {
+        const int64_t p = q_start + i;
+        const int64_t nv = p / S + 1;
+        const char *qrow = (const char *)q_idx_seq + i * G * dI * es;
+        if (oracle_index_pool_row(cfg, qrow, k_idx_seq, p, row)) {
+            free(best);
+            free(row);
+            free(pool);
+            return -1;
+        }
+        for (int g = 0; g < G; ++g)
+            for (int64_t beta = 0; beta < nv; ++beta)
+                if (row[g * nv + beta] > best[g * n_valid + beta])
+                    best[g * n_valid + beta] = row[g * nv + beta];
+    }
+    for (int g = 0; g < G; ++g) {
+        for (int64_t beta = 0; beta < n_valid; ++beta) {
+            pool[beta].score = best[g * n_valid + beta];
+            pool[beta].block = (int32_t)beta;
+        }
+        qsort(pool, (size_t)n_valid, sizeof(ranked_block), rank_cmp);
+        for (int k = 0; k < K && k < n_valid; ++k) {
+            sel[g * K + k] = pool[k].block;
+            if (scores) scores[g * K + k] = pool[k].score;
+        }
+    }
+    free(best);
+    free(row);
+    free(pool);
+    return 0;
+}
+
 static double tau_of(const oracle_cfg *cfg) {
     return cfg->softmax_scale > 0 ? cfg->softmax_scale : 1.0 / sqrt((double)cfg->head_dim);
 }
@@ -265,7 +338,7 @@ int oracle_dense_causal_row(const oracle_cfg *cfg, const uint16_t *q_row, const 
 /* Row-parallel drivers: a pthread pool pulling row numbers from a counter.   */
 
 typedef struct {
-    int kind; /* 0 index, 1 sparse, 2 dense, 3 pooled scores */
+    int kind; /* 0 index, 1 sparse, 2 dense, 3 pooled scores, 4 query-block index */
     const oracle_cfg *cfg;
     int32_t T;
     int64_t n_stride;
@@ -287,9 +360,18 @@ static int run_row(row_work *w, int64_t r) {
     const int G = cfg->groups, H = cfg->groups * cfg->heads_per_group;
     const int d = cfg->head_dim, dI = cfg->index_dim, K = cfg->topk;
     int32_t b = w->rows_b[r], i = w->rows_i[r];
-    if (b < 0 || i < 0 || i >= w->T) return -1;
+    if (b < 0 || i < 0 || (w->kind != 4 && i >= w->T)) return -1;
     int64_t p = (int64_t)w->q_start[b] + i;
-    if (p >= w->kv_lens[b] || w->kv_lens[b] > w->n_stride) return -1;
+    if (w->kind != 4 && (p >= w->kv_lens[b] || w->kv_lens[b] > w->n_stride)) return -1;
+    if (w->kind == 4) {
+        /* (sequence, query-block slot): rows_i holds the slot. */
+        const int64_t es = index_elem_size(cfg);
+        const char *qseq = (const char *)w->q_idx + ((int64_t)b * w->T * G * dI) * es;
+        const char *kseq = (const char *)w->k_idx + ((int64_t)b * w->n_stride * dI) * es;
+        if (w->kv_lens[b] > w->n_stride || w->q_start[b] < 0) return -1;
+        return oracle_index_topk_qblock(cfg, qseq, w->T, kseq, w->q_start[b], w->kv_lens[b], i,
+                                        w->sel + r * G * K, w->scores ? w->scores + r * G * K : NULL);
+    }
     if (w->kind == 0 || w->kind == 3) {
         int64_t es = index_elem_size(cfg);
         const char *qrow = (const char *)w->q_idx + (((int64_t)b * w->T + i) * G * dI) * es;
@@ -365,6 +447,18 @@ int oracle_index_topk_rows(const oracle_cfg *cfg, int32_t T, int64_t n_stride, c
     w.kind = 0; w.cfg = cfg; w.T = T; w.n_stride = n_stride; w.q_idx = q_idx; w.k_idx = k_idx;
     w.kv_lens = kv_lens; w.q_start = q_start; w.nrows = nrows; w.rows_b = rows_b;
     w.rows_i = rows_i; w.sel = sel; w.scores = scores;
+    return run_rows(&w, nthreads);
+}
+
+int oracle_index_topk_qblocks(const oracle_cfg *cfg, int32_t T, int64_t n_stride,
+                              const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                              const int32_t *q_start, int64_t nitems, const int32_t *items_b,
+                              const int32_t *items_slot, int32_t nthreads, int32_t *sel,
+                              double *scores) {
+    row_work w = { 0 };
+    w.kind = 4; w.cfg = cfg; w.T = T; w.n_stride = n_stride; w.q_idx = q_idx; w.k_idx = k_idx;
+    w.kv_lens = kv_lens; w.q_start = q_start; w.nrows = nitems; w.rows_b = items_b;
+    w.rows_i = items_slot; w.sel = sel; w.scores = scores;
     return run_rows(&w, nthreads);
 }
 

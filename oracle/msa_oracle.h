@@ -63,6 +63,19 @@ int oracle_index_topk_row(const oracle_cfg *cfg, const void *q_idx_row, const vo
                           int64_t p, int32_t *sel, double *scores);
 
 /*
+ * Query-block-shared selection (mlqm.cn article, section 核心原理: 128-token
+ * blocks, each interacting with its 16 most relevant blocks), for query block
+ * q_start / S + slot of one sequence: over the rows i of the call in that
+ * block (position q_start + i < kv_len), a key block's score is the largest
+ * of those rows' causal pooled scores; the top-K in (score desc, id asc)
+ * order is shared by the block's rows. q_idx_seq [T, G, d_I]; k_idx_seq
+ * [N, d_I]. Writes sel[G*K] and scores[G*K] (-1 / -inf when no row).
+ */
+int oracle_index_topk_qblock(const oracle_cfg *cfg, const void *q_idx_seq, int32_t T,
+                             const void *k_idx_seq, int64_t q_start, int64_t kv_len,
+                             int64_t slot, int32_t *sel, double *scores);
+
+/*
  * Sparse branch for one query row at position p:
  *   q_row  : [H, d] bf16 bits
  *   k_seq, v_seq : [G, n_stride, d] bf16 bits (this sequence's caches)
@@ -91,6 +104,14 @@ int oracle_index_topk_rows(const oracle_cfg *cfg, int32_t T, int64_t n_stride, c
                            const void *k_idx, const int32_t *kv_lens, const int32_t *q_start,
                            int64_t nrows, const int32_t *rows_b, const int32_t *rows_i,
                            int32_t nthreads, int32_t *sel, double *scores);
+
+/* Query-block selections for items (items_b[r], items_slot[r]) with the
+ * batched layouts above: sel / scores [nitems, G, K]. */
+int oracle_index_topk_qblocks(const oracle_cfg *cfg, int32_t T, int64_t n_stride,
+                              const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                              const int32_t *q_start, int64_t nitems, const int32_t *items_b,
+                              const int32_t *items_slot, int32_t nthreads, int32_t *sel,
+                              double *scores);
 
 /* pooled [nrows, G, nb_out]: blocks past the row's position are -inf. */
 int oracle_index_pool_rows(const oracle_cfg *cfg, int32_t T, int64_t n_stride, const void *q_idx,

@@ -422,10 +422,75 @@ def pin_cache_append(orc, seed=7):
     assert np.array_equal(nk[keep], old_k[keep]) and np.array_equal(nv[keep], old_v[keep])
 
 
+def pin_qblock_selection(orc, seed=8):
+    """Query-block-shared selection against brute force (numpy scores, a max
+    over the block's rows and keys, a sort), against the token-level
+    selection where they must agree (one-row blocks; blocks whose rows share
+    one index query select as their last row), against a split of the call
+    at block boundaries; and the slot map of qblock_rows_sel by hand."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    G, R, d, dI, S, K = 2, 1, 2, 3, 4, 3
+    L = 40
+    for q0, T in ((5, 17), (8, 12), (0, 40), (13, 1), (36, 4)):
+        pr = tiny_problem(rng, L, G, R, d, dI, S, K, B=1, T=T, q_start=[q0], kv_lens=[L])
+        cfg = pr["cfg"]
+        nslot = oracle.qblock_slots(T, S)
+        sel, sc = orc.index_topk_qblock(cfg, pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
+        assert sel.shape == (nslot, G, K)
+        qi, ki = pr["qi"][0].astype(np.float64), pr["ki"][0].astype(np.float64)
+        for slot in range(nslot):
+            qb = q0 // S + slot
+            rows = [i for i in range(T) if (q0 + i) // S == qb and q0 + i < L]
+            for g in range(G):
+                if not rows:
+                    assert (sel[slot, g] == -1).all() and np.isneginf(sc[slot, g]).all()
+                    continue
+                best = {}
+                for i in rows:
+                    p = q0 + i
+                    for j in range(p + 1):
+                        v = float(qi[i, g] @ ki[j])
+                        best[j // S] = max(best.get(j // S, -np.inf), v)
+                order = sorted(best.items(), key=lambda kv: (-kv[1], kv[0]))[:K]
+                want = [b for b, _ in order] + [-1] * (K - len(order))
+                assert list(sel[slot, g]) == want, (q0, T, slot, g, list(sel[slot, g]), want)
+                assert np.allclose(sc[slot, g][:len(order)], [v for _, v in order], rtol=0,
+                                   atol=0)
+    # One-row calls select as the token-level index branch.
+    pr = tiny_problem(rng, L, G, R, d, dI, S, K, B=2, T=1, kv_lens=[L, 23])
+    cfg = pr["cfg"]
+    sb, _ = orc.index_topk_qblock(cfg, pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
+    st, _ = orc.index_topk(cfg, pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
+    assert np.array_equal(sb, st)
+    # Rows sharing one index query: the block selects as its last row.
+    pr = tiny_problem(rng, L, G, R, d, dI, S, K, B=1, T=L, q_start=[0], kv_lens=[L])
+    cfg = pr["cfg"]
+    qi_b = pr["qi_b"].copy()
+    for qb in range(L // S):
+        qi_b[0, qb * S:qb * S + S] = qi_b[0, qb * S + 1]
+    sb, _ = orc.index_topk_qblock(cfg, qi_b, pr["ki_b"], pr["kv_lens"], pr["q_start"])
+    last = np.array([[0, qb * S + S - 1] for qb in range(L // S)], np.int32)
+    st, _ = orc.index_topk(cfg, qi_b, pr["ki_b"], pr["kv_lens"], pr["q_start"], rows=last)
+    assert np.array_equal(sb[:L // S], st)
+    # Two calls split at a block boundary select as one call.
+    whole, _ = orc.index_topk_qblock(cfg, pr["qi_b"], pr["ki_b"], pr["kv_lens"], pr["q_start"])
+    a, _ = orc.index_topk_qblock(cfg, pr["qi_b"][:, :16], pr["ki_b"], np.array([16], np.int32),
+                                 np.array([0], np.int32))
+    b, _ = orc.index_topk_qblock(cfg, pr["qi_b"][:, 16:], pr["ki_b"], pr["kv_lens"],
+                                 np.array([16], np.int32))
+    assert np.array_equal(whole[:4], a[:4]) and np.array_equal(whole[4:10], b[:6])
+    # Slot map: q_start 6, S 4 -> rows 0,1 in slot 0, rows 2..5 in slot 1, row 6 in slot 2.
+    blk = np.arange(1 * 3 * 1 * 1).reshape(1, 3, 1, 1)
+    rows_sel = oracle.qblock_rows_sel(blk, [6], 7, 4)
+    assert list(rows_sel[:, 0, 0]) == [0, 0, 1, 1, 1, 1, 2]
+
+
 ALL_PINS = [pin_decoders, pin_hand_example_selection, pin_hand_example_attention,
             pin_hand_example_variants, pin_brute_force_selection,
             pin_token_level_and_single_block, pin_selection_invariants, pin_sparse_vs_numpy,
-            pin_attention_invariants, pin_mixed_lengths_and_stride, pin_cache_append]
+            pin_attention_invariants, pin_mixed_lengths_and_stride, pin_cache_append,
+            pin_qblock_selection]
 
 
 def run_all(orc):

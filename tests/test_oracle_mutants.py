@@ -33,6 +33,12 @@ MUTANTS = [
      "const uint16_t *v_grp = v_seq;"),
     ("k_of_group0", "const uint16_t *k_grp = k_seq + (int64_t)g * n_stride * d;",
      "const uint16_t *k_grp = k_seq;"),
+    ("qblock_min_over_rows", "if (row[g * nv + beta] > best[g * n_valid + beta])",
+     "if (row[g * nv + beta] < best[g * n_valid + beta])"),
+    ("qblock_first_row_only", "for (int64_t i = i_lo; i <= i_hi; ++i) {",
+     "for (int64_t i = i_lo; i <= i_lo; ++i) {"),
+    ("qblock_slot_from_zero", "const int64_t qb = q_start / S + slot;",
+     "const int64_t qb = slot;"),
 ]
 
 
