@@ -97,8 +97,14 @@ def load():
     lib.msa_sparse_attn_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_cache_append.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.msa_index_topk_qblock.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.msa_sparse_attn_prefill_qblock.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                                   vp, vp, vp]
+    lib.msa_qblock_slots.argtypes = [i32]
+    lib.msa_qblock_slots.restype = i32
     for f in (lib.msa_index_topk, lib.msa_index_pool, lib.msa_sparse_attn_prefill,
-              lib.msa_sparse_attn_decode, lib.msa_decode, lib.msa_cache_append):
+              lib.msa_sparse_attn_decode, lib.msa_decode, lib.msa_cache_append,
+              lib.msa_index_topk_qblock, lib.msa_sparse_attn_prefill_qblock):
         f.restype = ctypes.c_int
     lib.msa_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
     lib.msa_workspace_size.restype = sz
@@ -382,3 +388,69 @@ def cache_append(cfg: Config, k_new, v_new, k_idx_new, pos0, k_cache, v_cache, k
         _check(load().msa_cache_append(ctypes.byref(cfg._c()), B, T, Nmax, _ptr(k_new),
                                        _ptr(v_new), _ptr(k_idx_new), _ptr(pos0), _ptr(k_cache),
                                        _ptr(v_cache), _ptr(k_idx), _stream(dev)))
+
+
+def qblock_slots(T: int) -> int:
+    """Query-block slots of a call with T rows per sequence (msa_qblock_slots)."""
+    return int(load().msa_qblock_slots(T))
+
+
+def index_topk_qblock(cfg: Config, q_idx, k_idx, kv_lens, q_start=None, sel=None,
+                      sel_scores=None, want_scores: bool = False):
+    """Query-block-shared selection: sel [B, NQ, G, K] int32 (and scores),
+    NQ = qblock_slots(T); slot s is query block q_start // S + s."""
+    dev = q_idx.device
+    _need(q_idx, "q_idx", _INDEX_DTYPES[cfg.index_dtype], 4)
+    _need(k_idx, "k_idx", _INDEX_DTYPES[cfg.index_dtype], 3, dev)
+    B, T, G, dI = q_idx.shape
+    Nmax = k_idx.shape[1]
+    if G != cfg.num_kv_groups or dI != cfg.index_dim or k_idx.shape[0] != B or \
+            k_idx.shape[2] != cfg.index_dim:
+        raise ValueError("q_idx/k_idx shapes do not match the config")
+    _lens(kv_lens, "kv_lens", B, dev)
+    if q_start is not None:
+        _lens(q_start, "q_start", B, dev)
+    shape = (B, qblock_slots(T), G, cfg.topk)
+    if sel is None:
+        sel = torch.empty(shape, dtype=torch.int32, device=dev)
+    _need(sel, "sel", (torch.int32,), 4, dev)
+    if tuple(sel.shape) != shape:
+        raise ValueError("sel must be [B, NQ, G, K]")
+    if want_scores and sel_scores is None:
+        sel_scores = torch.empty(shape, dtype=torch.float32, device=dev)
+    if sel_scores is not None:
+        _need(sel_scores, "sel_scores", (torch.float32,), 4, dev)
+        if tuple(sel_scores.shape) != shape:
+            raise ValueError("sel_scores must be [B, NQ, G, K]")
+    with _on_device(dev):
+        _check(load().msa_index_topk_qblock(ctypes.byref(cfg._c()), B, T, Nmax, _ptr(q_idx),
+                                            _ptr(k_idx), _ptr(kv_lens), _ptr(q_start), _ptr(sel),
+                                            _ptr(sel_scores), _stream(dev)))
+    return (sel, sel_scores) if (want_scores or sel_scores is not None) else sel
+
+
+def sparse_attn_prefill_qblock(cfg: Config, q, k_cache, v_cache, kv_lens, sel, q_start=None,
+                               out=None, lse=None, want_lse: bool = False):
+    """Sparse branch with query-block-shared selections sel [B, NQ, G, K]."""
+    dev = q.device
+    _need(q, "q", (torch.bfloat16,), 4)
+    _need(k_cache, "k_cache", (torch.bfloat16,), 4, dev)
+    _need(v_cache, "v_cache", (torch.bfloat16,), 4, dev)
+    B, T, H, d = q.shape
+    Nmax = k_cache.shape[2]
+    G = cfg.num_kv_groups
+    if H != cfg.num_heads or d != cfg.head_dim or tuple(k_cache.shape) != (B, G, Nmax, d) or \
+            tuple(v_cache.shape) != (B, G, Nmax, d):
+        raise ValueError("q/k_cache/v_cache shapes do not match the config")
+    _lens(kv_lens, "kv_lens", B, dev)
+    if q_start is not None:
+        _lens(q_start, "q_start", B, dev)
+    _need(sel, "sel", (torch.int32,), 4, dev)
+    if tuple(sel.shape) != (B, qblock_slots(T), G, cfg.topk):
+        raise ValueError("sel must be [B, NQ, G, K]")
+    out, lse = _outputs(cfg, dev, B, T, out, lse, want_lse)
+    with _on_device(dev):
+        _check(load().msa_sparse_attn_prefill_qblock(
+            ctypes.byref(cfg._c()), B, T, Nmax, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(kv_lens), _ptr(q_start), _ptr(sel), _ptr(out), _ptr(lse), _stream(dev)))
+    return (out, lse) if (want_lse or lse is not None) else out

@@ -181,6 +181,28 @@ msa_status check_pool_args(const msa_config *cfg, int32_t B, int32_t T, int32_t 
     return MSA_OK;
 }
 
+int32_t qblock_slots(int32_t T) { return T <= 0 ? 0 : (T - 1 + kBlock - 1) / kBlock + 1; }
+
+msa_status check_qblock_index_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                                   const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                                   const int32_t *q_start, const int32_t *sel,
+                                   const float *sel_scores) {
+    msa_status s = check_config(cfg);
+    if (s != MSA_OK) return s;
+    if ((s = check_dims(B, T, Nmax)) != MSA_OK) return s;
+    if (B == 0 || T == 0) return MSA_OK;
+    if ((int64_t)B * T * cfg->num_kv_groups > ((int64_t)1 << 31) - 1)
+        return fail(MSA_ERR_UNSUPPORTED, "B*T*G exceeds 2^31-1 rows");
+    if (!q_idx || !k_idx || !kv_lens || !sel)
+        return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx, kv_lens and sel must not be NULL");
+    if (!aligned(q_idx, 16) || !aligned(k_idx, 16))
+        return fail(MSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+    if (!aligned(kv_lens, 4) || (q_start && !aligned(q_start, 4)) || !aligned(sel, 4) ||
+        (sel_scores && !aligned(sel_scores, 4)))
+        return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
+    return MSA_OK;
+}
+
 msa_status check_append_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                              const void *k_new, const void *v_new, const void *k_idx_new,
                              const int32_t *pos0, const void *k_cache, const void *v_cache,
@@ -226,6 +248,7 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
     if (!aligned(kv_lens, 4) || (q_start && !aligned(q_start, 4)) || !aligned(sel, 4) ||
         (lse && !aligned(lse, 4)))
         return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
+    if (which < 0) return MSA_OK;  // a call without workspace
     if (which == MSA_WS_SPARSE_DECODE)
         return check_ws(workspace, ws_bytes, decode_ws(cfg, B, Nmax, false).total);
     return check_ws(workspace, ws_bytes, prefill_ws(cfg, B, T, Nmax).total);
@@ -290,5 +313,7 @@ const char *msa_status_string(msa_status s) {
 const char *msa_last_error(void) { return msa::g_err; }
 
 int32_t msa_version(void) { return 100; }
+
+int32_t msa_qblock_slots(int32_t T) { return msa::qblock_slots(T); }
 
 }  // extern "C"

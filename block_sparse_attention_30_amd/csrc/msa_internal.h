@@ -35,6 +35,11 @@ msa_status check_append_args(const msa_config *cfg, int32_t B, int32_t T, int32_
                              const void *k_new, const void *v_new, const void *k_idx_new,
                              const int32_t *pos0, const void *k_cache, const void *v_cache,
                              const void *k_idx);
+int32_t qblock_slots(int32_t T);
+msa_status check_qblock_index_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                                   const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                                   const int32_t *q_start, const int32_t *sel,
+                                   const float *sel_scores);
 msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                              const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *kv_lens, const int32_t *q_start, const int32_t *sel,

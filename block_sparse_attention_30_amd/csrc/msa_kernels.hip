@@ -39,6 +39,11 @@
 //                        calls can be captured in graphs).
 //   cache_append_kernel  (msa_cache_append) copies new K, V and index-key rows
 //                        into the caches, one wavefront per (sequence, row).
+//   idx_prefill_kernel<.., QB> and qb_attn_kernel  the query-block-shared
+//                        selection variant (msa_index_topk_qblock,
+//                        msa_sparse_attn_prefill_qblock): one top-K per
+//                        128-row query block; attention query-major with an
+//                        online softmax over the block's kept blocks.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -102,6 +107,9 @@ __device__ __forceinline__ f32x16 mfma32_f8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ int clamp_kv(int kv, int Nmax) { return kv < Nmax ? kv : Nmax; }
+
+// floor(a / b) for b > 0 (C division truncates toward zero).
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
@@ -551,12 +559,19 @@ __device__ __forceinline__ void topk_insert(float (&ts)[KC], int (&tb)[KC], floa
 // KC = 0: pooled block scores are written out. KC = 16 or 32: every lane owns
 // one row, keeps its top-KC blocks in registers while the blocks stream by,
 // and writes sel / sel_scores (first K) at the end; no pooled scores.
-template <bool F8, int KC>
+// QB (query-block-shared selection, KC > 0): the workgroup holds one query
+// block (the rows of the call at positions qblk*S .. qblk*S+S-1) for two groups,
+// waves 2h and 2h+1 the block's first and second 64 rows of group 2*gp + h.
+// A key block's score is the largest block max over those rows: a wave
+// reduction, then the two waves' values meet in LDS at the next block's
+// barrier, where the even wave (every lane alike) offers the block to its
+// running top-KC; sel is [B, nslots, G, K] with slot = qblk - floor(q_start/S).
+template <bool F8, int KC, bool QB = false>
 __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     const unsigned char *__restrict__ q_idx, const unsigned char *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
     float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int K,
-    int32_t *__restrict__ sel, float *__restrict__ sel_scores) {
+    int32_t *__restrict__ sel, float *__restrict__ sel_scores, int nslots = 0) {
     constexpr int kRowBytes = DI * (F8 ? 1 : 2);
     constexpr int kRow = kRowBytes + 16;
     constexpr int kPieces = S * kRowBytes / 16 / 256;  // 16-byte loads per thread per block
@@ -564,15 +579,26 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char lds[S * kRow];
     const int b = blockIdx.y;
     const int rows = T * G;
-    const int r0 = (gridDim.x - 1 - blockIdx.x) * kPfRows;  // longest rows first
+    const int xr = gridDim.x - 1 - blockIdx.x;  // longest rows first
+    const int r0 = xr * kPfRows;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kv = clamp_kv(kv_lens[b], Nmax);
     const int qs = q_start ? q_start[b] : kv - T;
-    const int r_last = min(r0 + kPfRows, rows) - 1;
-    const int p_hi = min(qs + r_last / G, kv - 1);
+    // QB: query block qblk (slot xr / npairs), groups 2*gp and 2*gp + 1.
+    const int npairs = (G + 1) / 2;
+    const int qblk = QB ? floor_div(qs, S) + xr / npairs : 0;
+    const int gp = QB ? xr % npairs : 0;
+    int p_lo, p_hi;
+    if constexpr (QB) {
+        p_lo = max(max(qblk * S, qs), 0);
+        p_hi = min(min(qblk * S + S - 1, qs + T - 1), kv - 1);
+    } else {
+        const int r_last = min(r0 + kPfRows, rows) - 1;
+        p_hi = min(qs + r_last / G, kv - 1);
+        p_lo = qs + r0 / G;
+    }
     if (KC == 0 && p_hi < 0) return;
-    const int p_lo = qs + r0 / G;
-    const int nblk = p_hi >= 0 ? p_hi / S + 1 : 0;
+    const int nblk = (p_hi >= 0 && p_hi >= p_lo) ? p_hi / S + 1 : 0;
 
     const int j = lane & 31, half = lane >> 5;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -581,11 +607,21 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     constexpr int kKb = F8 ? 64 : 32;
     u32x4 qb[2][kKs][F8 ? 2 : 1];
     int pcol[2];
+    const int my_g = QB ? 2 * gp + (wave >> 1) : 0;  // QB: this wave's group
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-        const int r = r0 + 64 * wave + 32 * ct + j;
-        const int p = qs + r / G;
-        const bool ok = r < rows && p >= 0 && p < kv;
+        int r, p;
+        bool ok;
+        if constexpr (QB) {
+            p = qblk * S + 64 * (wave & 1) + 32 * ct + j;
+            const int t = p - qs;
+            r = t * G + my_g;
+            ok = my_g < G && t >= 0 && t < T && p >= 0 && p < kv;
+        } else {
+            r = r0 + 64 * wave + 32 * ct + j;
+            p = qs + r / G;
+            ok = r < rows && p >= 0 && p < kv;
+        }
         pcol[ct] = ok ? p : -1;
         const unsigned char *qp = q_idx + ((size_t)b * rows + (ok ? r : 0)) * kRowBytes;
 #pragma unroll
@@ -618,6 +654,15 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
             if (tok >= kv) pre[i] = zero4;
         }
     };
+    // QB: the wave's value for the last block, and the two waves' values of
+    // the previous two blocks (one LDS pair per block parity).
+    __shared__ float s_qb[2][4];
+    float qb_own = -INFINITY;
+    auto qb_offer = [&](int blk_prev) {  // after a barrier: block blk_prev's score
+        if (wave & 1) return;
+        const float sc = fmaxf(qb_own, s_qb[blk_prev & 1][wave + 1]) + 0.0f;
+        if (sc > ts[KCS - 1]) topk_insert<KCS>(ts, tb, sc, blk_prev);
+    };
     // One block: stage it in LDS, prefetch the next, score it, then block max
     // and top-K insertion. MASK: the block reaches past the first row's
     // position, so keys past each row's position are masked; the blocks
@@ -628,6 +673,8 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
         const int tok0 = blk * S;
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
         __builtin_amdgcn_s_barrier();        // ... and every other wave's
+        if constexpr (QB)
+            if (blk > 0) qb_offer(blk - 1);
 #pragma unroll
         for (int i = 0; i < kPieces; ++i) {
             const int piece = tid + 256 * i;
@@ -683,6 +730,14 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
         if constexpr (KC == 0) {
             const int r = r0 + 64 * wave + 32 * half + j;
             if (pc >= tok0) pooled[((size_t)b * rows + r) * nb_max + blk] = v;
+        } else if constexpr (QB) {
+            // The wave's largest block max over its rows that reach the block;
+            // the partner wave's value is read after the next barrier.
+            float wv = pc >= tok0 ? v : -INFINITY;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) wv = fmaxf(wv, __shfl_xor(wv, off));
+            qb_own = wv;
+            if (lane == 0) s_qb[blk & 1][wave] = wv;
         } else {
             const bool offer = pc >= tok0 && v > ts[KC - 1];
             if (__ballot(offer)) {
@@ -695,7 +750,22 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     if (nblk > 0) load_block(0);
     for (int blk = 0; blk < n_plain; ++blk) do_block(BoolTag<false>{}, blk);
     for (int blk = n_plain; blk < nblk; ++blk) do_block(BoolTag<true>{}, blk);
-    if constexpr (KC > 0) {
+    if constexpr (QB) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        if (nblk > 0) qb_offer(nblk - 1);
+        const int slot = qblk - floor_div(qs, S);
+        if ((wave & 1) == 0 && my_g < G && lane == 0 && slot >= 0 && slot < nslots) {
+            const size_t o = (((size_t)b * nslots + slot) * G + my_g) * K;
+#pragma unroll
+            for (int i = 0; i < KC; ++i) {
+                if (i < K) {
+                    sel[o + i] = tb[i];
+                    if (sel_scores) sel_scores[o + i] = ts[i];
+                }
+            }
+        }
+    } else if constexpr (KC > 0) {
         const int r = r0 + 64 * wave + 32 * half + j;
         if (r < rows) {
             const size_t o = ((size_t)b * rows + r) * K;
@@ -1331,6 +1401,195 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
     }
 }
 
+// Sparse prefill with query-block-shared selections (the mlqm.cn article,
+// section 核心原理: 128-token blocks, each attending to its 16 most relevant
+// blocks). Every row of query block qblk attends over the same kept blocks,
+// so a workgroup keeps 8*et rows' queries (et = 16/R rows per 16-column
+// tile, two tiles per wave, four waves) in registers and streams the unit's
+// kept blocks through LDS with an online softmax across blocks: no partials,
+// each K/V block staged once per workgroup and used by every column.
+// Units are (sequence, slot, group); ncw workgroups split a unit's rows.
+// Workgroup ids id, id + 8, ... land on one XCD, so the ncw workgroups of a
+// unit (ids 8*(ncw*u') + x + 8*c) share that XCD's L2.
+__global__ __launch_bounds__(256, 2) void qb_attn_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
+    const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, const int32_t *__restrict__ sel, int T, int G, int R,
+    int Nmax, int K, int nslots, int ncw, int64_t nunits, float scale_log2,
+    bf16_t *__restrict__ out, float *__restrict__ lse) {
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[S * kKRow];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[S * kVRow];
+    __shared__ int s_sel[KMAX], s_blocks[KMAX], s_n;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    const int64_t id = blockIdx.x;
+    const int64_t unit = (id / 8 / ncw) * 8 + id % 8;
+    const int cw = (int)(id / 8 % ncw);
+    if (unit >= nunits) return;
+    const int g = (int)(unit % G);
+    const int64_t bs = unit / G;
+    const int slot = (int)(bs % nslots), b = (int)(bs / nslots);
+    const int H = G * R;
+    const int kv = clamp_kv(kv_lens[b], Nmax);
+    const int qs = q_start ? q_start[b] : kv - T;
+    const int qblk = floor_div(qs, S) + slot;
+    const int et = 16 / R;
+    const int ppw = kPfWaves * kPfNq * et;  // rows (positions) per workgroup
+    // Column col of tile nq: position qblk*S + pi, head col % R.
+    int trow[kPfNq], pcol[kPfNq];
+    bf16x8 qf[kPfNq][4];
+#pragma unroll
+    for (int nq = 0; nq < kPfNq; ++nq) {
+        const int pi = cw * ppw + (wave * kPfNq + nq) * et + col / R;
+        const int p = qblk * S + pi;
+        const int t = p - qs;
+        const bool in_call = col < et * R && pi < S && t >= 0 && t < T;
+        const bool valid = in_call && p >= 0 && p < kv;
+        trow[nq] = in_call ? t : -1;
+        pcol[nq] = valid ? p : -1;
+        const bf16_t *qp =
+            q + (((int64_t)b * T + (valid ? t : 0)) * H + (int64_t)g * R + col % R) * D + kg * 8;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) qf[nq][kc] = valid ? ld_bf16x8(qp + kc * 32) : zero_bf16x8();
+    }
+    // The unit's kept blocks: valid ids up to the block of its last row.
+    const int p_min = max(max(qblk * S, qs), 0);
+    const int p_max = min(min(qblk * S + S - 1, qs + T - 1), kv - 1);
+    if (tid < K) s_sel[tid] = sel[(((int64_t)b * nslots + slot) * G + g) * K + tid];
+    __syncthreads();
+    if (wave == 0) {
+        const int n = p_max >= p_min ? build_block_list(s_sel, K, p_max, s_blocks, lane) : 0;
+        if (lane == 0) s_n = n;
+    }
+    __syncthreads();
+    const int nblk = s_n;
+    float m2[kPfNq], lsum[kPfNq];
+    f32x4 o[kPfNq][8];
+#pragma unroll
+    for (int nq = 0; nq < kPfNq; ++nq) {
+        m2[nq] = -INFINITY;
+        lsum[nq] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[nq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int bi = 0; bi < nblk; ++bi) {
+        const int blk = s_blocks[bi];
+        const int tok_base = blk * S;
+        if (bi > 0) __syncthreads();  // the previous block's LDS reads are done
+        {
+            const int64_t bg = (int64_t)b * G + g;
+            const bf16_t *kb = k_cache + (bg * Nmax + tok_base) * D;
+            const bf16_t *vb = v_cache + (bg * Nmax + tok_base) * D;
+            const u32x4 z4 = {0u, 0u, 0u, 0u};
+            u32x4 kr[8], vr[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
+                const bool in = tok_base + tk < kv;
+                kr[i] = in ? ld16(kb + (size_t)tk * D + c * 8) : z4;
+                vr[i] = in ? ld16(vb + (size_t)tk * D + c * 8) : z4;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
+                *reinterpret_cast<u32x4 *>(k_lds + tk * kKRow + c * 16) = kr[i];
+                *reinterpret_cast<u32x4 *>(v_lds + tk * kVRow + c * 16) = vr[i];
+            }
+        }
+        __syncthreads();
+        // S^T: key tile kt x 16 columns; lane holds column col, keys kt*16 + 4*kg + r.
+        f32x4 sacc[kPfNq][8];
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+            if (kt % 2 == 0) __builtin_amdgcn_sched_barrier(0);
+            u32x4 ka[4];
+            const unsigned char *kp = k_lds + (kt * 16 + col) * kKRow + kg * 16;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) ka[kc] = *reinterpret_cast<const u32x4 *>(kp + kc * 64);
+#pragma unroll
+            for (int nq = 0; nq < kPfNq; ++nq) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) acc = mfma16(as_bf16x8(ka[kc]), qf[nq][kc], acc);
+                sacc[nq][kt] = acc;
+            }
+        }
+        // Online softmax across blocks (log2 domain). Only the query block's
+        // own key block reaches past a row's position.
+        const bool diag = blk == qblk;
+        bf16x8 pa[kPfNq][4];
+#pragma unroll
+        for (int nq = 0; nq < kPfNq; ++nq) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float sv = sacc[nq][kt][r];
+                    if (diag && tok_base + kt * 16 + 4 * kg + r > pcol[nq]) sv = -INFINITY;
+                    sacc[nq][kt][r] = sv;
+                    mx = fmaxf(mx, sv);
+                }
+            mx = max_xor16_32(mx, lane);
+            const float m_new = fmaxf(m2[nq], mx * scale_log2);
+            const float alpha = m2[nq] == -INFINITY ? 0.f : fast_exp2(m2[nq] - m_new);
+            const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+            float psum = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float pv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    pv[i] = fast_exp2(fmaf(sacc[nq][2 * c + (i >> 2)][i & 3], scale_log2, neg_m));
+                    psum += pv[i];
+                }
+                const u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                  pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+                pa[nq][c] = as_bf16x8(pk);
+            }
+            psum = sum_xor16_32(psum, lane);
+            lsum[nq] = lsum[nq] * alpha + psum;
+            m2[nq] = m_new;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[nq][dt][r] *= alpha;
+        }
+        // O^T += V^T x P^T (as in pf_attn_kernel): lane (col, kg) accumulates
+        // O[column col][d = dt*16 + 4*kg + r].
+#pragma unroll
+        for (int c = 0; c < S / 32; ++c) {
+            const unsigned char *vlo = v_lds + (c * 32 + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
+            const unsigned char *vhi = vlo + 16 * kVRow;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                if (dt % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+                const u32x2 lo = lds_read_tr16(vlo + dt * 32);
+                const u32x2 hi = lds_read_tr16(vhi + dt * 32);
+                const u32x4 vbv = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int nq = 0; nq < kPfNq; ++nq) o[nq][dt] = mfma16(as_bf16x8(vbv), pa[nq][c], o[nq][dt]);
+            }
+        }
+    }
+    // Rows of the call: the normalised output, or zeros / -inf for a row
+    // outside the cache.
+#pragma unroll
+    for (int nq = 0; nq < kPfNq; ++nq) {
+        if (trow[nq] < 0) continue;
+        const bool has = pcol[nq] >= 0 && lsum[nq] > 0.f;
+        const float inv = has ? 1.f / lsum[nq] : 0.f;
+        const int64_t hrow = ((int64_t)b * T + trow[nq]) * H + (int64_t)g * R + col % R;
+        bf16_t *op = out + hrow * D + 4 * kg;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<u32x2 *>(op + dt * 16) =
+                u32x2{pack_bf16x2(o[nq][dt][0] * inv, o[nq][dt][1] * inv),
+                      pack_bf16x2(o[nq][dt][2] * inv, o[nq][dt][3] * inv)};
+        if (lse && kg == 0) lse[hrow] = has ? m2[nq] * kLn2 + logf(lsum[nq]) : -INFINITY;
+    }
+}
+
 // One workgroup per (sequence, row of the pass, group): the kept slots are
 // listed once, their (m, l) staged in LDS, then every thread merges four
 // d-values of one head over the kept slots.
@@ -1798,6 +2057,58 @@ msa_status msa_sparse_attn_decode(const msa_config *cfg, int32_t B, int32_t Nmax
                                    reinterpret_cast<float *>(base + w.part_o_off),
                                    reinterpret_cast<float *>(base + w.part_ml_off),
                                    reinterpret_cast<hipStream_t>(stream));
+}
+
+msa_status msa_index_topk_qblock(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                                 const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                                 const int32_t *q_start, int32_t *sel, float *sel_scores,
+                                 void *stream) {
+    msa::clear_error();
+    msa_status s = msa::check_qblock_index_args(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start,
+                                                sel, sel_scores);
+    if (s != MSA_OK || B == 0 || T == 0) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int G = cfg->num_kv_groups, K = cfg->topk;
+    const int nslots = msa::qblock_slots(T);
+    const bool f8 = cfg->index_dtype == MSA_FP8_E4M3;
+    const unsigned char *qi = static_cast<const unsigned char *>(q_idx);
+    const unsigned char *ki = static_cast<const unsigned char *>(k_idx);
+    const int64_t nbm = ((int64_t)Nmax + S - 1) / S;
+    const dim3 grid((unsigned)((int64_t)nslots * ((G + 1) / 2)), (unsigned)B);
+#define MSA_IDX_QBLOCK(F8_, KC_)                                                                 \
+    idx_prefill_kernel<F8_, KC_, true><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, nullptr, \
+                                                             T, G, Nmax, nbm, K, sel,           \
+                                                             sel_scores, nslots)
+    if (f8 && K <= 16) MSA_IDX_QBLOCK(true, 16);
+    else if (f8) MSA_IDX_QBLOCK(true, 32);
+    else if (K <= 16) MSA_IDX_QBLOCK(false, 16);
+    else MSA_IDX_QBLOCK(false, 32);
+#undef MSA_IDX_QBLOCK
+    return launch_status("query-block index kernel");
+}
+
+msa_status msa_sparse_attn_prefill_qblock(const msa_config *cfg, int32_t B, int32_t T,
+                                          int32_t Nmax, const void *q, const void *k_cache,
+                                          const void *v_cache, const int32_t *kv_lens,
+                                          const int32_t *q_start, const int32_t *sel, void *out,
+                                          float *lse, void *stream) {
+    msa::clear_error();
+    msa_status s = msa::check_sparse_args(cfg, B, T, Nmax, q, k_cache, v_cache, kv_lens, q_start,
+                                          sel, out, lse, nullptr, 0, -1);
+    if (s != MSA_OK || B == 0 || T == 0) return s;
+    const int G = cfg->num_kv_groups, R = cfg->heads_per_group, K = cfg->topk;
+    const int nslots = msa::qblock_slots(T);
+    const int ppw = kPfWaves * kPfNq * (16 / R);
+    const int ncw = (S + ppw - 1) / ppw;
+    const int64_t nunits = (int64_t)B * nslots * G;
+    const int64_t nwg = (nunits + 7) / 8 * 8 * ncw;
+    if (nwg > 0x7FFFFFFF)
+        return msa::fail(MSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
+    qb_attn_kernel<<<(unsigned)nwg, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k_cache),
+        static_cast<const bf16_t *>(v_cache), kv_lens, q_start, sel, T, G, R, Nmax, K, nslots,
+        ncw, nunits, scale_log2_of(cfg), static_cast<bf16_t *>(out), lse);
+    return launch_status("query-block sparse attention kernel");
 }
 
 msa_status msa_cache_append(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,

@@ -160,6 +160,48 @@ msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void
                       void *stream);
 
 /*
+ * Query-block-shared selection, a variant of the index branch read from the
+ * mlqm.cn article, section 核心原理 (the sequence is cut into 128-token blocks
+ * and each block works with its 16 most relevant blocks). The query block of
+ * the row at position p is p / S, the same blocks as the keys. For each
+ * sequence, group and query block, over the rows of the call in that block
+ * (positions below kv_lens[b]), a key block's score is the largest pooled
+ * score P_B that any of those rows gives it (each row pooling causally, as
+ * above), and the top-K in (score desc, block asc) order, then -1 padding,
+ * is shared by every row of the query block.
+ *   sel        [B, NQ, G, K] int32, NQ = msa_qblock_slots(T); slot s holds
+ *              query block floor(q_start[b] / S) + s (a slot with no row of
+ *              the call gets -1);
+ *   sel_scores [B, NQ, G, K] fp32 (nullable), -inf for padding.
+ * Other layouts as msa_index_topk. Needs no workspace. Exact for integer
+ * index data, as msa_index_topk.
+ */
+msa_status msa_index_topk_qblock(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                                 const void *q_idx, const void *k_idx, const int32_t *kv_lens,
+                                 const int32_t *q_start, int32_t *sel, float *sel_scores,
+                                 void *stream);
+
+/*
+ * Sparse branch for query-block-shared selections: row i of sequence b
+ * (position p = q_start[b] + i) attends, for every head of group g, over the
+ * keys j <= p of the blocks in sel[b, p/S - floor(q_start[b]/S), g, :]
+ * (invalid or repeated ids are ignored, as in msa_sparse_attn_prefill).
+ * sel as written by msa_index_topk_qblock; other layouts and the output
+ * definition as msa_sparse_attn_prefill. Needs no workspace: every query
+ * block's rows attend over its kept blocks in one pass (online softmax).
+ */
+msa_status msa_sparse_attn_prefill_qblock(const msa_config *cfg, int32_t B, int32_t T,
+                                          int32_t Nmax, const void *q, const void *k_cache,
+                                          const void *v_cache, const int32_t *kv_lens,
+                                          const int32_t *q_start, const int32_t *sel, void *out,
+                                          float *lse, void *stream);
+
+/* Query-block slots NQ of a call with T rows per sequence: the number of
+ * 128-token blocks that T consecutive positions can touch, ceil((T-1)/128)+1
+ * (0 for T <= 0). */
+int32_t msa_qblock_slots(int32_t T);
+
+/*
  * Appends T new tokens per sequence to the caches that the calls above read
  * (the decode step's reading of the Tencent article §二 is that the new
  * token's K, V and index key are in the caches when it attends): for every

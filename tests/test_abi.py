@@ -32,6 +32,7 @@ def test_header_declares_the_three_entry_points():
     names = declared_functions()
     for n in ("msa_index_topk", "msa_index_pool", "msa_sparse_attn_prefill",
               "msa_sparse_attn_decode", "msa_decode", "msa_cache_append",
+              "msa_index_topk_qblock", "msa_sparse_attn_prefill_qblock", "msa_qblock_slots",
               "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_version"):
         assert n in names
 
@@ -176,6 +177,43 @@ def test_cache_append_validation(lib):
                                 FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
     assert b"NULL" in lib.msa_last_error() or b"aligned" in lib.msa_last_error() or \
         b"head_dim" in lib.msa_last_error()
+
+
+def test_qblock_slots_and_validation(lib):
+    # 128-token query blocks that T consecutive positions can touch.
+    for T, want in ((0, 0), (-3, 0), (1, 1), (2, 2), (128, 2), (129, 2), (130, 3), (256, 3),
+                    (32768, 257)):
+        assert lib.msa_qblock_slots(T) == want, T
+    assert msa.qblock_slots(131072) == 1025
+    c = cfg()
+
+    def idx(B=2, T=300, N=1024, **kw):
+        a = dict(qi=FAKE, ki=FAKE, kv=FAKE, qs=None, sel=FAKE, sc=None)
+        a.update(kw)
+        return lib.msa_index_topk_qblock(ctypes.byref(c), B, T, N, a["qi"], a["ki"], a["kv"],
+                                         a["qs"], a["sel"], a["sc"], None)
+
+    assert idx(B=0) == OK and idx(T=0) == OK
+    assert idx(qi=None) == INVALID and idx(sel=None) == INVALID and idx(kv=None) == INVALID
+    assert idx(ki=FAKE_MIS) == INVALID and idx(sc=ctypes.c_void_p(0x100002)) == INVALID
+    assert idx(B=70000) == UNSUPPORTED
+    assert lib.msa_index_topk_qblock(ctypes.byref(cfg(topk=33)), 1, 8, 128, FAKE, FAKE, FAKE,
+                                     None, FAKE, None, None) == UNSUPPORTED
+
+    def att(B=2, T=300, N=1024, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, kv=FAKE, qs=None, sel=FAKE, out=FAKE, lse=None)
+        a.update(kw)
+        return lib.msa_sparse_attn_prefill_qblock(ctypes.byref(c), B, T, N, a["q"], a["k"],
+                                                  a["v"], a["kv"], a["qs"], a["sel"], a["out"],
+                                                  a["lse"], None)
+
+    assert att(B=0) == OK
+    for name in ("q", "k", "v", "kv", "sel", "out"):
+        assert att(**{name: None}) == INVALID, name
+    assert att(v=FAKE_MIS) == INVALID and att(out=FAKE_MIS) == INVALID
+    assert lib.msa_sparse_attn_prefill_qblock(ctypes.byref(cfg(heads_per_group=17)), 1, 8, 128,
+                                              FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                                              None) == UNSUPPORTED
 
 
 def test_workspace_sizes_follow_shapes(lib):
