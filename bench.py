@@ -384,6 +384,58 @@ def run_prefill(torch, msa, w, steps=2, warmup=1):
     return res
 
 
+def qblock_rows(torch, sel_blk, q0, L):
+    """Per-row selections [1, L, G, K] from query-block selections [1, NQ, G, K]
+    (row i takes the selection of its block, slot (q0 + i)//128 - q0//128)."""
+    i = torch.arange(L, device="cuda", dtype=torch.int64)
+    slots = (q0 + i) // 128 - q0 // 128
+    return sel_blk[:, slots]
+
+
+def run_prefill_qblock(torch, msa, w, steps=2, warmup=1):
+    """The 131072-token prefill with query-block-shared selections (each
+    128-row query block keeps one top-16): msa_index_topk_qblock +
+    msa_sparse_attn_prefill_qblock, sparse flops counted exactly per row."""
+    from msa_synth import workloads as wl
+    alloc = pinned(torch)
+    kh, vh, kih = wl.gen_caches(w, alloc=alloc)
+    qh, qih = wl.gen_queries(w, alloc=alloc)
+    k, v, ki = to_dev(torch, kh), to_dev(torch, vh), to_dev(torch, kih, bf16=not w.index_fp8)
+    q, qi = to_dev(torch, qh), to_dev(torch, qih, bf16=not w.index_fp8)
+    del kh, vh, kih, qh, qih
+    kv = torch.tensor(w.kv_lens, dtype=torch.int32, device="cuda")
+    qs = torch.tensor(w.q_start, dtype=torch.int32, device="cuda")
+    cfg = msa.Config(num_kv_groups=w.G, heads_per_group=w.R, topk=w.topk)
+    sel = torch.empty((w.B, msa.qblock_slots(w.T), w.G, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.T, w.H, 128), dtype=torch.bfloat16, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    idx_ms, att_ms = [], []
+    for s in range(warmup + steps):
+        ev[0].record()
+        msa.index_topk_qblock(cfg, qi, ki, kv, qs, sel=sel)
+        ev[1].record()
+        msa.sparse_attn_prefill_qblock(cfg, q, k, v, kv, sel, q_start=qs, out=out)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if s >= warmup:
+            idx_ms.append(ev[0].elapsed_time(ev[1]))
+            att_ms.append(ev[1].elapsed_time(ev[2]))
+    L = w.T
+    f_idx = 2.0 * 128 * w.G * L * (L + 1) / 2
+    f_att, _ = sparse_work(torch, w, qblock_rows(torch, sel, w.q_start[0], L), w.q_start[0])
+    ti, ta = min(idx_ms), min(att_ms)
+    res = dict(workload=w.name + "_qblock", selection="query-block-shared (one top-16 per "
+               "128-row query block)", index_ms=round(ti, 3), sparse_ms=round(ta, 3),
+               index_tflops=round(f_idx / ti / 1e9, 2), sparse_tflops=round(f_att / ta / 1e9, 2),
+               sparse_flops=f_att,
+               index_frac_bf16_peak=round(f_idx / ti / 1e9 / BF16_PEAK_TFLOPS, 4),
+               sparse_frac_bf16_peak=round(f_att / ta / 1e9 / BF16_PEAK_TFLOPS, 4),
+               total_tflops=round((f_idx + f_att) / (ti + ta) / 1e9, 2))
+    del q, qi, k, v, ki, sel, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_chunked(torch, msa, w):
     """The 1M-token prefill in 32768-row chunks with E4M3 index data: every
     chunk runs msa_index_topk and msa_sparse_attn_prefill over the cache of
@@ -534,7 +586,8 @@ def main():
 
     if args.prefill_only:
         res = {"prefill": run_prefill(torch, msa, wl.workload(3), steps=args.steps,
-                                      warmup=args.warmup)}
+                                      warmup=args.warmup),
+               "prefill_qblock": run_prefill_qblock(torch, msa, wl.workload(3))}
         if not args.no_chunked:
             res["chunked_prefill"] = run_chunked(torch, msa, wl.workload(5))
         print(json.dumps(res), flush=True)
@@ -590,6 +643,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill:
         line["prefill"] = run_prefill(torch, msa, wl.workload(3))
+        line["prefill_qblock"] = run_prefill_qblock(torch, msa, wl.workload(3))
     if not args.no_prefill and not args.no_chunked:
         line["chunked_prefill"] = run_chunked(torch, msa, wl.workload(5))
     print(json.dumps(line), flush=True)
