@@ -1404,21 +1404,39 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
 // Sparse prefill with query-block-shared selections (the mlqm.cn article,
 // section 核心原理: 128-token blocks, each attending to its 16 most relevant
 // blocks). Every row of query block qblk attends over the same kept blocks,
-// so a workgroup keeps 8*et rows' queries (et = 16/R rows per 16-column
-// tile, two tiles per wave, four waves) in registers and streams the unit's
+// so a workgroup keeps 16*et rows' queries (et = 16/R rows per 16-column
+// tile, two tiles per wave, eight waves) in registers and streams the unit's
 // kept blocks through LDS with an online softmax across blocks: no partials,
 // each K/V block staged once per workgroup and used by every column.
-// Units are (sequence, slot, group); ncw workgroups split a unit's rows.
+//   Staging: direct global->LDS 16-byte loads (lane l of a load fills bytes
+// 16l..16l+15 of a 1 KiB run, four 256-byte rows), double-buffered, so block
+// i+1 streams in while block i is computed. Rows are unpadded and their
+// sixteen 16-byte pieces are XOR-swizzled by the row's low four bits
+// (qb_swz), which keeps the K reads (16 rows, same logical piece) on distinct
+// banks. Rows past the cache
+// are loaded from its last row (finite values that the mask and P = 0 drop).
+//   Units are (sequence, slot, group); ncw workgroups split a unit's rows.
 // Workgroup ids id, id + 8, ... land on one XCD, so the ncw workgroups of a
 // unit (ids 8*(ncw*u') + x + 8*c) share that XCD's L2.
-__global__ __launch_bounds__(256, 2) void qb_attn_kernel(
+constexpr int kQbWaves = 8;
+constexpr float kQbSlack = 8.f;  // log2 units a column's max may exceed its reference
+constexpr int kQbBuf = 2 * S * 256;  // K then V of one block, unpadded rows
+
+// Byte offset of logical 16-byte piece `piece` of staged row `row`: the
+// piece index is XORed with the row's low four bits, so the 16 rows a K read
+// touches (one logical piece) land on 16 different pieces.
+__device__ __forceinline__ int qb_swz_key(int row) { return row & 15; }
+__device__ __forceinline__ int qb_swz(int row, int piece) {
+    return row * 256 + ((piece ^ qb_swz_key(row)) << 4);
+}
+
+__global__ __launch_bounds__(512, 1) void qb_attn_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
     const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const int32_t *__restrict__ sel, int T, int G, int R,
     int Nmax, int K, int nslots, int ncw, int64_t nunits, float scale_log2,
     bf16_t *__restrict__ out, float *__restrict__ lse) {
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds[S * kKRow];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds[S * kVRow];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_kv[2][kQbBuf];
     __shared__ int s_sel[KMAX], s_blocks[KMAX], s_n;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, kg = lane >> 4;
@@ -1434,7 +1452,7 @@ __global__ __launch_bounds__(256, 2) void qb_attn_kernel(
     const int qs = q_start ? q_start[b] : kv - T;
     const int qblk = floor_div(qs, S) + slot;
     const int et = 16 / R;
-    const int ppw = kPfWaves * kPfNq * et;  // rows (positions) per workgroup
+    const int ppw = kQbWaves * kPfNq * et;  // rows (positions) per workgroup
     // Column col of tile nq: position qblk*S + pi, head col % R.
     int trow[kPfNq], pcol[kPfNq];
     bf16x8 qf[kPfNq][4];
@@ -1463,6 +1481,23 @@ __global__ __launch_bounds__(256, 2) void qb_attn_kernel(
     }
     __syncthreads();
     const int nblk = s_n;
+    const int64_t bg = (int64_t)b * G + g;
+    // Wave w stages 1 KiB runs w, w + 8, ... of the 64 KiB (K runs 0..31,
+    // V runs 32..63); lane l fills physical piece l & 15 of row 4*run + l/16.
+    auto stage = [&](int blk, unsigned char *buf) {
+#pragma unroll
+        for (int i = 0; i < 2 * S * 256 / 1024 / kQbWaves; ++i) {
+            const int run = wave + kQbWaves * i;
+            const int kvsel = run >= 32;
+            const int row = (run & 31) * 4 + (lane >> 4);
+            const int tok = min(blk * S + row, kv - 1);
+            const int piece = (lane & 15) ^ qb_swz_key(row);
+            const bf16_t *src = (kvsel ? v_cache : k_cache) + (bg * Nmax + tok) * D + piece * 8;
+            __builtin_amdgcn_global_load_lds(
+                (const void *)src, (__attribute__((address_space(3))) void *)(buf + run * 1024),
+                16, 0, 0);
+        }
+    };
     float m2[kPfNq], lsum[kPfNq];
     f32x4 o[kPfNq][8];
 #pragma unroll
@@ -1472,40 +1507,27 @@ __global__ __launch_bounds__(256, 2) void qb_attn_kernel(
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[nq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if (nblk > 0) stage(s_blocks[0], lds_kv[0]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's runs (and its queries) landed
+    __syncthreads();
     for (int bi = 0; bi < nblk; ++bi) {
         const int blk = s_blocks[bi];
         const int tok_base = blk * S;
-        if (bi > 0) __syncthreads();  // the previous block's LDS reads are done
-        {
-            const int64_t bg = (int64_t)b * G + g;
-            const bf16_t *kb = k_cache + (bg * Nmax + tok_base) * D;
-            const bf16_t *vb = v_cache + (bg * Nmax + tok_base) * D;
-            const u32x4 z4 = {0u, 0u, 0u, 0u};
-            u32x4 kr[8], vr[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
-                const bool in = tok_base + tk < kv;
-                kr[i] = in ? ld16(kb + (size_t)tk * D + c * 8) : z4;
-                vr[i] = in ? ld16(vb + (size_t)tk * D + c * 8) : z4;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
-                *reinterpret_cast<u32x4 *>(k_lds + tk * kKRow + c * 16) = kr[i];
-                *reinterpret_cast<u32x4 *>(v_lds + tk * kVRow + c * 16) = vr[i];
-            }
-        }
-        __syncthreads();
+        // The next block streams into the other buffer (last read in the
+        // previous iteration, before its closing barrier).
+        if (bi + 1 < nblk) stage(s_blocks[bi + 1], lds_kv[(bi + 1) & 1]);
+        const unsigned char *k_lds = lds_kv[bi & 1];
+        const unsigned char *v_lds = k_lds + S * 256;
         // S^T: key tile kt x 16 columns; lane holds column col, keys kt*16 + 4*kg + r.
         f32x4 sacc[kPfNq][8];
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
             if (kt % 2 == 0) __builtin_amdgcn_sched_barrier(0);
             u32x4 ka[4];
-            const unsigned char *kp = k_lds + (kt * 16 + col) * kKRow + kg * 16;
+            const int row = kt * 16 + col;
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) ka[kc] = *reinterpret_cast<const u32x4 *>(kp + kc * 64);
+            for (int kc = 0; kc < 4; ++kc)
+                ka[kc] = *reinterpret_cast<const u32x4 *>(k_lds + qb_swz(row, kc * 4 + kg));
 #pragma unroll
             for (int nq = 0; nq < kPfNq; ++nq) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1515,8 +1537,19 @@ __global__ __launch_bounds__(256, 2) void qb_attn_kernel(
             }
         }
         // Online softmax across blocks (log2 domain). Only the query block's
-        // own key block reaches past a row's position.
-        const bool diag = blk == qblk;
+        // own key block reaches past a row's position (a uniform branch). The
+        // reference m2 moves only when a column's block max exceeds it by more
+        // than kQbSlack (probabilities stay below 2^kQbSlack, exact after the
+        // final division), so O is rarely rescaled.
+        if (blk == qblk) {
+#pragma unroll
+            for (int nq = 0; nq < kPfNq; ++nq)
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (tok_base + kt * 16 + 4 * kg + r > pcol[nq]) sacc[nq][kt][r] = -INFINITY;
+        }
         bf16x8 pa[kPfNq][4];
 #pragma unroll
         for (int nq = 0; nq < kPfNq; ++nq) {
@@ -1524,15 +1557,11 @@ __global__ __launch_bounds__(256, 2) void qb_attn_kernel(
 #pragma unroll
             for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float sv = sacc[nq][kt][r];
-                    if (diag && tok_base + kt * 16 + 4 * kg + r > pcol[nq]) sv = -INFINITY;
-                    sacc[nq][kt][r] = sv;
-                    mx = fmaxf(mx, sv);
-                }
-            mx = max_xor16_32(mx, lane);
-            const float m_new = fmaxf(m2[nq], mx * scale_log2);
-            const float alpha = m2[nq] == -INFINITY ? 0.f : fast_exp2(m2[nq] - m_new);
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[nq][kt][r]);
+            mx = max_xor16_32(mx, lane) * scale_log2;
+            const bool move = mx > m2[nq] + kQbSlack;
+            const float m_new = move ? mx : m2[nq];
+            const float alpha = !move ? 1.f : (m2[nq] == -INFINITY ? 0.f : fast_exp2(m2[nq] - m_new));
             const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
             float psum = 0.f;
 #pragma unroll
@@ -1550,27 +1579,34 @@ __global__ __launch_bounds__(256, 2) void qb_attn_kernel(
             psum = sum_xor16_32(psum, lane);
             lsum[nq] = lsum[nq] * alpha + psum;
             m2[nq] = m_new;
+            if (__ballot(move)) {
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
+                for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[nq][dt][r] *= alpha;
+                    for (int r = 0; r < 4; ++r) o[nq][dt][r] *= alpha;
+            }
         }
-        // O^T += V^T x P^T (as in pf_attn_kernel): lane (col, kg) accumulates
-        // O[column col][d = dt*16 + 4*kg + r].
+        // O^T += V^T x P^T (as in pf_attn_kernel, swizzled rows): lane (col, kg)
+        // accumulates O[column col][d = dt*16 + 4*kg + r].
 #pragma unroll
         for (int c = 0; c < S / 32; ++c) {
-            const unsigned char *vlo = v_lds + (c * 32 + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
-            const unsigned char *vhi = vlo + 16 * kVRow;
+            const int rlo = c * 32 + 4 * kg + (col >> 2);  // rhi = rlo + 16, same swizzle
+            const int lp = (col & 3) >> 1, within = (col & 1) * 8;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 if (dt % 4 == 0) __builtin_amdgcn_sched_barrier(0);
-                const u32x2 lo = lds_read_tr16(vlo + dt * 32);
-                const u32x2 hi = lds_read_tr16(vhi + dt * 32);
+                const int off = qb_swz(rlo, dt * 2 + lp) + within;
+                const u32x2 lo = lds_read_tr16(v_lds + off);
+                const u32x2 hi = lds_read_tr16(v_lds + off + 16 * 256);
                 const u32x4 vbv = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
                 for (int nq = 0; nq < kPfNq; ++nq) o[nq][dt] = mfma16(as_bf16x8(vbv), pa[nq][c], o[nq][dt]);
             }
         }
+        // The next block has landed (this wave's runs) and every wave is done
+        // with this block's buffer.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
     }
     // Rows of the call: the normalised output, or zeros / -inf for a row
     // outside the cache.
@@ -2098,13 +2134,13 @@ msa_status msa_sparse_attn_prefill_qblock(const msa_config *cfg, int32_t B, int3
     if (s != MSA_OK || B == 0 || T == 0) return s;
     const int G = cfg->num_kv_groups, R = cfg->heads_per_group, K = cfg->topk;
     const int nslots = msa::qblock_slots(T);
-    const int ppw = kPfWaves * kPfNq * (16 / R);
+    const int ppw = kQbWaves * kPfNq * (16 / R);
     const int ncw = (S + ppw - 1) / ppw;
     const int64_t nunits = (int64_t)B * nslots * G;
     const int64_t nwg = (nunits + 7) / 8 * 8 * ncw;
     if (nwg > 0x7FFFFFFF)
         return msa::fail(MSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
-    qb_attn_kernel<<<(unsigned)nwg, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+    qb_attn_kernel<<<(unsigned)nwg, kQbWaves * 64, 0, reinterpret_cast<hipStream_t>(stream)>>>(
         static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k_cache),
         static_cast<const bf16_t *>(v_cache), kv_lens, q_start, sel, T, G, R, Nmax, K, nslots,
         ncw, nunits, scale_log2_of(cfg), static_cast<bf16_t *>(out), lse);
