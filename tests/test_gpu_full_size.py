@@ -10,7 +10,10 @@ configuration the benchmark uses:
   chunked prefill, 1048576 tokens in 32768-row   the first, a middle and the
   chunks, E4M3 index data                        last chunk, about 1500 sampled
                                                  rows in all (the oracle's cost
-                                                 per row grows with position).
+                                                 per row grows with position);
+  query-block-shared selections, 131072-token    24 sampled query blocks
+  prefill and two chunks of the 1M chunked       (selections), 8 rows of each
+  prefill                                        (attention).
 Selections are compared bit for bit, outputs and lse within the tolerances of
 the small parity tests. Inputs are the seeded synthetic workloads."""
 import numpy as np
@@ -183,3 +186,76 @@ def test_chunked_prefill_1M_fp8_sampled_rows(orc, chunked_1m, chunk, n_random):
     rows_i = stratified_rows(row0, C, C, n_random, seed=50 + chunk)
     check_prefill_rows(orc, w, host, dev, q_h, qi_h, row0, rows_i,
                        "%s chunk %d" % (w.name, chunk))
+
+
+def check_qblock(orc, w, host, dev, q_h, qi_h, row0, blocks, what, seed):
+    """msa_index_topk_qblock + msa_sparse_attn_prefill_qblock for query rows
+    [row0, row0 + T); the listed query-block slots' selections against the
+    oracle, then 8 rows of each (first, last, six seeded) against the oracle
+    attention with those selections."""
+    import oracle
+    T = q_h.shape[1]
+    cfg = lib_config(w)
+    kv_h = np.array([row0 + T], np.int32)
+    qs_h = np.array([row0], np.int32)
+    kv, qs = dev_i32(kv_h), dev_i32(qs_h)
+    say("%s: msa_index_topk_qblock T=%d q_start=%d" % (what, T, row0))
+    sel, sc = msa.index_topk_qblock(cfg, dev_index(qi_h), dev["ki"], kv, qs, want_scores=True)
+    say("%s: msa_sparse_attn_prefill_qblock" % what)
+    out, lse = msa.sparse_attn_prefill_qblock(cfg, dev_bf16(q_h), dev["k"], dev["v"], kv, sel,
+                                              q_start=qs, want_lse=True)
+    torch.cuda.synchronize()
+    g_sel = sel[0].cpu().numpy()
+    g_sc = sc[0].cpu().numpy().astype(np.float64)
+    items = np.array([(0, s_) for s_ in blocks], np.int32)
+    say("%s: oracle selections of %d query blocks" % (what, len(blocks)))
+    ocfg = ora_config(w)
+    osel, osc = orc.index_topk_qblock(ocfg, qi_h, host["ki"], kv_h, qs_h, items=items,
+                                      threads=THREADS)
+    mism = int((g_sel[blocks] != osel).any(axis=(1, 2)).sum())
+    say("%s: qblock sel items=%d mismatching=%d" % (what, len(blocks), mism))
+    assert mism == 0
+    assert np.array_equal(g_sc[blocks], osc)
+    rng = np.random.default_rng(seed)
+    rows = []
+    for s_ in blocks:
+        lo = max(0, s_ * 128 - row0 % 128)
+        hi = min(T, lo + 128 - (row0 % 128 if s_ == 0 else 0)) - 1
+        picks = {lo, hi} | {int(x) for x in rng.integers(lo, hi + 1, size=6)}
+        rows += [(0, i) for i in sorted(picks)]
+    rows = np.array(rows, np.int32)
+    idx = torch.from_numpy(rows[:, 1].astype(np.int64)).cuda()
+    g_out = bf16_out_to_f64(out[0].index_select(0, idx))
+    g_lse = lse[0].index_select(0, idx).cpu().numpy().astype(np.float64)
+    rsel = oracle.qblock_rows_sel(sel.cpu().numpy(), qs_h, T, 128, rows=rows)
+    oout, olse = orc.sparse_attn(ocfg, q_h, host["k"], host["v"], kv_h, qs_h, rsel, rows=rows,
+                                 threads=THREADS)
+    compare_out(g_out.reshape(oout.shape), oout, what)
+    compare_lse(g_lse.reshape(olse.shape), olse, what)
+    del sel, sc, out, lse
+    torch.cuda.empty_cache()
+
+
+def test_prefill_qblock_L131072_sampled_blocks(orc):
+    w = wl.workload(3)
+    say("generating %s" % w.name)
+    k_h, v_h, ki_h = wl.gen_caches(w)
+    q_h, qi_h = wl.gen_queries(w)
+    host = dict(k=k_h, v=v_h, ki=ki_h)
+    rng = np.random.default_rng(41)
+    blocks = sorted({0, 1, 2, 15, 16, 17, 255, 256, 511, 1023} |
+                    {int(x) for x in rng.integers(0, 1024, size=14)})
+    check_qblock(orc, w, host, upload_caches(k_h, v_h, ki_h), q_h, qi_h, 0, blocks,
+                 w.name + " qblock", seed=42)
+
+
+@pytest.mark.parametrize("chunk,nblocks", [(0, 12), (5, 4)])
+def test_chunked_prefill_1M_fp8_qblock_sampled_blocks(orc, chunked_1m, chunk, nblocks):
+    w, host, dev = chunked_1m
+    C = w.chunk
+    row0 = chunk * C
+    q_h, qi_h = wl.gen_queries(w, row0=row0, rows=C)
+    rng = np.random.default_rng(60 + chunk)
+    blocks = sorted({0, 255} | {int(x) for x in rng.integers(0, 256, size=nblocks - 2)})
+    check_qblock(orc, w, host, dev, q_h, qi_h, row0, blocks,
+                 "%s chunk %d qblock" % (w.name, chunk), seed=61 + chunk)
