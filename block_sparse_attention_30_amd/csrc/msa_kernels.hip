@@ -1373,18 +1373,33 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
             }
         }
         // Partials: m and l of column `col` are in every lane of the column.
+        // Lanes kg and kg^1 of a column trade halves (v_permlane16_swap) so
+        // that each holds 8 consecutive d-values of two dt steps: lane kg
+        // then stores 16 bytes at 64*j + 16*(2*(kg&1) + (kg>>1)) of the
+        // head's row, the column's four lanes one 64-byte run per store.
 #pragma unroll
         for (int nq = 0; nq < kPfNq; ++nq) {
+            const float inv = cent[nq] >= 0 ? 1.f / lrow[nq] : 0.f;
+            u32x4 w4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // E: dt = 2j (kept by even kg), O: dt = 2j+1 (kept by odd kg).
+                const uint32_t e0 = pack_bf16x2(o[nq][2 * j][0] * inv, o[nq][2 * j][1] * inv);
+                const uint32_t e1 = pack_bf16x2(o[nq][2 * j][2] * inv, o[nq][2 * j][3] * inv);
+                const uint32_t o0 = pack_bf16x2(o[nq][2 * j + 1][0] * inv, o[nq][2 * j + 1][1] * inv);
+                const uint32_t o1 = pack_bf16x2(o[nq][2 * j + 1][2] * inv, o[nq][2 * j + 1][3] * inv);
+                const auto r0 = __builtin_amdgcn_permlane16_swap(e0, o0, false, false);
+                const auto r1 = __builtin_amdgcn_permlane16_swap(e1, o1, false, false);
+                // Even kg: (own E, partner's E); odd kg: (partner's O, own O).
+                w4[j] = u32x4{r0[0], r1[0], r0[1], r1[1]};
+            }
             if (cent[nq] < 0) continue;
             const int64_t slot = (((int64_t)b * rows + (cent[nq] >> 5)) * ng + gl) * K + (cent[nq] & 31);
             if (kg == 0) part_ml[slot * R + col % R] = make_float2(mrow[nq], lrow[nq]);
-            bf16_t *op = part_o + (slot * R + col % R) * D + 4 * kg;
-            const float inv = 1.f / lrow[nq];
+            unsigned char *op = reinterpret_cast<unsigned char *>(part_o + (slot * R + col % R) * D) +
+                                16 * (2 * (kg & 1) + (kg >> 1));
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                *reinterpret_cast<u32x2 *>(op + dt * 16) =
-                    u32x2{pack_bf16x2(o[nq][dt][0] * inv, o[nq][dt][1] * inv),
-                          pack_bf16x2(o[nq][dt][2] * inv, o[nq][dt][3] * inv)};
+            for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4 *>(op + 64 * j) = w4[j];
         }
     };
     int entA[kPfNq], pcolA[kPfNq], entB[kPfNq], pcolB[kPfNq];
