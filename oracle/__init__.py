@@ -2,8 +2,9 @@
 
 ctypes front end of ``msa_oracle.c``: a plain fp64 statement of the method
 (index scoring, causal block max-pool, top-k, sparse softmax attention; plus
-textbook dense causal attention for invariants), and ``cache_append``, the
-cache write of new tokens, in plain numpy. Only the tests, the smoke
+textbook dense causal attention for invariants; the sparse branch's
+gradients for fixed selections), and ``cache_append``, the cache write of new
+tokens, in plain numpy. Only the tests, the smoke
 check and the benchmark's CPU-baseline leg may import this package; the GPU
 library never does, and the two share no code.
 
@@ -97,9 +98,12 @@ class Oracle:
         lib.oracle_dense_causal_rows.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, vp, i64, vp, vp,
                                                  i32, vp, vp]
         lib.oracle_index_topk_qblock.argtypes = [cfgp, vp, i32, vp, i64, i64, i64, vp, vp]
+        lib.oracle_sparse_attn_backward.argtypes = [cfgp, i32, i32, i64, vp, vp, vp, vp, vp, vp,
+                                                    vp, i32, vp, vp, vp]
         lib.oracle_index_topk_qblocks.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, i64, vp, vp,
                                                   i32, vp, vp]
-        for f in (lib.oracle_index_topk_qblock, lib.oracle_index_topk_qblocks,
+        for f in (lib.oracle_sparse_attn_backward,
+                  lib.oracle_index_topk_qblock, lib.oracle_index_topk_qblocks,
                   lib.oracle_index_pool_row, lib.oracle_index_pool_rows,
                   lib.oracle_index_topk_row, lib.oracle_sparse_attn_row,
                   lib.oracle_dense_causal_row, lib.oracle_index_topk_rows,
@@ -212,6 +216,31 @@ class Oracle:
         if rc:
             raise ValueError("oracle_sparse_attn_rows rejected its arguments")
         return out, lse
+
+    def sparse_attn_backward(self, cfg: Config, q, k_cache, v_cache, kv_lens, q_start, sel,
+                             dout, threads=None):
+        """Gradients of the sparse branch for fixed selections: dq [B,T,H,d],
+        dk and dv [B,G,N,d] (float64) for sel [B,T,G,K] and the upstream
+        gradient dout [B,T,H,d] (bf16 bits)."""
+        q = _c(q, np.uint16)
+        k_cache = _c(k_cache, np.uint16)
+        v_cache = _c(v_cache, np.uint16)
+        dout = _c(dout, np.uint16)
+        B, T = q.shape[0], q.shape[1]
+        n_stride = k_cache.shape[2]
+        H = cfg.groups * cfg.heads_per_group
+        sel = _c(sel, np.int32).reshape(B, T, cfg.groups, cfg.topk)
+        dq = np.empty((B, T, H, cfg.head_dim), np.float64)
+        dk = np.empty((B, cfg.groups, n_stride, cfg.head_dim), np.float64)
+        dv = np.empty_like(dk)
+        c = cfg.c()
+        rc = self.lib.oracle_sparse_attn_backward(
+            ctypes.byref(c), B, T, n_stride, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(_c(kv_lens, np.int32)), _ptr(_c(q_start, np.int32)), _ptr(sel), _ptr(dout),
+            threads or _threads(), _ptr(dq), _ptr(dk), _ptr(dv))
+        if rc:
+            raise ValueError("oracle_sparse_attn_backward rejected its arguments")
+        return dq, dk, dv
 
     def dense_causal(self, cfg: Config, q, k_cache, v_cache, kv_lens, q_start, rows=None,
                      threads=None):

@@ -334,11 +334,109 @@ int oracle_dense_causal_row(const oracle_cfg *cfg, const uint16_t *q_row, const 
     return 0;
 }
 
+/* Backward of the sparse branch. [T] §五 presents the two-branch design as
+ * trainable end to end; the selection is a discrete choice and carries no
+ * gradient, so for fixed selections the sparse branch is softmax attention
+ * over the kept keys and its gradients are the textbook ones. For sequence b
+ * and group g, every row i of the call at position p = q_start + i < kv_len,
+ * each head h of g, with J the row's attended keys and dout the upstream
+ * gradient of out:
+ *   P_j = softmax_j(tau q.k_j),  dP_j = dout.v_j,
+ *   dS_j = P_j (dP_j - sum_k P_k dP_k),
+ *   dq = tau sum_j dS_j k_j,  dk_j += tau dS_j q,  dv_j += P_j dout.
+ * q_seq, dout_seq [T, H, d] and k_grp, v_grp [n_stride, d] are bf16 bits;
+ * sel_seq [T, G, K]. Writes dq_seq [T, H, d] (heads of group g; zero for rows
+ * outside the cache or with nothing to attend to) and dk_grp, dv_grp
+ * [n_stride, d] (zero where no row attends). */
+int oracle_sparse_attn_backward_group(const oracle_cfg *cfg, int32_t T, int64_t n_stride,
+                                      const uint16_t *q_seq, const uint16_t *k_grp,
+                                      const uint16_t *v_grp, int64_t kv_len, int64_t q_start,
+                                      int32_t g, const int32_t *sel_seq, const uint16_t *dout_seq,
+                                      double *dq_seq, double *dk_grp, double *dv_grp) {
+    if (check_cfg(cfg) || T < 0 || kv_len > n_stride || g < 0 || g >= cfg->groups || !q_seq ||
+        !k_grp || !v_grp || !sel_seq || !dout_seq || !dq_seq || !dk_grp || !dv_grp)
+        return -1;
+    const int G = cfg->groups, R = cfg->heads_per_group, d = cfg->head_dim;
+    const int S = cfg->block_size, K = cfg->topk, H = G * R;
+    const double tau = tau_of(cfg);
+    for (int64_t x = 0; x < n_stride * d; ++x) dk_grp[x] = dv_grp[x] = 0.0;
+    const int64_t nmax = kv_len > 0 ? kv_len : 1;
+    char *chosen = malloc((size_t)(nmax / S + 1));
+    int64_t *keys = malloc(sizeof(int64_t) * (size_t)nmax);
+    double *P = malloc(sizeof(double) * (size_t)nmax);
+    double *dP = malloc(sizeof(double) * (size_t)nmax);
+    if (!chosen || !keys || !P || !dP) {
+        free(chosen);
+        free(keys);
+        free(P);
+        free(dP);
+        return -1;
+    }
+    for (int32_t i = 0; i < T; ++i) {
+        const int64_t p = q_start + i;
+        for (int r = 0; r < R; ++r)
+            for (int c = 0; c < d; ++c) dq_seq[((int64_t)i * H + g * R + r) * d + c] = 0.0;
+        if (p < 0 || p >= kv_len) continue;
+        const int64_t n_valid = p / S + 1;
+        memset(chosen, 0, (size_t)n_valid);
+        for (int k = 0; k < K; ++k) {
+            const int32_t blk = sel_seq[((int64_t)i * G + g) * K + k];
+            if (blk >= 0 && blk < n_valid) chosen[blk] = 1;
+        }
+        int64_t n = 0;
+        for (int64_t j = 0; j <= p; ++j)
+            if (chosen[j / S]) keys[n++] = j;
+        if (n == 0) continue;
+        for (int r = 0; r < R; ++r) {
+            const int64_t h = g * R + r;
+            const uint16_t *qh = q_seq + ((int64_t)i * H + h) * d;
+            const uint16_t *doh = dout_seq + ((int64_t)i * H + h) * d;
+            double m = -INFINITY;
+            for (int64_t a = 0; a < n; ++a) {
+                double acc = 0.0;
+                for (int c = 0; c < d; ++c)
+                    acc += oracle_bf16_value(qh[c]) * oracle_bf16_value(k_grp[keys[a] * d + c]);
+                P[a] = tau * acc;
+                if (P[a] > m) m = P[a];
+            }
+            double l = 0.0;
+            for (int64_t a = 0; a < n; ++a) {
+                P[a] = exp(P[a] - m);
+                l += P[a];
+            }
+            double delta = 0.0;
+            for (int64_t a = 0; a < n; ++a) {
+                P[a] /= l;
+                double acc = 0.0;
+                for (int c = 0; c < d; ++c)
+                    acc += oracle_bf16_value(doh[c]) * oracle_bf16_value(v_grp[keys[a] * d + c]);
+                dP[a] = acc;
+                delta += P[a] * acc;
+            }
+            double *dqh = dq_seq + ((int64_t)i * H + h) * d;
+            for (int64_t a = 0; a < n; ++a) {
+                const double ds = P[a] * (dP[a] - delta);
+                const int64_t j = keys[a];
+                for (int c = 0; c < d; ++c) {
+                    dqh[c] += tau * ds * oracle_bf16_value(k_grp[j * d + c]);
+                    dk_grp[j * d + c] += tau * ds * oracle_bf16_value(qh[c]);
+                    dv_grp[j * d + c] += P[a] * oracle_bf16_value(doh[c]);
+                }
+            }
+        }
+    }
+    free(chosen);
+    free(keys);
+    free(P);
+    free(dP);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Row-parallel drivers: a pthread pool pulling row numbers from a counter.   */
 
 typedef struct {
-    int kind; /* 0 index, 1 sparse, 2 dense, 3 pooled scores, 4 query-block index */
+    int kind; /* 0 index, 1 sparse, 2 dense, 3 pooled, 4 query-block index, 5 backward */
     const oracle_cfg *cfg;
     int32_t T;
     int64_t n_stride;
@@ -348,6 +446,8 @@ typedef struct {
     int64_t nrows;
     int32_t *sel;
     double *scores, *out, *lse, *pooled;
+    const uint16_t *dout; /* backward: upstream gradient; out holds dq */
+    double *dk, *dv;
     int64_t nb_out; /* pooled: blocks stored per (row, group) */
     int64_t next; /* shared row counter */
     int failed;
@@ -360,9 +460,22 @@ static int run_row(row_work *w, int64_t r) {
     const int G = cfg->groups, H = cfg->groups * cfg->heads_per_group;
     const int d = cfg->head_dim, dI = cfg->index_dim, K = cfg->topk;
     int32_t b = w->rows_b[r], i = w->rows_i[r];
-    if (b < 0 || i < 0 || (w->kind != 4 && i >= w->T)) return -1;
+    if (b < 0 || i < 0 || (w->kind < 4 && i >= w->T)) return -1;
     int64_t p = (int64_t)w->q_start[b] + i;
-    if (w->kind != 4 && (p >= w->kv_lens[b] || w->kv_lens[b] > w->n_stride)) return -1;
+    if (w->kind < 4 && (p >= w->kv_lens[b] || w->kv_lens[b] > w->n_stride)) return -1;
+    if (w->kind == 5) {
+        /* (sequence, group): rows_i holds the group. */
+        const int64_t H = (int64_t)G * cfg->heads_per_group;
+        if (w->kv_lens[b] > w->n_stride) return -1;
+        return oracle_sparse_attn_backward_group(
+            cfg, w->T, w->n_stride, w->q + (int64_t)b * w->T * H * d,
+            w->k_cache + ((int64_t)b * G + i) * w->n_stride * d,
+            w->v_cache + ((int64_t)b * G + i) * w->n_stride * d, w->kv_lens[b], w->q_start[b], i,
+            w->sel_in + (int64_t)b * w->T * G * K, w->dout + (int64_t)b * w->T * H * d,
+            w->out + (int64_t)b * w->T * H * d,
+            w->dk + ((int64_t)b * G + i) * w->n_stride * d,
+            w->dv + ((int64_t)b * G + i) * w->n_stride * d);
+    }
     if (w->kind == 4) {
         /* (sequence, query-block slot): rows_i holds the slot. */
         const int64_t es = index_elem_size(cfg);
@@ -460,6 +573,34 @@ int oracle_index_topk_qblocks(const oracle_cfg *cfg, int32_t T, int64_t n_stride
     w.kv_lens = kv_lens; w.q_start = q_start; w.nrows = nitems; w.rows_b = items_b;
     w.rows_i = items_slot; w.sel = sel; w.scores = scores;
     return run_rows(&w, nthreads);
+}
+
+int oracle_sparse_attn_backward(const oracle_cfg *cfg, int32_t B, int32_t T, int64_t n_stride,
+                                const uint16_t *q, const uint16_t *k_cache,
+                                const uint16_t *v_cache, const int32_t *kv_lens,
+                                const int32_t *q_start, const int32_t *sel, const uint16_t *dout,
+                                int32_t nthreads, double *dq, double *dk, double *dv) {
+    if (check_cfg(cfg) || B < 0) return -1;
+    const int64_t n = (int64_t)B * cfg->groups;
+    int32_t *ib = malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    int32_t *ig = malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    if (!ib || !ig) {
+        free(ib);
+        free(ig);
+        return -1;
+    }
+    for (int64_t x = 0; x < n; ++x) {
+        ib[x] = (int32_t)(x / cfg->groups);
+        ig[x] = (int32_t)(x % cfg->groups);
+    }
+    row_work w = { 0 };
+    w.kind = 5; w.cfg = cfg; w.T = T; w.n_stride = n_stride; w.q = q; w.k_cache = k_cache;
+    w.v_cache = v_cache; w.kv_lens = kv_lens; w.q_start = q_start; w.nrows = n; w.rows_b = ib;
+    w.rows_i = ig; w.sel_in = sel; w.dout = dout; w.out = dq; w.dk = dk; w.dv = dv;
+    const int rc = run_rows(&w, nthreads);
+    free(ib);
+    free(ig);
+    return rc;
 }
 
 int oracle_index_pool_rows(const oracle_cfg *cfg, int32_t T, int64_t n_stride, const void *q_idx,

@@ -86,6 +86,31 @@ int oracle_sparse_attn_row(const oracle_cfg *cfg, const uint16_t *q_row, const u
                            const uint16_t *v_seq, int64_t n_stride, int64_t p,
                            const int32_t *sel, double *out, double *lse);
 
+/*
+ * Backward of the sparse branch for fixed selections (the Tencent article's
+ * §五 presents the design as trainable; the discrete selection carries no
+ * gradient): for sequence data q_seq, dout_seq [T, H, d] (bf16 bits), one
+ * group's caches k_grp, v_grp [n_stride, d], sel_seq [T, G, K], writes
+ * dq_seq [T, H, d] for the heads of group g and dk_grp, dv_grp [n_stride, d]:
+ *   P = softmax(tau q.k) over the row's kept keys, dP_j = dout.v_j,
+ *   dS_j = P_j (dP_j - sum_k P_k dP_k), dq = tau sum dS_j k_j,
+ *   dk_j += tau dS_j q, dv_j += P_j dout.
+ */
+int oracle_sparse_attn_backward_group(const oracle_cfg *cfg, int32_t T, int64_t n_stride,
+                                      const uint16_t *q_seq, const uint16_t *k_grp,
+                                      const uint16_t *v_grp, int64_t kv_len, int64_t q_start,
+                                      int32_t g, const int32_t *sel_seq, const uint16_t *dout_seq,
+                                      double *dq_seq, double *dk_grp, double *dv_grp);
+
+/* Batched backward over every (sequence, group) on a thread pool: q, dout
+ * [B, T, H, d], caches [B, G, n_stride, d], sel [B, T, G, K]; dq [B, T, H, d],
+ * dk, dv [B, G, n_stride, d] (float64). */
+int oracle_sparse_attn_backward(const oracle_cfg *cfg, int32_t B, int32_t T, int64_t n_stride,
+                                const uint16_t *q, const uint16_t *k_cache,
+                                const uint16_t *v_cache, const int32_t *kv_lens,
+                                const int32_t *q_start, const int32_t *sel, const uint16_t *dout,
+                                int32_t nthreads, double *dq, double *dk, double *dv);
+
 /* Dense causal GQA softmax attention over every key j <= p (same layouts). */
 int oracle_dense_causal_row(const oracle_cfg *cfg, const uint16_t *q_row, const uint16_t *k_seq,
                             const uint16_t *v_seq, int64_t n_stride, int64_t p,

@@ -486,11 +486,101 @@ def pin_qblock_selection(orc, seed=8):
     assert list(rows_sel[:, 0, 0]) == [0, 0, 1, 1, 1, 1, 2]
 
 
+def pin_backward_finite_differences(orc, seed=9):
+    """Gradients of the sparse branch against central differences of the
+    forward oracle: inputs are multiples of 1/8 in (-1, 1) and one element
+    moves by +-1/64 (both exactly representable in bf16); the loss is
+    sum(out * dout) with a fixed selection that mixes blocks, skips some and
+    cuts the diagonal one."""
+    rng = np.random.default_rng(seed)
+    G, R, d, S, K, L = 2, 2, 4, 4, 2, 14
+    cfg = Config(groups=G, heads_per_group=R, head_dim=d, index_dim=2, block_size=S, topk=K)
+    H = G * R
+    q = rng.integers(-7, 8, size=(1, L, H, d)) / 8.0
+    k = rng.integers(-7, 8, size=(1, G, L, d)) / 8.0
+    v = rng.integers(-7, 8, size=(1, G, L, d)) / 8.0
+    dout = rng.integers(-7, 8, size=(1, L, H, d)) / 8.0
+    kv = np.array([L], np.int32)
+    qs = np.array([0], np.int32)
+    sel = np.full((1, L, G, K), -1, np.int32)
+    for i in range(L):
+        nb = i // S + 1
+        for g in range(G):
+            picks = rng.choice(nb, size=min(K, nb), replace=False)
+            sel[0, i, g, :len(picks)] = picks
+    dq, dk, dv = orc.sparse_attn_backward(cfg, bf16(q), bf16(k), bf16(v), kv, qs, sel, bf16(dout))
+
+    def loss(qq, kk, vv):
+        out, _ = orc.sparse_attn(cfg, bf16(qq), bf16(kk), bf16(vv), kv, qs,
+                                 sel.reshape(L, G, K))
+        return float((out.reshape(1, L, H, d) * dout).sum())
+
+    h = 1.0 / 64
+    checks = 0
+    for arr, grad, name in ((q, dq, "q"), (k, dk, "k"), (v, dv, "v")):
+        for _ in range(12):
+            idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += h
+            minus[idx] -= h
+            if name == "q":
+                num = (loss(plus, k, v) - loss(minus, k, v)) / (2 * h)
+            elif name == "k":
+                num = (loss(q, plus, v) - loss(q, minus, v)) / (2 * h)
+            else:
+                num = (loss(q, k, plus) - loss(q, k, minus)) / (2 * h)
+            assert abs(num - grad[idx]) <= 2e-3 + 2e-3 * abs(num), (name, idx, num, grad[idx])
+            checks += 1
+    assert checks == 36
+    # Keys of a block no row keeps get zero gradients.
+    sel2 = np.where(sel == 1, -1, sel)
+    _, dk2, dv2 = orc.sparse_attn_backward(cfg, bf16(q), bf16(k), bf16(v), kv, qs, sel2,
+                                           bf16(dout))
+    assert not dk2[:, :, S:2 * S].any() and not dv2[:, :, S:2 * S].any()
+    assert dk2[:, :, :S].any() and dv2[:, :, :S].any()
+
+
+def pin_backward_dense_autograd(orc, seed=10):
+    """With every causal block kept, the sparse branch is dense causal attention:
+    its gradients equal torch autograd of a float64 causal softmax attention
+    (matmul, mask, softmax) on the CPU."""
+    import torch
+    rng = np.random.default_rng(seed)
+    G, R, d, S, L = 2, 3, 8, 4, 19
+    K = (L - 1) // S + 1
+    cfg = Config(groups=G, heads_per_group=R, head_dim=d, index_dim=2, block_size=S, topk=K)
+    H = G * R
+    qb = bf16(rng.standard_normal((1, L, H, d)))
+    kb = bf16(rng.standard_normal((1, G, L, d)))
+    vb = bf16(rng.standard_normal((1, G, L, d)))
+    db = bf16(rng.standard_normal((1, L, H, d)))
+    sel = np.full((1, L, G, K), -1, np.int32)
+    for i in range(L):
+        sel[0, i, :, : i // S + 1] = np.arange(i // S + 1)
+    dq, dk, dv = orc.sparse_attn_backward(cfg, qb, kb, vb, np.array([L], np.int32),
+                                          np.array([0], np.int32), sel, db)
+    q = torch.tensor(as_f(qb)[0], requires_grad=True)          # [L, H, d]
+    k = torch.tensor(as_f(kb)[0], requires_grad=True)          # [G, L, d]
+    v = torch.tensor(as_f(vb)[0], requires_grad=True)
+    outs = []
+    mask = torch.tril(torch.ones(L, L, dtype=torch.bool))
+    for h in range(H):
+        g = h // R
+        z = (q[:, h, :] @ k[g].T) / math.sqrt(d)
+        z = z.masked_fill(~mask, float("-inf"))
+        outs.append(torch.softmax(z, dim=1) @ v[g])
+    out = torch.stack(outs, dim=1)
+    (out * torch.tensor(as_f(db)[0])).sum().backward()
+    assert np.allclose(dq[0], q.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dk[0], k.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dv[0], v.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
 ALL_PINS = [pin_decoders, pin_hand_example_selection, pin_hand_example_attention,
             pin_hand_example_variants, pin_brute_force_selection,
             pin_token_level_and_single_block, pin_selection_invariants, pin_sparse_vs_numpy,
             pin_attention_invariants, pin_mixed_lengths_and_stride, pin_cache_append,
-            pin_qblock_selection]
+            pin_qblock_selection, pin_backward_finite_differences, pin_backward_dense_autograd]
 
 
 def run_all(orc):

@@ -10,8 +10,16 @@ import oracle_pins as pins
 
 # (name, text in msa_oracle.c, replacement)
 MUTANTS = [
-    ("diagonal_key_dropped", "for (int64_t j = 0; j <= p; ++j)\n            if (chosen[j / S])",
-     "for (int64_t j = 0; j < p; ++j)\n            if (chosen[j / S])"),
+    ("diagonal_key_dropped",
+     "for (int64_t j = 0; j <= p; ++j)\n            if (chosen[j / S]) keys[n++] = j;\n"
+     "        const uint16_t *k_grp",
+     "for (int64_t j = 0; j < p; ++j)\n            if (chosen[j / S]) keys[n++] = j;\n"
+     "        const uint16_t *k_grp"),
+    ("backward_diagonal_key_dropped",
+     "for (int64_t j = 0; j <= p; ++j)\n            if (chosen[j / S]) keys[n++] = j;\n"
+     "        if (n == 0) continue;",
+     "for (int64_t j = 0; j < p; ++j)\n            if (chosen[j / S]) keys[n++] = j;\n"
+     "        if (n == 0) continue;"),
     ("pool_starts_at_zero", "double m = s[lo];", "double m = 0.0;"),
     ("pool_sums", "if (s[j] > m) m = s[j];", "m += s[j];"),
     ("ties_to_higher_block", "return (x->block > y->block) - (x->block < y->block);",
@@ -39,6 +47,12 @@ MUTANTS = [
      "for (int64_t i = i_lo; i <= i_lo; ++i) {"),
     ("qblock_slot_from_zero", "const int64_t qb = q_start / S + slot;",
      "const int64_t qb = slot;"),
+    ("backward_no_delta", "const double ds = P[a] * (dP[a] - delta);",
+     "const double ds = P[a] * dP[a];"),
+    ("backward_dv_unweighted", "dv_grp[j * d + c] += P[a] * oracle_bf16_value(doh[c]);",
+     "dv_grp[j * d + c] += oracle_bf16_value(doh[c]);"),
+    ("backward_dk_no_scale", "dk_grp[j * d + c] += tau * ds * oracle_bf16_value(qh[c]);",
+     "dk_grp[j * d + c] += ds * oracle_bf16_value(qh[c]);"),
 ]
 
 
