@@ -24,7 +24,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmsa.so")
 
 BF16, FP8_E4M3 = 0, 1
-WS_INDEX_TOPK, WS_SPARSE_PREFILL, WS_SPARSE_DECODE, WS_DECODE = 0, 1, 2, 3
+WS_INDEX_TOPK, WS_SPARSE_PREFILL, WS_SPARSE_DECODE, WS_DECODE, WS_SPARSE_BACKWARD = 0, 1, 2, 3, 4
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARG", 2: "MSA_ERR_UNSUPPORTED",
            3: "MSA_ERR_WORKSPACE", 4: "MSA_ERR_HIP"}
 
@@ -100,6 +100,9 @@ def load():
     lib.msa_index_topk_qblock.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.msa_sparse_attn_prefill_qblock.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                                    vp, vp, vp]
+    lib.msa_sparse_attn_backward.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_backward.restype = ctypes.c_int
     lib.msa_qblock_slots.argtypes = [i32]
     lib.msa_qblock_slots.restype = i32
     for f in (lib.msa_index_topk, lib.msa_index_pool, lib.msa_sparse_attn_prefill,
@@ -454,3 +457,38 @@ def sparse_attn_prefill_qblock(cfg: Config, q, k_cache, v_cache, kv_lens, sel, q
             ctypes.byref(cfg._c()), B, T, Nmax, _ptr(q), _ptr(k_cache), _ptr(v_cache),
             _ptr(kv_lens), _ptr(q_start), _ptr(sel), _ptr(out), _ptr(lse), _stream(dev)))
     return (out, lse) if (want_lse or lse is not None) else out
+
+
+def sparse_attn_backward(cfg: Config, q, k_cache, v_cache, kv_lens, sel, out, lse, dout,
+                         q_start=None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of the sparse branch for fixed selections: (dq [B,T,H,d],
+    dk [B,G,Nmax,d], dv [B,G,Nmax,d]) in float32, from the forward's out and
+    lse and the upstream gradient dout [B,T,H,d] bf16."""
+    dev, B, T, Nmax = _sparse_checks(cfg, q, k_cache, v_cache, kv_lens, sel)
+    if q_start is not None:
+        _lens(q_start, "q_start", B, dev)
+    H, d, G = cfg.num_heads, cfg.head_dim, cfg.num_kv_groups
+    _need(out, "out", (torch.bfloat16,), 4, dev)
+    _need(dout, "dout", (torch.bfloat16,), 4, dev)
+    _need(lse, "lse", (torch.float32,), 3, dev)
+    if tuple(out.shape) != (B, T, H, d) or tuple(dout.shape) != (B, T, H, d) or \
+            tuple(lse.shape) != (B, T, H):
+        raise ValueError("out/dout must be [B,T,H,d] and lse [B,T,H]")
+    if dq is None:
+        dq = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((B, G, Nmax, d), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((B, G, Nmax, d), dtype=torch.float32, device=dev)
+    for t_, name, shp in ((dq, "dq", (B, T, H, d)), (dk, "dk", (B, G, Nmax, d)),
+                          (dv, "dv", (B, G, Nmax, d))):
+        _need(t_, name, (torch.float32,), 4, dev)
+        if tuple(t_.shape) != shp:
+            raise ValueError("%s must be %s" % (name, shp))
+    ws, nws = _workspace(cfg, B, T, Nmax, WS_SPARSE_BACKWARD, dev, workspace)
+    with _on_device(dev):
+        _check(load().msa_sparse_attn_backward(
+            ctypes.byref(cfg._c()), B, T, Nmax, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(kv_lens), _ptr(q_start), _ptr(sel), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(ws), nws, _stream(dev)))
+    return dq, dk, dv

@@ -77,17 +77,19 @@ int32_t prefill_entries_per_tile(int32_t R) {
     return kPfRounds * kPfWaves * kPfNq * (16 / R);
 }
 
-PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) {
+PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, bool backward) {
     PrefillWs w{};
     const int64_t G = cfg->num_kv_groups, K = cfg->topk, R = cfg->heads_per_group;
-    w.kv_major = (int64_t)B * T * G >= kPfKvMajorMinRows;
+    w.kv_major = backward || (int64_t)B * T * G >= kPfKvMajorMinRows;
     if (!w.kv_major || B == 0 || T == 0) return w;
     // One pass covers every group and `rows` query rows of every sequence: the
     // largest power of two of rows (or all T) whose partials fit
     // kPfPartialBudget, with at most 2^24 (sequence, row, group) units. (Passes
     // of one group whose queries stay in the last-level cache were measured
     // slower: the list build is paid per pass.)
-    const size_t part_row = (size_t)B * G * K * R * (kHeadDim * 2 + 8);
+    // Per (row, group, slot, head): the forward keeps O / l in bf16 and (m, l);
+    // the backward keeps a dq partial in fp32.
+    const size_t part_row = (size_t)B * G * K * R * (backward ? kHeadDim * 4 : kHeadDim * 2 + 8);
     const int64_t max_units = (int64_t)1 << 24;
     int64_t rows = 1;
     while (rows * 2 <= T && (size_t)(rows * 2) * part_row <= kPfPartialBudget &&
@@ -110,8 +112,13 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) 
     w.tile_map_off = take((size_t)w.max_tiles * 4);
     w.rank_off = take((size_t)w.nslots * 4);
     w.list_off = take((size_t)w.nslots * 4);
-    w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 2);
-    w.part_ml_off = take((size_t)w.nslots * R * 8);
+    if (backward) {
+        w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 4);  // dq partials
+        w.delta_off = take((size_t)B * T * G * R * 4);            // dout . out per (row, head)
+    } else {
+        w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 2);
+        w.part_ml_off = take((size_t)w.nslots * R * 8);
+    }
     w.total = off;
     return w;
 }
@@ -201,6 +208,35 @@ msa_status check_qblock_index_args(const msa_config *cfg, int32_t B, int32_t T, 
         (sel_scores && !aligned(sel_scores, 4)))
         return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
     return MSA_OK;
+}
+
+msa_status check_backward_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                               const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *kv_lens, const int32_t *q_start,
+                               const int32_t *sel, const void *out, const float *lse,
+                               const void *dout, const float *dq, const float *dk,
+                               const float *dv, const void *workspace, size_t ws_bytes) {
+    msa_status s = check_config(cfg);
+    if (s != MSA_OK) return s;
+    if ((s = check_dims(B, T, Nmax)) != MSA_OK) return s;
+    if (B == 0 || T == 0) return MSA_OK;
+    const PrefillWs pw = prefill_ws(cfg, B, T, Nmax, true);
+    if (pw.nlists + 1 > ((int64_t)1 << 31) - 1 ||
+        pw.nslots * cfg->heads_per_group > ((int64_t)1 << 31) - 1 ||
+        pw.max_tiles >= ((int64_t)1 << 24))
+        return fail(MSA_ERR_UNSUPPORTED, "sparse backward lists exceed 2^31 entries");
+    if (!q || !k_cache || !v_cache || !kv_lens || !sel || !out || !lse || !dout || !dq || !dk ||
+        !dv)
+        return fail(MSA_ERR_INVALID_ARG,
+                    "q, k_cache, v_cache, kv_lens, sel, out, lse, dout, dq, dk and dv must not "
+                    "be NULL");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return fail(MSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (!aligned(kv_lens, 4) || (q_start && !aligned(q_start, 4)) || !aligned(sel, 4) ||
+        !aligned(lse, 4))
+        return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
+    return check_ws(workspace, ws_bytes, pw.total);
 }
 
 msa_status check_append_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
@@ -293,6 +329,8 @@ size_t msa_workspace_size(const msa_config *cfg, int32_t B, int32_t T, int32_t N
             return msa::decode_ws(cfg, B, Nmax, false).total;
         case MSA_WS_DECODE:
             return msa::decode_ws(cfg, B, Nmax, true).total;
+        case MSA_WS_SPARSE_BACKWARD:
+            return msa::prefill_ws(cfg, B, T, Nmax, true).total;
         default:
             msa::fail(MSA_ERR_INVALID_ARG, "unknown workspace kind %d", which);
             return (size_t)-1;

@@ -40,6 +40,12 @@ msa_status check_qblock_index_args(const msa_config *cfg, int32_t B, int32_t T, 
                                    const void *q_idx, const void *k_idx, const int32_t *kv_lens,
                                    const int32_t *q_start, const int32_t *sel,
                                    const float *sel_scores);
+msa_status check_backward_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                               const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *kv_lens, const int32_t *q_start,
+                               const int32_t *sel, const void *out, const float *lse,
+                               const void *dout, const float *dq, const float *dk,
+                               const float *dv, const void *workspace, size_t ws_bytes);
 msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                              const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *kv_lens, const int32_t *q_start, const int32_t *sel,
@@ -75,9 +81,13 @@ struct PrefillWs {
     int32_t entries_per_tile;
     int64_t nb_max, nlists, nslots, max_tiles;
     size_t counts_off, offsets_off, tile_first_off, tile_map_off, rank_off, list_off;
-    size_t part_o_off, part_ml_off, total;
+    size_t part_o_off, part_ml_off, delta_off, total;
 };
-PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
+// backward: the layout of msa_sparse_attn_backward (always KV-major; dq
+// partials in fp32 instead of the forward's partials; plus dout.out per
+// (row, head)).
+PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                     bool backward = false);
 
 // Decode attention: split partials [B*G][nsplit][R] x (128 + 2) fp32, after
 // the pooled scores when the call also runs the index branch (msa_decode).

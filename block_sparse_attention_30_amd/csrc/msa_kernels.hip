@@ -1701,6 +1701,368 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Backward of the sparse branch for fixed selections (the Tencent article,
+// §五: the two-branch design trains end to end; the selection itself carries
+// no gradient). With the forward's lse, P_j = exp2(s_j * tau*log2e -
+// lse*log2e) needs no second softmax pass, and with delta = dout . out per
+// (row, head), dS_j = P_j (dP_j - delta). Per pass of the forward's list
+// build (same lists, tiles and slots):
+//   bwd_dq_kernel     one workgroup per tile, waves own 16-column query tiles
+//                     (as pf_attn_kernel): S^T = K q^T and dP^T = V dout^T,
+//                     dS, then dq^T = K^T dS^T (K read transposed from LDS);
+//                     tau * dq partial per (row, group, slot, head), fp32;
+//   bwd_dkdv_kernel   one workgroup per list, each wave owns 32 keys of the
+//                     block with their K and V rows in registers: for each
+//                     batch of 32 columns staged in LDS, S = q K^T, dP = dout
+//                     V^T, dS, then dv^T += dout^T P and dk^T += q^T dS (16x16x16
+//                     MFMA, the columns as the reduction index); written after
+//                     the list (added to the earlier passes' values);
+//   bwd_dq_merge_kernel  dq of a (row, group) = sum of its kept slots' partials.
+// delta comes first from bwd_delta_kernel. No floating-point atomics: every
+// sum has one owner and a fixed order.
+typedef __attribute__((ext_vector_type(4))) short v4i16;
+
+__device__ __forceinline__ f32x4 mfma16k16(v4i16 a, v4i16 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4i16 pack_bf16x4(float a, float b, float c, float d) {
+    const uint32_t lo = pack_bf16x2(a, b), hi = pack_bf16x2(c, d);
+    return __builtin_bit_cast(v4i16, u32x2{lo, hi});
+}
+
+// delta[r] = sum_d dout[r, d] * out[r, d] for every (row, head) r: 16 lanes per
+// r, 16 bytes of each operand per lane.
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16_t *__restrict__ out,
+                                                        const bf16_t *__restrict__ dout,
+                                                        int64_t nrows, float *__restrict__ delta) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    const int c = lane & 15;
+    float acc = 0.f;
+    if (r < nrows) {
+        const u32x4 a = ld16(out + r * D + c * 8), d = ld16(dout + r * D + c * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc += __uint_as_float(a[i] << 16) * __uint_as_float(d[i] << 16);
+            acc += __uint_as_float(a[i] & 0xFFFF0000u) * __uint_as_float(d[i] & 0xFFFF0000u);
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
+    if (r < nrows && c == 0) delta[r] = acc;
+}
+
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
+    const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, const float *__restrict__ lse,
+    const bf16_t *__restrict__ dout, const float *__restrict__ delta,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tile_first,
+    const int32_t *__restrict__ tile_map, const int32_t *__restrict__ list, int64_t nlists,
+    int T, int G, int R, int Nmax, int K, int t0, int rows, int g0, int ng, int64_t nb_max,
+    int ch, float scale_log2, float tau, float *__restrict__ part_dq) {
+    // K rows padded for the transposing reads, V rows for plain row reads.
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[S * kVRow];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[S * kKRow];
+    const int w = blockIdx.x;
+    if (w >= tile_first[nlists]) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    const int li = tile_map[w];
+    const int beg = offsets[li] + (w - tile_first[li]) * ch;
+    const int nent = min(beg + ch, offsets[li + 1]) - beg;
+    const int64_t bgl = li / nb_max;
+    const int blk = (int)(li % nb_max);
+    const int b = (int)(bgl / ng), gl = (int)(bgl % ng), g = g0 + gl;
+    const int64_t bg = (int64_t)b * G + g;
+    const int H = G * R;
+    const int kv = clamp_kv(kv_lens[b], Nmax);
+    const int qs = q_start ? q_start[b] : kv - T;
+    {
+        const bf16_t *kb = k_cache + (bg * Nmax + (int64_t)blk * S) * D;
+        const bf16_t *vb = v_cache + (bg * Nmax + (int64_t)blk * S) * D;
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        u32x4 kr[8], vr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
+            const bool in = blk * S + tk < kv;
+            kr[i] = in ? ld16(kb + (size_t)tk * D + c * 8) : z4;
+            vr[i] = in ? ld16(vb + (size_t)tk * D + c * 8) : z4;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
+            *reinterpret_cast<u32x4 *>(k_lds + tk * kVRow + c * 16) = kr[i];
+            *reinterpret_cast<u32x4 *>(v_lds + tk * kKRow + c * 16) = vr[i];
+        }
+    }
+    __syncthreads();
+    const int et = 16 / R;
+    const int tok_base = blk * S;
+    for (int e0 = wave * et; e0 < nent; e0 += kPfWaves * et) {
+        // Column col: entry e0 + col/R, head col % R.
+        const int e = e0 + col / R;
+        const bool ok = col < et * R && e < nent;
+        const int ent = ok ? list[beg + e] : 0;
+        const int tl = ent >> 5;
+        const int pcol = ok ? qs + t0 + tl : -1;
+        const int64_t hrow = ((int64_t)b * T + t0 + tl) * H + (int64_t)g * R + col % R;
+        bf16x8 qf[4], dof[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            qf[kc] = ok ? ld_bf16x8(q + hrow * D + kc * 32 + kg * 8) : zero_bf16x8();
+            dof[kc] = ok ? ld_bf16x8(dout + hrow * D + kc * 32 + kg * 8) : zero_bf16x8();
+        }
+        const float lse2 = ok ? lse[hrow] * kLog2e : INFINITY;
+        const float dl = ok ? delta[hrow] : 0.f;
+        // S^T and dP^T for the block's 128 keys; lane holds column col,
+        // keys kt*16 + 4*kg + r.
+        f32x4 sacc[8], dpacc[8];
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+            if (kt % 2 == 0) __builtin_amdgcn_sched_barrier(0);
+            const unsigned char *kp = k_lds + (kt * 16 + col) * kVRow + kg * 16;
+            const unsigned char *vp = v_lds + (kt * 16 + col) * kKRow + kg * 16;
+            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                sa = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + kc * 64)), qf[kc], sa);
+                da = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + kc * 64)), dof[kc], da);
+            }
+            sacc[kt] = sa;
+            dpacc[kt] = da;
+        }
+        // dS in the P^T operand order of the forward (keys 4*kg + i of the
+        // lower and upper 16-key half of each 32-key chunk).
+        bf16x8 dsa[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float dsv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int kt = 2 * c + (i >> 2), r = i & 3;
+                const int tok = tok_base + kt * 16 + 4 * kg + r;
+                const float p = tok > pcol ? 0.f : fast_exp2(fmaf(sacc[kt][r], scale_log2, -lse2));
+                dsv[i] = p * (dpacc[kt][r] - dl);
+            }
+            const u32x4 pk = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
+                              pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
+            dsa[c] = as_bf16x8(pk);
+        }
+        // dq^T = K^T dS^T: K read transposed from LDS (the forward's V reads).
+        f32x4 dq[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const unsigned char *klo = k_lds + (c * 32 + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
+            const unsigned char *khi = klo + 16 * kVRow;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                if (dt % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+                const u32x2 lo = lds_read_tr16(klo + dt * 32);
+                const u32x2 hi = lds_read_tr16(khi + dt * 32);
+                const u32x4 kb4 = {lo[0], lo[1], hi[0], hi[1]};
+                dq[dt] = mfma16(as_bf16x8(kb4), dsa[c], dq[dt]);
+            }
+        }
+        if (ok) {
+            const int64_t slot = (((int64_t)b * rows + tl) * ng + gl) * K + (ent & 31);
+            float *op = part_dq + (slot * R + col % R) * D + 4 * kg;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                *reinterpret_cast<f32x4 *>(op + dt * 16) =
+                    f32x4{tau * dq[dt][0], tau * dq[dt][1], tau * dq[dt][2], tau * dq[dt][3]};
+        }
+    }
+}
+
+constexpr int kBwdCols = 32;  // columns (entry heads) per bwd_dkdv_kernel batch
+
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
+    const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, const float *__restrict__ lse,
+    const bf16_t *__restrict__ dout, const float *__restrict__ delta,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ list, int T, int G, int R,
+    int Nmax, int t0, int g0, int ng, int64_t nb_max, float scale_log2, float tau, int accumulate,
+    float *__restrict__ dk, float *__restrict__ dv) {
+    __shared__ __attribute__((aligned(16))) unsigned char q_s[kBwdCols * kVRow];
+    __shared__ __attribute__((aligned(16))) unsigned char do_s[kBwdCols * kVRow];
+    __shared__ float s_lse2[kBwdCols], s_dl[kBwdCols];
+    __shared__ int s_pc[kBwdCols];
+    const int64_t li = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    const int64_t bgl = li / nb_max;
+    const int blk = (int)(li % nb_max);
+    const int b = (int)(bgl / ng), g = g0 + (int)(bgl % ng);
+    const int64_t bg = (int64_t)b * G + g;
+    const int H = G * R;
+    const int kv = clamp_kv(kv_lens[b], Nmax);
+    const int qs = q_start ? q_start[b] : kv - T;
+    const int beg = offsets[li], nent = offsets[li + 1] - beg;
+    if (nent == 0 && accumulate) return;
+    // This wave's keys: blk*S + 32*wave + 16*kt2 + col.
+    u32x4 kb[2][4], vb[2][4];
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+        const int key = blk * S + 32 * wave + 16 * kt2 + col;
+        const bool in = key < kv;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const u32x4 z4 = {0u, 0u, 0u, 0u};
+            kb[kt2][kc] = in ? ld16(k_cache + (bg * Nmax + key) * D + kc * 32 + kg * 8) : z4;
+            vb[kt2][kc] = in ? ld16(v_cache + (bg * Nmax + key) * D + kc * 32 + kg * 8) : z4;
+        }
+    }
+    f32x4 dka[2][8], dva[2][8];
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) dka[kt2][dt] = dva[kt2][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int et = 16 / R;             // entries per 16 columns
+    const int epb = (kBwdCols / 16) * et;  // entries per batch
+    for (int e0 = 0; e0 < nent; e0 += epb) {
+        __syncthreads();  // the previous batch's LDS reads are done
+        // Stage the batch: column c = 16*(c/16) + (entry (c%16)/R, head (c%16)%R).
+        for (int x = tid; x < kBwdCols * 16; x += 256) {
+            const int c = x >> 4, piece = x & 15;
+            const int e = e0 + (c >> 4) * et + (c & 15) / R;
+            const bool ok = (c & 15) < et * R && e < nent;
+            u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = {0u, 0u, 0u, 0u};
+            if (ok) {
+                const int ent = list[beg + e];
+                const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R +
+                                     (c & 15) % R;
+                qv = ld16(q + hrow * D + piece * 8);
+                dv4 = ld16(dout + hrow * D + piece * 8);
+                if (piece == 0) {
+                    s_lse2[c] = lse[hrow] * kLog2e;
+                    s_dl[c] = delta[hrow];
+                    s_pc[c] = qs + t0 + (ent >> 5);
+                }
+            } else if (piece == 0) {
+                s_lse2[c] = INFINITY;
+                s_dl[c] = 0.f;
+                s_pc[c] = -1;
+            }
+            *reinterpret_cast<u32x4 *>(q_s + c * kVRow + piece * 16) = qv;
+            *reinterpret_cast<u32x4 *>(do_s + c * kVRow + piece * 16) = dv4;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ct = 0; ct < kBwdCols / 16; ++ct) {
+            // S = q K^T and dP = dout V^T: lane holds key col of tile kt2 and
+            // columns 16*ct + 4*kg + r.
+            const unsigned char *qrow = q_s + (16 * ct + col) * kVRow + kg * 16;
+            const unsigned char *drow = do_s + (16 * ct + col) * kVRow + kg * 16;
+            f32x4 sacc[2], dpacc[2];
+#pragma unroll
+            for (int kt2 = 0; kt2 < 2; ++kt2) {
+                f32x4 sa = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    sa = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(qrow + kc * 64)),
+                                as_bf16x8(kb[kt2][kc]), sa);
+                    da = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(drow + kc * 64)),
+                                as_bf16x8(vb[kt2][kc]), da);
+                }
+                sacc[kt2] = sa;
+                dpacc[kt2] = da;
+            }
+            v4i16 pb[2], dsb[2];
+#pragma unroll
+            for (int kt2 = 0; kt2 < 2; ++kt2) {
+                const int key = blk * S + 32 * wave + 16 * kt2 + col;
+                float pv[4], dsv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int c = 16 * ct + 4 * kg + r;
+                    const float p = key > s_pc[c] ? 0.f
+                                                  : fast_exp2(fmaf(sacc[kt2][r], scale_log2, -s_lse2[c]));
+                    pv[r] = p;
+                    dsv[r] = p * (dpacc[kt2][r] - s_dl[c]);
+                }
+                pb[kt2] = pack_bf16x4(pv[0], pv[1], pv[2], pv[3]);
+                dsb[kt2] = pack_bf16x4(dsv[0], dsv[1], dsv[2], dsv[3]);
+            }
+            // dv^T += dout^T P and dk^T += q^T dS over these 16 columns:
+            // dout^T / q^T read transposed from LDS (column rows 4*kg + i).
+            const unsigned char *dt_base = do_s + (16 * ct + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
+            const unsigned char *qt_base = q_s + (16 * ct + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const v4i16 da = __builtin_bit_cast(v4i16, lds_read_tr16(dt_base + dt * 32));
+                const v4i16 qa = __builtin_bit_cast(v4i16, lds_read_tr16(qt_base + dt * 32));
+#pragma unroll
+                for (int kt2 = 0; kt2 < 2; ++kt2) {
+                    dva[kt2][dt] = mfma16k16(da, pb[kt2], dva[kt2][dt]);
+                    dka[kt2][dt] = mfma16k16(qa, dsb[kt2], dka[kt2][dt]);
+                }
+            }
+        }
+    }
+    // Lane holds d = dt*16 + 4*kg + r of key col of tile kt2.
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+        const int key = blk * S + 32 * wave + 16 * kt2 + col;
+        if (key >= Nmax) continue;
+        float *kp = dk + (bg * Nmax + key) * D + 4 * kg;
+        float *vp = dv + (bg * Nmax + key) * D + 4 * kg;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            f32x4 kvv = dka[kt2][dt] * tau, vvv = dva[kt2][dt];
+            if (accumulate) {
+                kvv += *reinterpret_cast<const f32x4 *>(kp + dt * 16);
+                vvv += *reinterpret_cast<const f32x4 *>(vp + dt * 16);
+            }
+            *reinterpret_cast<f32x4 *>(kp + dt * 16) = kvv;
+            *reinterpret_cast<f32x4 *>(vp + dt * 16) = vvv;
+        }
+    }
+}
+
+// dq of one (sequence, row of the pass, group): the kept slots' partials
+// summed in slot order; zero for a row outside the cache.
+__global__ __launch_bounds__(256) void bwd_dq_merge_kernel(
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, const float *__restrict__ part_dq, int T, int G, int R,
+    int Nmax, int K, int t0, int rows, int g0, int ng, float *__restrict__ dq) {
+    __shared__ int32_t s_sel[KMAX];
+    __shared__ int32_t s_kept[KMAX];
+    __shared__ int32_t s_n;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t unit = blockIdx.x;
+    const int g = g0 + (int)(unit % ng);
+    const int64_t btl = unit / ng;
+    const int b = (int)(btl / rows), tl = (int)(btl % rows);
+    const int t = t0 + tl;
+    if (t >= T) return;
+    const int p = pf_row_pos(kv_lens, q_start, b, t, T, Nmax);
+    if (tid < K) s_sel[tid] = p >= 0 ? sel[(((int64_t)b * T + t) * G + g) * K + tid] : -1;
+    __syncthreads();
+    if (tid < 64) {
+        const bool keep = lane < K && p >= 0 && slot_kept(s_sel, lane, p / S + 1);
+        const uint64_t m = __ballot(keep);
+        if (keep) s_kept[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+        if (lane == 0) s_n = __popcll(m);
+    }
+    __syncthreads();
+    const int n = s_n;
+    const int H = G * R;
+    for (int idx = tid; idx < R * (D / 4); idx += 256) {
+        const int r = idx / (D / 4), d0 = (idx % (D / 4)) * 4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < n; ++i)
+            acc += *reinterpret_cast<const f32x4 *>(part_dq + ((unit * K + s_kept[i]) * R + r) * D + d0);
+        *reinterpret_cast<f32x4 *>(dq + (((int64_t)b * T + t) * H + (int64_t)g * R + r) * D + d0) = acc;
+    }
+}
+
 // Decode: the new token of sequence b sits at position kv - 1. Group g's
 // kept blocks give 4*nblk 32-token chunks; workgroup (b, g, split) has eight
 // waves and takes chunks [8*split, 8*split + 8), one per wave, so every load
@@ -2108,6 +2470,64 @@ msa_status msa_sparse_attn_decode(const msa_config *cfg, int32_t B, int32_t Nmax
                                    reinterpret_cast<float *>(base + w.part_o_off),
                                    reinterpret_cast<float *>(base + w.part_ml_off),
                                    reinterpret_cast<hipStream_t>(stream));
+}
+
+msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                                    const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *kv_lens, const int32_t *q_start,
+                                    const int32_t *sel, const void *out, const float *lse,
+                                    const void *dout, float *dq, float *dk, float *dv,
+                                    void *workspace, size_t ws_bytes, void *stream) {
+    msa::clear_error();
+    msa_status s = msa::check_backward_args(cfg, B, T, Nmax, q, k_cache, v_cache, kv_lens,
+                                            q_start, sel, out, lse, dout, dq, dk, dv, workspace,
+                                            ws_bytes);
+    if (s != MSA_OK || B == 0 || T == 0) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int G = cfg->num_kv_groups, R = cfg->heads_per_group, K = cfg->topk;
+    const float sl2 = scale_log2_of(cfg);
+    const float tau = sl2 / kLog2e;
+    const bf16_t *qp = static_cast<const bf16_t *>(q);
+    const bf16_t *kp = static_cast<const bf16_t *>(k_cache);
+    const bf16_t *vp = static_cast<const bf16_t *>(v_cache);
+    const bf16_t *dop = static_cast<const bf16_t *>(dout);
+    const msa::PrefillWs w = msa::prefill_ws(cfg, B, T, Nmax, true);
+    char *base = static_cast<char *>(workspace);
+    int32_t *counts = reinterpret_cast<int32_t *>(base + w.counts_off);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + w.offsets_off);
+    int32_t *tile_first = reinterpret_cast<int32_t *>(base + w.tile_first_off);
+    int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.tile_map_off);
+    int32_t *rank = reinterpret_cast<int32_t *>(base + w.rank_off);
+    int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
+    float *part_dq = reinterpret_cast<float *>(base + w.part_o_off);
+    float *delta = reinterpret_cast<float *>(base + w.delta_off);
+    const int64_t nrows = (int64_t)B * T * G * R;
+    bwd_delta_kernel<<<(unsigned)((nrows * 16 + 255) / 256), 256, 0, st>>>(
+        static_cast<const bf16_t *>(out), dop, nrows, delta);
+    const unsigned slot_blocks = (unsigned)((w.nslots + 255) / 256);
+    for (int32_t g0 = 0; g0 < G; g0 += w.groups)
+      for (int32_t t0 = 0; t0 < T; t0 += w.rows) {
+        const int ng = w.groups;
+        fill_i32_kernel<<<(unsigned)((w.nlists + 255) / 256), 256, 0, st>>>(counts, w.nlists, 0);
+        pf_count_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
+                                                     w.rows, g0, ng, w.nb_max, counts, rank);
+        pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets,
+                                           tile_first, tile_map);
+        pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, rank, offsets, B, T, G, K, t0, w.rows,
+                                                       g0, ng, w.nb_max, list);
+        bwd_dq_kernel<<<(unsigned)w.max_tiles, 256, 0, st>>>(
+            qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, tile_first, tile_map, list,
+            w.nlists, T, G, R, Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2,
+            tau, part_dq);
+        bwd_dkdv_kernel<<<(unsigned)w.nlists, 256, 0, st>>>(
+            qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, list, T, G, R, Nmax, t0, g0,
+            ng, w.nb_max, sl2, tau, t0 > 0 ? 1 : 0, dk, dv);
+        bwd_dq_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), 256, 0, st>>>(
+            sel, kv_lens, q_start, part_dq, T, G, R, Nmax, K, t0, w.rows, g0, ng, dq);
+        s = launch_status("sparse backward kernels");
+        if (s != MSA_OK) return s;
+    }
+    return MSA_OK;
 }
 
 msa_status msa_index_topk_qblock(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,

@@ -83,7 +83,8 @@ typedef enum {
     MSA_WS_INDEX_TOPK = 0,
     MSA_WS_SPARSE_PREFILL = 1,
     MSA_WS_SPARSE_DECODE = 2,
-    MSA_WS_DECODE = 3
+    MSA_WS_DECODE = 3,
+    MSA_WS_SPARSE_BACKWARD = 4
 } msa_ws_kind;
 
 /* Layer shapes; the names follow the pages' sparse_attention_config. */
@@ -158,6 +159,28 @@ msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void
                       const void *v_cache, const int32_t *kv_lens, int32_t *sel,
                       float *sel_scores, void *out, float *lse, void *workspace, size_t ws_bytes,
                       void *stream);
+
+/*
+ * Backward of the sparse branch for fixed selections (the Tencent article's
+ * §五 presents the two-branch design as trainable; the discrete selection
+ * carries no gradient). With J, P and tau as in the forward definition,
+ * dout the gradient of out, dP_j = dout.v_j and dS_j = P_j (dP_j - sum_k
+ * P_k dP_k):
+ *   dq[b,i,h,:] = tau sum_j dS_j K[b,g,j,:]
+ *   dk[b,g,j,:] = tau sum over (row, head of g) attending j of dS_j q
+ *   dv[b,g,j,:] = sum over (row, head of g) attending j of P_j dout
+ * Inputs: the forward's q, caches, kv_lens, q_start, sel, out (bf16) and lse
+ * (fp32, natural log, as msa_sparse_attn_prefill writes them), dout [B,T,H,d]
+ * bf16. Outputs, fp32 and overwritten whole: dq [B,T,H,d] (zero for rows
+ * outside the cache), dk, dv [B,G,Nmax,d] (zero where no row attends).
+ * Workspace MSA_WS_SPARSE_BACKWARD.
+ */
+msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
+                                    const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *kv_lens, const int32_t *q_start,
+                                    const int32_t *sel, const void *out, const float *lse,
+                                    const void *dout, float *dq, float *dk, float *dv,
+                                    void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Query-block-shared selection, a variant of the index branch read from the

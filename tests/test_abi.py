@@ -33,6 +33,7 @@ def test_header_declares_the_three_entry_points():
     for n in ("msa_index_topk", "msa_index_pool", "msa_sparse_attn_prefill",
               "msa_sparse_attn_decode", "msa_decode", "msa_cache_append",
               "msa_index_topk_qblock", "msa_sparse_attn_prefill_qblock", "msa_qblock_slots",
+              "msa_sparse_attn_backward",
               "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_version"):
         assert n in names
 
@@ -214,6 +215,30 @@ def test_qblock_slots_and_validation(lib):
     assert lib.msa_sparse_attn_prefill_qblock(ctypes.byref(cfg(heads_per_group=17)), 1, 8, 128,
                                               FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
                                               None) == UNSUPPORTED
+
+
+def test_backward_validation(lib):
+    c = cfg()
+    need = lib.msa_workspace_size(ctypes.byref(c), 1, 300, 1024, 4)
+    assert need >= 300 * 32 * 4 and need % 256 == 0   # at least delta per (row, head)
+
+    def call(B=1, T=300, N=1024, ws=FAKE, nws=None, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, kv=FAKE, sel=FAKE, out=FAKE, lse=FAKE, do=FAKE,
+                 dq=FAKE, dk=FAKE, dv=FAKE)
+        a.update(kw)
+        return lib.msa_sparse_attn_backward(ctypes.byref(c), B, T, N, a["q"], a["k"], a["v"],
+                                            a["kv"], None, a["sel"], a["out"], a["lse"],
+                                            a["do"], a["dq"], a["dk"], a["dv"], ws,
+                                            need if nws is None else nws, None)
+
+    assert call(B=0) == OK and call(T=0) == OK
+    for name in ("q", "k", "v", "kv", "sel", "out", "lse", "do", "dq", "dk", "dv"):
+        assert call(**{name: None}) == INVALID, name
+    for name in ("q", "out", "do", "dq", "dk"):
+        assert call(**{name: FAKE_MIS}) == INVALID, name
+    assert call(lse=ctypes.c_void_p(0x100002)) == INVALID
+    assert call(nws=need - 1) == WORKSPACE and call(ws=None) == WORKSPACE
+    assert call(B=70000) == UNSUPPORTED
 
 
 def test_workspace_sizes_follow_shapes(lib):
