@@ -367,10 +367,30 @@ def run_prefill(torch, msa, w, steps=2, warmup=1):
         if s >= warmup:
             idx_ms.append(ev[0].elapsed_time(ev[1]))
             att_ms.append(ev[1].elapsed_time(ev[2]))
+    # Backward of the sparse branch for the same selections (msa_sparse_attn_backward),
+    # from the forward's out and lse and a seeded upstream gradient.
+    lse = torch.empty((w.B, w.T, w.H), dtype=torch.float32, device="cuda")
+    msa.sparse_attn_prefill(cfg, q, k, v, kv, sel, q_start=qs, out=out, lse=lse)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0x4D53410B)
+    dout = torch.randn((w.B, w.T, w.H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    ws_b = msa.workspace(cfg, w.B, w.T, w.Nmax, msa.WS_SPARSE_BACKWARD)
+    grads = msa.sparse_attn_backward(cfg, q, k, v, kv, sel, out, lse, dout, q_start=qs,
+                                     workspace=ws_b)
+    bwd_ms = []
+    for s in range(steps):
+        ev[0].record()
+        msa.sparse_attn_backward(cfg, q, k, v, kv, sel, out, lse, dout, q_start=qs,
+                                 dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws_b)
+        ev[1].record()
+        torch.cuda.synchronize()
+        bwd_ms.append(ev[0].elapsed_time(ev[1]))
+    del grads, ws_b, dout, lse
     L = w.T
     f_idx = 2.0 * 128 * w.G * L * (L + 1) / 2
     f_att, kv_bytes = sparse_work(torch, w, sel, w.q_start[0])
     ti, ta = min(idx_ms), min(att_ms)
+    tb = min(bwd_ms)
     res = dict(workload=w.name, index_ms=round(ti, 3), sparse_ms=round(ta, 3),
                index_tflops=round(f_idx / ti / 1e9, 2), sparse_tflops=round(f_att / ta / 1e9, 2),
                index_flops=f_idx, sparse_flops=f_att,
@@ -378,7 +398,14 @@ def run_prefill(torch, msa, w, steps=2, warmup=1):
                sparse_frac_bf16_peak=round(f_att / ta / 1e9 / BF16_PEAK_TFLOPS, 4),
                sparse_schedule_bytes=kv_bytes,
                sparse_schedule_gbs=round(kv_bytes / ta / 1e6, 1),
-               total_tflops=round((f_idx + f_att) / (ti + ta) / 1e9, 2))
+               total_tflops=round((f_idx + f_att) / (ti + ta) / 1e9, 2),
+               backward_ms=round(tb, 3),
+               backward_flops=2 * f_att,
+               backward_tflops=round(2 * f_att / tb / 1e9, 2),
+               backward_frac_bf16_peak=round(2 * f_att / tb / 1e9 / BF16_PEAK_TFLOPS, 4),
+               backward_note="msa_sparse_attn_backward; flops = dP, dq, dk, dv products "
+                             "(8*d per row, head and attended key, twice the forward's; the "
+                             "kernels also recompute S twice)")
     del q, qi, k, v, ki, sel, out, ws_i
     torch.cuda.empty_cache()
     return res

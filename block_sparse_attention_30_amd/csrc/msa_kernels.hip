@@ -1712,9 +1712,9 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
 //                     (as pf_attn_kernel): S^T = K q^T and dP^T = V dout^T,
 //                     dS, then dq^T = K^T dS^T (K read transposed from LDS);
 //                     tau * dq partial per (row, group, slot, head), fp32;
-//   bwd_dkdv_kernel   one workgroup per list, each wave owns 32 keys of the
-//                     block with their K and V rows in registers: for each
-//                     batch of 32 columns staged in LDS, S = q K^T, dP = dout
+//   bwd_dkdv_kernel   one workgroup per list, each of 8 waves owns 16 keys of
+//                     the block with their K and V rows in registers: for each
+//                     batch of 64 columns staged in LDS, S = q K^T, dP = dout
 //                     V^T, dS, then dv^T += dout^T P and dk^T += q^T dS (16x16x16
 //                     MFMA, the columns as the reduction index); written after
 //                     the list (added to the earlier passes' values);
@@ -1880,9 +1880,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
 }
 
-constexpr int kBwdCols = 32;  // columns (entry heads) per bwd_dkdv_kernel batch
+constexpr int kBwdCols = 64;  // columns (entry heads) per bwd_dkdv_kernel batch
 
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+constexpr int kBwdWaves = 8;  // bwd_dkdv_kernel: wave w owns keys 16w .. 16w+15 of the block
+constexpr int kBwdThreads = kBwdWaves * 64;
+
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
     const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const float *__restrict__ lse,
@@ -1906,11 +1909,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int qs = q_start ? q_start[b] : kv - T;
     const int beg = offsets[li], nent = offsets[li + 1] - beg;
     if (nent == 0 && accumulate) return;
-    // This wave's keys: blk*S + 32*wave + 16*kt2 + col.
-    u32x4 kb[2][4], vb[2][4];
+    // This wave's keys: blk*S + 16*wave + col.
+    constexpr int KT = 1;
+    u32x4 kb[KT][4], vb[KT][4];
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-        const int key = blk * S + 32 * wave + 16 * kt2 + col;
+    for (int kt2 = 0; kt2 < KT; ++kt2) {
+        const int key = blk * S + 16 * wave + 16 * kt2 + col;
         const bool in = key < kv;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
@@ -1919,50 +1923,79 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
             vb[kt2][kc] = in ? ld16(v_cache + (bg * Nmax + key) * D + kc * 32 + kg * 8) : z4;
         }
     }
-    f32x4 dka[2][8], dva[2][8];
+    f32x4 dka[KT][8], dva[KT][8];
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
+    for (int kt2 = 0; kt2 < KT; ++kt2)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) dka[kt2][dt] = dva[kt2][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int et = 16 / R;             // entries per 16 columns
     const int epb = (kBwdCols / 16) * et;  // entries per batch
-    for (int e0 = 0; e0 < nent; e0 += epb) {
-        __syncthreads();  // the previous batch's LDS reads are done
-        // Stage the batch: column c = 16*(c/16) + (entry (c%16)/R, head (c%16)%R).
-        for (int x = tid; x < kBwdCols * 16; x += 256) {
-            const int c = x >> 4, piece = x & 15;
+    // Column c of a batch: entry (c/16)*et + (c%16)/R of the batch, head
+    // (c%16)%R. Thread x of the staging loop owns pieces x, x + 256, ... of
+    // the batch's 16 x kBwdCols 16-byte pieces (column piece >> 4); the next
+    // batch's pieces are loaded into registers while this batch computes.
+    constexpr int kSP = kBwdCols * 16 / kBwdThreads;  // pieces per thread
+    u32x4 pq[kSP], pd[kSP];
+    float plse = INFINITY, pdl = 0.f;
+    int ppc = -1;
+    auto fetch = [&](int e0) {
+#pragma unroll
+        for (int i = 0; i < kSP; ++i) {
+            const int x = tid + kBwdThreads * i, c = x >> 4, piece = x & 15;
             const int e = e0 + (c >> 4) * et + (c & 15) / R;
             const bool ok = (c & 15) < et * R && e < nent;
-            u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = {0u, 0u, 0u, 0u};
+            const u32x4 z4 = {0u, 0u, 0u, 0u};
+            pq[i] = pd[i] = z4;
             if (ok) {
                 const int ent = list[beg + e];
                 const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R +
                                      (c & 15) % R;
-                qv = ld16(q + hrow * D + piece * 8);
-                dv4 = ld16(dout + hrow * D + piece * 8);
-                if (piece == 0) {
-                    s_lse2[c] = lse[hrow] * kLog2e;
-                    s_dl[c] = delta[hrow];
-                    s_pc[c] = qs + t0 + (ent >> 5);
-                }
-            } else if (piece == 0) {
-                s_lse2[c] = INFINITY;
-                s_dl[c] = 0.f;
-                s_pc[c] = -1;
+                pq[i] = ld16(q + hrow * D + piece * 8);
+                pd[i] = ld16(dout + hrow * D + piece * 8);
             }
-            *reinterpret_cast<u32x4 *>(q_s + c * kVRow + piece * 16) = qv;
-            *reinterpret_cast<u32x4 *>(do_s + c * kVRow + piece * 16) = dv4;
+        }
+        if (tid < kBwdCols) {  // per-column values
+            const int c = tid;
+            const int e = e0 + (c >> 4) * et + (c & 15) / R;
+            const bool ok = (c & 15) < et * R && e < nent;
+            plse = INFINITY;
+            pdl = 0.f;
+            ppc = -1;
+            if (ok) {
+                const int ent = list[beg + e];
+                const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R +
+                                     (c & 15) % R;
+                plse = lse[hrow] * kLog2e;
+                pdl = delta[hrow];
+                ppc = qs + t0 + (ent >> 5);
+            }
+        }
+    };
+    if (nent > 0) fetch(0);
+    for (int e0 = 0; e0 < nent; e0 += epb) {
+        __syncthreads();  // the previous batch's LDS reads are done
+#pragma unroll
+        for (int i = 0; i < kSP; ++i) {
+            const int x = tid + kBwdThreads * i, c = x >> 4, piece = x & 15;
+            *reinterpret_cast<u32x4 *>(q_s + c * kVRow + piece * 16) = pq[i];
+            *reinterpret_cast<u32x4 *>(do_s + c * kVRow + piece * 16) = pd[i];
+        }
+        if (tid < kBwdCols) {
+            s_lse2[tid] = plse;
+            s_dl[tid] = pdl;
+            s_pc[tid] = ppc;
         }
         __syncthreads();
+        if (e0 + epb < nent) fetch(e0 + epb);
 #pragma unroll
         for (int ct = 0; ct < kBwdCols / 16; ++ct) {
             // S = q K^T and dP = dout V^T: lane holds key col of tile kt2 and
             // columns 16*ct + 4*kg + r.
             const unsigned char *qrow = q_s + (16 * ct + col) * kVRow + kg * 16;
             const unsigned char *drow = do_s + (16 * ct + col) * kVRow + kg * 16;
-            f32x4 sacc[2], dpacc[2];
+            f32x4 sacc[KT], dpacc[KT];
 #pragma unroll
-            for (int kt2 = 0; kt2 < 2; ++kt2) {
+            for (int kt2 = 0; kt2 < KT; ++kt2) {
                 f32x4 sa = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc) {
@@ -1974,10 +2007,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
                 sacc[kt2] = sa;
                 dpacc[kt2] = da;
             }
-            v4i16 pb[2], dsb[2];
+            v4i16 pb[KT], dsb[KT];
 #pragma unroll
-            for (int kt2 = 0; kt2 < 2; ++kt2) {
-                const int key = blk * S + 32 * wave + 16 * kt2 + col;
+            for (int kt2 = 0; kt2 < KT; ++kt2) {
+                const int key = blk * S + 16 * wave + 16 * kt2 + col;
                 float pv[4], dsv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -1999,7 +2032,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
                 const v4i16 da = __builtin_bit_cast(v4i16, lds_read_tr16(dt_base + dt * 32));
                 const v4i16 qa = __builtin_bit_cast(v4i16, lds_read_tr16(qt_base + dt * 32));
 #pragma unroll
-                for (int kt2 = 0; kt2 < 2; ++kt2) {
+                for (int kt2 = 0; kt2 < KT; ++kt2) {
                     dva[kt2][dt] = mfma16k16(da, pb[kt2], dva[kt2][dt]);
                     dka[kt2][dt] = mfma16k16(qa, dsb[kt2], dka[kt2][dt]);
                 }
@@ -2008,8 +2041,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     }
     // Lane holds d = dt*16 + 4*kg + r of key col of tile kt2.
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-        const int key = blk * S + 32 * wave + 16 * kt2 + col;
+    for (int kt2 = 0; kt2 < KT; ++kt2) {
+        const int key = blk * S + 16 * wave + 16 * kt2 + col;
         if (key >= Nmax) continue;
         float *kp = dk + (bg * Nmax + key) * D + 4 * kg;
         float *vp = dv + (bg * Nmax + key) * D + 4 * kg;
@@ -2519,7 +2552,7 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
             qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, tile_first, tile_map, list,
             w.nlists, T, G, R, Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2,
             tau, part_dq);
-        bwd_dkdv_kernel<<<(unsigned)w.nlists, 256, 0, st>>>(
+        bwd_dkdv_kernel<<<(unsigned)w.nlists, kBwdThreads, 0, st>>>(
             qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, list, T, G, R, Nmax, t0, g0,
             ng, w.nb_max, sl2, tau, t0 > 0 ? 1 : 0, dk, dv);
         bwd_dq_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), 256, 0, st>>>(
