@@ -88,8 +88,8 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
     // of one group whose queries stay in the last-level cache were measured
     // slower: the list build is paid per pass.)
     // Per (row, group, slot, head): the forward keeps O / l in bf16 and (m, l);
-    // the backward keeps a dq partial in fp32.
-    const size_t part_row = (size_t)B * G * K * R * (backward ? kHeadDim * 4 : kHeadDim * 2 + 8);
+    // the backward keeps a dq partial in bf16.
+    const size_t part_row = (size_t)B * G * K * R * (backward ? kHeadDim * 2 : kHeadDim * 2 + 8);
     const int64_t max_units = (int64_t)1 << 24;
     int64_t rows = 1;
     while (rows * 2 <= T && (size_t)(rows * 2) * part_row <= kPfPartialBudget &&
@@ -113,7 +113,7 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
     w.rank_off = take((size_t)w.nslots * 4);
     w.list_off = take((size_t)w.nslots * 4);
     if (backward) {
-        w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 4);  // dq partials
+        w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 2);  // dq partials, bf16
         w.delta_off = take((size_t)B * T * G * R * 4);            // dout . out per (row, head)
     } else {
         w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 2);

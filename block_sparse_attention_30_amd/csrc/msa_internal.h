@@ -84,7 +84,7 @@ struct PrefillWs {
     size_t part_o_off, part_ml_off, delta_off, total;
 };
 // backward: the layout of msa_sparse_attn_backward (always KV-major; dq
-// partials in fp32 instead of the forward's partials; plus dout.out per
+// partials in bf16 instead of the forward's partials; plus dout.out per
 // (row, head)).
 PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                      bool backward = false);

@@ -1711,14 +1711,15 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
 //   bwd_dq_kernel     one workgroup per tile, waves own 16-column query tiles
 //                     (as pf_attn_kernel): S^T = K q^T and dP^T = V dout^T,
 //                     dS, then dq^T = K^T dS^T (K read transposed from LDS);
-//                     tau * dq partial per (row, group, slot, head), fp32;
+//                     tau * dq partial per (row, group, slot, head), bf16;
 //   bwd_dkdv_kernel   one workgroup per list, each of 8 waves owns 16 keys of
 //                     the block with their K and V rows in registers: for each
 //                     batch of 64 columns staged in LDS, S = q K^T, dP = dout
 //                     V^T, dS, then dv^T += dout^T P and dk^T += q^T dS (16x16x16
 //                     MFMA, the columns as the reduction index); written after
 //                     the list (added to the earlier passes' values);
-//   bwd_dq_merge_kernel  dq of a (row, group) = sum of its kept slots' partials.
+//   bwd_dq_merge_kernel  dq of a (row, group) = fp32 sum of its kept slots'
+//                     partials.
 // delta comes first from bwd_delta_kernel. No floating-point atomics: every
 // sum has one owner and a fixed order.
 typedef __attribute__((ext_vector_type(4))) short v4i16;
@@ -1762,7 +1763,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ tile_first,
     const int32_t *__restrict__ tile_map, const int32_t *__restrict__ list, int64_t nlists,
     int T, int G, int R, int Nmax, int K, int t0, int rows, int g0, int ng, int64_t nb_max,
-    int ch, float scale_log2, float tau, float *__restrict__ part_dq) {
+    int ch, float scale_log2, float tau, bf16_t *__restrict__ part_dq) {
     // K rows padded for the transposing reads, V rows for plain row reads.
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[S * kVRow];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[S * kKRow];
@@ -1871,11 +1872,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
         if (ok) {
             const int64_t slot = (((int64_t)b * rows + tl) * ng + gl) * K + (ent & 31);
-            float *op = part_dq + (slot * R + col % R) * D + 4 * kg;
+            bf16_t *op = part_dq + (slot * R + col % R) * D + 4 * kg;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt)
-                *reinterpret_cast<f32x4 *>(op + dt * 16) =
-                    f32x4{tau * dq[dt][0], tau * dq[dt][1], tau * dq[dt][2], tau * dq[dt][3]};
+                *reinterpret_cast<u32x2 *>(op + dt * 16) =
+                    u32x2{pack_bf16x2(tau * dq[dt][0], tau * dq[dt][1]),
+                          pack_bf16x2(tau * dq[dt][2], tau * dq[dt][3])};
         }
     }
 }
@@ -2063,7 +2065,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 // summed in slot order; zero for a row outside the cache.
 __global__ __launch_bounds__(256) void bwd_dq_merge_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
-    const int32_t *__restrict__ q_start, const float *__restrict__ part_dq, int T, int G, int R,
+    const int32_t *__restrict__ q_start, const bf16_t *__restrict__ part_dq, int T, int G, int R,
     int Nmax, int K, int t0, int rows, int g0, int ng, float *__restrict__ dq) {
     __shared__ int32_t s_sel[KMAX];
     __shared__ int32_t s_kept[KMAX];
@@ -2090,8 +2092,14 @@ __global__ __launch_bounds__(256) void bwd_dq_merge_kernel(
     for (int idx = tid; idx < R * (D / 4); idx += 256) {
         const int r = idx / (D / 4), d0 = (idx % (D / 4)) * 4;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < n; ++i)
-            acc += *reinterpret_cast<const f32x4 *>(part_dq + ((unit * K + s_kept[i]) * R + r) * D + d0);
+        for (int i = 0; i < n; ++i) {
+            const u32x2 pv =
+                *reinterpret_cast<const u32x2 *>(part_dq + ((unit * K + s_kept[i]) * R + r) * D + d0);
+            acc[0] += __uint_as_float(pv[0] << 16);
+            acc[1] += __uint_as_float(pv[0] & 0xFFFF0000u);
+            acc[2] += __uint_as_float(pv[1] << 16);
+            acc[3] += __uint_as_float(pv[1] & 0xFFFF0000u);
+        }
         *reinterpret_cast<f32x4 *>(dq + (((int64_t)b * T + t) * H + (int64_t)g * R + r) * D + d0) = acc;
     }
 }
@@ -2532,7 +2540,7 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
     int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.tile_map_off);
     int32_t *rank = reinterpret_cast<int32_t *>(base + w.rank_off);
     int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
-    float *part_dq = reinterpret_cast<float *>(base + w.part_o_off);
+    bf16_t *part_dq = reinterpret_cast<bf16_t *>(base + w.part_o_off);
     float *delta = reinterpret_cast<float *>(base + w.delta_off);
     const int64_t nrows = (int64_t)B * T * G * R;
     bwd_delta_kernel<<<(unsigned)((nrows * 16 + 255) / 256), 256, 0, st>>>(

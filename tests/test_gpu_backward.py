@@ -74,8 +74,8 @@ def test_backward_chunk_ragged_and_rows_outside(orc):
 
 
 def test_backward_two_passes(orc):
-    # 16 heads per group, 32 slots: 2048 rows per pass, so two passes
-    run(orc, 1, 2100, 2100, 8, 16, 32, [2100], [0], seed=820)
+    # 16 groups x 16 heads, 32 slots: 2048 rows per pass, so two passes
+    run(orc, 1, 2100, 2100, 16, 16, 32, [2100], [0], seed=820)
 
 
 def test_backward_short_context_odd_heads(orc):
