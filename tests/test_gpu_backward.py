@@ -2,9 +2,10 @@
 oracle's fp64 gradients of the sparse branch for fixed selections: dq on
 every row, dk and dv on every cached key, within the backward tolerances:
 relative L2 <= 1e-2 and max-abs <= 1e-2 * max|reference| (the kernels round P
-and dS to bf16 before their MFMA sums, 2^-9 relative each, and form dout.out
-from the bf16 forward output, which dS = P (dP - dout.out) can amplify where
-dP and dout.out nearly cancel)."""
+and dS to bf16 before their MFMA sums, 2^-9 relative each, round each slot's
+dq partial to bf16 before the fp32 sum over the row's slots, and form
+dout.out from the bf16 forward output, which dS = P (dP - dout.out) can
+amplify where dP and dout.out nearly cancel)."""
 import numpy as np
 import pytest
 import torch
