@@ -18,7 +18,11 @@ timed on a bounded sample of the same decode batch.
 
 The 1M-token prefill in 32768-row chunks with E4M3 index data is timed too
 (index TFLOP/s against the fp8 MFMA peak), and the decode step with E4M3
-index data on the same caches.
+index data on the same caches. The 131072-token prefill also times the
+sparse branch's backward (msa_sparse_attn_backward), and both prefills are
+timed again with query-block-shared selections (msa_index_topk_qblock +
+msa_sparse_attn_prefill_qblock). Prefill legs report the minimum and the
+median over five timed steps after one warm-up.
 
 Back-to-back steps re-read the same caches, so part of a working set that
 fits the 256 MB last-level cache may be served from it; each decode leg also
@@ -337,7 +341,7 @@ def sparse_work(torch, w, sel, q0):
     return f_att, nbytes
 
 
-def run_prefill(torch, msa, w, steps=2, warmup=1):
+def run_prefill(torch, msa, w, steps=5, warmup=1):
     import numpy as np
     from msa_synth import workloads as wl
     t0 = time.time()
@@ -391,6 +395,7 @@ def run_prefill(torch, msa, w, steps=2, warmup=1):
     f_att, kv_bytes = sparse_work(torch, w, sel, w.q_start[0])
     ti, ta = min(idx_ms), min(att_ms)
     tb = min(bwd_ms)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
     res = dict(workload=w.name, index_ms=round(ti, 3), sparse_ms=round(ta, 3),
                index_tflops=round(f_idx / ti / 1e9, 2), sparse_tflops=round(f_att / ta / 1e9, 2),
                index_flops=f_idx, sparse_flops=f_att,
@@ -399,6 +404,9 @@ def run_prefill(torch, msa, w, steps=2, warmup=1):
                sparse_schedule_bytes=kv_bytes,
                sparse_schedule_gbs=round(kv_bytes / ta / 1e6, 1),
                total_tflops=round((f_idx + f_att) / (ti + ta) / 1e9, 2),
+               timed_steps=steps, times_are="min over the timed steps",
+               index_ms_median=round(med(idx_ms), 3), sparse_ms_median=round(med(att_ms), 3),
+               backward_ms_median=round(med(bwd_ms), 3),
                backward_ms=round(tb, 3),
                backward_flops=2 * f_att,
                backward_tflops=round(2 * f_att / tb / 1e9, 2),
@@ -419,7 +427,7 @@ def qblock_rows(torch, sel_blk, q0, L):
     return sel_blk[:, slots]
 
 
-def run_prefill_qblock(torch, msa, w, steps=2, warmup=1):
+def run_prefill_qblock(torch, msa, w, steps=5, warmup=1):
     """The 131072-token prefill with query-block-shared selections (each
     128-row query block keeps one top-16): msa_index_topk_qblock +
     msa_sparse_attn_prefill_qblock, sparse flops counted exactly per row."""
@@ -451,8 +459,11 @@ def run_prefill_qblock(torch, msa, w, steps=2, warmup=1):
     f_idx = 2.0 * 128 * w.G * L * (L + 1) / 2
     f_att, _ = sparse_work(torch, w, qblock_rows(torch, sel, w.q_start[0], L), w.q_start[0])
     ti, ta = min(idx_ms), min(att_ms)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
     res = dict(workload=w.name + "_qblock", selection="query-block-shared (one top-16 per "
                "128-row query block)", index_ms=round(ti, 3), sparse_ms=round(ta, 3),
+               timed_steps=steps, times_are="min over the timed steps",
+               index_ms_median=round(med(idx_ms), 3), sparse_ms_median=round(med(att_ms), 3),
                index_tflops=round(f_idx / ti / 1e9, 2), sparse_tflops=round(f_att / ta / 1e9, 2),
                sparse_flops=f_att,
                index_frac_bf16_peak=round(f_idx / ti / 1e9 / BF16_PEAK_TFLOPS, 4),
