@@ -89,7 +89,13 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
     // slower: the list build is paid per pass.)
     // Per (row, group, slot, head): the forward keeps O / l in bf16 and (m, l);
     // the backward keeps a dq partial in bf16.
-    const size_t part_row = (size_t)B * G * K * R * (backward ? kHeadDim * 2 : kHeadDim * 2 + 8);
+    // (The backward's per-tile dk/dv partials, 2*S*d fp32 per tile of
+    // entries_per_tile entries, add 2*S*d*4 / entries_per_tile bytes per slot.)
+    const size_t part_row =
+        (size_t)B * G * K *
+        (backward ? (size_t)R * kHeadDim * 2 +
+                        (size_t)2 * kBlock * kHeadDim * 4 / prefill_entries_per_tile(R)
+                  : (size_t)R * (kHeadDim * 2 + 8));
     const int64_t max_units = (int64_t)1 << 24;
     int64_t rows = 1;
     while (rows * 2 <= T && (size_t)(rows * 2) * part_row <= kPfPartialBudget &&
@@ -114,6 +120,7 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
     w.list_off = take((size_t)w.nslots * 4);
     if (backward) {
         w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 2);  // dq partials, bf16
+        w.part_ml_off = take((size_t)w.max_tiles * 2 * kBlock * kHeadDim * 4);  // dk/dv per tile
         w.delta_off = take((size_t)B * T * G * R * 4);            // dout . out per (row, head)
     } else {
         w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 2);

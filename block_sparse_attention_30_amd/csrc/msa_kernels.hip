@@ -1712,12 +1712,14 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
 //                     (as pf_attn_kernel): S^T = K q^T and dP^T = V dout^T,
 //                     dS, then dq^T = K^T dS^T (K read transposed from LDS);
 //                     tau * dq partial per (row, group, slot, head), bf16;
-//   bwd_dkdv_kernel   one workgroup per list, each of 8 waves owns 16 keys of
+//   bwd_dkdv_kernel   one workgroup per tile, each of 8 waves owns 16 keys of
 //                     the block with their K and V rows in registers: for each
 //                     batch of 64 columns staged in LDS, S = q K^T, dP = dout
 //                     V^T, dS, then dv^T += dout^T P and dk^T += q^T dS (16x16x16
-//                     MFMA, the columns as the reduction index); written after
-//                     the list (added to the earlier passes' values);
+//                     MFMA, the columns as the reduction index); an fp32
+//                     partial per tile;
+//   bwd_dkdv_reduce_kernel  per list: dk, dv = sum of its tiles' partials in
+//                     tile order (added to the earlier passes' values);
 //   bwd_dq_merge_kernel  dq of a (row, group) = fp32 sum of its kept slots'
 //                     partials.
 // delta comes first from bwd_delta_kernel. No floating-point atomics: every
@@ -1885,6 +1887,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 constexpr int kBwdCols = 64;  // columns (entry heads) per bwd_dkdv_kernel batch
 
 constexpr int kBwdWaves = 8;  // bwd_dkdv_kernel: wave w owns keys 16w .. 16w+15 of the block
+constexpr int kBwdKt = 128 / 16 / kBwdWaves;  // 16-key tiles per wave
 constexpr int kBwdThreads = kBwdWaves * 64;
 
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
@@ -1892,16 +1895,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const float *__restrict__ lse,
     const bf16_t *__restrict__ dout, const float *__restrict__ delta,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ list, int T, int G, int R,
-    int Nmax, int t0, int g0, int ng, int64_t nb_max, float scale_log2, float tau, int accumulate,
-    float *__restrict__ dk, float *__restrict__ dv) {
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tile_first,
+    const int32_t *__restrict__ tile_map, const int32_t *__restrict__ list, int64_t nlists, int T,
+    int G, int R, int Nmax, int t0, int g0, int ng, int64_t nb_max, int ch, float scale_log2,
+    float *__restrict__ part_kv) {
     __shared__ __attribute__((aligned(16))) unsigned char q_s[kBwdCols * kVRow];
     __shared__ __attribute__((aligned(16))) unsigned char do_s[kBwdCols * kVRow];
     __shared__ float s_lse2[kBwdCols], s_dl[kBwdCols];
     __shared__ int s_pc[kBwdCols];
-    const int64_t li = blockIdx.x;
+    const int w = blockIdx.x;
+    if (w >= tile_first[nlists]) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, kg = lane >> 4;
+    const int li = tile_map[w];
+    const int beg = offsets[li] + (w - tile_first[li]) * ch;
+    const int nent = min(beg + ch, offsets[li + 1]) - beg;
     const int64_t bgl = li / nb_max;
     const int blk = (int)(li % nb_max);
     const int b = (int)(bgl / ng), g = g0 + (int)(bgl % ng);
@@ -1909,14 +1917,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const int H = G * R;
     const int kv = clamp_kv(kv_lens[b], Nmax);
     const int qs = q_start ? q_start[b] : kv - T;
-    const int beg = offsets[li], nent = offsets[li + 1] - beg;
-    if (nent == 0 && accumulate) return;
-    // This wave's keys: blk*S + 16*wave + col.
-    constexpr int KT = 1;
+    // This wave's keys: blk*S + 16*(KT*wave + kt2) + col.
+    constexpr int KT = kBwdKt;
     u32x4 kb[KT][4], vb[KT][4];
 #pragma unroll
     for (int kt2 = 0; kt2 < KT; ++kt2) {
-        const int key = blk * S + 16 * wave + 16 * kt2 + col;
+        const int key = blk * S + 16 * (KT * wave + kt2) + col;
         const bool in = key < kv;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
@@ -2012,7 +2018,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
             v4i16 pb[KT], dsb[KT];
 #pragma unroll
             for (int kt2 = 0; kt2 < KT; ++kt2) {
-                const int key = blk * S + 16 * wave + 16 * kt2 + col;
+                const int key = blk * S + 16 * (KT * wave + kt2) + col;
                 float pv[4], dsv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -2041,23 +2047,48 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
             }
         }
     }
-    // Lane holds d = dt*16 + 4*kg + r of key col of tile kt2.
+    // The tile's partial: [K rows 0..127][d] then [V rows][d], fp32 (tau not
+    // yet applied to dK). Lane holds d = dt*16 + 4*kg + r of key col.
+    float *pk = part_kv + (int64_t)w * 2 * S * D;
 #pragma unroll
     for (int kt2 = 0; kt2 < KT; ++kt2) {
-        const int key = blk * S + 16 * wave + 16 * kt2 + col;
-        if (key >= Nmax) continue;
-        float *kp = dk + (bg * Nmax + key) * D + 4 * kg;
-        float *vp = dv + (bg * Nmax + key) * D + 4 * kg;
+        const int kr = 16 * (KT * wave + kt2) + col;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            f32x4 kvv = dka[kt2][dt] * tau, vvv = dva[kt2][dt];
-            if (accumulate) {
-                kvv += *reinterpret_cast<const f32x4 *>(kp + dt * 16);
-                vvv += *reinterpret_cast<const f32x4 *>(vp + dt * 16);
-            }
-            *reinterpret_cast<f32x4 *>(kp + dt * 16) = kvv;
-            *reinterpret_cast<f32x4 *>(vp + dt * 16) = vvv;
+            *reinterpret_cast<f32x4 *>(pk + (int64_t)kr * D + dt * 16 + 4 * kg) = dka[kt2][dt];
+            *reinterpret_cast<f32x4 *>(pk + (int64_t)(S + kr) * D + dt * 16 + 4 * kg) = dva[kt2][dt];
         }
+    }
+}
+
+// dk, dv of one list's block: the sum of its tiles' partials in tile order
+// (tau applied to dk), added to the earlier passes' values when accumulate;
+// a list without entries contributes zero.
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(
+    const int32_t *__restrict__ tile_first, const float *__restrict__ part_kv, int G, int Nmax,
+    int g0, int ng, int64_t nb_max, float tau, int accumulate, float *__restrict__ dk,
+    float *__restrict__ dv) {
+    const int64_t li = blockIdx.x;
+    const int64_t bgl = li / nb_max;
+    const int blk = (int)(li % nb_max);
+    const int b = (int)(bgl / ng), g = g0 + (int)(bgl % ng);
+    const int64_t bg = (int64_t)b * G + g;
+    const int t_lo = tile_first[li], t_hi = tile_first[li + 1];
+    if (t_lo == t_hi && accumulate) return;
+    // Thread x owns four consecutive floats of one row of K or V, 2*S*D/4
+    // groups in all.
+    for (int x = threadIdx.x; x < 2 * S * D / 4; x += 256) {
+        const int row = x / (D / 4), d0 = (x % (D / 4)) * 4;  // row < S: K, else V
+        const int kr = row < S ? row : row - S;
+        const int key = blk * S + kr;
+        if (key >= Nmax) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int t = t_lo; t < t_hi; ++t)
+            acc += *reinterpret_cast<const f32x4 *>(part_kv + ((int64_t)t * 2 * S + row) * D + d0);
+        float *dst = (row < S ? dk : dv) + (bg * Nmax + key) * D + d0;
+        if (row < S) acc *= tau;
+        if (accumulate) acc += *reinterpret_cast<const f32x4 *>(dst);
+        *reinterpret_cast<f32x4 *>(dst) = acc;
     }
 }
 
@@ -2541,6 +2572,7 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
     int32_t *rank = reinterpret_cast<int32_t *>(base + w.rank_off);
     int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
     bf16_t *part_dq = reinterpret_cast<bf16_t *>(base + w.part_o_off);
+    float *part_kv = reinterpret_cast<float *>(base + w.part_ml_off);
     float *delta = reinterpret_cast<float *>(base + w.delta_off);
     const int64_t nrows = (int64_t)B * T * G * R;
     bwd_delta_kernel<<<(unsigned)((nrows * 16 + 255) / 256), 256, 0, st>>>(
@@ -2560,9 +2592,11 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
             qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, tile_first, tile_map, list,
             w.nlists, T, G, R, Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2,
             tau, part_dq);
-        bwd_dkdv_kernel<<<(unsigned)w.nlists, kBwdThreads, 0, st>>>(
-            qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, list, T, G, R, Nmax, t0, g0,
-            ng, w.nb_max, sl2, tau, t0 > 0 ? 1 : 0, dk, dv);
+        bwd_dkdv_kernel<<<(unsigned)w.max_tiles, kBwdThreads, 0, st>>>(
+            qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, tile_first, tile_map, list,
+            w.nlists, T, G, R, Nmax, t0, g0, ng, w.nb_max, w.entries_per_tile, sl2, part_kv);
+        bwd_dkdv_reduce_kernel<<<(unsigned)w.nlists, 256, 0, st>>>(
+            tile_first, part_kv, G, Nmax, g0, ng, w.nb_max, tau, t0 > 0 ? 1 : 0, dk, dv);
         bwd_dq_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), 256, 0, st>>>(
             sel, kv_lens, q_start, part_dq, T, G, R, Nmax, K, t0, w.rows, g0, ng, dq);
         s = launch_status("sparse backward kernels");
