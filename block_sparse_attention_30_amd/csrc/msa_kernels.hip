@@ -112,12 +112,13 @@ __device__ __forceinline__ int clamp_kv(int kv, int Nmax) { return kv < Nmax ? k
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 // Two fp32 values rounded to bf16 (nearest even) and packed, low half first:
 // one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, v);
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 // 2^x with the hardware instruction (no denormal rescaling; arguments here
@@ -1726,10 +1727,6 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
 // sum has one owner and a fixed order.
 typedef __attribute__((ext_vector_type(4))) short v4i16;
 
-__device__ __forceinline__ f32x4 mfma16k16(v4i16 a, v4i16 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ v4i16 pack_bf16x4(float a, float b, float c, float d) {
     const uint32_t lo = pack_bf16x2(a, b), hi = pack_bf16x2(c, d);
     return __builtin_bit_cast(v4i16, u32x2{lo, hi});
@@ -1776,6 +1773,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int li = tile_map[w];
     const int beg = offsets[li] + (w - tile_first[li]) * ch;
     const int nent = min(beg + ch, offsets[li + 1]) - beg;
+    if (nent <= 0) return;
     const int64_t bgl = li / nb_max;
     const int blk = (int)(li % nb_max);
     const int b = (int)(bgl / ng), gl = (int)(bgl % ng), g = g0 + gl;
@@ -1805,22 +1803,45 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     __syncthreads();
     const int et = 16 / R;
     const int tok_base = blk * S;
-    for (int e0 = wave * et; e0 < nent; e0 += kPfWaves * et) {
-        // Column col: entry e0 + col/R, head col % R.
-        const int e = e0 + col / R;
-        const bool ok = col < et * R && e < nent;
-        const int ent = ok ? list[beg + e] : 0;
-        const int tl = ent >> 5;
-        const int pcol = ok ? qs + t0 + tl : -1;
-        const int64_t hrow = ((int64_t)b * T + t0 + tl) * H + (int64_t)g * R + col % R;
-        bf16x8 qf[4], dof[4];
+    const int step = kPfWaves * et;
+    // Column col of a step: entry e0 + col/R, head col % R. A column past
+    // the tile's entries still loads a valid entry's data (the last one) and
+    // is masked by its position -1, so every load is unconditional and the
+    // loads of the next step stay in flight: its list entry one step
+    // earlier, its q, dout, lse and delta right after this step's score
+    // products have consumed q and dout.
+    auto col_ok = [&](int e0) { return col < et * R && e0 + col / R < nent; };
+    auto entry_at = [&](int e0) { return list[beg + min(e0 + col / R, nent - 1)]; };
+    bf16x8 qf[4], dof[4];
+    float lse_n, dl_n;
+    auto load_ops = [&](int ent) {
+        const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R + col % R;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-            qf[kc] = ok ? ld_bf16x8(q + hrow * D + kc * 32 + kg * 8) : zero_bf16x8();
-            dof[kc] = ok ? ld_bf16x8(dout + hrow * D + kc * 32 + kg * 8) : zero_bf16x8();
+            qf[kc] = ld_bf16x8(q + hrow * D + kc * 32 + kg * 8);
+            dof[kc] = ld_bf16x8(dout + hrow * D + kc * 32 + kg * 8);
         }
-        const float lse2 = ok ? lse[hrow] * kLog2e : INFINITY;
-        const float dl = ok ? delta[hrow] : 0.f;
+        lse_n = lse[hrow];
+        dl_n = delta[hrow];
+    };
+    int ent_c = entry_at(wave * et), ent_n = entry_at(wave * et + step);
+    load_ops(ent_c);
+    // A step's dq partial is stored in the next step, before that step's
+    // loads are issued, so the wait for those loads never waits for stores.
+    u32x2 pend[8];
+    bf16_t *pend_at = nullptr;
+    auto store_pending = [&]() {
+        if (pend_at) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<u32x2 *>(pend_at + dt * 16) = pend[dt];
+        }
+    };
+    for (int e0 = wave * et; e0 < nent; e0 += step) {
+        const int ent = ent_c;
+        const bool ok = col_ok(e0);
+        const int tl = ent >> 5;
+        const int pcol = ok ? qs + t0 + tl : -1;
+        const float lse2 = lse_n * kLog2e, dl = dl_n;
         // S^T and dP^T for the block's 128 keys; lane holds column col,
         // keys kt*16 + 4*kg + r.
         f32x4 sacc[8], dpacc[8];
@@ -1838,6 +1859,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             sacc[kt] = sa;
             dpacc[kt] = da;
         }
+        store_pending();
+        if (e0 + step < nent) {
+            ent_c = ent_n;
+            load_ops(ent_c);
+            ent_n = entry_at(e0 + 2 * step);
+        }
         // dS in the P^T operand order of the forward (keys 4*kg + i of the
         // lower and upper 16-key half of each 32-key chunk).
         bf16x8 dsa[4];
@@ -1848,7 +1875,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             for (int i = 0; i < 8; ++i) {
                 const int kt = 2 * c + (i >> 2), r = i & 3;
                 const int tok = tok_base + kt * 16 + 4 * kg + r;
-                const float p = tok > pcol ? 0.f : fast_exp2(fmaf(sacc[kt][r], scale_log2, -lse2));
+                const float ex = fast_exp2(fmaf(sacc[kt][r], scale_log2, -lse2));
+                const float p = tok > pcol ? 0.f : ex;
                 dsv[i] = p * (dpacc[kt][r] - dl);
             }
             const u32x4 pk = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
@@ -1872,19 +1900,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 dq[dt] = mfma16(as_bf16x8(kb4), dsa[c], dq[dt]);
             }
         }
-        if (ok) {
-            const int64_t slot = (((int64_t)b * rows + tl) * ng + gl) * K + (ent & 31);
-            bf16_t *op = part_dq + (slot * R + col % R) * D + 4 * kg;
+        const int64_t slot = (((int64_t)b * rows + tl) * ng + gl) * K + (ent & 31);
+        pend_at = ok ? part_dq + (slot * R + col % R) * D + 4 * kg : nullptr;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                *reinterpret_cast<u32x2 *>(op + dt * 16) =
-                    u32x2{pack_bf16x2(tau * dq[dt][0], tau * dq[dt][1]),
-                          pack_bf16x2(tau * dq[dt][2], tau * dq[dt][3])};
-        }
+        for (int dt = 0; dt < 8; ++dt)
+            pend[dt] = u32x2{pack_bf16x2(tau * dq[dt][0], tau * dq[dt][1]),
+                             pack_bf16x2(tau * dq[dt][2], tau * dq[dt][3])};
     }
+    store_pending();
 }
 
 constexpr int kBwdCols = 64;  // columns (entry heads) per bwd_dkdv_kernel batch
+// Columns of one tile: entries_per_tile * R, the same for every R.
+constexpr int kBwdTileCols = msa::kPfRounds * msa::kPfWaves * msa::kPfNq * 16;
 
 constexpr int kBwdWaves = 8;  // bwd_dkdv_kernel: wave w owns keys 16w .. 16w+15 of the block
 constexpr int kBwdKt = 128 / 16 / kBwdWaves;  // 16-key tiles per wave
@@ -1901,8 +1929,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     float *__restrict__ part_kv) {
     __shared__ __attribute__((aligned(16))) unsigned char q_s[kBwdCols * kVRow];
     __shared__ __attribute__((aligned(16))) unsigned char do_s[kBwdCols * kVRow];
-    __shared__ float s_lse2[kBwdCols], s_dl[kBwdCols];
-    __shared__ int s_pc[kBwdCols];
+    // Per tile column (entry e, head r at column e*R + r): lse in log2 units,
+    // delta and the query position; per entry: its row in the pass.
+    __shared__ __attribute__((aligned(16))) float s_lse2[kBwdTileCols], s_dl[kBwdTileCols];
+    __shared__ __attribute__((aligned(16))) int s_pc[kBwdTileCols], s_row[kBwdTileCols];
     const int w = blockIdx.x;
     if (w >= tile_first[nlists]) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1936,51 +1966,44 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     for (int kt2 = 0; kt2 < KT; ++kt2)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) dka[kt2][dt] = dva[kt2][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int et = 16 / R;             // entries per 16 columns
-    const int epb = (kBwdCols / 16) * et;  // entries per batch
-    // Column c of a batch: entry (c/16)*et + (c%16)/R of the batch, head
-    // (c%16)%R. Thread x of the staging loop owns pieces x, x + 256, ... of
-    // the batch's 16 x kBwdCols 16-byte pieces (column piece >> 4); the next
-    // batch's pieces are loaded into registers while this batch computes.
+    // Batches of kBwdCols tile columns: column c of the batch at cb is tile
+    // column cb + c, i.e. entry (cb + c) / R, head (cb + c) % R. Thread x of
+    // the staging loop owns pieces x, x + kBwdThreads, ... of the batch's
+    // 16 x kBwdCols 16-byte pieces (column piece >> 4); the next batch's
+    // pieces are loaded into registers while this batch computes.
     constexpr int kSP = kBwdCols * 16 / kBwdThreads;  // pieces per thread
+    const int ncol = nent * R;
+    for (int tc = tid; tc < kBwdTileCols; tc += kBwdThreads) {
+        float l2 = INFINITY, dl = 0.f;
+        int pc = -1;
+        if (tc < ncol) {
+            const int ent = list[beg + tc / R];
+            const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R + tc % R;
+            l2 = lse[hrow] * kLog2e;
+            dl = delta[hrow];
+            pc = qs + t0 + (ent >> 5);
+            if (tc % R == 0) s_row[tc / R] = ent >> 5;
+        }
+        s_lse2[tc] = l2;
+        s_dl[tc] = dl;
+        s_pc[tc] = pc;
+    }
+    __syncthreads();
     u32x4 pq[kSP], pd[kSP];
-    float plse = INFINITY, pdl = 0.f;
-    int ppc = -1;
-    auto fetch = [&](int e0) {
+    // A column past the tile's entries loads the last column's data (its
+    // position -1 zeroes its P and dS), so the loads are unconditional.
+    auto fetch = [&](int cb) {
 #pragma unroll
         for (int i = 0; i < kSP; ++i) {
             const int x = tid + kBwdThreads * i, c = x >> 4, piece = x & 15;
-            const int e = e0 + (c >> 4) * et + (c & 15) / R;
-            const bool ok = (c & 15) < et * R && e < nent;
-            const u32x4 z4 = {0u, 0u, 0u, 0u};
-            pq[i] = pd[i] = z4;
-            if (ok) {
-                const int ent = list[beg + e];
-                const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R +
-                                     (c & 15) % R;
-                pq[i] = ld16(q + hrow * D + piece * 8);
-                pd[i] = ld16(dout + hrow * D + piece * 8);
-            }
-        }
-        if (tid < kBwdCols) {  // per-column values
-            const int c = tid;
-            const int e = e0 + (c >> 4) * et + (c & 15) / R;
-            const bool ok = (c & 15) < et * R && e < nent;
-            plse = INFINITY;
-            pdl = 0.f;
-            ppc = -1;
-            if (ok) {
-                const int ent = list[beg + e];
-                const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R +
-                                     (c & 15) % R;
-                plse = lse[hrow] * kLog2e;
-                pdl = delta[hrow];
-                ppc = qs + t0 + (ent >> 5);
-            }
+            const int tc = min(cb + c, ncol - 1);
+            const int64_t hrow = ((int64_t)b * T + t0 + s_row[tc / R]) * H + (int64_t)g * R + tc % R;
+            pq[i] = ld16(q + hrow * D + piece * 8);
+            pd[i] = ld16(dout + hrow * D + piece * 8);
         }
     };
-    if (nent > 0) fetch(0);
-    for (int e0 = 0; e0 < nent; e0 += epb) {
+    if (ncol > 0) fetch(0);
+    for (int cb = 0; cb < ncol; cb += kBwdCols) {
         __syncthreads();  // the previous batch's LDS reads are done
 #pragma unroll
         for (int i = 0; i < kSP; ++i) {
@@ -1988,61 +2011,79 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
             *reinterpret_cast<u32x4 *>(q_s + c * kVRow + piece * 16) = pq[i];
             *reinterpret_cast<u32x4 *>(do_s + c * kVRow + piece * 16) = pd[i];
         }
-        if (tid < kBwdCols) {
-            s_lse2[tid] = plse;
-            s_dl[tid] = pdl;
-            s_pc[tid] = ppc;
-        }
         __syncthreads();
-        if (e0 + epb < nent) fetch(e0 + epb);
+        if (cb + kBwdCols < ncol) fetch(cb + kBwdCols);
+        const float *b_lse2 = s_lse2 + cb;
+        const float *b_dl = s_dl + cb;
+        const int *b_pc = s_pc + cb;
 #pragma unroll
-        for (int ct = 0; ct < kBwdCols / 16; ++ct) {
-            // S = q K^T and dP = dout V^T: lane holds key col of tile kt2 and
-            // columns 16*ct + 4*kg + r.
-            const unsigned char *qrow = q_s + (16 * ct + col) * kVRow + kg * 16;
-            const unsigned char *drow = do_s + (16 * ct + col) * kVRow + kg * 16;
-            f32x4 sacc[KT], dpacc[KT];
+        for (int cp = 0; cp < kBwdCols / 32; ++cp) {
+            // Two 16-column tiles per step: P and dS of both, then one
+            // 16x16x32 product per d tile whose k-slots 8*kg .. 8*kg+3 are
+            // columns 32*cp + 4*kg + 0..3 and slots 8*kg+4 .. 8*kg+7 columns
+            // 32*cp + 16 + 4*kg + 0..3 (the same order in both operands).
+            v4i16 pb[2][KT], dsb[2][KT];
 #pragma unroll
-            for (int kt2 = 0; kt2 < KT; ++kt2) {
-                f32x4 sa = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    sa = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(qrow + kc * 64)),
-                                as_bf16x8(kb[kt2][kc]), sa);
-                    da = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(drow + kc * 64)),
-                                as_bf16x8(vb[kt2][kc]), da);
-                }
-                sacc[kt2] = sa;
-                dpacc[kt2] = da;
-            }
-            v4i16 pb[KT], dsb[KT];
-#pragma unroll
-            for (int kt2 = 0; kt2 < KT; ++kt2) {
-                const int key = blk * S + 16 * (KT * wave + kt2) + col;
-                float pv[4], dsv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int c = 16 * ct + 4 * kg + r;
-                    const float p = key > s_pc[c] ? 0.f
-                                                  : fast_exp2(fmaf(sacc[kt2][r], scale_log2, -s_lse2[c]));
-                    pv[r] = p;
-                    dsv[r] = p * (dpacc[kt2][r] - s_dl[c]);
-                }
-                pb[kt2] = pack_bf16x4(pv[0], pv[1], pv[2], pv[3]);
-                dsb[kt2] = pack_bf16x4(dsv[0], dsv[1], dsv[2], dsv[3]);
-            }
-            // dv^T += dout^T P and dk^T += q^T dS over these 16 columns:
-            // dout^T / q^T read transposed from LDS (column rows 4*kg + i).
-            const unsigned char *dt_base = do_s + (16 * ct + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
-            const unsigned char *qt_base = q_s + (16 * ct + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const v4i16 da = __builtin_bit_cast(v4i16, lds_read_tr16(dt_base + dt * 32));
-                const v4i16 qa = __builtin_bit_cast(v4i16, lds_read_tr16(qt_base + dt * 32));
+            for (int hf = 0; hf < 2; ++hf) {
+                const int ct = 2 * cp + hf;
+                // S = q K^T and dP = dout V^T: lane holds key col of tile kt2
+                // and columns 16*ct + 4*kg + r.
+                const unsigned char *qrow = q_s + (16 * ct + col) * kVRow + kg * 16;
+                const unsigned char *drow = do_s + (16 * ct + col) * kVRow + kg * 16;
 #pragma unroll
                 for (int kt2 = 0; kt2 < KT; ++kt2) {
-                    dva[kt2][dt] = mfma16k16(da, pb[kt2], dva[kt2][dt]);
-                    dka[kt2][dt] = mfma16k16(qa, dsb[kt2], dka[kt2][dt]);
+                    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kc = 0; kc < 4; ++kc) {
+                        sa = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(qrow + kc * 64)),
+                                    as_bf16x8(kb[kt2][kc]), sa);
+                        da = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(drow + kc * 64)),
+                                    as_bf16x8(vb[kt2][kc]), da);
+                    }
+                    // Branch-free: exp of every element (a padding column has
+                    // lse = +inf, so 0), then the causal select.
+                    const int key = blk * S + 16 * (KT * wave + kt2) + col;
+                    const int c0 = 16 * ct + 4 * kg;
+                    const f32x4 l4 = *reinterpret_cast<const f32x4 *>(b_lse2 + c0);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(b_dl + c0);
+                    const u32x4 p4 = *reinterpret_cast<const u32x4 *>(b_pc + c0);
+                    float pv[4], dsv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float e = fast_exp2(fmaf(sa[r], scale_log2, -l4[r]));
+                        const float p = key > (int)p4[r] ? 0.f : e;
+                        pv[r] = p;
+                        dsv[r] = p * (da[r] - d4[r]);
+                    }
+                    pb[hf][kt2] = pack_bf16x4(pv[0], pv[1], pv[2], pv[3]);
+                    dsb[hf][kt2] = pack_bf16x4(dsv[0], dsv[1], dsv[2], dsv[3]);
+                }
+            }
+            // dv^T += dout^T P and dk^T += q^T dS over these 32 columns:
+            // dout^T / q^T read transposed from LDS (column rows 4*kg + i of
+            // each half).
+            const unsigned char *dt_lo = do_s + (32 * cp + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
+            const unsigned char *qt_lo = q_s + (32 * cp + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
+            bf16x8 pb8[KT], ds8[KT];
+#pragma unroll
+            for (int kt2 = 0; kt2 < KT; ++kt2) {
+                pb8[kt2] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(pb[0][kt2], pb[1][kt2], 0, 1, 2, 3, 4, 5, 6, 7));
+                ds8[kt2] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(dsb[0][kt2], dsb[1][kt2], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const u32x2 dlo = lds_read_tr16(dt_lo + dt * 32);
+                const u32x2 dhi = lds_read_tr16(dt_lo + 16 * kVRow + dt * 32);
+                const u32x2 qlo = lds_read_tr16(qt_lo + dt * 32);
+                const u32x2 qhi = lds_read_tr16(qt_lo + 16 * kVRow + dt * 32);
+                const u32x4 d4 = {dlo[0], dlo[1], dhi[0], dhi[1]};
+                const u32x4 q4 = {qlo[0], qlo[1], qhi[0], qhi[1]};
+#pragma unroll
+                for (int kt2 = 0; kt2 < KT; ++kt2) {
+                    dva[kt2][dt] = mfma16(as_bf16x8(d4), pb8[kt2], dva[kt2][dt]);
+                    dka[kt2][dt] = mfma16(as_bf16x8(q4), ds8[kt2], dka[kt2][dt]);
                 }
             }
         }
