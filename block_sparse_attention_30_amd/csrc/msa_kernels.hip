@@ -1709,16 +1709,14 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
 // lse*log2e) needs no second softmax pass, and with delta = dout . out per
 // (row, head), dS_j = P_j (dP_j - delta). Per pass of the forward's list
 // build (same lists, tiles and slots):
-//   bwd_dq_kernel     one workgroup per tile, waves own 16-column query tiles
-//                     (as pf_attn_kernel): S^T = K q^T and dP^T = V dout^T,
-//                     dS, then dq^T = K^T dS^T (K read transposed from LDS);
-//                     tau * dq partial per (row, group, slot, head), bf16;
-//   bwd_dkdv_kernel   one workgroup per tile, each of 8 waves owns 16 keys of
+//   bwd_tile_kernel   one workgroup per tile, each of 8 waves owns 16 keys of
 //                     the block with their K and V rows in registers: for each
-//                     batch of 64 columns staged in LDS, S = q K^T, dP = dout
-//                     V^T, dS, then dv^T += dout^T P and dk^T += q^T dS (16x16x16
-//                     MFMA, the columns as the reduction index); an fp32
-//                     partial per tile;
+//                     batch of 64 columns staged in LDS (two buffers), S = q
+//                     K^T, dP = dout V^T, dS, then dv^T += dout^T P and dk^T
+//                     += q^T dS (the columns as the reduction index); the
+//                     batch's dS goes to LDS, where dq^T = K^T dS^T over the
+//                     block's 128 keys gives tau * dq per (row, group, slot,
+//                     head), bf16; an fp32 [dk; dv] partial per tile;
 //   bwd_dkdv_reduce_kernel  per list: dk, dv = sum of its tiles' partials in
 //                     tile order (added to the earlier passes' values);
 //   bwd_dq_merge_kernel  dq of a (row, group) = fp32 sum of its kept slots'
@@ -1754,185 +1752,36 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16_t *__restrict
     if (r < nrows && c == 0) delta[r] = acc;
 }
 
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
-    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
-    const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
-    const int32_t *__restrict__ q_start, const float *__restrict__ lse,
-    const bf16_t *__restrict__ dout, const float *__restrict__ delta,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tile_first,
-    const int32_t *__restrict__ tile_map, const int32_t *__restrict__ list, int64_t nlists,
-    int T, int G, int R, int Nmax, int K, int t0, int rows, int g0, int ng, int64_t nb_max,
-    int ch, float scale_log2, float tau, bf16_t *__restrict__ part_dq) {
-    // K rows padded for the transposing reads, V rows for plain row reads.
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds[S * kVRow];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds[S * kKRow];
-    const int w = blockIdx.x;
-    if (w >= tile_first[nlists]) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, kg = lane >> 4;
-    const int li = tile_map[w];
-    const int beg = offsets[li] + (w - tile_first[li]) * ch;
-    const int nent = min(beg + ch, offsets[li + 1]) - beg;
-    if (nent <= 0) return;
-    const int64_t bgl = li / nb_max;
-    const int blk = (int)(li % nb_max);
-    const int b = (int)(bgl / ng), gl = (int)(bgl % ng), g = g0 + gl;
-    const int64_t bg = (int64_t)b * G + g;
-    const int H = G * R;
-    const int kv = clamp_kv(kv_lens[b], Nmax);
-    const int qs = q_start ? q_start[b] : kv - T;
-    {
-        const bf16_t *kb = k_cache + (bg * Nmax + (int64_t)blk * S) * D;
-        const bf16_t *vb = v_cache + (bg * Nmax + (int64_t)blk * S) * D;
-        const u32x4 z4 = {0u, 0u, 0u, 0u};
-        u32x4 kr[8], vr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
-            const bool in = blk * S + tk < kv;
-            kr[i] = in ? ld16(kb + (size_t)tk * D + c * 8) : z4;
-            vr[i] = in ? ld16(vb + (size_t)tk * D + c * 8) : z4;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int piece = tid + 256 * i, tk = piece >> 4, c = piece & 15;
-            *reinterpret_cast<u32x4 *>(k_lds + tk * kVRow + c * 16) = kr[i];
-            *reinterpret_cast<u32x4 *>(v_lds + tk * kKRow + c * 16) = vr[i];
-        }
-    }
-    __syncthreads();
-    const int et = 16 / R;
-    const int tok_base = blk * S;
-    const int step = kPfWaves * et;
-    // Column col of a step: entry e0 + col/R, head col % R. A column past
-    // the tile's entries still loads a valid entry's data (the last one) and
-    // is masked by its position -1, so every load is unconditional and the
-    // loads of the next step stay in flight: its list entry one step
-    // earlier, its q, dout, lse and delta right after this step's score
-    // products have consumed q and dout.
-    auto col_ok = [&](int e0) { return col < et * R && e0 + col / R < nent; };
-    auto entry_at = [&](int e0) { return list[beg + min(e0 + col / R, nent - 1)]; };
-    bf16x8 qf[4], dof[4];
-    float lse_n, dl_n;
-    auto load_ops = [&](int ent) {
-        const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R + col % R;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            qf[kc] = ld_bf16x8(q + hrow * D + kc * 32 + kg * 8);
-            dof[kc] = ld_bf16x8(dout + hrow * D + kc * 32 + kg * 8);
-        }
-        lse_n = lse[hrow];
-        dl_n = delta[hrow];
-    };
-    int ent_c = entry_at(wave * et), ent_n = entry_at(wave * et + step);
-    load_ops(ent_c);
-    // A step's dq partial is stored in the next step, before that step's
-    // loads are issued, so the wait for those loads never waits for stores.
-    u32x2 pend[8];
-    bf16_t *pend_at = nullptr;
-    auto store_pending = [&]() {
-        if (pend_at) {
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<u32x2 *>(pend_at + dt * 16) = pend[dt];
-        }
-    };
-    for (int e0 = wave * et; e0 < nent; e0 += step) {
-        const int ent = ent_c;
-        const bool ok = col_ok(e0);
-        const int tl = ent >> 5;
-        const int pcol = ok ? qs + t0 + tl : -1;
-        const float lse2 = lse_n * kLog2e, dl = dl_n;
-        // S^T and dP^T for the block's 128 keys; lane holds column col,
-        // keys kt*16 + 4*kg + r.
-        f32x4 sacc[8], dpacc[8];
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt) {
-            if (kt % 2 == 0) __builtin_amdgcn_sched_barrier(0);
-            const unsigned char *kp = k_lds + (kt * 16 + col) * kVRow + kg * 16;
-            const unsigned char *vp = v_lds + (kt * 16 + col) * kKRow + kg * 16;
-            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                sa = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + kc * 64)), qf[kc], sa);
-                da = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + kc * 64)), dof[kc], da);
-            }
-            sacc[kt] = sa;
-            dpacc[kt] = da;
-        }
-        store_pending();
-        if (e0 + step < nent) {
-            ent_c = ent_n;
-            load_ops(ent_c);
-            ent_n = entry_at(e0 + 2 * step);
-        }
-        // dS in the P^T operand order of the forward (keys 4*kg + i of the
-        // lower and upper 16-key half of each 32-key chunk).
-        bf16x8 dsa[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float dsv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int kt = 2 * c + (i >> 2), r = i & 3;
-                const int tok = tok_base + kt * 16 + 4 * kg + r;
-                const float ex = fast_exp2(fmaf(sacc[kt][r], scale_log2, -lse2));
-                const float p = tok > pcol ? 0.f : ex;
-                dsv[i] = p * (dpacc[kt][r] - dl);
-            }
-            const u32x4 pk = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
-                              pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
-            dsa[c] = as_bf16x8(pk);
-        }
-        // dq^T = K^T dS^T: K read transposed from LDS (the forward's V reads).
-        f32x4 dq[8];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const unsigned char *klo = k_lds + (c * 32 + 4 * kg + (col >> 2)) * kVRow + (col & 3) * 8;
-            const unsigned char *khi = klo + 16 * kVRow;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                if (dt % 4 == 0) __builtin_amdgcn_sched_barrier(0);
-                const u32x2 lo = lds_read_tr16(klo + dt * 32);
-                const u32x2 hi = lds_read_tr16(khi + dt * 32);
-                const u32x4 kb4 = {lo[0], lo[1], hi[0], hi[1]};
-                dq[dt] = mfma16(as_bf16x8(kb4), dsa[c], dq[dt]);
-            }
-        }
-        const int64_t slot = (((int64_t)b * rows + tl) * ng + gl) * K + (ent & 31);
-        pend_at = ok ? part_dq + (slot * R + col % R) * D + 4 * kg : nullptr;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-            pend[dt] = u32x2{pack_bf16x2(tau * dq[dt][0], tau * dq[dt][1]),
-                             pack_bf16x2(tau * dq[dt][2], tau * dq[dt][3])};
-    }
-    store_pending();
-}
-
-constexpr int kBwdCols = 64;  // columns (entry heads) per bwd_dkdv_kernel batch
+constexpr int kBwdCols = 64;  // columns (entry heads) per bwd_tile_kernel batch
 // Columns of one tile: entries_per_tile * R, the same for every R.
 constexpr int kBwdTileCols = msa::kPfRounds * msa::kPfWaves * msa::kPfNq * 16;
+constexpr int kDsRow = 160;  // bytes per staged dS key row: 64 bf16 columns + 32 pad
 
-constexpr int kBwdWaves = 8;  // bwd_dkdv_kernel: wave w owns keys 16w .. 16w+15 of the block
+constexpr int kBwdWaves = 8;  // bwd_tile_kernel: wave w owns keys 16w .. 16w+15 of the block
 constexpr int kBwdKt = 128 / 16 / kBwdWaves;  // 16-key tiles per wave
 constexpr int kBwdThreads = kBwdWaves * 64;
 
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_tile_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
     const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const float *__restrict__ lse,
     const bf16_t *__restrict__ dout, const float *__restrict__ delta,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ tile_first,
     const int32_t *__restrict__ tile_map, const int32_t *__restrict__ list, int64_t nlists, int T,
-    int G, int R, int Nmax, int t0, int g0, int ng, int64_t nb_max, int ch, float scale_log2,
-    float *__restrict__ part_kv) {
-    __shared__ __attribute__((aligned(16))) unsigned char q_s[kBwdCols * kVRow];
-    __shared__ __attribute__((aligned(16))) unsigned char do_s[kBwdCols * kVRow];
+    int G, int R, int Nmax, int K, int t0, int rows, int g0, int ng, int64_t nb_max, int ch,
+    float scale_log2, float tau, bf16_t *__restrict__ part_dq, float *__restrict__ part_kv) {
+    // Two buffers of a batch's q and dout rows: batch i+1 is staged into one
+    // while batch i is read from the other, one barrier per batch.
+    __shared__ __attribute__((aligned(16))) unsigned char q_buf[2][kBwdCols * kVRow];
+    __shared__ __attribute__((aligned(16))) unsigned char do_buf[2][kBwdCols * kVRow];
     // Per tile column (entry e, head r at column e*R + r): lse in log2 units,
-    // delta and the query position; per entry: its row in the pass.
+    // delta, the query position and the dq partial's slot (-1: none).
     __shared__ __attribute__((aligned(16))) float s_lse2[kBwdTileCols], s_dl[kBwdTileCols];
-    __shared__ __attribute__((aligned(16))) int s_pc[kBwdTileCols], s_row[kBwdTileCols];
+    __shared__ __attribute__((aligned(16))) int s_pc[kBwdTileCols], s_slot[kBwdTileCols];
+    // The block's K rows (read transposed for dq) and a batch's dS, one row of
+    // 64 bf16 columns per key.
+    __shared__ __attribute__((aligned(16))) unsigned char k_s[S * kVRow];
+    __shared__ __attribute__((aligned(16))) unsigned char ds_s[S * kDsRow];
     const int w = blockIdx.x;
     if (w >= tile_first[nlists]) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1942,7 +1791,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const int nent = min(beg + ch, offsets[li + 1]) - beg;
     const int64_t bgl = li / nb_max;
     const int blk = (int)(li % nb_max);
-    const int b = (int)(bgl / ng), g = g0 + (int)(bgl % ng);
+    const int b = (int)(bgl / ng), gl = (int)(bgl % ng), g = g0 + gl;
     const int64_t bg = (int64_t)b * G + g;
     const int H = G * R;
     const int kv = clamp_kv(kv_lens[b], Nmax);
@@ -1961,6 +1810,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
             vb[kt2][kc] = in ? ld16(v_cache + (bg * Nmax + key) * D + kc * 32 + kg * 8) : z4;
         }
     }
+#pragma unroll
+    for (int kt2 = 0; kt2 < KT; ++kt2)
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+            *reinterpret_cast<u32x4 *>(k_s + (16 * (KT * wave + kt2) + col) * kVRow + kc * 64 + kg * 16) =
+                kb[kt2][kc];
     f32x4 dka[KT][8], dva[KT][8];
 #pragma unroll
     for (int kt2 = 0; kt2 < KT; ++kt2)
@@ -1975,21 +1830,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const int ncol = nent * R;
     for (int tc = tid; tc < kBwdTileCols; tc += kBwdThreads) {
         float l2 = INFINITY, dl = 0.f;
-        int pc = -1;
+        int pc = -1, slot = -1;
         if (tc < ncol) {
             const int ent = list[beg + tc / R];
             const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R + tc % R;
             l2 = lse[hrow] * kLog2e;
             dl = delta[hrow];
             pc = qs + t0 + (ent >> 5);
-            if (tc % R == 0) s_row[tc / R] = ent >> 5;
+            slot = (int)((((int64_t)b * rows + (ent >> 5)) * ng + gl) * K + (ent & 31));
         }
         s_lse2[tc] = l2;
         s_dl[tc] = dl;
         s_pc[tc] = pc;
+        s_slot[tc] = slot;
     }
     __syncthreads();
     u32x4 pq[kSP], pd[kSP];
+    const int qs_row0 = -qs;  // row in the call = position - q_start
     // A column past the tile's entries loads the last column's data (its
     // position -1 zeroes its P and dS), so the loads are unconditional.
     auto fetch = [&](int cb) {
@@ -1997,22 +1854,34 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
         for (int i = 0; i < kSP; ++i) {
             const int x = tid + kBwdThreads * i, c = x >> 4, piece = x & 15;
             const int tc = min(cb + c, ncol - 1);
-            const int64_t hrow = ((int64_t)b * T + t0 + s_row[tc / R]) * H + (int64_t)g * R + tc % R;
+            const int64_t hrow = ((int64_t)b * T + qs_row0 + s_pc[tc]) * H + (int64_t)g * R + tc % R;
             pq[i] = ld16(q + hrow * D + piece * 8);
             pd[i] = ld16(dout + hrow * D + piece * 8);
         }
     };
-    if (ncol > 0) fetch(0);
-    for (int cb = 0; cb < ncol; cb += kBwdCols) {
-        __syncthreads();  // the previous batch's LDS reads are done
+    auto stage = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < kSP; ++i) {
             const int x = tid + kBwdThreads * i, c = x >> 4, piece = x & 15;
-            *reinterpret_cast<u32x4 *>(q_s + c * kVRow + piece * 16) = pq[i];
-            *reinterpret_cast<u32x4 *>(do_s + c * kVRow + piece * 16) = pd[i];
+            *reinterpret_cast<u32x4 *>(q_buf[buf] + c * kVRow + piece * 16) = pq[i];
+            *reinterpret_cast<u32x4 *>(do_buf[buf] + c * kVRow + piece * 16) = pd[i];
         }
-        __syncthreads();
-        if (cb + kBwdCols < ncol) fetch(cb + kBwdCols);
+    };
+    if (ncol > 0) {
+        fetch(0);
+        stage(0);
+        if (kBwdCols < ncol) fetch(kBwdCols);
+    }
+    __syncthreads();
+    for (int cb = 0, cur = 0; cb < ncol; cb += kBwdCols, cur ^= 1) {
+        // The other buffer was last read in the previous batch, which ended
+        // with a barrier.
+        if (cb + kBwdCols < ncol) {
+            stage(cur ^ 1);
+            if (cb + 2 * kBwdCols < ncol) fetch(cb + 2 * kBwdCols);
+        }
+        const unsigned char *q_s = q_buf[cur];
+        const unsigned char *do_s = do_buf[cur];
         const float *b_lse2 = s_lse2 + cb;
         const float *b_dl = s_dl + cb;
         const int *b_pc = s_pc + cb;
@@ -2057,6 +1926,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
                     }
                     pb[hf][kt2] = pack_bf16x4(pv[0], pv[1], pv[2], pv[3]);
                     dsb[hf][kt2] = pack_bf16x4(dsv[0], dsv[1], dsv[2], dsv[3]);
+                    *reinterpret_cast<v4i16 *>(ds_s + (16 * (KT * wave + kt2) + col) * kDsRow +
+                                               (16 * ct + 4 * kg) * 2) = dsb[hf][kt2];
                 }
             }
             // dv^T += dout^T P and dk^T += q^T dS over these 32 columns:
@@ -2087,6 +1958,52 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
                 }
             }
         }
+        __syncthreads();  // the batch's dS is in LDS
+        // dq^T = K^T dS^T for the batch, tau applied: wave w owns column
+        // tiles 2*(w&1) + j and d tiles 2*(w>>1) + i; K^T and dS^T are read
+        // transposed from LDS, keys 4*kg + 0..3 and 16 + 4*kg + 0..3 of each
+        // 32-key chunk in both operands.
+        {
+            f32x4 dqa[2][2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) dqa[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cc = 0; cc < S / 32; ++cc) {
+                const int krow = cc * 32 + 4 * kg + (col >> 2);
+                bf16x8 bq[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const unsigned char *p = ds_s + krow * kDsRow + (2 * (wave & 1) + j) * 32 + (col & 3) * 8;
+                    const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 16 * kDsRow);
+                    bq[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const unsigned char *p = k_s + krow * kVRow + (2 * (wave >> 1) + i) * 32 + (col & 3) * 8;
+                    const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 16 * kVRow);
+                    const bf16x8 ka = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) dqa[i][j] = mfma16(ka, bq[j], dqa[i][j]);
+                }
+            }
+            // Lane holds column 16*ct + col, d = 16*dt + 4*kg + r.
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int tc = cb + 16 * (2 * (wave & 1) + j) + col;
+                const int slot = s_slot[tc];
+                if (slot >= 0) {
+                    bf16_t *op = part_dq + ((int64_t)slot * R + tc % R) * D + 4 * kg;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        *reinterpret_cast<u32x2 *>(op + (2 * (wave >> 1) + i) * 16) =
+                            u32x2{pack_bf16x2(tau * dqa[i][j][0], tau * dqa[i][j][1]),
+                                  pack_bf16x2(tau * dqa[i][j][2], tau * dqa[i][j][3])};
+                }
+            }
+        }
+        __syncthreads();  // this batch's buffers are read, the next one is staged
     }
     // The tile's partial: [K rows 0..127][d] then [V rows][d], fp32 (tau not
     // yet applied to dK). Lane holds d = dt*16 + 4*kg + r of key col.
@@ -2629,13 +2546,10 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
                                            tile_first, tile_map);
         pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, rank, offsets, B, T, G, K, t0, w.rows,
                                                        g0, ng, w.nb_max, list);
-        bwd_dq_kernel<<<(unsigned)w.max_tiles, 256, 0, st>>>(
+        bwd_tile_kernel<<<(unsigned)w.max_tiles, kBwdThreads, 0, st>>>(
             qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, tile_first, tile_map, list,
             w.nlists, T, G, R, Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2,
-            tau, part_dq);
-        bwd_dkdv_kernel<<<(unsigned)w.max_tiles, kBwdThreads, 0, st>>>(
-            qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, tile_first, tile_map, list,
-            w.nlists, T, G, R, Nmax, t0, g0, ng, w.nb_max, w.entries_per_tile, sl2, part_kv);
+            tau, part_dq, part_kv);
         bwd_dkdv_reduce_kernel<<<(unsigned)w.nlists, 256, 0, st>>>(
             tile_first, part_kv, G, Nmax, g0, ng, w.nb_max, tau, t0 > 0 ? 1 : 0, dk, dv);
         bwd_dq_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), 256, 0, st>>>(
