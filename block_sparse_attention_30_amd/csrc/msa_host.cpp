@@ -126,6 +126,7 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
         w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 2);
         w.part_ml_off = take((size_t)w.nslots * R * 8);
     }
+    w.trash_off = take(kPfTrashBytes);
     w.total = off;
     return w;
 }

@@ -81,8 +81,13 @@ struct PrefillWs {
     int32_t entries_per_tile;
     int64_t nb_max, nlists, nslots, max_tiles;
     size_t counts_off, offsets_off, tile_first_off, tile_map_off, rank_off, list_off;
-    size_t part_o_off, part_ml_off, delta_off, total;
+    size_t part_o_off, part_ml_off, delta_off;
+    // Target of the stores of columns that hold no entry (their values are
+    // discarded), so the attention kernels store unconditionally.
+    size_t trash_off;
+    size_t total;
 };
+constexpr size_t kPfTrashBytes = 8192;  // >= one entry's R*d bf16 values and R (m, l) pairs
 // backward: the layout of msa_sparse_attn_backward (always KV-major; dq
 // partials in bf16 instead of the forward's partials; plus dout.out per
 // (row, head)).

@@ -1078,6 +1078,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
 constexpr int kKRow = 272;  // staged K row bytes: 256 + 16 pad
 constexpr int kPfWaves = msa::kPfWaves;
 constexpr int kPfNq = msa::kPfNq;
+// Most entries of one tile (R = 1): entries_per_tile * R is the same for all R.
+constexpr int kPfTileEntriesMax = msa::kPfRounds * msa::kPfWaves * msa::kPfNq * 16;
 
 __device__ __forceinline__ bool slot_kept(const int32_t *sel_row, int k, int n_valid) {
     const int blk = sel_row[k];
@@ -1219,9 +1221,10 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
     const int32_t *__restrict__ tile_first, const int32_t *__restrict__ tile_map,
     const int32_t *__restrict__ list, int64_t nlists, int T, int G, int R, int Nmax, int K,
     int t0, int rows, int g0, int ng, int64_t nb_max, int ch, float scale_log2,
-    bf16_t *__restrict__ part_o, float2 *__restrict__ part_ml) {
+    bf16_t *__restrict__ part_o, float2 *__restrict__ part_ml, unsigned char *__restrict__ trash) {
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[S * kKRow];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[S * kVRow];
+    __shared__ int s_ent[kPfTileEntriesMax];  // the tile's list entries
     const int w = blockIdx.x;
     if (w >= tile_first[nlists]) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1229,6 +1232,7 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
     const int li = tile_map[w];
     const int beg = offsets[li] + (w - tile_first[li]) * ch;
     const int nent = min(beg + ch, offsets[li + 1]) - beg;
+    if (nent <= 0) return;
     const int64_t bgl = li / nb_max;  // (sequence, group of the pass)
     const int blk = (int)(li % nb_max);
     const int b = (int)(bgl / ng), gl = (int)(bgl % ng), g = g0 + gl;
@@ -1255,6 +1259,7 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
             *reinterpret_cast<u32x4 *>(k_lds + tk * kKRow + c * 16) = kr[i];
             *reinterpret_cast<u32x4 *>(v_lds + tk * kVRow + c * 16) = vr[i];
         }
+        for (int i = tid; i < nent; i += 256) s_ent[i] = list[beg + i];
     }
     __syncthreads();
     const int et = 16 / R;  // entries per 16-column query tile
@@ -1262,20 +1267,24 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
     // Column `col` of query tile nq in a round: entry e0 + nq*et + col/R, head
     // col%R. Two register sets alternate between rounds: right after a round's
     // score MFMAs its set is reloaded with the queries of the round after
-    // next, so those loads have about a round and a half to land.
+    // next, so those loads have about a round and a half to land. The entries
+    // come from LDS and a column past the tile's entries loads the last
+    // entry's queries (its results are never stored; columns do not mix), so
+    // the query loads are unconditional and never wait for the list.
     auto load_round = [&](int e0, int (&ent)[kPfNq], int (&pcol)[kPfNq],
                           bf16x8 (&qf)[kPfNq][4]) {
 #pragma unroll
         for (int nq = 0; nq < kPfNq; ++nq) {
             const int e = e0 + nq * et + col / R;
             const bool ok = col < et * R && e < nent;
-            ent[nq] = ok ? list[beg + e] : -1;
-            const int tl = ok ? (ent[nq] >> 5) : 0;
+            const int raw = s_ent[min(e, nent - 1)];
+            ent[nq] = ok ? raw : -1;
+            const int tl = raw >> 5;
             pcol[nq] = ok ? qs + t0 + tl : -1;
             const bf16_t *qp =
                 q + (((int64_t)b * T + t0 + tl) * H + (int64_t)g * R + col % R) * D + kg * 8;
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) qf[nq][kc] = ok ? ld_bf16x8(qp + kc * 32) : zero_bf16x8();
+            for (int kc = 0; kc < 4; ++kc) qf[nq][kc] = ld_bf16x8(qp + kc * 32);
         }
     };
     const int round_step = kPfWaves * kPfNq * et;
@@ -1307,7 +1316,10 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
             cent[nq] = ent[nq];
             cpcol[nq] = pcol[nq];
         }
-        if (e0 + 2 * round_step < nent) load_round(e0 + 2 * round_step, ent, pcol, qf);
+        // Unconditional (a step past the tile loads valid rows), so the wait
+        // for a round's queries counts the same loads and stores on every
+        // path and need not wait for this round's stores.
+        load_round(e0 + 2 * round_step, ent, pcol, qf);
         // Softmax over the block's 128 keys in one pass (the block is whole).
         // Only a block that reaches past some column's position is masked.
         bool diag = false;
@@ -1394,11 +1406,18 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
                 // Even kg: (own E, partner's E); odd kg: (partner's O, own O).
                 w4[j] = u32x4{r0[0], r1[0], r0[1], r1[1]};
             }
-            if (cent[nq] < 0) continue;
-            const int64_t slot = (((int64_t)b * rows + (cent[nq] >> 5)) * ng + gl) * K + (cent[nq] & 31);
-            if (kg == 0) part_ml[slot * R + col % R] = make_float2(mrow[nq], lrow[nq]);
-            unsigned char *op = reinterpret_cast<unsigned char *>(part_o + (slot * R + col % R) * D) +
-                                16 * (2 * (kg & 1) + (kg >> 1));
+            // A column without an entry (and the m, l copies of lanes kg > 0)
+            // store into the trash area instead of branching around.
+            const bool has = cent[nq] >= 0;
+            const int64_t slot =
+                (((int64_t)b * rows + (cent[nq] >> 5)) * ng + gl) * K + (cent[nq] & 31);
+            float2 *mlp = has && kg == 0 ? part_ml + slot * R + col % R
+                                         : reinterpret_cast<float2 *>(trash + 4096) + col;
+            *mlp = make_float2(mrow[nq], lrow[nq]);
+            unsigned char *op =
+                (has ? reinterpret_cast<unsigned char *>(part_o + (slot * R + col % R) * D)
+                     : trash + (col % R) * D * 2) +
+                16 * (2 * (kg & 1) + (kg >> 1));
 #pragma unroll
             for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4 *>(op + 64 * j) = w4[j];
         }
@@ -1406,8 +1425,8 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
     int entA[kPfNq], pcolA[kPfNq], entB[kPfNq], pcolB[kPfNq];
     bf16x8 qA[kPfNq][4], qB[kPfNq][4];
     int e0 = wave * kPfNq * et;
-    if (e0 < nent) load_round(e0, entA, pcolA, qA);
-    if (e0 + round_step < nent) load_round(e0 + round_step, entB, pcolB, qB);
+    load_round(e0, entA, pcolA, qA);
+    load_round(e0 + round_step, entB, pcolB, qB);
     while (e0 < nent) {
         do_round(e0, entA, pcolA, qA);
         e0 += round_step;
@@ -2451,7 +2470,8 @@ msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, 
                                                        g0, ng, w.nb_max, list);
         pf_attn_kernel<<<(unsigned)w.max_tiles, 256, 0, st>>>(
             qp, kp, vp, kv_lens, q_start, offsets, tile_first, tile_map, list, w.nlists, T, G, R,
-            Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2, part_o, part_ml);
+            Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2, part_o, part_ml,
+            reinterpret_cast<unsigned char *>(base + w.trash_off));
         pf_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), 256, 0, st>>>(
             sel, kv_lens, q_start, part_o, part_ml, T, G, R, Nmax, K, t0, w.rows, g0, ng, op, lse);
         s = launch_status("sparse prefill kernels");
