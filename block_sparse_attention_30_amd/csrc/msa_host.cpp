@@ -91,11 +91,15 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
     // the backward keeps a dq partial in bf16.
     // (The backward's per-tile dk/dv partials, 2*S*d fp32 per tile of
     // entries_per_tile entries, add 2*S*d*4 / entries_per_tile bytes per slot.)
+    // The list build adds a row bitmap and its word prefixes per list: 8 bytes
+    // per 32 rows of each of the B*G*nb lists.
+    const int64_t nb = ((int64_t)Nmax + kBlock - 1) / kBlock;
     const size_t part_row =
         (size_t)B * G * K *
-        (backward ? (size_t)R * kHeadDim * 2 +
-                        (size_t)2 * kBlock * kHeadDim * 4 / prefill_entries_per_tile(R)
-                  : (size_t)R * (kHeadDim * 2 + 8));
+            (backward ? (size_t)R * kHeadDim * 2 +
+                            (size_t)2 * kBlock * kHeadDim * 4 / prefill_entries_per_tile(R)
+                      : (size_t)R * (kHeadDim * 2 + 8)) +
+        (size_t)B * G * nb / 4;
     const int64_t max_units = (int64_t)1 << 24;
     int64_t rows = 1;
     while (rows * 2 <= T && (size_t)(rows * 2) * part_row <= kPfPartialBudget &&
@@ -112,11 +116,13 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
     w.max_tiles = (w.nslots + w.entries_per_tile - 1) / w.entries_per_tile + w.nlists;
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
+    w.bit_words = (int32_t)((rows + 31) / 32);
+    w.bits_off = take((size_t)w.nlists * w.bit_words * 4);
+    w.wpre_off = take((size_t)w.nlists * w.bit_words * 4);
     w.counts_off = take((size_t)w.nlists * 4);
     w.offsets_off = take((size_t)(w.nlists + 1) * 4);
     w.tile_first_off = take((size_t)(w.nlists + 1) * 4);
     w.tile_map_off = take((size_t)w.max_tiles * 4);
-    w.rank_off = take((size_t)w.nslots * 4);
     w.list_off = take((size_t)w.nslots * 4);
     if (backward) {
         w.part_o_off = take((size_t)w.nslots * R * kHeadDim * 2);  // dq partials, bf16

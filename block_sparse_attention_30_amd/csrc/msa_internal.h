@@ -64,10 +64,10 @@ IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
 // Sparse prefill. Below kPfKvMajorMinRows (B*T*G) rows the query-major kernel
 // runs (no workspace). Otherwise the KV-major path works in passes over
 // `groups` groups and `rows` query rows of every sequence (see prefill_ws). Per pass the workspace holds the
-// per-(sequence, group, block) list sizes, offsets and tile starts, the
-// tile -> list map, the rank of every (row, group, slot) in its list, the
-// lists, and per-(row, group, slot, head) partials: O / l in bf16 [d] and
-// (m, l) as two fp32.
+// per-(sequence, group, block) row bitmaps with their word prefix counts,
+// list sizes, offsets and tile starts, the tile -> list map, the lists, and
+// per-(row, group, slot, head) partials: O / l in bf16 [d] and (m, l) as two
+// fp32.
 constexpr int64_t kPfKvMajorMinRows = 256;
 constexpr size_t kPfPartialBudget = (size_t)5 << 30;
 constexpr int kPfWaves = 4;       // waves per attention workgroup
@@ -80,7 +80,8 @@ struct PrefillWs {
     int32_t groups;  // groups per pass
     int32_t entries_per_tile;
     int64_t nb_max, nlists, nslots, max_tiles;
-    size_t counts_off, offsets_off, tile_first_off, tile_map_off, rank_off, list_off;
+    int32_t bit_words;  // 32-bit words of a list's row bitmap: ceil(rows / 32)
+    size_t bits_off, wpre_off, counts_off, offsets_off, tile_first_off, tile_map_off, list_off;
     size_t part_o_off, part_ml_off, delta_off;
     // Target of the stores of columns that hold no entry (their values are
     // discarded), so the attention kernels store unconditionally.

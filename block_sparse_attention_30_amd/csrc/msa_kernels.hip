@@ -1060,11 +1060,10 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
 // a kept block of one group is staged in LDS once per workgroup and every
 // (row, head) that kept it attends over it there. Per pass of `rows` query
 // rows of every sequence:
-//   pf_count_kernel   each kept (row, group, slot) takes a rank in the list of
-//                     its (sequence, group, block), from an atomic counter;
-//   pf_scan_kernel    one workgroup: list offsets, tile starts (tiles of CH
-//                     entries) and the tile -> list map;
-//   pf_scatter_kernel entry (row << 5 | slot) goes to offset + rank;
+//   list build        each kept (row, group, slot) goes into the list of its
+//                     (sequence, group, block), in row order (the kernels
+//                     below build_pass_lists: a bitmap per list, its prefix
+//                     popcounts, offsets and tiles of CH entries, scatter);
 //   pf_attn_kernel    one workgroup per tile: K and V of the block in LDS,
 //                     then R heads per entry attend over its 128 keys
 //                     (16x16x32 MFMA, the chunk step of attend_chunk with
@@ -1073,8 +1072,9 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
 //   pf_merge_kernel   one workgroup per (row, group): log-sum-exp merge of the
 //                     kept slots' partials into out and lse.
 // A slot is kept when its block id is a causal block of the row (0 <= id <=
-// p/S) and no earlier slot of the row holds the same id; list order does not
-// change any result, since every partial has its own place.
+// p/S) and no earlier slot of the row holds the same id. The forward's results
+// do not depend on the list order (every partial has its own place); the
+// backward's dk and dv sum over the lists, so the order is fixed.
 constexpr int kKRow = 272;  // staged K row bytes: 256 + 16 pad
 constexpr int kPfWaves = msa::kPfWaves;
 constexpr int kPfNq = msa::kPfNq;
@@ -1131,11 +1131,21 @@ __device__ __forceinline__ int pf_row_pos(const int32_t *kv_lens, const int32_t 
     return (p >= 0 && p < kv) ? p : -1;
 }
 
+// List build of a pass: a counting sort of the kept (row, group, slot)
+// entries by block that keeps row order inside every list, so lists and tiles
+// come out the same on every run (the backward sums over them):
+//   pf_mark_kernel     sets bit tl of the kept block's row bitmap (an atomic
+//                      OR, whose result does not depend on the order);
+//   pf_rank_kernel     per list: exclusive prefix popcounts of its bitmap
+//                      words and its entry count;
+//   pf_scan_kernel     list offsets and tiles;
+//   pf_scatter_kernel  an entry's rank is its word's prefix plus the popcount
+//                      of the lower bits of its word.
 // Thread per (sequence, row of the pass, group, slot).
-__global__ __launch_bounds__(256) void pf_count_kernel(
+__global__ __launch_bounds__(256) void pf_mark_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, int B, int T, int G, int Nmax, int K, int t0, int rows,
-    int g0, int ng, int64_t nb_max, int32_t *__restrict__ counts, int32_t *__restrict__ rank) {
+    int g0, int ng, int64_t nb_max, int W, uint32_t *__restrict__ bits) {
     const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (slot >= (int64_t)B * rows * ng * K) return;
     const int k = (int)(slot % K);
@@ -1145,13 +1155,37 @@ __global__ __launch_bounds__(256) void pf_count_kernel(
     const int b = (int)(btl / rows), tl = (int)(btl % rows);
     const int t = t0 + tl;
     const int p = pf_row_pos(kv_lens, q_start, b, t, T, Nmax);
-    int r = -1;
-    if (p >= 0) {
-        const int32_t *sr = sel + (((int64_t)b * T + t) * G + g0 + gl) * K;
-        if (slot_kept(sr, k, p / S + 1))
-            r = atomicAdd(&counts[((int64_t)b * ng + gl) * nb_max + sr[k]], 1);
+    if (p < 0) return;
+    const int32_t *sr = sel + (((int64_t)b * T + t) * G + g0 + gl) * K;
+    if (!slot_kept(sr, k, p / S + 1)) return;
+    const int64_t li = ((int64_t)b * ng + gl) * nb_max + sr[k];
+    atomicOr(&bits[li * W + (tl >> 5)], 1u << (tl & 31));
+}
+
+// Wave per list.
+__global__ __launch_bounds__(256) void pf_rank_kernel(const uint32_t *__restrict__ bits,
+                                                      int64_t nlists, int W,
+                                                      int32_t *__restrict__ wpre,
+                                                      int32_t *__restrict__ counts) {
+    const int64_t li = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (li >= nlists) return;
+    const uint32_t *bw = bits + li * W;
+    int32_t *pw = wpre + li * W;
+    int run = 0;
+    for (int w0 = 0; w0 < W; w0 += 64) {
+        const int i = w0 + lane;
+        const int c = i < W ? __popc(bw[i]) : 0;
+        int x = c;  // inclusive scan over the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (i < W) pw[i] = run + x - c;
+        run += __shfl(x, 63);
     }
-    rank[slot] = r;
+    if (lane == 0) counts[li] = run;
 }
 
 // One workgroup of 1024 threads: exclusive scans of the list sizes and of
@@ -1198,20 +1232,54 @@ __global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict
 }
 
 __global__ __launch_bounds__(256) void pf_scatter_kernel(
-    const int32_t *__restrict__ sel, const int32_t *__restrict__ rank,
-    const int32_t *__restrict__ offsets, int B, int T, int G, int K, int t0, int rows, int g0,
-    int ng, int64_t nb_max, int32_t *__restrict__ list) {
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, const uint32_t *__restrict__ bits,
+    const int32_t *__restrict__ wpre, const int32_t *__restrict__ offsets, int B, int T, int G,
+    int Nmax, int K, int t0, int rows, int g0, int ng, int64_t nb_max, int W,
+    int32_t *__restrict__ list) {
     const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (slot >= (int64_t)B * rows * ng * K) return;
-    const int r = rank[slot];
-    if (r < 0) return;
     const int k = (int)(slot % K);
     const int64_t unit = slot / K;
     const int gl = (int)(unit % ng);
     const int64_t btl = unit / ng;
     const int b = (int)(btl / rows), tl = (int)(btl % rows);
-    const int blk = sel[(((int64_t)b * T + t0 + tl) * G + g0 + gl) * K + k];
-    list[offsets[((int64_t)b * ng + gl) * nb_max + blk] + r] = (tl << 5) | k;
+    const int t = t0 + tl;
+    const int p = pf_row_pos(kv_lens, q_start, b, t, T, Nmax);
+    if (p < 0) return;
+    const int32_t *sr = sel + (((int64_t)b * T + t) * G + g0 + gl) * K;
+    if (!slot_kept(sr, k, p / S + 1)) return;
+    const int64_t li = ((int64_t)b * ng + gl) * nb_max + sr[k];
+    const int64_t wi = li * W + (tl >> 5);
+    const int r = wpre[wi] + __popc(bits[wi] & ((1u << (tl & 31)) - 1u));
+    list[offsets[li] + r] = (tl << 5) | k;
+}
+
+// The list build of one pass (rows t0 .. t0 + rows - 1, groups g0 .. g0 + ng - 1).
+void build_pass_lists(const msa::PrefillWs &w, char *base, const int32_t *sel,
+                      const int32_t *kv_lens, const int32_t *q_start, int B, int T, int G,
+                      int Nmax, int K, int t0, int g0, hipStream_t st) {
+    const int ng = w.groups;
+    const int W = w.bit_words;
+    uint32_t *bits = reinterpret_cast<uint32_t *>(base + w.bits_off);
+    int32_t *wpre = reinterpret_cast<int32_t *>(base + w.wpre_off);
+    int32_t *counts = reinterpret_cast<int32_t *>(base + w.counts_off);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + w.offsets_off);
+    int32_t *tile_first = reinterpret_cast<int32_t *>(base + w.tile_first_off);
+    int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.tile_map_off);
+    int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
+    const int64_t nwords = w.nlists * W;
+    const unsigned slot_blocks = (unsigned)((w.nslots + 255) / 256);
+    fill_i32_kernel<<<(unsigned)((nwords + 255) / 256), 256, 0, st>>>(
+        reinterpret_cast<int32_t *>(bits), nwords, 0);
+    pf_mark_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
+                                                w.rows, g0, ng, w.nb_max, W, bits);
+    pf_rank_kernel<<<(unsigned)((w.nlists + 3) / 4), 256, 0, st>>>(bits, w.nlists, W, wpre, counts);
+    pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets, tile_first,
+                                       tile_map);
+    pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, bits, wpre, offsets, B,
+                                                   T, G, Nmax, K, t0, w.rows, g0, ng, w.nb_max, W,
+                                                   list);
 }
 
 __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
@@ -2453,21 +2521,13 @@ msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, 
     int32_t *offsets = reinterpret_cast<int32_t *>(base + w.offsets_off);
     int32_t *tile_first = reinterpret_cast<int32_t *>(base + w.tile_first_off);
     int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.tile_map_off);
-    int32_t *rank = reinterpret_cast<int32_t *>(base + w.rank_off);
     int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
     bf16_t *part_o = reinterpret_cast<bf16_t *>(base + w.part_o_off);
     float2 *part_ml = reinterpret_cast<float2 *>(base + w.part_ml_off);
-    const unsigned slot_blocks = (unsigned)((w.nslots + 255) / 256);
     for (int32_t g0 = 0; g0 < G; g0 += w.groups)
       for (int32_t t0 = 0; t0 < T; t0 += w.rows) {
         const int ng = w.groups;
-        fill_i32_kernel<<<(unsigned)((w.nlists + 255) / 256), 256, 0, st>>>(counts, w.nlists, 0);
-        pf_count_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
-                                                     w.rows, g0, ng, w.nb_max, counts, rank);
-        pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets,
-                                           tile_first, tile_map);
-        pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, rank, offsets, B, T, G, K, t0, w.rows,
-                                                       g0, ng, w.nb_max, list);
+        build_pass_lists(w, base, sel, kv_lens, q_start, B, T, G, Nmax, K, t0, g0, st);
         pf_attn_kernel<<<(unsigned)w.max_tiles, 256, 0, st>>>(
             qp, kp, vp, kv_lens, q_start, offsets, tile_first, tile_map, list, w.nlists, T, G, R,
             Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2, part_o, part_ml,
@@ -2547,7 +2607,6 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
     int32_t *offsets = reinterpret_cast<int32_t *>(base + w.offsets_off);
     int32_t *tile_first = reinterpret_cast<int32_t *>(base + w.tile_first_off);
     int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.tile_map_off);
-    int32_t *rank = reinterpret_cast<int32_t *>(base + w.rank_off);
     int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
     bf16_t *part_dq = reinterpret_cast<bf16_t *>(base + w.part_o_off);
     float *part_kv = reinterpret_cast<float *>(base + w.part_ml_off);
@@ -2555,17 +2614,10 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
     const int64_t nrows = (int64_t)B * T * G * R;
     bwd_delta_kernel<<<(unsigned)((nrows * 16 + 255) / 256), 256, 0, st>>>(
         static_cast<const bf16_t *>(out), dop, nrows, delta);
-    const unsigned slot_blocks = (unsigned)((w.nslots + 255) / 256);
     for (int32_t g0 = 0; g0 < G; g0 += w.groups)
       for (int32_t t0 = 0; t0 < T; t0 += w.rows) {
         const int ng = w.groups;
-        fill_i32_kernel<<<(unsigned)((w.nlists + 255) / 256), 256, 0, st>>>(counts, w.nlists, 0);
-        pf_count_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
-                                                     w.rows, g0, ng, w.nb_max, counts, rank);
-        pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets,
-                                           tile_first, tile_map);
-        pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, rank, offsets, B, T, G, K, t0, w.rows,
-                                                       g0, ng, w.nb_max, list);
+        build_pass_lists(w, base, sel, kv_lens, q_start, B, T, G, Nmax, K, t0, g0, st);
         bwd_tile_kernel<<<(unsigned)w.max_tiles, kBwdThreads, 0, st>>>(
             qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, tile_first, tile_map, list,
             w.nlists, T, G, R, Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2,

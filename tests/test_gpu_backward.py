@@ -81,3 +81,31 @@ def test_backward_two_passes(orc):
 
 def test_backward_short_context_odd_heads(orc):
     run(orc, 1, 257, 257, 3, 5, 16, [257], [0], seed=830)
+
+
+def test_backward_bitwise_repeatable():
+    # 4096 rows over 32 blocks: most lists span several tiles, so dk and dv
+    # are sums over many tiles; two calls must agree bit for bit (the lists
+    # keep row order, no floating-point atomics).
+    B, T, N, G, R, K = 1, 4096, 4096, 2, 8, 16
+    seed = 840
+    H = G * R
+    q = ms.fill_normal_bf16(np.empty((B, T, H, 128), np.uint16), seed + 1)
+    k = ms.fill_normal_bf16(np.empty((B, G, N, 128), np.uint16), seed + 2)
+    v = ms.fill_normal_bf16(np.empty((B, G, N, 128), np.uint16), seed + 3)
+    qi = ms.fill_int_bf16(np.empty((B, T, G, 128), np.uint16), seed + 4, -4, 4)
+    ki = ms.fill_int_bf16(np.empty((B, N, 128), np.uint16), seed + 5, -4, 4)
+    do = ms.fill_normal_bf16(np.empty((B, T, H, 128), np.uint16), seed + 6)
+    cfg = lib_cfg(G, R, K)
+    kv, qs = dev_i32(np.array([N], np.int32)), dev_i32(np.array([0], np.int32))
+    dq_, dk_, dv_, ddo = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_bf16(do)
+    say("forward and backward twice B=%d T=%d N=%d G=%d R=%d K=%d" % (B, T, N, G, R, K))
+    sel = msa.index_topk(cfg, dev_index(qi), dev_index(ki), kv, qs)
+    res = []
+    for _ in range(2):
+        out, lse = msa.sparse_attn_prefill(cfg, dq_, dk_, dv_, kv, sel, q_start=qs, want_lse=True)
+        res.append((out, lse) + tuple(msa.sparse_attn_backward(cfg, dq_, dk_, dv_, kv, sel, out,
+                                                               lse, ddo, q_start=qs)))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("out", "lse", "dq", "dk", "dv"), res[0], res[1]):
+        assert torch.equal(a, b), name
