@@ -91,21 +91,23 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
     // the backward keeps a dq partial in bf16.
     // (The backward's per-tile dk/dv partials, 2*S*d fp32 per tile of
     // entries_per_tile entries, add 2*S*d*4 / entries_per_tile bytes per slot.)
-    // The list build adds a row bitmap and its word prefixes per list: 8 bytes
-    // per 32 rows of each of the B*G*nb lists.
-    const int64_t nb = ((int64_t)Nmax + kBlock - 1) / kBlock;
     const size_t part_row =
         (size_t)B * G * K *
-            (backward ? (size_t)R * kHeadDim * 2 +
-                            (size_t)2 * kBlock * kHeadDim * 4 / prefill_entries_per_tile(R)
-                      : (size_t)R * (kHeadDim * 2 + 8)) +
-        (size_t)B * G * nb / 4;
+        (backward ? (size_t)R * kHeadDim * 2 +
+                        (size_t)2 * kBlock * kHeadDim * 4 / prefill_entries_per_tile(R)
+                  : (size_t)R * (kHeadDim * 2 + 8));
+    // The list build keeps a row bitmap and its word prefixes per list: 8
+    // bytes per 32 rows of each of the B*G*nb lists, within kPfBitmapBudget.
+    const int64_t nb = ((int64_t)Nmax + kBlock - 1) / kBlock;
+    const size_t bits_row = (size_t)B * G * nb / 4 + 1;
     const int64_t max_units = (int64_t)1 << 24;
     int64_t rows = 1;
-    while (rows * 2 <= T && (size_t)(rows * 2) * part_row <= kPfPartialBudget &&
-           rows * 2 * B * G <= max_units)
-        rows *= 2;
-    if ((size_t)T * part_row <= kPfPartialBudget && (int64_t)T * B * G <= max_units) rows = T;
+    auto fits = [&](int64_t r) {
+        return (size_t)r * part_row <= kPfPartialBudget && (size_t)r * bits_row <= kPfBitmapBudget &&
+               r * B * G <= max_units;
+    };
+    while (rows * 2 <= T && fits(rows * 2)) rows *= 2;
+    if (fits(T)) rows = T;
     const int64_t groups = G;
     w.rows = (int32_t)rows;
     w.groups = (int32_t)groups;

@@ -70,6 +70,7 @@ IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax);
 // fp32.
 constexpr int64_t kPfKvMajorMinRows = 256;
 constexpr size_t kPfPartialBudget = (size_t)5 << 30;
+constexpr size_t kPfBitmapBudget = (size_t)1 << 30;
 constexpr int kPfWaves = 4;       // waves per attention workgroup
 constexpr int kPfNq = 2;          // 16-column query tiles per wave
 constexpr int kPfRounds = 16;     // passes of every wave over its tiles per workgroup

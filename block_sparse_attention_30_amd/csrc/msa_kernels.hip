@@ -1856,7 +1856,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_tile_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ tile_first,
     const int32_t *__restrict__ tile_map, const int32_t *__restrict__ list, int64_t nlists, int T,
     int G, int R, int Nmax, int K, int t0, int rows, int g0, int ng, int64_t nb_max, int ch,
-    float scale_log2, float tau, bf16_t *__restrict__ part_dq, float *__restrict__ part_kv) {
+    float scale_log2, float tau, bf16_t *__restrict__ part_dq, float *__restrict__ part_kv,
+    unsigned char *__restrict__ trash) {
     // Two buffers of a batch's q and dout rows: batch i+1 is staged into one
     // while batch i is read from the other, one barrier per batch.
     __shared__ __attribute__((aligned(16))) unsigned char q_buf[2][kBwdCols * kVRow];
@@ -2080,14 +2081,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_tile_kernel(
             for (int j = 0; j < 2; ++j) {
                 const int tc = cb + 16 * (2 * (wave & 1) + j) + col;
                 const int slot = s_slot[tc];
-                if (slot >= 0) {
-                    bf16_t *op = part_dq + ((int64_t)slot * R + tc % R) * D + 4 * kg;
+                // A column without an entry stores into the trash area (no
+                // branch, so waits count the same stores on every path).
+                bf16_t *op = (slot >= 0 ? part_dq + ((int64_t)slot * R + tc % R) * D
+                                        : reinterpret_cast<bf16_t *>(trash) + (tc % R) * D) +
+                             4 * kg;
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        *reinterpret_cast<u32x2 *>(op + (2 * (wave >> 1) + i) * 16) =
-                            u32x2{pack_bf16x2(tau * dqa[i][j][0], tau * dqa[i][j][1]),
-                                  pack_bf16x2(tau * dqa[i][j][2], tau * dqa[i][j][3])};
-                }
+                for (int i = 0; i < 2; ++i)
+                    *reinterpret_cast<u32x2 *>(op + (2 * (wave >> 1) + i) * 16) =
+                        u32x2{pack_bf16x2(tau * dqa[i][j][0], tau * dqa[i][j][1]),
+                              pack_bf16x2(tau * dqa[i][j][2], tau * dqa[i][j][3])};
             }
         }
         __syncthreads();  // this batch's buffers are read, the next one is staged
@@ -2621,7 +2624,7 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
         bwd_tile_kernel<<<(unsigned)w.max_tiles, kBwdThreads, 0, st>>>(
             qp, kp, vp, kv_lens, q_start, lse, dop, delta, offsets, tile_first, tile_map, list,
             w.nlists, T, G, R, Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2,
-            tau, part_dq, part_kv);
+            tau, part_dq, part_kv, reinterpret_cast<unsigned char *>(base + w.trash_off));
         bwd_dkdv_reduce_kernel<<<(unsigned)w.nlists, 256, 0, st>>>(
             tile_first, part_kv, G, Nmax, g0, ng, w.nb_max, tau, t0 > 0 ? 1 : 0, dk, dv);
         bwd_dq_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), 256, 0, st>>>(
