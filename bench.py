@@ -413,7 +413,7 @@ def run_prefill(torch, msa, w, steps=5, warmup=1):
                backward_frac_bf16_peak=round(2 * f_att / tb / 1e9 / BF16_PEAK_TFLOPS, 4),
                backward_note="msa_sparse_attn_backward; flops = dP, dq, dk, dv products "
                              "(8*d per row, head and attended key, twice the forward's; the "
-                             "kernels also recompute S twice)")
+                             "tile kernel also recomputes S once)")
     del q, qi, k, v, ki, sel, out, ws_i
     torch.cuda.empty_cache()
     return res
@@ -559,11 +559,18 @@ def run_chunked(torch, msa, w):
     return res
 
 
+# The sources the decode index kernel is built from: its own file, the shared
+# device helpers and the internal constants.
+DECODE_KERNEL_SOURCES = ("msa_internal.h", "msa_device.h", "msa_decode.hip")
+
+
 def kernel_source_digest():
     import hashlib
-    path = os.path.join(ROOT, "block_sparse_attention_30_amd", "csrc", "msa_kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in DECODE_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_30_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel, workload):

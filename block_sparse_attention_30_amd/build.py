@@ -16,6 +16,8 @@ LIBRARY = os.path.join(PKG, "libmsa.so")
 # separate object: nothing in libmsa uses it.
 PROBE_LIBRARY = os.path.join(PKG, "libmsa_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
+# Kernel sources (each with its entry points), sharing msa_device.h.
+KERNEL_SOURCES = ("msa_decode.hip", "msa_prefill.hip", "msa_backward.hip")
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -44,11 +46,14 @@ def build(verbose: bool = False) -> str:
     try:
         run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE,
              "-c", os.path.join(CSRC, "msa_host.cpp"), "-o", host_o])
-        kern_o = os.path.join(BUILD_DIR, "msa_kernels.o")
-        run([_hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
-             os.path.join(CSRC, "msa_kernels.hip"), "-o", kern_o])
+        kern_o = []
+        for name in KERNEL_SOURCES:
+            obj = os.path.join(BUILD_DIR, name.replace(".hip", ".o"))
+            run([_hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+                 os.path.join(CSRC, name), "-o", obj])
+            kern_o.append(obj)
         tmp = LIBRARY + ".tmp%d" % os.getpid()
-        run([_hipcc(), "-shared", "-fPIC", kern_o, host_o, "-o", tmp,
+        run([_hipcc(), "-shared", "-fPIC"] + kern_o + [host_o, "-o", tmp,
              "-Wl,-rpath,/opt/rocm/lib"])
         probe_tmp = PROBE_LIBRARY + ".tmp%d" % os.getpid()
         run([_hipcc()] + HIPCC_FLAGS + ["-shared", os.path.join(CSRC, "read_probe.hip"), "-o",

@@ -1,5 +1,6 @@
 // Private interface between the host-only validation unit (msa_host.cpp) and
-// the kernel unit (msa_kernels.hip). Not installed; not part of the ABI.
+// the kernel units (msa_decode.hip, msa_prefill.hip, msa_backward.hip). Not
+// installed; not part of the ABI.
 #pragma once
 
 #include <stddef.h>
