@@ -38,14 +38,24 @@ namespace {
 // Prefill index scores. A workgroup owns 256 consecutive (query, group) rows
 // of one sequence; wave w owns rows [64w, 64w+64) as two 32-column MFMA tiles
 // whose index queries stay in registers (B operand). For each causal KV block
-// the 128-token k_idx tile is staged once in LDS (rows padded by 16 bytes so
-// that 16 lanes reading 16 bytes each hit distinct banks) and read as the A
-// operand by all four waves. D lane l holds column (l & 31) and rows
+// the 128-token k_idx tile is staged once in LDS by direct global->LDS loads
+// into one of two buffers (the next block streams in while this one is used;
+// one barrier per block) and read as the A operand by all four waves. Rows are
+// unpadded; the 16-byte pieces of a row are XOR-swizzled (idx_swz) so that 16
+// lanes reading the same piece of 16 rows hit distinct banks. D lane l holds column (l & 31) and rows
 // 8*(i>>2) + 4*(l>>5) + (i&3), so the block max of a column is an in-lane max
 // over the four row tiles plus one exchange with lane l^32. bf16 keys use
 // 32x32x16 bf16 MFMAs (8 per row tile and column tile), OCP E4M3 keys
 // 32x32x64 f8f6f4 MFMAs with unit scales (2 per row tile and column tile).
 constexpr int kPfRows = 256;
+
+// Physical 16-byte slot of logical piece `piece` of k_idx row `row` in the
+// staged tile: bf16 rows (16 pieces) swizzle by row & 15; E4M3 rows (8 pieces,
+// two rows per 256 bytes of banks) by (row >> 1) & 7.
+template <bool F8>
+__device__ __forceinline__ int idx_swz(int row, int piece) {
+    return F8 ? piece ^ ((row >> 1) & 7) : piece ^ (row & 15);
+}
 
 template <bool V>
 struct BoolTag {
@@ -86,10 +96,10 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int K,
     int32_t *__restrict__ sel, float *__restrict__ sel_scores, int nslots = 0) {
     constexpr int kRowBytes = DI * (F8 ? 1 : 2);
-    constexpr int kRow = kRowBytes + 16;
-    constexpr int kPieces = S * kRowBytes / 16 / 256;  // 16-byte loads per thread per block
-    constexpr int kKs = F8 ? 2 : 8;                     // MFMA K steps over the index dim
-    __shared__ __attribute__((aligned(16))) unsigned char lds[S * kRow];
+    constexpr int kRowPieces = kRowBytes / 16;
+    constexpr int kRuns = S * kRowBytes / 1024 / 4;  // 1 KiB staging loads per wave per block
+    constexpr int kKs = F8 ? 2 : 8;                  // MFMA K steps over the index dim
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_buf[2][S * kRowBytes];
     const int b = blockIdx.y;
     const int rows = T * G;
     const int xr = gridDim.x - 1 - blockIdx.x;  // longest rows first
@@ -152,19 +162,21 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
         tb[i] = -1;
     }
     const unsigned char *kseq = k_idx + (size_t)b * Nmax * kRowBytes;
-    // The next block's k_idx rows are loaded into registers while the current
-    // block is being used from LDS.
-    u32x4 pre[kPieces];
-    // Loads are unconditional (clamped to the last key, kv >= 1 whenever a
-    // block exists) and tokens past kv are zeroed afterwards.
-    auto load_block = [&](int blk) {
+    // Stage block blk into buffer `buf`: wave w loads 1 KiB runs w, w + 4, ...
+    // of the tile; lane l fills physical slot l % kRowPieces of row
+    // run * (1024 / kRowBytes) + l / kRowPieces. Loads are clamped to the last
+    // key (kv >= 1 whenever a block exists); keys past kv lie past every row's
+    // position and are masked.
+    auto stage = [&](int blk, unsigned char *buf) {
 #pragma unroll
-        for (int i = 0; i < kPieces; ++i) {
-            const int piece = tid + 256 * i;
-            const int tk = piece / (kRowBytes / 16), c = piece % (kRowBytes / 16);
-            const int tok = blk * S + tk;
-            pre[i] = ld16(kseq + (size_t)min(tok, kv - 1) * kRowBytes + c * 16);
-            if (tok >= kv) pre[i] = zero4;
+        for (int i = 0; i < kRuns; ++i) {
+            const int run = wave + 4 * i;
+            const int row = run * (1024 / kRowBytes) + lane / kRowPieces;
+            const int piece = idx_swz<F8>(row, lane % kRowPieces);
+            const int tok = min(blk * S + row, kv - 1);
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(kseq + (size_t)tok * kRowBytes + piece * 16),
+                (__attribute__((address_space(3))) void *)(buf + run * 1024), 16, 0, 0);
         }
     };
     // QB: the wave's value for the last block, and the two waves' values of
@@ -184,19 +196,16 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     auto do_block = [&](auto mask_tag, int blk) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int tok0 = blk * S;
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
-        __builtin_amdgcn_s_barrier();        // ... and every other wave's
+        // This wave's staging loads of block blk have landed (vmcnt(0)) and its
+        // LDS reads of block blk - 1 are done (lgkmcnt(0)); after the barrier
+        // every wave's have, so blk is complete in its buffer and the other
+        // buffer is free for blk + 1.
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
         if constexpr (QB)
             if (blk > 0) qb_offer(blk - 1);
-#pragma unroll
-        for (int i = 0; i < kPieces; ++i) {
-            const int piece = tid + 256 * i;
-            const int tk = piece / (kRowBytes / 16), c = piece % (kRowBytes / 16);
-            *reinterpret_cast<u32x4 *>(lds + tk * kRow + c * 16) = pre[i];
-        }
-        if (blk + 1 < nblk) load_block(blk + 1);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block's LDS rows are written
-        __builtin_amdgcn_s_barrier();
+        if (blk + 1 < nblk) stage(blk + 1, lds_buf[(blk + 1) & 1]);
+        const unsigned char *lds = lds_buf[blk & 1];
         float cm0 = -INFINITY, cm1 = -INFINITY;
         // Two row tiles at a time: four independent accumulator chains.
 #pragma unroll
@@ -207,10 +216,14 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
                     const int rt = 2 * rp + h2;
-                    const unsigned char *ap = lds + (rt * 32 + j) * kRow + ks * kKb + half * (kKb / 2);
+                    // Logical bytes ks*kKb + half*kKb/2 of row rt*32 + j.
+                    const int row = rt * 32 + j;
+                    const int p0 = (ks * kKb + half * (kKb / 2)) / 16;
+                    const unsigned char *ap = lds + row * kRowBytes + idx_swz<F8>(row, p0) * 16;
                     if constexpr (F8) {
+                        const unsigned char *ap1 = lds + row * kRowBytes + idx_swz<F8>(row, p0 + 1) * 16;
                         const i32x8 a = cat_i32x8(*reinterpret_cast<const u32x4 *>(ap),
-                                                  *reinterpret_cast<const u32x4 *>(ap + 16));
+                                                  *reinterpret_cast<const u32x4 *>(ap1));
                         acc[h2][0] = mfma32_f8(a, cat_i32x8(qb[0][ks][0], qb[0][ks][F8 ? 1 : 0]), acc[h2][0]);
                         acc[h2][1] = mfma32_f8(a, cat_i32x8(qb[1][ks][0], qb[1][ks][F8 ? 1 : 0]), acc[h2][1]);
                     } else {
@@ -260,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     };
     // Blocks [0, n_plain) end at or before the first row's position.
     const int n_plain = p_lo >= 0 ? min((p_lo + 1) / S, nblk) : 0;
-    if (nblk > 0) load_block(0);
+    if (nblk > 0) stage(0, lds_buf[0]);
     for (int blk = 0; blk < n_plain; ++blk) do_block(BoolTag<false>{}, blk);
     for (int blk = n_plain; blk < nblk; ++blk) do_block(BoolTag<true>{}, blk);
     if constexpr (QB) {
