@@ -287,8 +287,9 @@ int oracle_sparse_attn_row(const oracle_cfg *cfg, const uint16_t *q_row, const u
             if (b >= 0 && b < n_valid) chosen[b] = 1;
         }
         int64_t n = 0;
-        for (int64_t j = 0; j <= p; ++j)
-            if (chosen[j / S]) keys[n++] = j;
+        for (int64_t blk = 0; blk < n_valid; ++blk)
+            if (chosen[blk])
+                for (int64_t j = blk * S; j <= p && j < (blk + 1) * S; ++j) keys[n++] = j;
         const uint16_t *k_grp = k_seq + (int64_t)g * n_stride * d;
         const uint16_t *v_grp = v_seq + (int64_t)g * n_stride * d;
         for (int r = 0; r < R; ++r) {
@@ -384,8 +385,9 @@ int oracle_sparse_attn_backward_group(const oracle_cfg *cfg, int32_t T, int64_t 
             if (blk >= 0 && blk < n_valid) chosen[blk] = 1;
         }
         int64_t n = 0;
-        for (int64_t j = 0; j <= p; ++j)
-            if (chosen[j / S]) keys[n++] = j;
+        for (int64_t blk = 0; blk < n_valid; ++blk)
+            if (chosen[blk])
+                for (int64_t j = blk * S; j <= p && j < (blk + 1) * S; ++j) keys[n++] = j;
         if (n == 0) continue;
         for (int r = 0; r < R; ++r) {
             const int64_t h = g * R + r;

@@ -13,7 +13,10 @@ configuration the benchmark uses:
                                                  per row grows with position);
   query-block-shared selections, 131072-token    24 sampled query blocks
   prefill and two chunks of the 1M chunked       (selections), 8 rows of each
-  prefill                                        (attention).
+  prefill                                        (attention);
+  sparse backward, 131072-token prefill with     dq on about 80 sampled rows,
+  seeded selections                              dk and dv on one whole block
+                                                 per group.
 Selections are compared bit for bit, outputs and lse within the tolerances of
 the small parity tests. Inputs are the seeded synthetic workloads."""
 import numpy as np
@@ -21,6 +24,7 @@ import pytest
 import torch
 
 import block_sparse_attention_30_amd as msa
+import msa_synth as ms
 from gpu_helpers import (bf16_out_to_f64, compare_lse, compare_out, dev_bf16, dev_i32,
                          dev_index, oracle_cfg, say)
 from msa_synth import workloads as wl
@@ -259,3 +263,89 @@ def test_chunked_prefill_1M_fp8_qblock_sampled_blocks(orc, chunked_1m, chunk, nb
     blocks = sorted({0, 255} | {int(x) for x in rng.integers(0, 256, size=nblocks - 2)})
     check_qblock(orc, w, host, dev, q_h, qi_h, row0, blocks,
                  "%s chunk %d qblock" % (w.name, chunk), seed=61 + chunk)
+
+
+def structured_selection(T, G, K, S, seed):
+    """Seeded selections [T, G, K] for a prefill whose row t sits at position
+    t: every row keeps its own (diagonal) block d = t // S and K - 1 distinct
+    earlier blocks, (a*k + c) mod d for k = 1 .. K-1 with a prime a above the
+    block count (so the K - 1 values are distinct once d >= K - 1), or every
+    earlier block when there are fewer; -1 pads. A test input of the backward,
+    which takes the selections as given."""
+    rng = np.random.default_rng(seed)
+    diag = np.arange(T, dtype=np.int64) // S
+    primes = np.array([1031, 1033, 1039, 1049, 1051, 1061, 1063, 1069], np.int64)
+    assert diag[-1] < primes.min()
+    sel = np.full((T, G, K), -1, np.int32)
+    ks = np.arange(1, K, dtype=np.int64)
+    for g in range(G):
+        a = primes[rng.integers(0, primes.size, size=T)]
+        c = rng.integers(0, 1 << 20, size=T)
+        sel[:, g, 0] = diag
+        cand = (a[:, None] * ks[None, :] + c[:, None]) % np.maximum(diag, 1)[:, None]
+        full = diag >= K - 1
+        sel[full, g, 1:] = cand[full]
+        for t in np.flatnonzero(~full):
+            sel[t, g, 1:1 + diag[t]] = np.arange(diag[t])
+    return sel
+
+
+def test_backward_L131072_sampled(orc):
+    """msa_sparse_attn_backward on the 131072-token prefill (four passes of
+    32768 rows, as the benchmark runs it) with seeded selections: dq on about
+    80 sampled rows and dk, dv on every key of one block per group, whose
+    attending rows span several tiles (and for one block two passes). The oracle runs on the same
+    inputs with the selections of every other row removed: a row's dq depends
+    on that row alone, and a key's dk and dv only on the rows that kept its
+    block, so the sampled values are exact."""
+    w = wl.workload(3)
+    G, R, K, S, T, N = w.G, w.R, w.topk, 128, w.T, w.Nmax
+    say("generating %s backward inputs" % w.name)
+    k_h, v_h, _ = wl.gen_caches(w)
+    q_h, _ = wl.gen_queries(w)
+    dout_h = ms.fill_normal_bf16(np.empty_like(q_h), 9301)
+    sel_h = structured_selection(T, G, K, S, seed=9302)[None]
+    kv_h, qs_h = np.array([N], np.int32), np.array([0], np.int32)
+    cfg = lib_config(w)
+    q, k, v, dout = dev_bf16(q_h), dev_bf16(k_h), dev_bf16(v_h), dev_bf16(dout_h)
+    kv, qs, sel = dev_i32(kv_h), dev_i32(qs_h), dev_i32(sel_h)
+    say("%s: forward and backward on the GPU" % w.name)
+    out, lse = msa.sparse_attn_prefill(cfg, q, k, v, kv, sel, q_start=qs, want_lse=True)
+    gq, gk, gv = msa.sparse_attn_backward(cfg, q, k, v, kv, sel, out, lse, dout, q_start=qs)
+    torch.cuda.synchronize()
+    rows = stratified_rows(0, T, 32768, 64, seed=9303)
+    # One block per group; block 760 is kept by rows of the third and the
+    # fourth pass (its dk and dv add up over passes), the others by the last.
+    blocks = [760, 880, 950, 1010]
+    g_dq = gq[0].index_select(0, torch.from_numpy(rows).cuda()).cpu().numpy().astype(np.float64)
+    g_dk = [gk[0, g, blocks[g] * S:(blocks[g] + 1) * S].cpu().numpy().astype(np.float64)
+            for g in range(G)]
+    g_dv = [gv[0, g, blocks[g] * S:(blocks[g] + 1) * S].cpu().numpy().astype(np.float64)
+            for g in range(G)]
+    del q, k, v, dout, out, lse, gq, gk, gv, sel
+    torch.cuda.empty_cache()
+    keep = np.zeros((T, G), bool)
+    keep[rows, :] = True
+    for g in range(G):
+        keep[:, g] |= (sel_h[0, :, g, :] == blocks[g]).any(axis=1)
+    say("%s: oracle on %s rows per group" % (w.name, keep.sum(axis=0).tolist()))
+    sel_o = np.where(keep[None, :, :, None], sel_h, -1).astype(np.int32)
+    oq, ok_, ov = orc.sparse_attn_backward(oracle_cfg(G, R, K), q_h, k_h, v_h, kv_h, qs_h,
+                                           sel_o, dout_h, threads=THREADS)
+    compare_grad(g_dq, oq[0, rows], "dq (sampled rows)")
+    compare_grad(np.concatenate(g_dk), np.concatenate(
+        [ok_[0, g, blocks[g] * S:(blocks[g] + 1) * S] for g in range(G)]), "dk (one block per group)")
+    compare_grad(np.concatenate(g_dv), np.concatenate(
+        [ov[0, g, blocks[g] * S:(blocks[g] + 1) * S] for g in range(G)]), "dv (one block per group)")
+
+
+def compare_grad(got, want, what):
+    """The backward tolerances of the small parity tests: relative L2 <= 1e-2,
+    max-abs <= 1e-2 * max|reference|."""
+    scale = float(np.abs(want).max())
+    err = float(np.abs(got - want).max())
+    rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
+    say("%s: max_abs=%.3e (ref max %.3e) rel_l2=%.3e" % (what, err, scale, rel))
+    assert scale > 0.0, what
+    assert rel <= 1e-2, (what, rel)
+    assert err <= 1e-2 * scale, (what, err, scale)

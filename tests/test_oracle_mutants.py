@@ -11,15 +11,11 @@ import oracle_pins as pins
 # (name, text in msa_oracle.c, replacement)
 MUTANTS = [
     ("diagonal_key_dropped",
-     "for (int64_t j = 0; j <= p; ++j)\n            if (chosen[j / S]) keys[n++] = j;\n"
-     "        const uint16_t *k_grp",
-     "for (int64_t j = 0; j < p; ++j)\n            if (chosen[j / S]) keys[n++] = j;\n"
-     "        const uint16_t *k_grp"),
+     "j <= p && j < (blk + 1) * S; ++j) keys[n++] = j;\n        const uint16_t *k_grp",
+     "j < p && j < (blk + 1) * S; ++j) keys[n++] = j;\n        const uint16_t *k_grp"),
     ("backward_diagonal_key_dropped",
-     "for (int64_t j = 0; j <= p; ++j)\n            if (chosen[j / S]) keys[n++] = j;\n"
-     "        if (n == 0) continue;",
-     "for (int64_t j = 0; j < p; ++j)\n            if (chosen[j / S]) keys[n++] = j;\n"
-     "        if (n == 0) continue;"),
+     "j <= p && j < (blk + 1) * S; ++j) keys[n++] = j;\n        if (n == 0) continue;",
+     "j < p && j < (blk + 1) * S; ++j) keys[n++] = j;\n        if (n == 0) continue;"),
     ("pool_starts_at_zero", "double m = s[lo];", "double m = 0.0;"),
     ("pool_sums", "if (s[j] > m) m = s[j];", "m += s[j];"),
     ("ties_to_higher_block", "return (x->block > y->block) - (x->block < y->block);",
