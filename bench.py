@@ -102,11 +102,12 @@ def _stream_read(torch, lib, buf, wgs, sink):
         raise RuntimeError("stream-read probe failed: %d" % rc)
 
 
-def cold_ms(torch, fn, steps, warmup, flush_cache=True):
+def cold_ms(torch, fn, steps, warmup, flush_cache=True, per_step=None):
     """Average ms of fn(s) with the last-level cache flushed before each step:
     a 1 GiB buffer is read between steps (reads, so no dirty lines are left to
     write back during the step) and every step is bracketed by its own event
-    pair (the events add a few microseconds per step)."""
+    pair (the events add a few microseconds per step). The per-step times go
+    into the list `per_step` when one is given."""
     lib = _probe_lib()
     flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
@@ -123,7 +124,10 @@ def cold_ms(torch, fn, steps, warmup, flush_cache=True):
         evs[s][1].record()
     torch.cuda.synchronize()
     del flush, sink
-    return sum(a.elapsed_time(b) for a, b in evs) / steps
+    times = [a.elapsed_time(b) for a, b in evs]
+    if per_step is not None:
+        per_step.extend(times)
+    return sum(times) / steps
 
 
 def run_decode(torch, msa, w, steps, warmup, nsets=8):
@@ -232,11 +236,14 @@ def run_decode(torch, msa, w, steps, warmup, nsets=8):
     ms_total, _ = timed(step, 0)
     wall = time.perf_counter() - wall0
     ms_cold = cold_ms(torch, step, steps, warmup)
-    ms_ev = cold_ms(torch, step, steps, warmup, flush_cache=False)
+    ev_times = []
+    ms_ev = cold_ms(torch, step, steps, warmup, flush_cache=False, per_step=ev_times)
+    ev_times.sort()
     host = dict(k=np_view(kh), v=np_view(vh), ki=np_view(kih), q=np_view(sets[0][0]),
                 qi=np_view(sets[0][1]))
     return dict(ms_per_step=ms_total, wall_s=wall, graph_ms=ms_graph, two_call_ms=ms_two,
-                cold_ms=ms_cold, events_ms=ms_ev,
+                cold_ms=ms_cold, events_ms=ms_ev, events_min_ms=ev_times[0],
+                events_median_ms=ev_times[len(ev_times) // 2],
                 idx_ms=idx_ms, att_ms=att_ms, pool_ms=pool_ms, host=host, k=k, v=v)
 
 
@@ -341,7 +348,33 @@ def sparse_work(torch, w, sel, q0):
     return f_att, nbytes
 
 
-def run_prefill(torch, msa, w, steps=5, warmup=1):
+def cpu_baseline_prefill(w, host, n_rows=128, seed=0x4D534143):
+    """The oracle (as written, untuned) on a uniform random sample of the
+    prefill's rows (index top-k + sparse attention per row); the sampled rate
+    stands for the whole prefill, whose per-row cost the uniform sample
+    averages."""
+    import numpy as np
+    import oracle
+    orc = oracle.default()
+    ocfg = oracle.Config(groups=w.G, heads_per_group=w.R, topk=w.topk,
+                         index_dtype=oracle.E4M3 if w.index_fp8 else oracle.BF16)
+    rows_i = np.sort(np.random.default_rng(seed).choice(w.T, n_rows, replace=False))
+    rows = np.stack([np.zeros_like(rows_i), rows_i], axis=1).astype(np.int32)
+    kv = np.array(w.kv_lens, np.int32)
+    qs = np.array(w.q_start, np.int32)
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    t0 = time.perf_counter()
+    sel, _ = orc.index_topk(ocfg, host["qi"], host["ki"], kv, qs, rows=rows, threads=threads)
+    orc.sparse_attn(ocfg, host["q"], host["k"], host["v"], kv, qs, sel, rows=rows,
+                    threads=threads)
+    dt = time.perf_counter() - t0
+    return dict(value=round(n_rows / dt, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample="%d uniform random rows of the %d-token prefill (all groups and heads): "
+                       "index top-k + sparse attention, %.2f s wall; the rate stands for the "
+                       "whole prefill (extrapolated)" % (n_rows, w.T, dt))
+
+
+def run_prefill(torch, msa, w, steps=5, warmup=1, cpu_baseline=False):
     import numpy as np
     from msa_synth import workloads as wl
     t0 = time.time()
@@ -351,6 +384,8 @@ def run_prefill(torch, msa, w, steps=5, warmup=1):
     log("prefill inputs generated in %.1fs" % (time.time() - t0))
     k, v, ki = to_dev(torch, kh), to_dev(torch, vh), to_dev(torch, kih, bf16=not w.index_fp8)
     q, qi = to_dev(torch, qh), to_dev(torch, qih, bf16=not w.index_fp8)
+    host = dict(k=np_view(kh), v=np_view(vh), ki=np_view(kih), q=np_view(qh),
+                qi=np_view(qih)) if cpu_baseline else None
     del kh, vh, kih, qh, qih
     kv = torch.tensor(w.kv_lens, dtype=torch.int32, device="cuda")
     qs = torch.tensor(w.q_start, dtype=torch.int32, device="cuda")
@@ -416,6 +451,11 @@ def run_prefill(torch, msa, w, steps=5, warmup=1):
                              "tile kernel also recomputes S once)")
     del q, qi, k, v, ki, sel, out, ws_i
     torch.cuda.empty_cache()
+    if host is not None:
+        cb = cpu_baseline_prefill(w, host)
+        cb["gpu_tokens_per_s"] = round(L / ((ti + ta) * 1e-3), 1)
+        cb["gpu_over_oracle"] = round(cb["gpu_tokens_per_s"] / cb["value"], 1)
+        res["cpu_baseline"] = cb
     return res
 
 
@@ -691,7 +731,9 @@ def main():
                      "msa_index_topk": round(res["idx_ms"], 5),
                      "msa_sparse_attn_decode": round(res["att_ms"], 5),
                      "msa_decode_cold_cache": round(res["cold_ms"], 5),
-                     "msa_decode_per_step_events_warm": round(res["events_ms"], 5)},
+                     "msa_decode_per_step_events_warm": round(res["events_ms"], 5),
+                     "msa_decode_per_step_events_warm_min": round(res["events_min_ms"], 5),
+                     "msa_decode_per_step_events_warm_median": round(res["events_median_ms"], 5)},
         "cold_cache_GB/s": round(nbytes / (res["cold_ms"] * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel<false> (bf16 keys, via msa_index_pool)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -715,7 +757,8 @@ def main():
                                                     args.warmup)
     torch.cuda.empty_cache()
     if not args.no_prefill:
-        line["prefill"] = run_prefill(torch, msa, wl.workload(3))
+        line["prefill"] = run_prefill(torch, msa, wl.workload(3),
+                                      cpu_baseline=not args.no_cpu_baseline)
         line["prefill_qblock"] = run_prefill_qblock(torch, msa, wl.workload(3))
     if not args.no_prefill and not args.no_chunked:
         line["chunked_prefill"] = run_chunked(torch, msa, wl.workload(5))
