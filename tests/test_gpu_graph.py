@@ -77,3 +77,56 @@ def test_graph_replays_match_eager():
         # partials merge in a different order.
         assert torch.equal(sel, sel2)
         assert (out.float() - out2.float()).abs().max().item() <= 2e-2
+
+
+def test_graph_backward_and_qblock_match_eager():
+    """msa_sparse_attn_backward (list build, tile kernel, reductions),
+    msa_index_topk_qblock and msa_sparse_attn_prefill_qblock captured in one
+    graph: every replay equals the eager calls on the same inputs, bit for
+    bit."""
+    G, R, K, T = 2, 8, 8, 700
+    cfg = lib_cfg(G, R, K)
+    kv = torch.tensor([T], dtype=torch.int32, device="cuda")
+    qs = torch.tensor([0], dtype=torch.int32, device="cuda")
+    buf = rand_inputs(1, T, T, G, R, seed=3)
+    dout = rand_inputs(1, T, T, G, R, seed=4)["q"]
+    sel = msa.index_topk(cfg, buf["qi"], buf["ki"], kv, qs)
+    out, lse = msa.sparse_attn_prefill(cfg, buf["q"], buf["k"], buf["v"], kv, sel, q_start=qs,
+                                       want_lse=True)
+    ws_b = msa.workspace(cfg, 1, T, T, msa.WS_SPARSE_BACKWARD)
+    dq, dk, dv = msa.sparse_attn_backward(cfg, buf["q"], buf["k"], buf["v"], kv, sel, out, lse,
+                                          dout, q_start=qs, workspace=ws_b)
+    nq = msa.qblock_slots(T)
+    qsel = torch.empty((1, nq, G, K), dtype=torch.int32, device="cuda")
+    qout = torch.empty((1, T, G * R, 128), dtype=torch.bfloat16, device="cuda")
+    qlse = torch.empty((1, T, G * R), dtype=torch.float32, device="cuda")
+
+    def calls():
+        msa.sparse_attn_backward(cfg, buf["q"], buf["k"], buf["v"], kv, sel, out, lse, dout,
+                                 q_start=qs, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        msa.index_topk_qblock(cfg, buf["qi"], buf["ki"], kv, qs, sel=qsel)
+        msa.sparse_attn_prefill_qblock(cfg, buf["q"], buf["k"], buf["v"], kv, qsel, q_start=qs,
+                                       out=qout, lse=qlse)
+
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        new = rand_inputs(1, T, T, G, R, seed=30 + rep)
+        for k_ in buf:
+            buf[k_].copy_(new[k_])
+        dout.copy_(rand_inputs(1, T, T, G, R, seed=40 + rep)["q"])
+        torch.cuda.synchronize()
+        say("graph replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (dq, dk, dv, qsel, qout, qlse)]
+        _ = torch.ones(1000, device="cuda").sum().item()  # eager work between replays
+        calls()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv", "qsel", "qout", "qlse"), got,
+                              (dq, dk, dv, qsel, qout, qlse)):
+            assert torch.equal(a, b), (rep, name)
