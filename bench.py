@@ -21,8 +21,9 @@ The 1M-token prefill in 32768-row chunks with E4M3 index data is timed too
 index data on the same caches. The 131072-token prefill also times the
 sparse branch's backward (msa_sparse_attn_backward), and both prefills are
 timed again with query-block-shared selections (msa_index_topk_qblock +
-msa_sparse_attn_prefill_qblock). Prefill legs report the minimum and the
-median over five timed steps after one warm-up.
+msa_sparse_attn_prefill_qblock), and the index projections of its tokens
+(msa_index_project, hidden size 6144 as a stand-in). Prefill legs report the
+minimum and the median over five timed steps after one warm-up.
 
 Back-to-back steps re-read the same caches, so part of a working set that
 fits the 256 MB last-level cache may be served from it; each decode leg also
@@ -459,6 +460,41 @@ def run_prefill(torch, msa, w, steps=5, warmup=1, cpu_baseline=False):
     return res
 
 
+def run_projection(torch, msa, M=131072, h=6144, G=4, steps=5, warmup=1):
+    """Index projections (msa_index_project) for the 131072 tokens of the
+    prefill: hidden [M, h] x w[(G+1)*dI, h]^T, bf16 in and out. The pages give
+    no hidden size; 6144 is a stand-in."""
+    import numpy as np
+    import msa_synth as ms
+    hid = torch.empty((M, h), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty(((G + 1) * 128, h), dtype=torch.bfloat16, device="cuda")
+    hh = ms.fill_normal_bf16(np.empty((M, h), np.uint16), 0x4D534150)
+    hid.copy_(torch.from_numpy(hh.view(np.int16)).view(torch.bfloat16))
+    wh = ms.fill_normal_bf16(np.empty(((G + 1) * 128, h), np.uint16), 0x4D534151)
+    w.copy_(torch.from_numpy(wh.view(np.int16)).view(torch.bfloat16) / float(np.sqrt(h)))
+    del hh, wh
+    cfg = msa.Config(num_kv_groups=G, heads_per_group=8, topk=16)
+    q, k = msa.index_project(cfg, hid, w)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    times = []
+    for s in range(warmup + steps):
+        ev[0].record()
+        msa.index_project(cfg, hid, w, q_idx=q, k_idx=k)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if s >= warmup:
+            times.append(ev[0].elapsed_time(ev[1]))
+    t = min(times)
+    flops = 2.0 * M * h * (G + 1) * 128
+    del hid, w, q, k
+    torch.cuda.empty_cache()
+    return dict(workload="index_projection_L131072_h6144", ms=round(t, 4),
+                ms_median=round(sorted(times)[len(times) // 2], 4), flops=flops,
+                tflops=round(flops / t / 1e9, 2),
+                frac_bf16_peak=round(flops / t / 1e9 / BF16_PEAK_TFLOPS, 4),
+                note="hidden size 6144 is a stand-in (the pages give none)")
+
+
 def qblock_rows(torch, sel_blk, q0, L):
     """Per-row selections [1, L, G, K] from query-block selections [1, NQ, G, K]
     (row i takes the selection of its block, slot (q0 + i)//128 - q0//128)."""
@@ -700,7 +736,8 @@ def main():
     if args.prefill_only:
         res = {"prefill": run_prefill(torch, msa, wl.workload(3), steps=args.steps,
                                       warmup=args.warmup),
-               "prefill_qblock": run_prefill_qblock(torch, msa, wl.workload(3))}
+               "prefill_qblock": run_prefill_qblock(torch, msa, wl.workload(3)),
+               "index_projection": run_projection(torch, msa)}
         if not args.no_chunked:
             res["chunked_prefill"] = run_chunked(torch, msa, wl.workload(5))
         print(json.dumps(res), flush=True)
@@ -760,6 +797,7 @@ def main():
         line["prefill"] = run_prefill(torch, msa, wl.workload(3),
                                       cpu_baseline=not args.no_cpu_baseline)
         line["prefill_qblock"] = run_prefill_qblock(torch, msa, wl.workload(3))
+        line["index_projection"] = run_projection(torch, msa)
     if not args.no_prefill and not args.no_chunked:
         line["chunked_prefill"] = run_chunked(torch, msa, wl.workload(5))
     print(json.dumps(line), flush=True)

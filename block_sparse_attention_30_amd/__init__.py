@@ -103,6 +103,8 @@ def load():
     lib.msa_sparse_attn_backward.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_backward.restype = ctypes.c_int
+    lib.msa_index_project.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp]
+    lib.msa_index_project.restype = ctypes.c_int
     lib.msa_qblock_slots.argtypes = [i32]
     lib.msa_qblock_slots.restype = i32
     for f in (lib.msa_index_topk, lib.msa_index_pool, lib.msa_sparse_attn_prefill,
@@ -391,6 +393,40 @@ def cache_append(cfg: Config, k_new, v_new, k_idx_new, pos0, k_cache, v_cache, k
         _check(load().msa_cache_append(ctypes.byref(cfg._c()), B, T, Nmax, _ptr(k_new),
                                        _ptr(v_new), _ptr(k_idx_new), _ptr(pos0), _ptr(k_cache),
                                        _ptr(v_cache), _ptr(k_idx), _stream(dev)))
+
+
+def index_project(cfg: Config, hidden, w, q_idx=None, k_idx=None, want_keys: bool = True):
+    """Index projections (msa_index_project): hidden [..., h] bf16 (M rows in
+    all) and w [(G+1)*dI, h] bf16 give q_idx [..., G, dI] and, with
+    want_keys, k_idx [..., dI] (bf16). Returns (q_idx, k_idx or None)."""
+    if not isinstance(hidden, torch.Tensor) or not hidden.is_cuda:
+        raise ValueError("hidden must be a GPU tensor (libmsa has no CPU path)")
+    dev = hidden.device
+    _need(w, "w", (torch.bfloat16,), 2, dev)
+    if hidden.dtype != torch.bfloat16 or not hidden.is_contiguous() or hidden.dim() < 1:
+        raise ValueError("hidden must be a contiguous bf16 tensor [..., h]")
+    h = hidden.shape[-1]
+    lead = tuple(hidden.shape[:-1])
+    M = 1
+    for n in lead:
+        M *= n
+    G, dI = cfg.num_kv_groups, cfg.index_dim
+    if tuple(w.shape) != ((G + 1) * dI, h):
+        raise ValueError("w must be [(G+1)*dI, h] = %s" % (((G + 1) * dI, h),))
+    if q_idx is None:
+        q_idx = torch.empty(lead + (G, dI), dtype=torch.bfloat16, device=dev)
+    if want_keys and k_idx is None:
+        k_idx = torch.empty(lead + (dI,), dtype=torch.bfloat16, device=dev)
+    if q_idx.dtype != torch.bfloat16 or not q_idx.is_contiguous() or \
+            tuple(q_idx.shape) != lead + (G, dI) or q_idx.device != dev:
+        raise ValueError("q_idx must be a contiguous bf16 tensor %s" % (lead + (G, dI),))
+    if k_idx is not None and (k_idx.dtype != torch.bfloat16 or not k_idx.is_contiguous() or
+                              tuple(k_idx.shape) != lead + (dI,) or k_idx.device != dev):
+        raise ValueError("k_idx must be a contiguous bf16 tensor %s" % (lead + (dI,),))
+    with _on_device(dev):
+        _check(load().msa_index_project(ctypes.byref(cfg._c()), M, h, _ptr(hidden), _ptr(w),
+                                        _ptr(q_idx), _ptr(k_idx), _stream(dev)))
+    return q_idx, k_idx
 
 
 def qblock_slots(T: int) -> int:

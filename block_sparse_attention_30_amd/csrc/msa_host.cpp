@@ -255,6 +255,27 @@ msa_status check_backward_args(const msa_config *cfg, int32_t B, int32_t T, int3
     return check_ws(workspace, ws_bytes, pw.total);
 }
 
+msa_status check_project_args(const msa_config *cfg, int32_t M, int32_t hidden_dim,
+                              const void *hidden, const void *w, const void *q_idx,
+                              const void *k_idx) {
+    msa_status s = check_config(cfg);
+    if (s != MSA_OK) return s;
+    if (cfg->index_dtype != MSA_BF16)
+        return fail(MSA_ERR_UNSUPPORTED,
+                    "index projections write bf16 index data (index_dtype must be MSA_BF16)");
+    if (M < 0) return fail(MSA_ERR_INVALID_ARG, "M must be >= 0");
+    if (hidden_dim < 64 || hidden_dim % 64 != 0)
+        return fail(MSA_ERR_UNSUPPORTED, "hidden_dim %d unsupported (need a multiple of 64)",
+                    hidden_dim);
+    if (M == 0) return MSA_OK;
+    if (!hidden || !w || !q_idx)
+        return fail(MSA_ERR_INVALID_ARG, "hidden, w and q_idx must not be NULL");
+    if (!aligned(hidden, 16) || !aligned(w, 16) || !aligned(q_idx, 16) ||
+        (k_idx && !aligned(k_idx, 16)))
+        return fail(MSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    return MSA_OK;
+}
+
 msa_status check_append_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                              const void *k_new, const void *v_new, const void *k_idx_new,
                              const int32_t *pos0, const void *k_cache, const void *v_cache,

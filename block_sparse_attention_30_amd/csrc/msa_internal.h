@@ -32,6 +32,9 @@ msa_status check_index_args(const msa_config *cfg, int32_t B, int32_t T, int32_t
 msa_status check_pool_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                            const void *q_idx, const void *k_idx, const int32_t *kv_lens,
                            const int32_t *q_start, const float *pooled);
+msa_status check_project_args(const msa_config *cfg, int32_t M, int32_t hidden_dim,
+                              const void *hidden, const void *w, const void *q_idx,
+                              const void *k_idx);
 msa_status check_append_args(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                              const void *k_new, const void *v_new, const void *k_idx_new,
                              const int32_t *pos0, const void *k_cache, const void *v_cache,

@@ -242,6 +242,29 @@ msa_status msa_cache_append(const msa_config *cfg, int32_t B, int32_t T, int32_t
                             const int32_t *pos0, void *k_cache, void *v_cache, void *k_idx,
                             void *stream);
 
+/*
+ * Index projections, the step ahead of the index branch: the Tencent
+ * article (§二) forms one lightweight index query per GQA group from each
+ * token's hidden state (n' x h x d -> n' x 1 x d), and the index keys it
+ * scores against come from the tokens in the same way. The pages give no
+ * weights, hidden size or quantisation; this call is the plain linear map:
+ * for M token rows,
+ *   q_idx[m, g, c] = sum_k hidden[m, k] * w[g*dI + c, k]      (g < G)
+ *   k_idx[m, c]    = sum_k hidden[m, k] * w[G*dI + c, k]
+ * accumulated in fp32 and rounded to bf16 (nearest even).
+ * Layouts: hidden [M, hidden_dim] bf16; w [(G+1)*dI, hidden_dim] bf16 (the G
+ * index-query projections, then the index-key projection, one output feature
+ * per row); q_idx [M, G, dI] bf16 (for B sequences of T rows: [B, T, G, dI],
+ * the layout msa_index_topk reads); k_idx [M, dI] bf16, nullable (then only
+ * the queries are computed; msa_cache_append places new keys in the cache).
+ * hidden_dim must be a multiple of 64; cfg->index_dtype must be MSA_BF16
+ * (E4M3 index data need a quantisation the pages do not define:
+ * MSA_ERR_UNSUPPORTED). Needs no workspace.
+ */
+msa_status msa_index_project(const msa_config *cfg, int32_t M, int32_t hidden_dim,
+                             const void *hidden, const void *w, void *q_idx, void *k_idx,
+                             void *stream);
+
 /* Workspace bytes the named call needs for these shapes (0 if none); returns
  * (size_t)-1 for an invalid configuration. For MSA_WS_SPARSE_DECODE and
  * MSA_WS_DECODE, T is 1. */

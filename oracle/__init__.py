@@ -3,8 +3,8 @@
 ctypes front end of ``msa_oracle.c``: a plain fp64 statement of the method
 (index scoring, causal block max-pool, top-k, sparse softmax attention; plus
 textbook dense causal attention for invariants; the sparse branch's
-gradients for fixed selections), and ``cache_append``, the cache write of new
-tokens, in plain numpy. Only the tests, the smoke
+gradients for fixed selections), and in plain numpy ``cache_append``, the
+cache write of new tokens, and ``index_project``, the index projections. Only the tests, the smoke
 check and the benchmark's CPU-baseline leg may import this package; the GPU
 library never does, and the two share no code.
 
@@ -304,6 +304,42 @@ def cache_append(k_new, v_new, k_idx_new, pos0, k_cache, v_cache, k_idx):
                 v_cache[b, g, pos, :] = v_new[b, t, g, :]
             k_idx[b, pos, :] = k_idx_new[b, t, :]
     return k_cache, v_cache, k_idx
+
+
+def _bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) as float64: the top half of an fp32."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def _f64_to_bf16_bits(x) -> np.ndarray:
+    """float64 values rounded once to bf16 (8 significant bits, nearest, ties
+    to even) as bit patterns; the values here are finite and within the
+    normal bf16 range."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)                      # x = m * 2**e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # np.rint rounds ties to even
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def index_project(hidden, w, groups, index_dim=128):
+    """Index projections, the step ahead of the index branch (Tencent article,
+    section 二: one lightweight index query per GQA group from each token's
+    hidden state; the index keys from the tokens the same way): with hidden
+    [M, h] and w [(G+1)*dI, h] as bf16 bits, the exact sums
+      q[m, g, c] = sum_k hidden[m, k] * w[g*dI + c, k]     (g < G)
+      k[m, c]    = sum_k hidden[m, k] * w[G*dI + c, k]
+    in float64 (a matmul), and the same rounded once to bf16 bits.
+    Returns (q [M,G,dI] float64, k [M,dI] float64, q bits, k bits)."""
+    h64 = _bf16_bits_to_f64(hidden)
+    w64 = _bf16_bits_to_f64(w)
+    G, dI = groups, index_dim
+    if w64.shape != ((G + 1) * dI, h64.shape[-1]):
+        raise ValueError("w must be [(G+1)*dI, h]")
+    c = h64 @ w64.T                          # [M, (G+1)*dI]
+    q = c[:, :G * dI].reshape(-1, G, dI)
+    k = c[:, G * dI:]
+    return q, k, _f64_to_bf16_bits(q), _f64_to_bf16_bits(k)
 
 
 def _threads() -> int:

@@ -576,11 +576,51 @@ def pin_backward_dense_autograd(orc, seed=10):
     assert np.allclose(dv[0], v.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
+def pin_index_project(orc, seed=11):
+    """Index projections against values the linear map fixes: one-hot weight
+    rows copy one hidden element each (so every output is a known input bit
+    pattern, whatever the head), constant weights per head give h times the
+    head's constant (the head order: G index queries, then the index key),
+    and a sum that lies exactly halfway between two bf16 values rounds to the
+    even one."""
+    import oracle
+    b1 = lambda x: int(np.asarray(bf16(x)).reshape(-1)[0])   # one bf16 bit pattern
+    rng = np.random.default_rng(seed)
+    G, dI, h, M = 3, 8, 16, 5
+    hid = bf16(rng.standard_normal((M, h)))
+    pick = rng.integers(0, h, size=(G + 1) * dI)
+    w = np.zeros(((G + 1) * dI, h), np.uint16)
+    w[np.arange((G + 1) * dI), pick] = 0x3F80               # 1.0
+    q, k, qb, kb = oracle.index_project(hid, w, G, dI)
+    want = hid[:, pick]                                       # [M, (G+1)*dI] bits
+    assert np.array_equal(qb.reshape(M, G * dI), want[:, :G * dI])
+    assert np.array_equal(kb, want[:, G * dI:])
+    # Constant weights per head: head g (g = G is the index key) uses 2^-(g+1).
+    ones = np.full((M, h), 0x3F80, np.uint16)
+    wc = np.concatenate([np.full((dI, h), b1(2.0 ** -(g + 1)), np.uint16)
+                         for g in range(G + 1)])
+    q, k, qb, kb = oracle.index_project(ones, wc, G, dI)
+    for g in range(G):
+        assert np.all(q[:, g, :] == h * 2.0 ** -(g + 1)), g
+    assert np.all(k == h * 2.0 ** -(G + 1))
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: it rounds to 1.0 (even);
+    # 1 + 3 * 2^-8 rounds up to 1 + 2^-6.
+    hv = np.zeros((2, h), np.uint16)
+    hv[0, 0], hv[0, 1] = 0x3F80, b1(2.0 ** -8)
+    hv[1, 0], hv[1, 1] = 0x3F80, b1(3 * 2.0 ** -8)
+    wt = np.zeros(((G + 1) * dI, h), np.uint16)
+    wt[:, 0] = wt[:, 1] = 0x3F80
+    q, k, qb, kb = oracle.index_project(hv, wt, G, dI)
+    assert np.all(qb[0] == 0x3F80) and np.all(kb[0] == 0x3F80)
+    assert np.all(qb[1] == b1(1 + 2.0 ** -6)) and np.all(q[1] == 1 + 3 * 2.0 ** -8)
+
+
 ALL_PINS = [pin_decoders, pin_hand_example_selection, pin_hand_example_attention,
             pin_hand_example_variants, pin_brute_force_selection,
             pin_token_level_and_single_block, pin_selection_invariants, pin_sparse_vs_numpy,
             pin_attention_invariants, pin_mixed_lengths_and_stride, pin_cache_append,
-            pin_qblock_selection, pin_backward_finite_differences, pin_backward_dense_autograd]
+            pin_qblock_selection, pin_backward_finite_differences, pin_backward_dense_autograd,
+            pin_index_project]
 
 
 def run_all(orc):

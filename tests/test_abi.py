@@ -33,7 +33,7 @@ def test_header_declares_the_three_entry_points():
     for n in ("msa_index_topk", "msa_index_pool", "msa_sparse_attn_prefill",
               "msa_sparse_attn_decode", "msa_decode", "msa_cache_append",
               "msa_index_topk_qblock", "msa_sparse_attn_prefill_qblock", "msa_qblock_slots",
-              "msa_sparse_attn_backward",
+              "msa_sparse_attn_backward", "msa_index_project",
               "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_version"):
         assert n in names
 
@@ -254,6 +254,29 @@ def test_workspace_sizes_follow_shapes(lib):
     # (sequence, group)
     dd = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 3)
     assert a + d <= dd <= a + d + 16 * 4 * 4 + 256 and dd % 256 == 0
+
+
+def test_index_project_validation(lib):
+    c = cfg()
+
+    def call(M=300, h=256, **kw):
+        a = dict(hid=FAKE, w=FAKE, q=FAKE, k=FAKE)
+        a.update(kw)
+        return lib.msa_index_project(ctypes.byref(c), M, h, a["hid"], a["w"], a["q"], a["k"],
+                                     None)
+
+    assert call(M=0) == OK                                # nothing to compute
+    for name in ("hid", "w", "q"):
+        assert call(**{name: None}) == INVALID, name
+    for name in ("hid", "w", "q", "k"):
+        assert call(**{name: FAKE_MIS}) == INVALID, name
+    assert call(M=-1) == INVALID
+    assert call(h=0) == UNSUPPORTED and call(h=100) == UNSUPPORTED
+    assert lib.msa_index_project(ctypes.byref(cfg(index_dtype=msa.FP8_E4M3)), 8, 64, FAKE, FAKE, FAKE,
+                                 FAKE, None) == UNSUPPORTED
+    assert b"bf16" in lib.msa_last_error()
+    assert lib.msa_index_project(ctypes.byref(cfg(index_dim=64)), 8, 64, FAKE, FAKE, FAKE,
+                                 FAKE, None) == UNSUPPORTED
 
 
 def test_python_binding_rejects_cpu_tensors():
