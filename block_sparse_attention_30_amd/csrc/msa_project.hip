@@ -115,6 +115,17 @@ __global__ __launch_bounds__(kPjWaves * 64, 1) void idx_proj_kernel(
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) acc[t][u] = mfma32(a[ks][t], bt[ks][u], acc[t][u]);
+        // Interleave: the first step's four operand reads, then one MFMA per
+        // read of the next steps' operands.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     // acc[t][u] lane l: token tw + 32u + (l & 31), features
     // fw + 32t + 8*(i>>2) + 4*(l>>5) + (i&3): four consecutive features per
