@@ -879,9 +879,9 @@ __global__ __launch_bounds__(512, 1) void qb_attn_kernel(
         const unsigned char *v_lds = k_lds + S * 256;
         // S^T: key tile kt x 16 columns; lane holds column col, keys kt*16 + 4*kg + r.
         f32x4 sacc[kPfNq][8];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
-            if (kt % 2 == 0) __builtin_amdgcn_sched_barrier(0);
             u32x4 ka[4];
             const int row = kt * 16 + col;
 #pragma unroll
@@ -895,6 +895,16 @@ __global__ __launch_bounds__(512, 1) void qb_attn_kernel(
                 sacc[nq][kt] = acc;
             }
         }
+        // Reads run two key tiles ahead of the products.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int i = 0; i < 24; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        __builtin_amdgcn_sched_barrier(0);
         // Online softmax across blocks (log2 domain). Only the query block's
         // own key block reaches past a row's position (a uniform branch). The
         // reference m2 moves only when a column's block max exceeds it by more
@@ -947,13 +957,13 @@ __global__ __launch_bounds__(512, 1) void qb_attn_kernel(
         }
         // O^T += V^T x P^T (as in pf_attn_kernel, swizzled rows): lane (col, kg)
         // accumulates O[column col][d = dt*16 + 4*kg + r].
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < S / 32; ++c) {
             const int rlo = c * 32 + 4 * kg + (col >> 2);  // rhi = rlo + 16, same swizzle
             const int lp = (col & 3) >> 1, within = (col & 1) * 8;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                if (dt % 4 == 0) __builtin_amdgcn_sched_barrier(0);
                 const int off = qb_swz(rlo, dt * 2 + lp) + within;
                 const u32x2 lo = lds_read_tr16(v_lds + off);
                 const u32x2 hi = lds_read_tr16(v_lds + off + 16 * 256);
@@ -962,6 +972,16 @@ __global__ __launch_bounds__(512, 1) void qb_attn_kernel(
                 for (int nq = 0; nq < kPfNq; ++nq) o[nq][dt] = mfma16(as_bf16x8(vbv), pa[nq][c], o[nq][dt]);
             }
         }
+        // Reads run four d-tiles ahead of the products.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int i = 0; i < 56; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
         // The next block has landed (this wave's runs) and every wave is done
         // with this block's buffer.
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
