@@ -90,14 +90,14 @@ def _probe_lib():
     lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_30_amd", "libmsa_probe.so"))
     lib.msa_probe_stream_read.restype = ctypes.c_int
     lib.msa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                          ctypes.c_void_p, ctypes.c_void_p]
+                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
-def _stream_read(torch, lib, buf, wgs, sink):
+def _stream_read(torch, lib, buf, wgs, sink, nontemporal=0):
     import ctypes
     rc = lib.msa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), wgs,
-                                   ctypes.c_void_p(sink.data_ptr()),
+                                   nontemporal, ctypes.c_void_p(sink.data_ptr()),
                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     if rc != 0:
         raise RuntimeError("stream-read probe failed: %d" % rc)
@@ -680,17 +680,18 @@ def copy_calibration(torch, mib=512, reps=5):
 
 
 def read_ceiling(torch, mib=512, reps=20):
-    """The HBM read ceiling measured live: a plain streaming read of `mib` MiB
+    """The HBM read ceiling measured live: a streaming read of `mib` MiB
     (16-byte loads, nothing stored) from the benchmark's probe library, best
-    of two workgroup counts, back-to-back launches between two events."""
+    of plain and nontemporal loads and of two workgroup counts, back-to-back
+    launches between two events."""
     lib = _probe_lib()
     nbytes = mib << 20
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
     best = 0.0
-    for wgs in (2048, 16384):
+    for nt, wgs in ((0, 2048), (0, 16384), (1, 2048), (1, 16384)):
         def launch():
-            _stream_read(torch, lib, buf, wgs, sink)
+            _stream_read(torch, lib, buf, wgs, sink, nt)
         for _ in range(3):
             launch()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -782,8 +783,9 @@ def main():
     ceiling = read_ceiling(torch)
     line["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling, 4)
     line["read_ceiling"] = {"value": ceiling, "unit": "GB/s",
-                            "what": "plain streaming read of 512 MiB (16-byte loads, best of "
-                                    "2048 and 16384 workgroups), measured in this run"}
+                            "what": "streaming read of 512 MiB (16-byte loads, best of plain and "
+                                    "nontemporal loads and of 2048 and 16384 workgroups), "
+                                    "measured in this run"}
     if args.calibrate_copy:
         line["copy_calibration"] = copy_calibration(torch)
     if not args.no_cpu_baseline:

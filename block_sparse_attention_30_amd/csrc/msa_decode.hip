@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 #pragma unroll
         for (int i = 0; i < Geo::kLoads; ++i) {
             const int tok = t0 + Geo::kRowsPerLoad * i + lrow;
-            v[i] = tok < kv ? ld16(kbytes + (size_t)tok * Geo::kRowBytes + lcol) : zero4;
+            v[i] = tok < kv ? ld16_stream(kbytes + (size_t)tok * Geo::kRowBytes + lcol) : zero4;
         }
     };
     load_step(0);
@@ -268,7 +268,8 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     WaveAttn st;
     wave_attn_init(st);
     if (c < L.nblk * 4) {
-        attend_chunk(st, qf, k_cache + ((size_t)b * G + g) * Nmax * D,
+        // Each kept chunk is read by this wave alone: streaming loads.
+        attend_chunk<true>(st, qf, k_cache + ((size_t)b * G + g) * Nmax * D,
                      v_cache + ((size_t)b * G + g) * Nmax * D, L.blocks[c >> 2] * S + (c & 3) * 32,
                      p, scale_log2, L.vrows + wave * kVWave, lane);
     }

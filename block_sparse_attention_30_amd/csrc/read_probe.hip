@@ -11,8 +11,10 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Workgroup w reads 16-byte words [w * per_wg, (w + 1) * per_wg), eight loads
-// per thread in flight; a value is written only if the xor of everything read
-// equals a marker, so the loads are kept but nothing is stored in practice.
+// per thread in flight, plain or nontemporal loads; a value is written only if
+// the xor of everything read equals a marker, so the loads are kept but
+// nothing is stored in practice.
+template <bool NT>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restrict__ p,
                                                           size_t per_wg, unsigned *sink) {
     constexpr int U = 8;
@@ -23,7 +25,8 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restric
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t j = i + (size_t)u * 256;
-            v[u] = j < per_wg ? base[j] : u32x4{0u, 0u, 0u, 0u};
+            if (j < per_wg) v[u] = NT ? __builtin_nontemporal_load(base + j) : base[j];
+            else v[u] = u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) acc ^= v[u];
@@ -37,13 +40,20 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restric
 extern "C" {
 
 // Reads `bytes` of `buf` (a multiple of 16 * wgs) with `wgs` workgroups on
-// `stream`; `sink` holds at least `wgs` uint32. Returns 0, or -1 on bad
-// arguments, or the HIP error code of the launch.
-int msa_probe_stream_read(const void *buf, size_t bytes, int wgs, void *sink, void *stream) {
+// `stream`, with nontemporal loads if `nontemporal` is nonzero; `sink` holds
+// at least `wgs` uint32. Returns 0, or -1 on bad arguments, or the HIP error
+// code of the launch.
+int msa_probe_stream_read(const void *buf, size_t bytes, int wgs, int nontemporal, void *sink,
+                          void *stream) {
     if (!buf || !sink || wgs <= 0 || bytes == 0 || bytes % (16 * (size_t)wgs) != 0) return -1;
     const size_t per_wg = bytes / 16 / (size_t)wgs;
-    stream_read_kernel<<<(unsigned)wgs, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
-        static_cast<const u32x4 *>(buf), per_wg, static_cast<unsigned *>(sink));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (nontemporal)
+        stream_read_kernel<true><<<(unsigned)wgs, 256, 0, st>>>(
+            static_cast<const u32x4 *>(buf), per_wg, static_cast<unsigned *>(sink));
+    else
+        stream_read_kernel<false><<<(unsigned)wgs, 256, 0, st>>>(
+            static_cast<const u32x4 *>(buf), per_wg, static_cast<unsigned *>(sink));
     return (int)hipGetLastError();
 }
 

@@ -295,10 +295,11 @@ def test_read_probe_loads_and_rejects_bad_arguments():
     probe = ctypes.CDLL(path)
     fn = probe.msa_probe_stream_read
     fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
-                   ctypes.c_void_p]
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
     dummy = ctypes.c_void_p(0x1000)
-    assert fn(None, 1 << 20, 64, dummy, None) == -1
-    assert fn(dummy, 1 << 20, 64, None, None) == -1
-    assert fn(dummy, 1 << 20, 0, dummy, None) == -1
-    assert fn(dummy, (1 << 20) + 16, 64, dummy, None) == -1   # not a multiple of 16 * wgs
+    for nt in (0, 1):
+        assert fn(None, 1 << 20, 64, nt, dummy, None) == -1
+        assert fn(dummy, 1 << 20, 64, nt, None, None) == -1
+        assert fn(dummy, 1 << 20, 0, nt, dummy, None) == -1
+        assert fn(dummy, (1 << 20) + 16, 64, nt, dummy, None) == -1   # not a multiple of 16 * wgs
