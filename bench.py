@@ -297,7 +297,7 @@ def run_decode_fp8_index(torch, msa, w, k, v, steps, warmup, nsets=8):
             "algorithmic_bytes_per_step": nbytes,
             "cold_cache_ms_per_step": round(ms_cold, 5),
             "cold_cache_GB/s": round(nbytes / (ms_cold * 1e-3) / 1e9, 2),
-            "idx_scan_kernel<true> (via msa_index_pool)": {
+            "idx_scan_kernel<true, false> (E4M3 keys, cached loads, via msa_index_pool)": {
                 "ms": round(ms_pool, 5), "bytes": scan_bytes,
                 "GB/s": round(scan_bytes / (ms_pool * 1e-3) / 1e9, 2)}}
 
@@ -773,7 +773,7 @@ def main():
                      "msa_decode_per_step_events_warm_min": round(res["events_min_ms"], 5),
                      "msa_decode_per_step_events_warm_median": round(res["events_median_ms"], 5)},
         "cold_cache_GB/s": round(nbytes / (res["cold_ms"] * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel<false> (bf16 keys, via msa_index_pool)",
+        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel<false, true> (bf16 keys, streaming loads, via msa_index_pool)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("idx_scan_kernel", w.name),

@@ -44,6 +44,9 @@ namespace {
 // bf16 keys use four 16x16x32 bf16 MFMAs per 16-token tile; OCP E4M3 keys one
 // 16x16x128 f8f6f4 MFMA (unit scales). Index data are small integers in
 // practice, so both sums are exact in fp32.
+// MI355X's last-level (Infinity) cache, 256 MiB.
+constexpr int64_t kLastLevelCacheBytes = 256ll << 20;
+
 template <bool F8>
 struct ScanGeom {
     static constexpr int kRowBytes = DI * (F8 ? 1 : 2);     // one token's key
@@ -56,7 +59,7 @@ struct ScanGeom {
     static constexpr int kWaveLds = kStep * kRow;
 };
 
-template <bool F8>
+template <bool F8, bool Stream>
 __global__ __launch_bounds__(256) void idx_scan_kernel(
     const unsigned char *__restrict__ q_idx, const unsigned char *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
@@ -119,7 +122,8 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 #pragma unroll
         for (int i = 0; i < Geo::kLoads; ++i) {
             const int tok = t0 + Geo::kRowsPerLoad * i + lrow;
-            v[i] = tok < kv ? ld16_stream(kbytes + (size_t)tok * Geo::kRowBytes + lcol) : zero4;
+            const unsigned char *src = kbytes + (size_t)tok * Geo::kRowBytes + lcol;
+            v[i] = tok < kv ? (Stream ? ld16_stream(src) : ld16(src)) : zero4;
         }
     };
     load_step(0);
@@ -460,12 +464,17 @@ msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nm
     if (rows <= msa::kScanMaxRows) {
         const int64_t per_wg = scan_blocks_per_wg(B, nb_max);
         const dim3 grid((unsigned)((nb_max + per_wg - 1) / per_wg), (unsigned)B);
+        // Index keys that do not fit the last-level cache are streamed past
+        // it (nontemporal loads); a cache that fits stays there between calls.
+        const bool stream = (int64_t)B * Nmax * DI * (f8 ? 1 : 2) > kLastLevelCacheBytes;
+        auto launch = [&](auto kern) {
+            kern<<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G, Nmax, nb_max,
+                                       (int)per_wg, zero_counters);
+        };
         if (f8)
-            idx_scan_kernel<true><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
-                                                        Nmax, nb_max, (int)per_wg, zero_counters);
+            stream ? launch(idx_scan_kernel<true, true>) : launch(idx_scan_kernel<true, false>);
         else
-            idx_scan_kernel<false><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
-                                                         Nmax, nb_max, (int)per_wg, zero_counters);
+            stream ? launch(idx_scan_kernel<false, true>) : launch(idx_scan_kernel<false, false>);
         return launch_status("decode index kernel");
     }
     return launch_prefill_pooled(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start, pooled, nb_max,
