@@ -742,8 +742,10 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
                 (has ? reinterpret_cast<unsigned char *>(part_o + (slot * R + col % R) * D)
                      : trash + (col % R) * D * 2) +
                 16 * (2 * (kg & 1) + (kg >> 1));
+            // Written once, read once by the merge: streaming (nontemporal) stores.
 #pragma unroll
-            for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4 *>(op + 64 * j) = w4[j];
+            for (int j = 0; j < 4; ++j)
+                __builtin_nontemporal_store(w4[j], reinterpret_cast<u32x4 *>(op + 64 * j));
         }
     };
     int entA[kPfNq], pcolA[kPfNq], entB[kPfNq], pcolB[kPfNq];
