@@ -28,8 +28,8 @@ minimum and the median over five timed steps after one warm-up.
 Back-to-back steps re-read the same caches, so part of a working set that
 fits the 256 MB last-level cache may be served from it; each decode leg also
 reports a cold-cache time (a 1 GiB read between steps, per-step events). A
-plain streaming read of 512 MiB, timed in the same run, gives the measured HBM
-read ceiling next to the published 8 TB/s.
+streaming read of 512 MiB (best of plain and nontemporal loads), timed in the
+same run, gives the measured HBM read ceiling next to the published 8 TB/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-chunked]
 """

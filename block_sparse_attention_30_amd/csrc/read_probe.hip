@@ -1,5 +1,5 @@
-// A plain streaming read of a device buffer, for the benchmark's measured
-// HBM read ceiling (the bandwidth a kernel that only loads can reach on this
+// A streaming read of a device buffer (plain or nontemporal loads), for the
+// benchmark's measured HBM read ceiling (the bandwidth a kernel that only loads can reach on this
 // GPU, to set beside the published peak). Not part of the MSA library: it is
 // built into its own shared object and loaded by the benchmark only.
 #include <hip/hip_runtime.h>
