@@ -211,6 +211,7 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
 #pragma unroll
         for (int rp = 0; rp < 2; ++rp) {
             f32x16 acc[2][2] = {};
+            if constexpr (!F8) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks) {
 #pragma unroll
@@ -232,6 +233,19 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
                         acc[h2][1] = mfma32(a, as_bf16x8(qb[1][ks][0]), acc[h2][1]);
                     }
                 }
+            }
+            // bf16: the row tiles' operand reads run ahead of the MFMAs, two
+            // products per read after the first four reads.
+            if constexpr (!F8) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                for (int i = 0; i < 2 * kKs - 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
