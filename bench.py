@@ -25,6 +25,13 @@ msa_sparse_attn_prefill_qblock), and the index projections of its tokens
 (msa_index_project, hidden size 6144 as a stand-in). Prefill legs report the
 minimum and the median over five timed steps after one warm-up.
 
+The 4 x 1048576-token decode (uniform lengths, then mixed lengths {256k,
+512k, 768k, 1M} on the same caches) is timed the same way, each against the
+70%-of-HBM-peak step time; the 4096-token one-group prefill reports latency
+(it is too small to fill the chip); the 1M chunked prefill times five passes
+of its 32 chunks after one untimed pass. A loop of independent MFMAs gives
+the measured bf16 and fp8 matrix ceilings next to the published peaks.
+
 Back-to-back steps re-read the same caches, so part of a working set that
 fits the 256 MB last-level cache may be served from it; each decode leg also
 reports a cold-cache time (a 1 GiB read between steps, per-step events). A
@@ -32,6 +39,7 @@ streaming read of 512 MiB (best of plain and nontemporal loads), timed in the
 same run, gives the measured HBM read ceiling next to the published 8 TB/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-chunked]
+       [--decode-only] [--prefill-only] [--no-cpu-baseline] [--calibrate-copy]
 """
 from __future__ import annotations
 
@@ -75,8 +83,9 @@ def np_view(t):
 
 
 def decode_bytes(w):
-    """Algorithmic HBM bytes of one decode step (every index key once, kept blocks once)."""
-    k_idx = w.B * w.Nmax * 128 * (1 if w.index_fp8 else 2)
+    """Algorithmic HBM bytes of one decode step (every index key of every
+    sequence once, kept blocks once, queries, outputs and selections)."""
+    k_idx = sum(w.kv_lens) * 128 * (1 if w.index_fp8 else 2)
     kept = 0
     for n in w.kv_lens:  # workload lengths are whole blocks, so each kept block is 128 keys
         kept += w.G * min(w.topk, (n - 1) // 128 + 1) * 128 * 128 * 2 * 2
@@ -302,29 +311,73 @@ def run_decode_fp8_index(torch, msa, w, k, v, steps, warmup, nsets=8):
                 "GB/s": round(scan_bytes / (ms_pool * 1e-3) / 1e9, 2)}}
 
 
-def cpu_baseline_decode(w, host, budget_rows=None):
-    """The oracle (as written, untuned) on the first query set of the decode batch."""
+# Host threads one GPU's job may use on a shared machine (the host's cores are
+# split between its GPUs); the oracle uses all of them.
+CPU_SHARE = 16
+
+
+def host_cpu():
+    """CPU model, logical CPUs of the host, CPUs this process may run on, and
+    the threads the oracle uses: every CPU of the process, at most the one-GPU
+    share of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return dict(cpu_model=model, host_logical_cpus=os.cpu_count() or 1,
+                process_cpus=avail, threads=max(1, min(avail, CPU_SHARE)))
+
+
+def cpu_baseline_decode(w, sets, budget_rows=None):
+    """The oracle (as written, untuned) on the decode batch: every row of the
+    first query sets, as many sets as give every host thread a row (the oracle
+    threads over rows)."""
     import numpy as np
     import oracle
     orc = oracle.default()
     ocfg = oracle.Config(groups=w.G, heads_per_group=w.R, topk=w.topk,
                          index_dtype=oracle.E4M3 if w.index_fp8 else oracle.BF16)
+    cpu = host_cpu()
+    nsets = max(1, min(len(sets), -(-cpu["threads"] // w.B)))
     rows = w.B if budget_rows is None else min(budget_rows, w.B)
-    threads = max(1, min(os.cpu_count() or 1, 16, rows))
-    kv = np.array(w.kv_lens[:rows], np.int32)
+    threads = max(1, min(cpu["threads"], rows * nsets))
+    # The query sets stacked as one batch over the same caches: the caches
+    # are repeated by view (sequence b of set s reads cache b).
+    host = sets[0]
+    kv1 = np.array(w.kv_lens[:rows], np.int32)
+    kv = np.tile(kv1, nsets)
     qs = kv - 1
     sl = slice(0, rows)
+    q = np.concatenate([st["q"][sl] for st in sets[:nsets]])
+    qi = np.concatenate([st["qi"][sl] for st in sets[:nsets]])
+    ki = np.broadcast_to(host["ki"][sl][None], (nsets,) + host["ki"][sl].shape).reshape(
+        (nsets * rows,) + host["ki"].shape[1:])
+    k = np.broadcast_to(host["k"][sl][None], (nsets,) + host["k"][sl].shape).reshape(
+        (nsets * rows,) + host["k"].shape[1:])
+    v = np.broadcast_to(host["v"][sl][None], (nsets,) + host["v"][sl].shape).reshape(
+        (nsets * rows,) + host["v"].shape[1:])
     t0 = time.perf_counter()
-    sel, _ = orc.index_topk(ocfg, host["qi"][sl], host["ki"][sl], kv, qs, threads=threads)
-    orc.sparse_attn(ocfg, host["q"][sl], host["k"][sl], host["v"][sl], kv, qs, sel,
-                    threads=threads)
+    sel, _ = orc.index_topk(ocfg, qi, ki, kv, qs, threads=threads)
+    orc.sparse_attn(ocfg, q, k, v, kv, qs, sel, threads=threads)
     dt = time.perf_counter() - t0
     sub = w.__class__(**{**w.__dict__, "B": rows, "kv_lens": list(w.kv_lens[:rows])})
     nbytes, _ = decode_bytes(sub)
-    return dict(value=round(nbytes / dt / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
-                sample="%d of %d decode rows (all 4 groups, 32 heads, %d-token contexts): "
-                       "index top-k + sparse attention, %.2f s wall" %
-                       (rows, w.B, w.Nmax, dt))
+    res = dict(value=round(nsets * nbytes / dt / 1e9, 4), unit="GB/s", cores=threads,
+               kind="oracle",
+               sample="%d decode steps (query sets) of %d rows (all %d groups, %d heads, "
+                      "%d-token contexts): index top-k + sparse attention, %.2f s wall" %
+                      (nsets, rows, w.G, w.H, w.Nmax, dt))
+    res.update({k_: v_ for k_, v_ in cpu.items() if k_ != "threads"})
+    return res
 
 
 def sparse_work(torch, w, sel, q0):
@@ -363,16 +416,19 @@ def cpu_baseline_prefill(w, host, n_rows=128, seed=0x4D534143):
     rows = np.stack([np.zeros_like(rows_i), rows_i], axis=1).astype(np.int32)
     kv = np.array(w.kv_lens, np.int32)
     qs = np.array(w.q_start, np.int32)
-    threads = max(1, min(os.cpu_count() or 1, 16))
+    cpu = host_cpu()
+    threads = cpu["threads"]
     t0 = time.perf_counter()
     sel, _ = orc.index_topk(ocfg, host["qi"], host["ki"], kv, qs, rows=rows, threads=threads)
     orc.sparse_attn(ocfg, host["q"], host["k"], host["v"], kv, qs, sel, rows=rows,
                     threads=threads)
     dt = time.perf_counter() - t0
-    return dict(value=round(n_rows / dt, 2), unit="tokens/s", cores=threads, kind="oracle",
-                sample="%d uniform random rows of the %d-token prefill (all groups and heads): "
-                       "index top-k + sparse attention, %.2f s wall; the rate stands for the "
-                       "whole prefill (extrapolated)" % (n_rows, w.T, dt))
+    res = dict(value=round(n_rows / dt, 2), unit="tokens/s", cores=threads, kind="oracle",
+               sample="%d uniform random rows of the %d-token prefill (all groups and heads): "
+                      "index top-k + sparse attention, %.2f s wall; the rate stands for the "
+                      "whole prefill (extrapolated)" % (n_rows, w.T, dt))
+    res.update({k_: v_ for k_, v_ in cpu.items() if k_ != "threads"})
+    return res
 
 
 def run_prefill(torch, msa, w, steps=5, warmup=1, cpu_baseline=False):
@@ -550,12 +606,12 @@ def run_prefill_qblock(torch, msa, w, steps=5, warmup=1):
     return res
 
 
-def run_chunked(torch, msa, w):
+def run_chunked(torch, msa, w, passes=5):
     """The 1M-token prefill in 32768-row chunks with E4M3 index data: every
     chunk runs msa_index_topk and msa_sparse_attn_prefill over the cache of
     the tokens before and in it. Inputs are generated once and resident in
-    HBM; one untimed pass, then one timed pass of all chunks."""
-    import numpy as np
+    HBM; one untimed pass, then `passes` timed passes of all 32 chunks (each
+    call between its own events); min and median over the passes."""
     from msa_synth import workloads as wl
     t0 = time.time()
     alloc = pinned(torch)
@@ -568,69 +624,205 @@ def run_chunked(torch, msa, w):
     qi = qi.view(torch.float8_e4m3fn)
     ki = ki.view(torch.float8_e4m3fn)
     C, L = w.chunk, w.Nmax
+    nch = L // C
     cfg = msa.Config(num_kv_groups=w.G, heads_per_group=w.R, topk=w.topk, index_dtype=msa.FP8_E4M3)
     ws_p = msa.workspace(cfg, 1, C, L, msa.WS_SPARSE_PREFILL)
     sel = torch.empty((1, C, w.G, w.topk), dtype=torch.int32, device="cuda")
-    out = torch.empty((1, C, w.H, 128), dtype=torch.bfloat16, device="cuda")
-    lens = [torch.tensor([(c + 1) * C], dtype=torch.int32, device="cuda") for c in range(L // C)]
-    starts = [torch.tensor([c * C], dtype=torch.int32, device="cuda") for c in range(L // C)]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L // C)]
-    f_att = 0.0
-    for rep in range(2):
-        timed_pass = rep == 1
-        for c in range(L // C):
-            rows = slice(c * C, (c + 1) * C)
-            if timed_pass:
-                ev[c][0].record()
-            msa.index_topk(cfg, qi[:, rows], ki, lens[c], starts[c], sel=sel)
-            if timed_pass:
-                ev[c][1].record()
-            msa.sparse_attn_prefill(cfg, q[:, rows], k, v, lens[c], sel, q_start=starts[c],
-                                    out=out, workspace=ws_p)
-            if timed_pass:
-                ev[c][2].record()
-                torch.cuda.synchronize()
-                f_att += sparse_work(torch, w, sel, c * C)[0]
-        torch.cuda.synchronize()
-    ti = sum(e[0].elapsed_time(e[1]) for e in ev)
-    ta = sum(e[1].elapsed_time(e[2]) for e in ev)
-    # The same chunks with query-block-shared selections.
     selq = torch.empty((1, msa.qblock_slots(C), w.G, w.topk), dtype=torch.int32, device="cuda")
-    fq_att = 0.0
-    for rep in range(2):
-        timed_pass = rep == 1
-        for c in range(L // C):
-            rows = slice(c * C, (c + 1) * C)
-            if timed_pass:
+    out = torch.empty((1, C, w.H, 128), dtype=torch.bfloat16, device="cuda")
+    lens = [torch.tensor([(c + 1) * C], dtype=torch.int32, device="cuda") for c in range(nch)]
+    starts = [torch.tensor([c * C], dtype=torch.int32, device="cuda") for c in range(nch)]
+
+    def one_variant(index_call, attn_call, sel_buf, rows_sel):
+        """Times `passes` passes after one untimed pass that also counts the
+        sparse flops of every chunk (the selections repeat from pass to pass)."""
+        f_att = 0.0
+        ti, ta = [], []
+        for rep in range(1 + passes):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nch)]
+            for c in range(nch):
+                rows = slice(c * C, (c + 1) * C)
                 ev[c][0].record()
-            msa.index_topk_qblock(cfg, qi[:, rows], ki, lens[c], starts[c], sel=selq)
-            if timed_pass:
+                index_call(qi[:, rows], lens[c], starts[c], sel_buf)
                 ev[c][1].record()
-            msa.sparse_attn_prefill_qblock(cfg, q[:, rows], k, v, lens[c], selq,
-                                           q_start=starts[c], out=out)
-            if timed_pass:
+                attn_call(q[:, rows], lens[c], starts[c], sel_buf)
                 ev[c][2].record()
-                torch.cuda.synchronize()
-                fq_att += sparse_work(torch, w, qblock_rows(torch, selq, c * C, C), c * C)[0]
-        torch.cuda.synchronize()
-    tqi = sum(e[0].elapsed_time(e[1]) for e in ev)
-    tqa = sum(e[1].elapsed_time(e[2]) for e in ev)
+                if rep == 0:
+                    torch.cuda.synchronize()
+                    f_att += sparse_work(torch, w, rows_sel(sel_buf, c), c * C)[0]
+            torch.cuda.synchronize()
+            if rep > 0:
+                ti.append(sum(e[0].elapsed_time(e[1]) for e in ev))
+                ta.append(sum(e[1].elapsed_time(e[2]) for e in ev))
+        return f_att, ti, ta
+
+    f_att, ti_l, ta_l = one_variant(
+        lambda qi_c, kv_c, qs_c, sb: msa.index_topk(cfg, qi_c, ki, kv_c, qs_c, sel=sb),
+        lambda q_c, kv_c, qs_c, sb: msa.sparse_attn_prefill(cfg, q_c, k, v, kv_c, sb,
+                                                             q_start=qs_c, out=out,
+                                                             workspace=ws_p),
+        sel, lambda sb, c: sb)
+    fq_att, tqi_l, tqa_l = one_variant(
+        lambda qi_c, kv_c, qs_c, sb: msa.index_topk_qblock(cfg, qi_c, ki, kv_c, qs_c, sel=sb),
+        lambda q_c, kv_c, qs_c, sb: msa.sparse_attn_prefill_qblock(cfg, q_c, k, v, kv_c, sb,
+                                                                    q_start=qs_c, out=out),
+        selq, lambda sb, c: qblock_rows(torch, sb, c * C, C))
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    ti, ta, tqi, tqa = min(ti_l), min(ta_l), min(tqi_l), min(tqa_l)
     f_idx = 2.0 * 128 * w.G * L * (L + 1) / 2
     qblock = dict(selection="query-block-shared (one top-16 per 128-row query block)",
                   index_ms=round(tqi, 2), sparse_ms=round(tqa, 2),
+                  index_ms_median=round(med(tqi_l), 2), sparse_ms_median=round(med(tqa_l), 2),
                   index_tflops=round(f_idx / tqi / 1e9, 2),
                   index_frac_fp8_peak=round(f_idx / tqi / 1e9 / FP8_PEAK_TFLOPS, 4),
                   sparse_tflops=round(fq_att / tqa / 1e9, 2),
                   sparse_frac_bf16_peak=round(fq_att / tqa / 1e9 / BF16_PEAK_TFLOPS, 4),
                   total_tflops=round((f_idx + fq_att) / (tqi + tqa) / 1e9, 2))
-    res = dict(workload=w.name, chunks=L // C, index_ms=round(ti, 2), sparse_ms=round(ta, 2),
+    res = dict(workload=w.name, chunks=nch, timed_passes=passes,
+               times_are="min over the timed passes (each the sum of its 32 chunks' calls)",
+               index_ms=round(ti, 2), sparse_ms=round(ta, 2),
+               index_ms_median=round(med(ti_l), 2), sparse_ms_median=round(med(ta_l), 2),
                index_tflops=round(f_idx / ti / 1e9, 2),
                index_frac_fp8_peak=round(f_idx / ti / 1e9 / FP8_PEAK_TFLOPS, 4),
+               sparse_flops=f_att,
                sparse_tflops=round(f_att / ta / 1e9, 2),
                sparse_frac_bf16_peak=round(f_att / ta / 1e9 / BF16_PEAK_TFLOPS, 4),
                total_tflops=round((f_idx + f_att) / (ti + ta) / 1e9, 2),
                note="index in E4M3 (mixed precision total)", qblock=qblock)
     del q, qi, k, v, ki, sel, selq, out, ws_p
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_decode_long(torch, msa, steps, warmup, nsets=8):
+    """The 4 x 1048576-token decode: uniform lengths, then the mixed lengths
+    {262144, 524288, 786432, 1048576} on the same caches (the mixed workload
+    has the same contents). For each: msa_decode back to back between two
+    events with eight query sets rotating, the same with a 1 GiB read between
+    steps (cold cache), and the index scan alone (msa_index_pool) against the
+    HBM peak."""
+    from msa_synth import workloads as wl
+    wu, wm = wl.workload(4), wl.workload(4, mixed=True)
+    t0 = time.time()
+    alloc = pinned(torch)
+    kh, vh, kih = wl.gen_caches(wu, alloc=alloc)
+    sets = [wl.gen_queries(wu, set_id=s, alloc=alloc) for s in range(nsets)]
+    log("1M decode inputs generated in %.1fs" % (time.time() - t0))
+    k, v, ki = to_dev(torch, kh), to_dev(torch, vh), to_dev(torch, kih)
+    qs = [(to_dev(torch, q), to_dev(torch, qi)) for q, qi in sets]
+    del kh, vh, kih, sets
+    cfg = msa.Config(num_kv_groups=wu.G, heads_per_group=wu.R, topk=wu.topk)
+    ws = msa.workspace(cfg, wu.B, 1, wu.Nmax, msa.WS_DECODE)
+    sel = torch.empty((wu.B, 1, wu.G, wu.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((wu.B, 1, wu.H, 128), dtype=torch.bfloat16, device="cuda")
+    nbm = -(-wu.Nmax // 128)
+    pooled = torch.full((wu.B, 1, wu.G, nbm), float("-inf"), dtype=torch.float32, device="cuda")
+
+    def back_to_back(fn):
+        for s in range(warmup):
+            fn(s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for s in range(steps):
+            fn(warmup + s)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    res = {}
+    for w in (wu, wm):
+        kv = torch.tensor(w.kv_lens, dtype=torch.int32, device="cuda")
+
+        def step(s):
+            msa.decode(cfg, qs[s % nsets][0], qs[s % nsets][1], ki, k, v, kv, sel=sel, out=out,
+                       workspace=ws)
+
+        ms_step = back_to_back(step)
+        per = []
+        ms_cold = cold_ms(torch, step, steps, warmup, per_step=per)
+        per.sort()
+        ms_pool = back_to_back(lambda s: msa.index_pool(cfg, qs[s % nsets][1], ki, kv,
+                                                        pooled=pooled))
+        nbytes, kidx_bytes = decode_bytes(w)
+        scan_bytes = (kidx_bytes + w.B * w.G * 128 * 2 +
+                      sum(w.G * (-(-n // 128)) * 4 for n in w.kv_lens))
+        target_ms = nbytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3
+        gbs = nbytes / (ms_step * 1e-3) / 1e9
+        res[w.name] = {
+            "ms_per_step": round(ms_step, 5), "GB/s": round(gbs, 2),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": nbytes,
+            "target_ms_at_70pct": round(target_ms, 5),
+            "meets_70pct": ms_step <= target_ms,
+            "cold_cache_ms_per_step": round(ms_cold, 5),
+            "cold_cache_min_ms": round(per[0], 5),
+            "cold_cache_median_ms": round(per[len(per) // 2], 5),
+            "cold_cache_GB/s": round(nbytes / (ms_cold * 1e-3) / 1e9, 2),
+            "idx_scan_kernel<false, true> (bf16 keys, streaming loads, via msa_index_pool)": {
+                "ms": round(ms_pool, 5), "bytes": scan_bytes,
+                "GB/s": round(scan_bytes / (ms_pool * 1e-3) / 1e9, 2),
+                "frac_hbm_peak": round(scan_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    del k, v, ki, qs, ws, sel, out, pooled
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_small_prefill(torch, msa, steps=20, warmup=3):
+    """The 4096-token prefill with one group of two heads: latency of
+    msa_index_topk, msa_sparse_attn_prefill and the pair, and of the
+    last-token decode step (msa_decode with the 4096-token cache), each call
+    between its own events; min and median over `steps`."""
+    from msa_synth import workloads as wl
+    w = wl.workload(1)
+    kh, vh, kih = wl.gen_caches(w)
+    qh, qih = wl.gen_queries(w)
+    k, v, ki = (torch.from_numpy(a.view("int16")).cuda().view(torch.bfloat16)
+                for a in (kh, vh, kih))
+    q, qi = (torch.from_numpy(a.view("int16")).cuda().view(torch.bfloat16) for a in (qh, qih))
+    kv = torch.tensor(w.kv_lens, dtype=torch.int32, device="cuda")
+    qs = torch.tensor(w.q_start, dtype=torch.int32, device="cuda")
+    cfg = msa.Config(num_kv_groups=w.G, heads_per_group=w.R, topk=w.topk)
+    ws_i = msa.workspace(cfg, w.B, w.T, w.Nmax, msa.WS_INDEX_TOPK)
+    ws_p = msa.workspace(cfg, w.B, w.T, w.Nmax, msa.WS_SPARSE_PREFILL)
+    ws_d = msa.workspace(cfg, w.B, 1, w.Nmax, msa.WS_DECODE)
+    sel = torch.empty((w.B, w.T, w.G, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.T, w.H, 128), dtype=torch.bfloat16, device="cuda")
+    dsel = torch.empty((w.B, 1, w.G, w.topk), dtype=torch.int32, device="cuda")
+    dout = torch.empty((w.B, 1, w.H, 128), dtype=torch.bfloat16, device="cuda")
+    q_last, qi_last = q[:, -1:].contiguous(), qi[:, -1:].contiguous()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    t_idx, t_att, t_pair, t_dec = [], [], [], []
+    for s in range(warmup + steps):
+        ev[0].record()
+        msa.index_topk(cfg, qi, ki, kv, qs, sel=sel, workspace=ws_i)
+        ev[1].record()
+        msa.sparse_attn_prefill(cfg, q, k, v, kv, sel, q_start=qs, out=out, workspace=ws_p)
+        ev[2].record()
+        torch.cuda.synchronize()
+        ev[3].record()
+        msa.decode(cfg, q_last, qi_last, ki, k, v, kv, sel=dsel, out=dout, workspace=ws_d)
+        ev[4].record()
+        torch.cuda.synchronize()
+        if s >= warmup:
+            t_idx.append(ev[0].elapsed_time(ev[1]) * 1e3)
+            t_att.append(ev[1].elapsed_time(ev[2]) * 1e3)
+            t_pair.append(ev[0].elapsed_time(ev[2]) * 1e3)
+            t_dec.append(ev[3].elapsed_time(ev[4]) * 1e3)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    L = w.T
+    f_idx = 2.0 * 128 * w.G * L * (L + 1) / 2
+    f_att, _ = sparse_work(torch, w, sel, 0)
+    res = {"workload": w.name, "unit": "us", "timed_steps": steps,
+           "prefill_us_min": round(min(t_pair), 2), "prefill_us_median": round(med(t_pair), 2),
+           "index_topk_us_min": round(min(t_idx), 2), "index_topk_us_median": round(med(t_idx), 2),
+           "sparse_attn_us_min": round(min(t_att), 2),
+           "sparse_attn_us_median": round(med(t_att), 2),
+           "last_token_decode_us_min": round(min(t_dec), 2),
+           "last_token_decode_us_median": round(med(t_dec), 2),
+           "index_flops": f_idx, "sparse_flops": f_att,
+           "note": "latency figures (32 query tiles; the work is too small to fill the chip)"}
+    del k, v, ki, q, qi, sel, out, dsel, dout, ws_i, ws_p, ws_d
     torch.cuda.empty_cache()
     return res
 
@@ -706,6 +898,46 @@ def read_ceiling(torch, mib=512, reps=20):
     return round(best, 1)
 
 
+def mfma_ceiling(torch, wgs=1024, reps=10):
+    """The MFMA throughput measured live: the probe library's loop of
+    independent 32x32x16 bf16 (or 32x32x64 E4M3) MFMAs with no memory
+    traffic, on 1024 workgroups of four waves (four per SIMD), back-to-back
+    launches between two events, after the chip has run the loop for a few
+    launches (the clock under sustained matrix load)."""
+    import ctypes
+    lib = _probe_lib()
+    lib.msa_probe_mfma.restype = ctypes.c_int
+    lib.msa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+    res = {}
+    for fp8, iters, peak, name in ((0, 4096, BF16_PEAK_TFLOPS, "bf16"),
+                                   (1, 2048, FP8_PEAK_TFLOPS, "fp8")):
+        flops = ctypes.c_double(0.0)
+
+        def launch():
+            rc = lib.msa_probe_mfma(fp8, wgs, iters, ctypes.c_void_p(sink.data_ptr()),
+                                    ctypes.byref(flops),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError("MFMA probe failed: %d" % rc)
+        for _ in range(5):
+            launch()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            launch()
+        b.record()
+        torch.cuda.synchronize()
+        tf = flops.value / (a.elapsed_time(b) / reps * 1e-3) / 1e12
+        res[name] = {"value": round(tf, 1), "unit": "TFLOP/s", "frac_of_peak": round(tf / peak, 4)}
+    res["what"] = ("independent MFMAs from registers (32x32x16 bf16; 32x32x64 E4M3 with unit "
+                   "scales), 1024 workgroups of four waves, measured in this run")
+    del sink
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -720,6 +952,9 @@ def main():
                     help="skip the 1M-token chunked prefill with E4M3 index data")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling its kernels)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the 16 x 131072 decode legs (bf16 and E4M3 index data), "
+                         "for profiling their kernels")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this MSA build has no multi-GPU path "
@@ -786,15 +1021,21 @@ def main():
                             "what": "streaming read of 512 MiB (16-byte loads, best of plain and "
                                     "nontemporal loads and of 2048 and 16384 workgroups), "
                                     "measured in this run"}
+    line["mfma_ceiling"] = mfma_ceiling(torch)
     if args.calibrate_copy:
         line["copy_calibration"] = copy_calibration(torch)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_decode(w, res["host"])
+        line["cpu_baseline"] = cpu_baseline_decode(w, [res["host"]])
     res.pop("host")
     line["decode_fp8_index"] = run_decode_fp8_index(torch, msa, wl.workload(2, fp8_index=True),
                                                     res.pop("k"), res.pop("v"), args.steps,
                                                     args.warmup)
     torch.cuda.empty_cache()
+    if args.decode_only:
+        print(json.dumps(line), flush=True)
+        return
+    line["decode_1M"] = run_decode_long(torch, msa, args.steps, args.warmup)
+    line["prefill_L4096_G1"] = run_small_prefill(torch, msa)
     if not args.no_prefill:
         line["prefill"] = run_prefill(torch, msa, wl.workload(3),
                                       cpu_baseline=not args.no_cpu_baseline)

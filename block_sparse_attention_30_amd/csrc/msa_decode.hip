@@ -47,6 +47,15 @@ namespace {
 // MI355X's last-level (Infinity) cache, 256 MiB.
 constexpr int64_t kLastLevelCacheBytes = 256ll << 20;
 
+// A split partial word that this call has not written yet (msa_decode): a
+// NaN pattern the arithmetic never produces (hardware NaNs are the canonical
+// quiet NaN or carry a bf16 input's payload, whose low 16 bits are zero).
+constexpr uint32_t kUnpublished = 0xFFFFFFFFu;
+// Bound of the wait for a partial word (each wait sleeps 64 clocks): the
+// words are stored before their split's arrival is counted, so the wait ends
+// at once in practice; the bound keeps every wave's exit guaranteed.
+constexpr int kPublishSpin = 1 << 20;
+
 template <bool F8>
 struct ScanGeom {
     static constexpr int kRowBytes = DI * (F8 ? 1 : 2);     // one token's key
@@ -64,15 +73,28 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     const unsigned char *__restrict__ q_idx, const unsigned char *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
     float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int blocks_per_wg,
-    int32_t *__restrict__ zero_counters) {
+    int32_t *__restrict__ zero_counters, uint32_t *__restrict__ unpublish, int64_t n_unpublish) {
     typedef ScanGeom<F8> Geo;
     __shared__ __attribute__((aligned(16))) unsigned char lds[4 * Geo::kWaveLds];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // Zero the arrival counters the decode attention kernel of the same call
-    // uses (one per (sequence, group)); the kernel boundary orders the two.
+    // Reset the decode attention kernel's state of the same call (msa_decode):
+    // zero its arrival counters (one per (sequence, group)) and mark every
+    // word of its split partials unpublished, each workgroup a slice; the
+    // kernel boundary orders these stores before that kernel.
     if (zero_counters && blockIdx.x == 0)
         for (int i = threadIdx.x; i < G; i += 256) zero_counters[(int64_t)b * G + i] = 0;
+    if (unpublish) {
+        const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
+        const int64_t per = (n_unpublish + nwg - 1) / nwg;
+        const int64_t lo = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * per;
+        const int64_t hi = min(lo + per, n_unpublish);
+        // Agent-scope (write-through) stores: plain ones would be left dirty
+        // in the L2 for the end-of-kernel write-back (measured slower).
+        for (int64_t i = lo + threadIdx.x; i < hi; i += 256)
+            __hip_atomic_store(&unpublish[i], kUnpublished, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
     const int rows = T * G;
     const int kv = clamp_kv(kv_lens[b], Nmax);
     const int qs = q_start ? q_start[b] : kv - T;
@@ -205,6 +227,17 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(
     }
 }
 
+// The value of split partial word *p once its split has stored it: v is a
+// first agent-scope read of it; re-read (bounded) while it is still the
+// kUnpublished mark of this call.
+__device__ __forceinline__ float published(const float *p, float v) {
+    for (int spin = 0; __float_as_uint(v) == kUnpublished && spin < kPublishSpin; ++spin) {
+        __builtin_amdgcn_s_sleep(1);
+        v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return v;
+}
+
 // Decode: the new token of sequence b sits at position kv - 1. Group g's
 // kept blocks give 4*nblk 32-token chunks; workgroup (b, g, split) has eight
 // waves and takes chunks [8*split, 8*split + 8), one per wave, so every load
@@ -217,8 +250,9 @@ constexpr int kDecWaves = 8;
 constexpr int kDecChunks = kDecWaves;  // chunks per split
 
 struct DecodeLds {
-    unsigned char vrows[kDecWaves * kVWave];  // V chunks; then [8][16][128] fp32 outputs
-    uint64_t keys[64];                        // top-k list
+    // Ranking: [8][64] keys of the waves' lists, then [8][32] keys of their
+    // sorted top-K; then the V chunks; then [8][16][128] fp32 outputs.
+    __attribute__((aligned(16))) unsigned char vrows[kDecWaves * kVWave];
     int sel[KMAX];
     int blocks[KMAX];
     int nblk;
@@ -245,11 +279,14 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     bf16x8 qf[4];
     load_query(qf, q + ((int64_t)b * H + (int64_t)g * R) * D, R, lane);
     if (pooled) {
+        // All eight waves rank a share of the row, wave 0 merges their lists.
+        // n_load = nb_max: the row's pooled scores are loaded while kv_lens is
+        // still in flight.
+        uint64_t *kbuf = reinterpret_cast<uint64_t *>(L.vrows);
+        const uint64_t top = block_topk_row<kDecWaves>(pooled + unit * nb_max,
+                                                       p >= 0 ? p / S + 1 : 0, (int)nb_max, K,
+                                                       lane, wave, kbuf, kbuf + kDecWaves * 64);
         if (wave == 0) {
-            // n_load = nb_max: the row's pooled scores are loaded while kv_lens
-            // is still in flight.
-            const uint64_t top = wave_topk_row(pooled + unit * nb_max, p >= 0 ? p / S + 1 : 0,
-                                               (int)nb_max, K, lane, L.keys);
             if (lane < K) {
                 const int blk = top ? key_block(top) : -1;
                 L.sel[lane] = blk;
@@ -311,8 +348,8 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
         }
         const int64_t pu = (unit * nsplit + split) * R + h;
         if (counters) {
-            // Device-scope stores: written through to memory, where the
-            // merging workgroup (possibly on another XCD) reads them.
+            // Agent-scope stores (written through the XCD's L2): the merging
+            // workgroup may run on another XCD, behind another L2.
             __hip_atomic_store(&part_o[pu * D + dd], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (dd == 0) {
                 __hip_atomic_store(&part_ml[pu * 2], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -329,9 +366,15 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     }
     if (!counters) return;
     // The last of the nsplit workgroups of (sequence, group) to arrive merges
-    // all partials. Every thread's partial stores have completed (vmcnt(0))
-    // before the workgroup's arrival is counted; the merging workgroup reads
-    // the partials with device-scope loads, after its own arrival.
+    // all partials. No fence orders the partials before the arrival (an
+    // agent-scope release writes back the whole L2 and costs more than the
+    // merge): instead every partial word is an agent-scope atomic that this
+    // call writes exactly once, over the kUnpublished value the index kernel
+    // of the same call stored, and the merging workgroup reads each word until
+    // it holds its split's value. Coherence of a single atomic location makes
+    // that value the one the split stored; the arrival counter only chooses
+    // the merging workgroup. The stores have completed before the arrival is
+    // counted (vmcnt(0)), so the first read finds them.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (tid == 0)
@@ -352,6 +395,13 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
                 pm[j] = __hip_atomic_load(&part_ml[pu * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 pl[j] = __hip_atomic_load(&part_ml[pu * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 pv[j] = __hip_atomic_load(&part_o[pu * D + dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t pu = pu0 + (int64_t)min(sp0 + j, nsplit - 1) * R;
+                pm[j] = published(&part_ml[pu * 2], pm[j]);
+                pl[j] = published(&part_ml[pu * 2 + 1], pl[j]);
+                pv[j] = published(&part_o[pu * D + dd], pv[j]);
                 if (sp0 + j >= nsplit) pm[j] = -INFINITY;
             }
             float Mb = M;
@@ -414,6 +464,14 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
     if (lse && dd == 0) lse[uh] = Lsum > 0.f ? M * kLn2 + logf(Lsum) : -INFINITY;
 }
 
+// Sets n words to v (the decode attention state when the MFMA index kernel,
+// which does not reset it, produces the pooled scores).
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n,
+                                                       uint32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
 // Blocks per decode-scan workgroup: about 4096 workgroups over the batch
 // (measured best on the 16 x 131072 decode, where it is one block per wave),
 // at least 4 (one per wave), a multiple of 4.
@@ -455,7 +513,7 @@ namespace msa {
 msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                          const void *q_idx, const void *k_idx, const int32_t *kv_lens,
                          const int32_t *q_start, float *pooled, int64_t nb_max, hipStream_t st,
-                         int32_t *zero_counters) {
+                         int32_t *zero_counters, uint32_t *unpublish, int64_t n_unpublish) {
     const int G = cfg->num_kv_groups;
     const int rows = T * G;
     const bool f8 = cfg->index_dtype == MSA_FP8_E4M3;
@@ -469,13 +527,24 @@ msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nm
         const bool stream = (int64_t)B * Nmax * DI * (f8 ? 1 : 2) > kLastLevelCacheBytes;
         auto launch = [&](auto kern) {
             kern<<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G, Nmax, nb_max,
-                                       (int)per_wg, zero_counters);
+                                       (int)per_wg, zero_counters, unpublish, n_unpublish);
         };
         if (f8)
             stream ? launch(idx_scan_kernel<true, true>) : launch(idx_scan_kernel<true, false>);
         else
             stream ? launch(idx_scan_kernel<false, true>) : launch(idx_scan_kernel<false, false>);
         return launch_status("decode index kernel");
+    }
+    if (zero_counters) {
+        // The MFMA index kernel does not reset the decode attention state.
+        const int64_t n = (int64_t)B * G;
+        fill_u32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
+            reinterpret_cast<uint32_t *>(zero_counters), n, 0u);
+        if (unpublish)
+            fill_u32_kernel<<<(unsigned)((n_unpublish + 255) / 256), 256, 0, st>>>(
+                unpublish, n_unpublish, kUnpublished);
+        msa_status s = launch_status("decode state reset kernel");
+        if (s != MSA_OK) return s;
     }
     return launch_prefill_pooled(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start, pooled, nb_max,
                                  st);
@@ -535,8 +604,11 @@ msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void
     char *base = static_cast<char *>(workspace);
     float *pooled = reinterpret_cast<float *>(base + w.pooled_off);
     int32_t *counters = reinterpret_cast<int32_t *>(base + w.counters_off);
+    // The split partials, O then (m, l), are one contiguous run of words.
+    const int64_t n_part = (int64_t)B * cfg->num_kv_groups * msa::decode_splits(cfg) *
+                           cfg->heads_per_group * (D + 2);
     s = msa::launch_pooled(cfg, B, 1, Nmax, q_idx, k_idx, kv_lens, nullptr, pooled, w.nb_max, st,
-                      counters);
+                           counters, reinterpret_cast<uint32_t *>(base + w.part_o_off), n_part);
     if (s != MSA_OK) return s;
     // The attention kernel ranks each (sequence, group) row itself from the
     // pooled scores, attends over the kept blocks, and the last split of each

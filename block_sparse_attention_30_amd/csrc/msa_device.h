@@ -18,7 +18,8 @@ namespace msa {
 msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                          const void *q_idx, const void *k_idx, const int32_t *kv_lens,
                          const int32_t *q_start, float *pooled, int64_t nb_max, hipStream_t st,
-                         int32_t *zero_counters = nullptr);
+                         int32_t *zero_counters = nullptr, uint32_t *unpublish = nullptr,
+                         int64_t n_unpublish = 0);
 // The MFMA path of launch_pooled (msa_prefill.hip).
 msa_status launch_prefill_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                                  const void *q_idx, const void *k_idx, const int32_t *kv_lens,
@@ -240,8 +241,9 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
 // best keys in lanes 0..K-1 (descending), 0 elsewhere.
 // n_load (>= n) entries of cand may be read: the first batch is loaded
 // before n is known to be positive, so its loads can be issued at once.
+// cand[i] is the score of block blk0 + i (keys carry the absolute block id).
 __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int n_load, int K,
-                                                  int lane, uint64_t *buf) {
+                                                  int lane, uint64_t *buf, int blk0 = 0) {
     constexpr int kBatch = 16;
     const bool one_batch = n <= 64 * kBatch;  // then pass 2 reuses pass 1's registers
     float v[kBatch];
@@ -259,7 +261,7 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
 #pragma unroll
         for (int c = 0; c < kBatch; ++c) {
             const int i = base + c * 64 + lane;
-            const uint64_t k = i < n ? score_key(v[c], i) : 0;
+            const uint64_t k = i < n ? score_key(v[c], blk0 + i) : 0;
             lmax = k > lmax ? k : lmax;
         }
     }
@@ -287,7 +289,7 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
 #pragma unroll
         for (int c = 0; c < kBatch; ++c) {
             const int i = c * 64 + lane;
-            const uint64_t kk = i < n ? score_key(v[c], i) : 0;
+            const uint64_t kk = i < n ? score_key(v[c], blk0 + i) : 0;
             my += (kk > thr && kk != lmax) ? 1 : 0;
         }
         int excl = 0, total = 0;
@@ -302,7 +304,7 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
 #pragma unroll
             for (int c = 0; c < kBatch; ++c) {
                 const int i = c * 64 + lane;
-                const uint64_t kk = i < n ? score_key(v[c], i) : 0;
+                const uint64_t kk = i < n ? score_key(v[c], blk0 + i) : 0;
                 if (kk > thr && kk != lmax) buf[pos++] = kk;
             }
             cnt = total;
@@ -315,7 +317,7 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
 #pragma unroll
         for (int c = 0; c < kBatch; ++c) {
             const int i = base + c * 64 + lane;
-            const uint64_t kk = i < n ? score_key(v[c], i) : 0;
+            const uint64_t kk = i < n ? score_key(v[c], blk0 + i) : 0;
             bool q = kk > thr && kk != lmax;
             uint64_t qm = __ballot(q);
             while (qm) {
@@ -338,6 +340,109 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
     }
     if (cnt) merge();
     return top;
+}
+
+// Bitonic stages 2*RUN .. 64 over one key per lane, for lanes that already
+// form runs of RUN keys with even runs descending and odd runs ascending (the
+// state after stage RUN); ends descending, lane 0 the largest. RUN = 1 is a
+// full sort.
+template <int RUN>
+__device__ __forceinline__ uint64_t bitonic_from_runs(uint64_t x, int lane) {
+    if constexpr (RUN <= 1) x = bitonic_step<2, 1>(x, lane);
+    if constexpr (RUN <= 2) {
+        x = bitonic_step<4, 2>(x, lane);
+        x = bitonic_step<4, 1>(x, lane);
+    }
+    if constexpr (RUN <= 4) {
+        x = bitonic_step<8, 4>(x, lane);
+        x = bitonic_step<8, 2>(x, lane);
+        x = bitonic_step<8, 1>(x, lane);
+    }
+    if constexpr (RUN <= 8) {
+        x = bitonic_step<16, 8>(x, lane);
+        x = bitonic_step<16, 4>(x, lane);
+        x = bitonic_step<16, 2>(x, lane);
+        x = bitonic_step<16, 1>(x, lane);
+    }
+    if constexpr (RUN <= 16) {
+        x = bitonic_step<32, 16>(x, lane);
+        x = bitonic_step<32, 8>(x, lane);
+        x = bitonic_step<32, 4>(x, lane);
+        x = bitonic_step<32, 2>(x, lane);
+        x = bitonic_step<32, 1>(x, lane);
+    }
+    x = bitonic_step<64, 32>(x, lane);
+    x = bitonic_step<64, 16>(x, lane);
+    x = bitonic_step<64, 8>(x, lane);
+    x = bitonic_step<64, 4>(x, lane);
+    x = bitonic_step<64, 2>(x, lane);
+    return bitonic_step<64, 1>(x, lane);
+}
+
+// The 64 largest of two descending-sorted lane registers, descending: the
+// elementwise max of a and b reversed is a bitonic sequence holding them, and
+// the last stage's steps sort it.
+__device__ __forceinline__ uint64_t merge_sorted_desc(uint64_t a, uint64_t b, int lane) {
+    const uint64_t br = shfl_u64(b, 63 - lane);
+    uint64_t x = a > br ? a : br;
+    x = bitonic_step<64, 32>(x, lane);
+    x = bitonic_step<64, 16>(x, lane);
+    x = bitonic_step<64, 8>(x, lane);
+    x = bitonic_step<64, 4>(x, lane);
+    x = bitonic_step<64, 2>(x, lane);
+    return bitonic_step<64, 1>(x, lane);
+}
+
+// One 64-key register of the NW sorted runs of Kp keys in `runs` (register r
+// holds keys r*64 .. r*64+63), loaded with odd runs reversed, then sorted.
+template <int KP>
+__device__ __forceinline__ uint64_t load_runs_sorted(const uint64_t *runs, int nkeys, int r,
+                                                     int lane) {
+    const int i = r * 64 + lane;
+    const int pos = lane % KP, run0 = i - pos;
+    const int j = ((lane / KP) & 1) ? run0 + KP - 1 - pos : i;
+    const uint64_t x = i < nkeys ? runs[j] : 0;
+    return bitonic_from_runs<KP>(x, lane);
+}
+
+template <int KP>
+__device__ __forceinline__ uint64_t merge_runs(const uint64_t *runs, int nkeys, int lane) {
+    const int nreg = (nkeys + 63) / 64;  // 1, 2 or 4
+    uint64_t a = load_runs_sorted<KP>(runs, nkeys, 0, lane);
+    if (nreg == 1) return a;
+    a = merge_sorted_desc(a, load_runs_sorted<KP>(runs, nkeys, 1, lane), lane);
+    if (nreg == 2) return a;
+    const uint64_t c = merge_sorted_desc(load_runs_sorted<KP>(runs, nkeys, 2, lane),
+                                         load_runs_sorted<KP>(runs, nkeys, 3, lane), lane);
+    return merge_sorted_desc(a, c, lane);
+}
+
+// Top-K (K <= 32) of one row by the NW (<= 8) waves of a workgroup: wave w
+// ranks a contiguous share of the row's n pooled scores with wave_topk_row
+// and writes its K best keys, zero-padded to Kp (the next power of two), to
+// `runs` (LDS, NW * 32 keys); after a barrier wave 0 merges the NW sorted
+// runs. `bufs` is NW * 64 keys of LDS (wave_topk_row's lists). Every thread of
+// the workgroup must call it. Returns the K best keys, descending, in lanes
+// 0..K-1 of wave 0; 0 in every other lane and wave. Up to n_load >= n scores
+// may be read (see wave_topk_row).
+template <int NW>
+__device__ __forceinline__ uint64_t block_topk_row(const float *cand, int n, int n_load, int K,
+                                                   int lane, int wave, uint64_t *bufs,
+                                                   uint64_t *runs) {
+    const int chunk = (n_load + NW - 1) / NW;
+    const int b0 = wave * chunk;
+    const int nw = min(max(n - b0, 0), chunk), nlw = min(max(n_load - b0, 0), chunk);
+    const uint64_t mine = wave_topk_row(cand + b0, nw, nlw, K, lane, bufs + wave * 64, b0);
+    const int kp = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : K <= 16 ? 16 : 32;
+    if (lane < kp) runs[wave * kp + lane] = mine;  // lanes K..kp-1 hold 0
+    __syncthreads();
+    if (wave != 0) return 0;
+    const int nkeys = NW * kp;
+    // Up to 64 keys (Kp <= 8) are one register, sorted whole (runs of one).
+    const uint64_t x = kp <= 8 ? merge_runs<1>(runs, nkeys, lane)
+                     : kp == 16 ? merge_runs<16>(runs, nkeys, lane)
+                                : merge_runs<32>(runs, nkeys, lane);
+    return lane < K ? x : 0;
 }
 
 // ---------------------------------------------------------------------------

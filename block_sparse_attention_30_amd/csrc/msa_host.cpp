@@ -147,10 +147,16 @@ DecodeWs decode_ws(const msa_config *cfg, int32_t B, int32_t Nmax, bool with_ind
     DecodeWs w{};
     w.nb_max = ((int64_t)Nmax + kBlock - 1) / kBlock;
     w.pooled_off = 0;
-    const size_t pooled = with_index ? index_ws(cfg, B, 1, Nmax).total : 0;
+    // Pooled block scores of every (sequence, group) row, whichever index
+    // kernel writes them (the streaming one for G <= kScanMaxRows, the MFMA
+    // prefill one above).
+    const size_t pooled =
+        with_index ? round_up((size_t)B * cfg->num_kv_groups * (size_t)w.nb_max * 4, kWsAlign) : 0;
     const size_t units = (size_t)B * cfg->num_kv_groups * decode_splits(cfg) * cfg->heads_per_group;
     w.part_o_off = pooled;
-    w.part_ml_off = round_up(w.part_o_off + units * kHeadDim * 4, kWsAlign);
+    // (m, l) directly after O (units * 512 bytes keep the alignment): the
+    // decode kernels treat the partials as one run of units * (d + 2) words.
+    w.part_ml_off = w.part_o_off + units * kHeadDim * 4;
     w.counters_off = round_up(w.part_ml_off + units * 2 * 4, kWsAlign);
     const size_t counters = with_index ? (size_t)B * cfg->num_kv_groups * 4 : 0;
     w.total = round_up(w.counters_off + counters, kWsAlign);

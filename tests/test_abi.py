@@ -256,6 +256,21 @@ def test_workspace_sizes_follow_shapes(lib):
     assert a + d <= dd <= a + d + 16 * 4 * 4 + 256 and dd % 256 == 0
 
 
+def test_decode_workspace_holds_pooled_scores_above_16_groups(lib):
+    """msa_decode with more than 16 groups takes the MFMA index kernel, which
+    writes the pooled scores of all B*G rows into the same workspace: the size
+    must hold them (plus the split partials and counters) for every G."""
+    for G in (16, 17, 64):
+        c = cfg(num_kv_groups=G, heads_per_group=1)
+        B, N = 1, 1 << 20
+        nb = N // 128
+        pooled = B * G * nb * 4
+        parts = lib.msa_workspace_size(ctypes.byref(c), B, 1, N, 2)
+        dd = lib.msa_workspace_size(ctypes.byref(c), B, 1, N, 3)
+        assert dd >= pooled + parts + B * G * 4, (G, dd)
+        assert dd % 256 == 0
+
+
 def test_index_project_validation(lib):
     c = cfg()
 

@@ -7,9 +7,12 @@ configuration the benchmark uses:
                                                  mixed {256k, 512k, 768k, 1M};
   both decode batches with E4M3 index data       every row (uniform lengths);
   prefill, 131072 tokens (4 groups x 8 heads)    a stratified sample of 2048 rows;
-  chunked prefill, 1048576 tokens in 32768-row   the first, a middle and the
-  chunks, E4M3 index data                        last chunk, about 1500 sampled
-                                                 rows in all (the oracle's cost
+  chunked prefill, 1048576 tokens in 32768-row   all 32 chunks: the first, a
+  chunks, E4M3 index data                        middle and the last chunk on
+                                                 1515 sampled rows, every other
+                                                 chunk on its first and last
+                                                 row and 17 seeded rows (2066
+                                                 rows in all; the oracle's cost
                                                  per row grows with position);
   query-block-shared selections, 131072-token    24 sampled query blocks
   prefill and two chunks of the 1M chunked       (selections), 8 rows of each
@@ -190,6 +193,33 @@ def test_chunked_prefill_1M_fp8_sampled_rows(orc, chunked_1m, chunk, n_random):
     rows_i = stratified_rows(row0, C, C, n_random, seed=50 + chunk)
     check_prefill_rows(orc, w, host, dev, q_h, qi_h, row0, rows_i,
                        "%s chunk %d" % (w.name, chunk))
+
+
+# The chunks the dense samples above leave out, in four groups of similar
+# oracle cost (a row's cost grows with its position).
+OTHER_CHUNKS = [c for c in range(32) if c not in (0, 15, 31)]
+CHUNK_GROUPS = [OTHER_CHUNKS[0:10], OTHER_CHUNKS[10:17], OTHER_CHUNKS[17:23], OTHER_CHUNKS[23:]]
+
+
+@pytest.mark.parametrize("group", range(len(CHUNK_GROUPS)))
+def test_chunked_prefill_1M_fp8_every_chunk(orc, chunked_1m, group):
+    """Every other chunk of the 1M chunked prefill, each run on the GPU as
+    the benchmark runs it: its first and last row and 17 seeded rows against
+    the oracle. With the dense samples of chunks 0, 15 and 31 (1515 rows) the
+    chunked prefill is checked on 2066 rows, the first and last row of all 32
+    chunks among them."""
+    w, host, dev = chunked_1m
+    C = w.chunk
+    for chunk in CHUNK_GROUPS[group]:
+        row0 = chunk * C
+        q_h, qi_h = wl.gen_queries(w, row0=row0, rows=C)
+        rng = np.random.default_rng(70 + chunk)
+        picks = {0, C - 1}
+        while len(picks) < 19:
+            picks.add(int(rng.integers(1, C - 1)))
+        rows_i = np.array(sorted(picks), np.int64)
+        check_prefill_rows(orc, w, host, dev, q_h, qi_h, row0, rows_i,
+                           "%s chunk %d" % (w.name, chunk))
 
 
 def check_qblock(orc, w, host, dev, q_h, qi_h, row0, blocks, what, seed):

@@ -192,7 +192,11 @@ def run_fused_decode(pr, G, R, K, kv_lens, workspace=None, fp8=False):
 @pytest.mark.parametrize("G,R,K,lens,fp8", [
     (4, 8, 16, [3000, 2999, 1, 129, 2048, 128, 0, 5000], False), (1, 2, 16, [4096], False),
     (3, 5, 7, [700, 513], False), (2, 16, 32, [4500, 4500, 17], False),
-    (4, 8, 16, [3000, 2999, 1, 129, 2048, 128, 0, 5000], True)])
+    (4, 8, 16, [3000, 2999, 1, 129, 2048, 128, 0, 5000], True),
+    # more than 16 groups: the MFMA index kernel writes the pooled scores
+    (17, 1, 16, [3000, 1, 2500, 130], False),
+    # K = 1 and K = 3: the ranking merges runs of 1 and 4 keys
+    (2, 4, 1, [20000, 300], False), (3, 2, 3, [20000, 777, 5], False)])
 def test_decode_step_matches_oracle_and_two_calls(orc, G, R, K, lens, fp8):
     Nmax = max(max(lens), 1)
     lim = 16 if fp8 else 4
