@@ -96,6 +96,11 @@ def load():
                                             vp, sz, vp]
     lib.msa_sparse_attn_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_decode.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_decode_no_alloc.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp]
+    lib.msa_decode_no_alloc.restype = ctypes.c_int
+    lib.msa_decode_no_alloc_max_scratch.argtypes = []
+    lib.msa_decode_no_alloc_max_scratch.restype = sz
     lib.msa_cache_append.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.msa_index_topk_qblock.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.msa_sparse_attn_prefill_qblock.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, vp,
@@ -365,6 +370,42 @@ def decode(cfg: Config, q, q_idx, k_idx, k_cache, v_cache, kv_lens, sel=None, se
     if want_scores or want_lse or sel_scores is not None or lse is not None:
         return sel, sel_scores, out, lse
     return sel, out
+
+
+def decode_no_alloc(cfg: Config, q, q_idx, k_idx, k_cache, v_cache, kv_lens, sel, out,
+                    sel_scores=None, lse=None):
+    """msa_decode_no_alloc: the decode step of `decode` with the library's fixed
+    scratch array instead of a workspace. The outputs are the caller's (sel
+    [B,1,G,K] int32, out [B,1,H,d] bf16, optional sel_scores and lse), so the
+    call allocates nothing on the device."""
+    dev, B, T, Nmax = _sparse_checks(cfg, q, k_cache, v_cache, kv_lens, sel, T_expected=1)
+    _need(q_idx, "q_idx", _INDEX_DTYPES[cfg.index_dtype], 4, dev)
+    _need(k_idx, "k_idx", _INDEX_DTYPES[cfg.index_dtype], 3, dev)
+    if tuple(q_idx.shape) != (B, 1, cfg.num_kv_groups, cfg.index_dim) or \
+            tuple(k_idx.shape) != (B, Nmax, cfg.index_dim):
+        raise ValueError("q_idx must be [B,1,G,dI] and k_idx [B,Nmax,dI]")
+    _need(out, "out", (torch.bfloat16,), 4, dev)
+    if tuple(out.shape) != (B, 1, cfg.num_heads, cfg.head_dim):
+        raise ValueError("out must be [B,1,H,d]")
+    if sel_scores is not None:
+        _need(sel_scores, "sel_scores", (torch.float32,), 4, dev)
+        if sel_scores.shape != sel.shape:
+            raise ValueError("sel_scores must be [B,1,G,K]")
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), 3, dev)
+        if tuple(lse.shape) != (B, 1, cfg.num_heads):
+            raise ValueError("lse must be [B,1,H]")
+    with _on_device(dev):
+        _check(load().msa_decode_no_alloc(ctypes.byref(cfg._c()), B, Nmax, _ptr(q), _ptr(q_idx),
+                                          _ptr(k_idx), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(kv_lens), _ptr(sel), _ptr(sel_scores), _ptr(out),
+                                          _ptr(lse), _stream(dev)))
+    return sel, out
+
+
+def decode_no_alloc_max_scratch() -> int:
+    """Bytes of msa_decode_no_alloc's fixed scratch array (per GPU)."""
+    return int(load().msa_decode_no_alloc_max_scratch())
 
 
 def cache_append(cfg: Config, k_new, v_new, k_idx_new, pos0, k_cache, v_cache, k_idx):

@@ -17,7 +17,8 @@ LIBRARY = os.path.join(PKG, "libmsa.so")
 PROBE_LIBRARY = os.path.join(PKG, "libmsa_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 # Kernel sources (each with its entry points), sharing msa_device.h.
-KERNEL_SOURCES = ("msa_decode.hip", "msa_prefill.hip", "msa_backward.hip", "msa_project.hip")
+KERNEL_SOURCES = ("msa_decode.hip", "msa_prefill.hip", "msa_backward.hip", "msa_project.hip",
+                  "msa_noalloc.hip")
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

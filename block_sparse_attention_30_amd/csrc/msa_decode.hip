@@ -599,9 +599,23 @@ msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void
                                           kv_lens, sel, sel_scores, out, lse, workspace,
                                           ws_bytes);
     if (s != MSA_OK || B == 0) return s;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    return msa::decode_step(cfg, B, Nmax, q, q_idx, k_idx, k_cache, v_cache, kv_lens, sel,
+                            sel_scores, out, lse, static_cast<char *>(workspace),
+                            reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace msa {
+
+// The launches of one decode step (msa_decode) on checked arguments, with the
+// step's scratch memory (layout decode_ws(cfg, B, Nmax, true)) at `base`.
+msa_status decode_step(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                       const void *q_idx, const void *k_idx, const void *k_cache,
+                       const void *v_cache, const int32_t *kv_lens, int32_t *sel,
+                       float *sel_scores, void *out, float *lse, char *base, hipStream_t st) {
+    msa_status s;
     const msa::DecodeWs w = msa::decode_ws(cfg, B, Nmax, true);
-    char *base = static_cast<char *>(workspace);
     float *pooled = reinterpret_cast<float *>(base + w.pooled_off);
     int32_t *counters = reinterpret_cast<int32_t *>(base + w.counters_off);
     // The split partials, O then (m, l), are one contiguous run of words.
@@ -619,4 +633,4 @@ msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void
                                    reinterpret_cast<float *>(base + w.part_ml_off), st, counters);
 }
 
-}  // extern "C"
+}  // namespace msa

@@ -30,6 +30,13 @@ msa_status launch_scan_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t
                             const void *q_idx, const void *k_idx, const int32_t *kv_lens,
                             const int32_t *q_start, int32_t *sel, float *sel_scores,
                             void *workspace, hipStream_t st);
+// The launches of one decode step (msa_decode.hip) on checked arguments, its
+// scratch memory (layout decode_ws(cfg, B, Nmax, true)) at `base`: shared by
+// msa_decode (caller workspace) and msa_decode_no_alloc (fixed scratch).
+msa_status decode_step(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                       const void *q_idx, const void *k_idx, const void *k_cache,
+                       const void *v_cache, const int32_t *kv_lens, int32_t *sel,
+                       float *sel_scores, void *out, float *lse, char *base, hipStream_t st);
 // The KV-major list build of one pass (msa_prefill.hip), shared by the
 // sparse prefill and its backward.
 void build_pass_lists(const PrefillWs &w, char *base, const int32_t *sel, const int32_t *kv_lens,

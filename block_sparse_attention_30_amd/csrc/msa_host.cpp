@@ -338,6 +338,16 @@ msa_status check_decode_args(const msa_config *cfg, int32_t B, int32_t Nmax, con
                              const void *v_cache, const int32_t *kv_lens, const int32_t *sel,
                              const float *sel_scores, const void *out, const float *lse,
                              const void *workspace, size_t ws_bytes) {
+    msa_status s = check_decode_shapes(cfg, B, Nmax, q, q_idx, k_idx, k_cache, v_cache, kv_lens,
+                                       sel, sel_scores, out, lse);
+    if (s != MSA_OK || B == 0) return s;
+    return check_ws(workspace, ws_bytes, decode_ws(cfg, B, Nmax, true).total);
+}
+
+msa_status check_decode_shapes(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                               const void *q_idx, const void *k_idx, const void *k_cache,
+                               const void *v_cache, const int32_t *kv_lens, const int32_t *sel,
+                               const float *sel_scores, const void *out, const float *lse) {
     msa_status s = check_config(cfg);
     if (s != MSA_OK) return s;
     if ((s = check_dims(B, 1, Nmax)) != MSA_OK) return s;
@@ -353,7 +363,7 @@ msa_status check_decode_args(const msa_config *cfg, int32_t B, int32_t Nmax, con
     if (!aligned(kv_lens, 4) || !aligned(sel, 4) || (sel_scores && !aligned(sel_scores, 4)) ||
         (lse && !aligned(lse, 4)))
         return fail(MSA_ERR_INVALID_ARG, "int32/fp32 arrays must be 4-byte aligned");
-    return check_ws(workspace, ws_bytes, decode_ws(cfg, B, Nmax, true).total);
+    return MSA_OK;
 }
 
 }  // namespace msa

@@ -112,6 +112,11 @@ struct DecodeWs {
 };
 DecodeWs decode_ws(const msa_config *cfg, int32_t B, int32_t Nmax, bool with_index);
 
+// check_decode_args without the workspace (msa_decode_no_alloc).
+msa_status check_decode_shapes(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                               const void *q_idx, const void *k_idx, const void *k_cache,
+                               const void *v_cache, const int32_t *kv_lens, const int32_t *sel,
+                               const float *sel_scores, const void *out, const float *lse);
 msa_status check_decode_args(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
                              const void *q_idx, const void *k_idx, const void *k_cache,
                              const void *v_cache, const int32_t *kv_lens, const int32_t *sel,

@@ -161,6 +161,30 @@ msa_status msa_decode(const msa_config *cfg, int32_t B, int32_t Nmax, const void
                       void *stream);
 
 /*
+ * msa_decode for callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * step and the same kernels, with its scratch memory (pooled block scores,
+ * split partials, arrival counters) in a fixed array inside the library
+ * instead of a caller workspace. The array holds
+ * msa_decode_no_alloc_max_scratch() bytes (32 MiB) on every GPU the library
+ * runs on, from that GPU's first call until the process ends; the first call
+ * on a device looks up the array's address there. Shapes that need more
+ * scratch than that (msa_workspace_size(cfg, B, 1, Nmax, MSA_WS_DECODE)) are
+ * rejected with MSA_ERR_WORKSPACE before any launch. Arguments, outputs and
+ * errors otherwise as msa_decode. Every call on one GPU shares that GPU's
+ * array: calls that may overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller; a call's kernels reset the
+ * state they need, so nothing carries over from the previous call.
+ */
+msa_status msa_decode_no_alloc(const msa_config *cfg, int32_t B, int32_t Nmax, const void *q,
+                               const void *q_idx, const void *k_idx, const void *k_cache,
+                               const void *v_cache, const int32_t *kv_lens, int32_t *sel,
+                               float *sel_scores, void *out, float *lse, void *stream);
+
+/* Bytes of the fixed scratch array msa_decode_no_alloc uses on each GPU. */
+size_t msa_decode_no_alloc_max_scratch(void);
+
+/*
  * Backward of the sparse branch for fixed selections (the Tencent article's
  * §五 presents the two-branch design as trainable; the discrete selection
  * carries no gradient). With J, P and tau as in the forward definition,

@@ -33,7 +33,8 @@ def test_header_declares_the_three_entry_points():
     for n in ("msa_index_topk", "msa_index_pool", "msa_sparse_attn_prefill",
               "msa_sparse_attn_decode", "msa_decode", "msa_cache_append",
               "msa_index_topk_qblock", "msa_sparse_attn_prefill_qblock", "msa_qblock_slots",
-              "msa_sparse_attn_backward", "msa_index_project",
+              "msa_sparse_attn_backward", "msa_index_project", "msa_decode_no_alloc",
+              "msa_decode_no_alloc_max_scratch",
               "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_version"):
         assert n in names
 
@@ -155,6 +156,28 @@ def test_decode_step_validation(lib):
     assert call(ki=FAKE_MIS, nws=need) == INVALID
     assert call(nws=need - 1) == WORKSPACE
     assert call(ws=None, nws=need) == WORKSPACE
+
+
+def test_decode_no_alloc_validation(lib):
+    """msa_decode_no_alloc rejects bad arguments and shapes whose scratch
+    exceeds its fixed array on the host, before any HIP call."""
+    c = cfg()
+    cap = lib.msa_decode_no_alloc_max_scratch()
+    assert cap == 32 << 20
+
+    def call(B=2, N=1024, **kw):
+        a = dict(q=FAKE, qi=FAKE, ki=FAKE, k=FAKE, v=FAKE, kv=FAKE, sel=FAKE, out=FAKE)
+        a.update(kw)
+        return lib.msa_decode_no_alloc(ctypes.byref(c), B, N, a["q"], a["qi"], a["ki"], a["k"],
+                                       a["v"], a["kv"], a["sel"], None, a["out"], None, None)
+
+    assert call(B=0) == OK
+    assert call(qi=None) == INVALID
+    assert call(k=FAKE_MIS) == INVALID
+    big = (256, 1 << 20)
+    assert lib.msa_workspace_size(ctypes.byref(c), big[0], 1, big[1], 3) > cap
+    assert call(B=big[0], N=big[1]) == WORKSPACE
+    assert b"scratch" in lib.msa_last_error()
 
 
 def test_cache_append_validation(lib):
