@@ -130,11 +130,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_tile_kernel(
         int pc = -1, slot = -1;
         if (tc < ncol) {
             const int ent = list[beg + tc / R];
-            const int64_t hrow = ((int64_t)b * T + t0 + (ent >> 5)) * H + (int64_t)g * R + tc % R;
+            const int64_t hrow =
+                ((int64_t)b * T + t0 + (ent >> kEntShift)) * H + (int64_t)g * R + tc % R;
             l2 = lse[hrow] * kLog2e;
             dl = delta[hrow];
-            pc = qs + t0 + (ent >> 5);
-            slot = (int)((((int64_t)b * rows + (ent >> 5)) * ng + gl) * K + (ent & 31));
+            pc = qs + t0 + (ent >> kEntShift);
+            slot = (int)((((int64_t)b * rows + (ent >> kEntShift)) * ng + gl) * K +
+                         (ent & kEntMask));
         }
         s_lse2[tc] = l2;
         s_dl[tc] = dl;

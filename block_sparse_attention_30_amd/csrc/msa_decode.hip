@@ -250,7 +250,7 @@ constexpr int kDecWaves = 8;
 constexpr int kDecChunks = kDecWaves;  // chunks per split
 
 struct DecodeLds {
-    // Ranking: [8][64] keys of the waves' lists, then [8][32] keys of their
+    // Ranking: [8][64] keys of the waves' lists, then [8][64] keys of their
     // sorted top-K; then the V chunks; then [8][16][128] fp32 outputs.
     __attribute__((aligned(16))) unsigned char vrows[kDecWaves * kVWave];
     int sel[KMAX];
@@ -551,8 +551,9 @@ msa_status launch_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nm
                                  st);
 }
 
-// msa_index_topk for T*G <= kScanMaxRows: pooled scores from the streaming
-// kernel into the workspace, then a wavefront per row ranks them.
+// msa_index_topk for T*G <= kScanMaxRows (pooled scores from the streaming
+// kernel) or K > kPrefillRegTopk (from the MFMA prefill kernel): pooled scores
+// into the workspace, then a wavefront per row ranks them.
 msa_status launch_scan_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                             const void *q_idx, const void *k_idx, const int32_t *kv_lens,
                             const int32_t *q_start, int32_t *sel, float *sel_scores,

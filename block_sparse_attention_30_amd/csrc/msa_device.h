@@ -234,7 +234,21 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
     return x;
 }
 
-// Top-K of one row by a single wavefront, K <= 32. `cand` holds the row's n
+// The 64 largest of two descending-sorted lane registers, descending: the
+// elementwise max of a and b reversed is a bitonic sequence holding them, and
+// the last stage's steps sort it.
+__device__ __forceinline__ uint64_t merge_sorted_desc(uint64_t a, uint64_t b, int lane) {
+    const uint64_t br = shfl_u64(b, 63 - lane);
+    uint64_t x = a > br ? a : br;
+    x = bitonic_step<64, 32>(x, lane);
+    x = bitonic_step<64, 16>(x, lane);
+    x = bitonic_step<64, 8>(x, lane);
+    x = bitonic_step<64, 4>(x, lane);
+    x = bitonic_step<64, 2>(x, lane);
+    return bitonic_step<64, 1>(x, lane);
+}
+
+// Top-K of one row by a single wavefront, K <= 64. `cand` holds the row's n
 // pooled scores; `buf` is 64 keys of this wave's LDS.
 //   Pass 1: every lane takes the best key of its strided share. The K best of
 //           those 64 lane maxima are a valid running top-K, and the K-th is a
@@ -242,7 +256,10 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
 //   Pass 2: keys above the threshold that are not their lane's maximum (those
 //           were ranked in pass 1) are appended to the LDS list; when the
 //           list is full, or at the end, the list and the current top-K are
-//           sorted together and the threshold rises.
+//           ranked together and the threshold rises: for K <= 32 the top-K
+//           and a list of up to 64 - K keys are sorted as one register; for
+//           K > 32 the list (up to 64 keys) is sorted on its own and merged
+//           with the top-K register (merge_sorted_desc).
 // On random scores pass 2 finds only a handful of keys: a row costs two
 // 64-key sorts and one read of its scores (two if n > 1024). Returns the K
 // best keys in lanes 0..K-1 (descending), 0 elsewhere.
@@ -275,14 +292,21 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
     const uint64_t srt = wave_sort_desc(lmax, lane);
     uint64_t top = lane < K ? srt : 0;
     uint64_t thr = shfl_u64(srt, K - 1);
-    const int cap = 64 - K;
+    const bool big = K > 32;  // wavefront-uniform
+    const int cap = big ? 64 : 64 - K;
     const uint64_t below = (1ull << lane) - 1ull;
     int cnt = 0;  // wavefront-uniform
     auto merge = [&]() {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the list writes have landed
         __builtin_amdgcn_wave_barrier();
-        uint64_t x = lane < K ? top : ((lane - K) < cnt ? buf[lane - K] : 0);
-        x = wave_sort_desc(x, lane);
+        uint64_t x;
+        if (big) {
+            const uint64_t y = wave_sort_desc(lane < cnt ? buf[lane] : 0, lane);
+            x = merge_sorted_desc(top, y, lane);
+        } else {
+            x = lane < K ? top : ((lane - K) < cnt ? buf[lane - K] : 0);
+            x = wave_sort_desc(x, lane);
+        }
         top = lane < K ? x : 0;
         thr = shfl_u64(x, K - 1);
         cnt = 0;
@@ -355,6 +379,7 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
 // full sort.
 template <int RUN>
 __device__ __forceinline__ uint64_t bitonic_from_runs(uint64_t x, int lane) {
+    if constexpr (RUN >= 64) return x;  // one run: already sorted
     if constexpr (RUN <= 1) x = bitonic_step<2, 1>(x, lane);
     if constexpr (RUN <= 2) {
         x = bitonic_step<4, 2>(x, lane);
@@ -386,20 +411,6 @@ __device__ __forceinline__ uint64_t bitonic_from_runs(uint64_t x, int lane) {
     return bitonic_step<64, 1>(x, lane);
 }
 
-// The 64 largest of two descending-sorted lane registers, descending: the
-// elementwise max of a and b reversed is a bitonic sequence holding them, and
-// the last stage's steps sort it.
-__device__ __forceinline__ uint64_t merge_sorted_desc(uint64_t a, uint64_t b, int lane) {
-    const uint64_t br = shfl_u64(b, 63 - lane);
-    uint64_t x = a > br ? a : br;
-    x = bitonic_step<64, 32>(x, lane);
-    x = bitonic_step<64, 16>(x, lane);
-    x = bitonic_step<64, 8>(x, lane);
-    x = bitonic_step<64, 4>(x, lane);
-    x = bitonic_step<64, 2>(x, lane);
-    return bitonic_step<64, 1>(x, lane);
-}
-
 // One 64-key register of the NW sorted runs of Kp keys in `runs` (register r
 // holds keys r*64 .. r*64+63), loaded with odd runs reversed, then sorted.
 template <int KP>
@@ -412,22 +423,25 @@ __device__ __forceinline__ uint64_t load_runs_sorted(const uint64_t *runs, int n
     return bitonic_from_runs<KP>(x, lane);
 }
 
-template <int KP>
+// The NREG registers of runs (NW sorted runs of KP keys) merged pairwise into
+// the 64 largest keys, descending.
+template <int KP, int NREG>
 __device__ __forceinline__ uint64_t merge_runs(const uint64_t *runs, int nkeys, int lane) {
-    const int nreg = (nkeys + 63) / 64;  // 1, 2 or 4
-    uint64_t a = load_runs_sorted<KP>(runs, nkeys, 0, lane);
-    if (nreg == 1) return a;
-    a = merge_sorted_desc(a, load_runs_sorted<KP>(runs, nkeys, 1, lane), lane);
-    if (nreg == 2) return a;
-    const uint64_t c = merge_sorted_desc(load_runs_sorted<KP>(runs, nkeys, 2, lane),
-                                         load_runs_sorted<KP>(runs, nkeys, 3, lane), lane);
-    return merge_sorted_desc(a, c, lane);
+    uint64_t r[NREG];
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) r[i] = load_runs_sorted<KP>(runs, nkeys, i, lane);
+#pragma unroll
+    for (int step = 1; step < NREG; step *= 2)
+#pragma unroll
+        for (int i = 0; i + step < NREG; i += 2 * step)
+            r[i] = merge_sorted_desc(r[i], r[i + step], lane);
+    return r[0];
 }
 
-// Top-K (K <= 32) of one row by the NW (<= 8) waves of a workgroup: wave w
+// Top-K (K <= 64) of one row by the NW (<= 8) waves of a workgroup: wave w
 // ranks a contiguous share of the row's n pooled scores with wave_topk_row
 // and writes its K best keys, zero-padded to Kp (the next power of two), to
-// `runs` (LDS, NW * 32 keys); after a barrier wave 0 merges the NW sorted
+// `runs` (LDS, NW * 64 keys); after a barrier wave 0 merges the NW sorted
 // runs. `bufs` is NW * 64 keys of LDS (wave_topk_row's lists). Every thread of
 // the workgroup must call it. Returns the K best keys, descending, in lanes
 // 0..K-1 of wave 0; 0 in every other lane and wave. Up to n_load >= n scores
@@ -440,15 +454,17 @@ __device__ __forceinline__ uint64_t block_topk_row(const float *cand, int n, int
     const int b0 = wave * chunk;
     const int nw = min(max(n - b0, 0), chunk), nlw = min(max(n_load - b0, 0), chunk);
     const uint64_t mine = wave_topk_row(cand + b0, nw, nlw, K, lane, bufs + wave * 64, b0);
-    const int kp = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : K <= 16 ? 16 : 32;
+    const int kp = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : K <= 16 ? 16 : K <= 32 ? 32 : 64;
     if (lane < kp) runs[wave * kp + lane] = mine;  // lanes K..kp-1 hold 0
     __syncthreads();
     if (wave != 0) return 0;
     const int nkeys = NW * kp;
     // Up to 64 keys (Kp <= 8) are one register, sorted whole (runs of one).
-    const uint64_t x = kp <= 8 ? merge_runs<1>(runs, nkeys, lane)
-                     : kp == 16 ? merge_runs<16>(runs, nkeys, lane)
-                                : merge_runs<32>(runs, nkeys, lane);
+    constexpr int R16 = (NW * 16 + 63) / 64, R32 = (NW * 32 + 63) / 64, R64 = NW;
+    const uint64_t x = kp <= 8 ? merge_runs<1, 1>(runs, nkeys, lane)
+                     : kp == 16 ? merge_runs<16, R16>(runs, nkeys, lane)
+                     : kp == 32 ? merge_runs<32, R32>(runs, nkeys, lane)
+                                : merge_runs<64, R64>(runs, nkeys, lane);
     return lane < K ? x : 0;
 }
 
@@ -699,6 +715,11 @@ float scale_log2_of(const msa_config *cfg) {
     const float tau = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)cfg->head_dim);
     return tau * kLog2e;
 }
+
+// A KV-major list entry: the row of the pass and the selection slot, as
+// (row << kEntShift) | slot (slots < 64).
+constexpr int kEntShift = 6;
+constexpr int kEntMask = (1 << kEntShift) - 1;
 
 __device__ __forceinline__ bool slot_kept(const int32_t *sel_row, int k, int n_valid) {
     const int blk = sel_row[k];

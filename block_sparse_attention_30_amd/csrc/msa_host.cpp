@@ -43,7 +43,7 @@ msa_status check_config(const msa_config *c) {
     if (c->block_size != kBlock)
         return fail(MSA_ERR_UNSUPPORTED, "block_size %d unsupported (need 128)", c->block_size);
     if (c->topk > kMaxTopk)
-        return fail(MSA_ERR_UNSUPPORTED, "topk %d unsupported (need 1..32)", c->topk);
+        return fail(MSA_ERR_UNSUPPORTED, "topk %d unsupported (need 1..64)", c->topk);
     if (c->heads_per_group > kMaxHeadsPerGroup)
         return fail(MSA_ERR_UNSUPPORTED, "heads_per_group %d unsupported (need 1..16)",
                     c->heads_per_group);
@@ -64,11 +64,13 @@ IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) {
     IndexWs w{};
     w.nb_max = ((int64_t)Nmax + kBlock - 1) / kBlock;
     w.pooled_off = 0;
-    // Only the streaming (decode) path keeps pooled scores; the prefill kernel
-    // ranks rows in registers.
+    // The streaming (decode) path and the prefill path with K above the
+    // register top-K keep pooled scores; the prefill kernel otherwise ranks
+    // rows in registers.
     const bool scan = (int64_t)T * cfg->num_kv_groups <= kScanMaxRows;
+    const bool pooled = scan || cfg->topk > kPrefillRegTopk;
     w.pooled_bytes =
-        scan ? (size_t)B * (size_t)T * (size_t)cfg->num_kv_groups * (size_t)w.nb_max * 4 : 0;
+        pooled ? (size_t)B * (size_t)T * (size_t)cfg->num_kv_groups * (size_t)w.nb_max * 4 : 0;
     w.total = round_up(w.pooled_bytes, kWsAlign);
     return w;
 }
@@ -218,6 +220,10 @@ msa_status check_qblock_index_args(const msa_config *cfg, int32_t B, int32_t T, 
                                    const float *sel_scores) {
     msa_status s = check_config(cfg);
     if (s != MSA_OK) return s;
+    if (cfg->topk > kPrefillRegTopk)
+        return fail(MSA_ERR_UNSUPPORTED,
+                    "query-block selection keeps its top-K in registers: topk %d above %d",
+                    cfg->topk, kPrefillRegTopk);
     if ((s = check_dims(B, T, Nmax)) != MSA_OK) return s;
     if (B == 0 || T == 0) return MSA_OK;
     if ((int64_t)B * T * cfg->num_kv_groups > ((int64_t)1 << 31) - 1)

@@ -13,7 +13,11 @@ namespace msa {
 constexpr int kHeadDim = 128;
 constexpr int kIndexDim = 128;
 constexpr int kBlock = 128;
-constexpr int kMaxTopk = 32;
+constexpr int kMaxTopk = 64;
+// The prefill index kernel keeps a row's top-K in registers up to this K;
+// above it msa_index_topk writes pooled scores to the workspace and ranks
+// them per row (the decode path's ranking).
+constexpr int kPrefillRegTopk = 32;
 constexpr int kMaxHeadsPerGroup = 16;
 constexpr int kScanMaxRows = 16;  // T*G at or below this uses the streaming index kernel
 constexpr size_t kWsAlign = 256;
@@ -57,8 +61,9 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
                              size_t ws_bytes, int32_t which);
 
 // Workspace layout: the streaming index path (T*G <= kScanMaxRows, and
-// msa_decode) keeps the pooled block scores of every row, [B*T*G][ceil(Nmax/S)]
-// fp32. The prefill index path needs none.
+// msa_decode) and the prefill path with K > kPrefillRegTopk keep the pooled
+// block scores of every row, [B*T*G][ceil(Nmax/S)] fp32. The prefill index
+// path with K <= kPrefillRegTopk needs none.
 struct IndexWs {
     size_t pooled_off, pooled_bytes, total;
     int64_t nb_max;  // ceil(Nmax / S)

@@ -549,7 +549,7 @@ __global__ __launch_bounds__(256) void pf_scatter_kernel(
     const int64_t li = ((int64_t)b * ng + gl) * nb_max + sr[k];
     const int64_t wi = li * W + (tl >> 5);
     const int r = wpre[wi] + __popc(bits[wi] & ((1u << (tl & 31)) - 1u));
-    list[offsets[li] + r] = (tl << 5) | k;
+    list[offsets[li] + r] = (tl << kEntShift) | k;
 }
 
 __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
             const bool ok = col < et * R && e < nent;
             const int raw = s_ent[min(e, nent - 1)];
             ent[nq] = ok ? raw : -1;
-            const int tl = raw >> 5;
+            const int tl = raw >> kEntShift;
             pcol[nq] = ok ? qs + t0 + tl : -1;
             const bf16_t *qp =
                 q + (((int64_t)b * T + t0 + tl) * H + (int64_t)g * R + col % R) * D + kg * 8;
@@ -748,7 +748,8 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(
             // store into the trash area instead of branching around.
             const bool has = cent[nq] >= 0;
             const int64_t slot =
-                (((int64_t)b * rows + (cent[nq] >> 5)) * ng + gl) * K + (cent[nq] & 31);
+                (((int64_t)b * rows + (cent[nq] >> kEntShift)) * ng + gl) * K +
+                (cent[nq] & kEntMask);
             float2 *mlp = has && kg == 0 ? part_ml + slot * R + col % R
                                          : reinterpret_cast<float2 *>(trash + 4096) + col;
             *mlp = make_float2(mrow[nq], lrow[nq]);
@@ -1148,7 +1149,7 @@ msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t N
     if (s != MSA_OK || B == 0 || T == 0) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int G = cfg->num_kv_groups, K = cfg->topk;
-    if (T * G > msa::kScanMaxRows) {
+    if (T * G > msa::kScanMaxRows && K <= msa::kPrefillRegTopk) {
         // Prefill: scores, block max and the row's top-K in one kernel.
         const bool f8 = cfg->index_dtype == MSA_FP8_E4M3;
         const unsigned char *qi = static_cast<const unsigned char *>(q_idx);
@@ -1165,6 +1166,8 @@ msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t N
 #undef MSA_IDX_PREFILL
         return launch_status("prefill index kernel");
     }
+    // Decode shapes, and prefill with K above the register top-K: pooled
+    // scores into the workspace, then a wavefront ranks each row.
     return msa::launch_scan_topk(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start, sel, sel_scores,
                                  workspace, st);
 }

@@ -55,8 +55,9 @@
  * out of bounds. msa_last_error() describes the most recent failure on the
  * calling thread.
  *
- * Support limits: d = dI = S = 128; 1 <= K <= 32; 1 <= R <= 16; G >= 1;
- * B <= 65535. Results are deterministic (no floating-point atomics).
+ * Support limits: d = dI = S = 128; 1 <= K <= 64; 1 <= R <= 16; G >= 1;
+ * B <= 65535 (the query-block variant: K <= 32). Results are deterministic
+ * (no floating-point atomics).
  */
 #ifndef MSA_H
 #define MSA_H
@@ -94,7 +95,7 @@ typedef struct {
     int32_t head_dim;        /* d (must be 128)                               */
     int32_t index_dim;       /* dI, sparse_index_dim (must be 128)            */
     int32_t block_size;      /* S, sparse_block_size (must be 128)            */
-    int32_t topk;            /* K, sparse_topk_blocks (1..32)                 */
+    int32_t topk;            /* K, sparse_topk_blocks (1..64)                 */
     float softmax_scale;     /* tau; 0 selects 1/sqrt(d)                      */
     int32_t index_dtype;     /* msa_dtype of q_idx and k_idx                  */
 } msa_config;
@@ -103,7 +104,10 @@ typedef struct {
  * Index branch (Tencent article §二): scores, causal block max-pool and top-k
  * for B*T*G rows. Writes sel (and sel_scores if non-NULL: the pooled score of
  * each kept block, -inf for padding). T small enough that T*G <= 16 uses a
- * streaming kernel (decode); larger T uses an MFMA kernel (prefill). Chunked
+ * streaming kernel (decode); larger T uses an MFMA kernel (prefill), which
+ * ranks each row's blocks in registers for K <= 32 (no workspace) and for
+ * K > 32 writes the pooled scores to the workspace and ranks them per row
+ * (msa_workspace_size gives B*T*G*ceil(Nmax/S)*4 bytes then). Chunked
  * prefill is q_start[b] > 0 with the earlier keys already in k_idx.
  */
 msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
@@ -221,7 +225,8 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
  *              the call gets -1);
  *   sel_scores [B, NQ, G, K] fp32 (nullable), -inf for padding.
  * Other layouts as msa_index_topk. Needs no workspace. Exact for integer
- * index data, as msa_index_topk.
+ * index data, as msa_index_topk. K <= 32 (the ranking is kept in registers);
+ * larger K returns MSA_ERR_UNSUPPORTED.
  */
 msa_status msa_index_topk_qblock(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                                  const void *q_idx, const void *k_idx, const int32_t *kv_lens,

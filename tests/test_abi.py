@@ -82,7 +82,7 @@ def test_index_validation(lib):
     assert index_call(lib, cfg(head_dim=64)) == UNSUPPORTED
     assert index_call(lib, cfg(index_dim=64)) == UNSUPPORTED
     assert index_call(lib, cfg(block_size=64)) == UNSUPPORTED
-    assert index_call(lib, cfg(topk=33)) == UNSUPPORTED
+    assert index_call(lib, cfg(topk=65)) == UNSUPPORTED
     assert index_call(lib, cfg(topk=0)) == INVALID
     assert index_call(lib, cfg(heads_per_group=17)) == UNSUPPORTED
     assert index_call(lib, cfg(index_dtype=7)) == INVALID
@@ -277,6 +277,27 @@ def test_workspace_sizes_follow_shapes(lib):
     # (sequence, group)
     dd = lib.msa_workspace_size(ctypes.byref(c), 16, 1, 131072, 3)
     assert a + d <= dd <= a + d + 16 * 4 * 4 + 256 and dd % 256 == 0
+
+
+def test_topk_limits_and_prefill_workspace_above_32(lib):
+    """K up to 64; the prefill index path keeps its top-K in registers up to
+    K = 32 (no workspace) and above that ranks pooled scores from the
+    workspace; the query-block variant keeps K <= 32."""
+    B, T, N = 1, 4096, 8192
+    assert lib.msa_workspace_size(ctypes.byref(cfg(topk=32)), B, T, N, 0) == 0
+    w64 = lib.msa_workspace_size(ctypes.byref(cfg(topk=64)), B, T, N, 0)
+    assert w64 >= B * T * 4 * (N // 128) * 4 and w64 % 256 == 0
+    assert lib.msa_workspace_size(ctypes.byref(cfg(topk=65)), B, T, N, 0) == ctypes.c_size_t(-1).value
+    c = cfg(topk=64)
+    need = lib.msa_workspace_size(ctypes.byref(c), 2, 64, 1024, 0)
+    assert need >= 2 * 64 * 4 * 8 * 4
+    assert index_call(lib, c, T=64, nws=need - 1) == WORKSPACE  # rejected before any launch
+    assert index_call(lib, c, T=64, ws=None, nws=need) == WORKSPACE
+    c33 = cfg(topk=33)
+    st = lib.msa_index_topk_qblock(ctypes.byref(c33), 1, 256, 1024, FAKE, FAKE, FAKE, None, FAKE,
+                                   None, None)
+    assert st == UNSUPPORTED
+    assert b"topk" in lib.msa_last_error()
 
 
 def test_decode_workspace_holds_pooled_scores_above_16_groups(lib):

@@ -89,11 +89,13 @@ def test_decode_ragged_lengths(orc):
     check_all_rows(orc, pr, G, R, K, lens, None, decode=True, what="decode ragged")
 
 
-def test_chunked_prefill_ragged_cache(orc):
+@pytest.mark.parametrize("K", [16, 64])
+def test_chunked_prefill_ragged_cache(orc, K):
     """Query rows start mid-cache; the cache stride is not a multiple of 128."""
-    G, R, K, Nmax, T = 4, 8, 16, 1000, 300
-    pr = random_problem(2, T, Nmax, G, R, seed=300)
-    check_all_rows(orc, pr, G, R, K, [1000, 400], [700, 50], what="chunked ragged")
+    G, R, Nmax, T = 4, 8, 1000 if K == 16 else 9000, 300
+    pr = random_problem(2, T, Nmax, G, R, seed=300 + K)
+    lens = [Nmax, Nmax // 2]
+    check_all_rows(orc, pr, G, R, K, lens, [Nmax - 300, 50], what="chunked ragged K%d" % K)
 
 
 @pytest.mark.parametrize("G,R,K,T,N", [(1, 1, 1, 40, 300), (3, 5, 7, 5, 700), (3, 5, 7, 6, 700),
@@ -196,7 +198,9 @@ def run_fused_decode(pr, G, R, K, kv_lens, workspace=None, fp8=False):
     # more than 16 groups: the MFMA index kernel writes the pooled scores
     (17, 1, 16, [3000, 1, 2500, 130], False),
     # K = 1 and K = 3: the ranking merges runs of 1 and 4 keys
-    (2, 4, 1, [20000, 300], False), (3, 2, 3, [20000, 777, 5], False)])
+    (2, 4, 1, [20000, 300], False), (3, 2, 3, [20000, 777, 5], False),
+    # K = 40 and 64: runs of 64 keys, eight registers merged; 32 splits
+    (4, 8, 64, [20000, 9000, 130, 8192], False), (2, 4, 40, [3000, 70000], True)])
 def test_decode_step_matches_oracle_and_two_calls(orc, G, R, K, lens, fp8):
     Nmax = max(max(lens), 1)
     lim = 16 if fp8 else 4
@@ -339,10 +343,15 @@ def test_kv_major_prefill_workspace_reuse(orc):
 
 
 @pytest.mark.parametrize("G,R,K,T,N,fp8", [(2, 16, 32, 300, 4500, True), (4, 16, 16, 100, 3000, False),
-                                          (1, 3, 5, 700, 2000, False), (3, 1, 32, 200, 6000, True)])
+                                          (1, 3, 5, 700, 2000, False), (3, 1, 32, 200, 6000, True),
+                                          (2, 8, 64, 300, 12000, False), (2, 4, 48, 150, 9000, True),
+                                          (1, 2, 64, 40, 20000, False)])
 def test_prefill_paths_more_shapes(orc, G, R, K, T, N, fp8):
     """E4M3 with K = 32 (32-slot register top-K), R = 16 (one entry per query
-    tile), R = 3 (tiles of 5 entries), R = 1; all through the KV-major path."""
+    tile), R = 3 (tiles of 5 entries), R = 1; all through the KV-major path;
+    K = 48 and 64 (above the register top-K: pooled scores, then a ranking
+    per row; list entries with slots above 31), the last one on the
+    query-major path (80 (row, group) pairs)."""
     lim = 16 if fp8 else 4
     pr = random_problem(2, T, N, G, R, seed=1900 + G + R + K + T, fp8=fp8, idx_lo=-lim, idx_hi=lim)
     check_all_rows(orc, pr, G, R, K, [N, N - 300], None, fp8=fp8,
