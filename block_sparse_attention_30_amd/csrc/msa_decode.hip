@@ -12,14 +12,16 @@
 //                        groups through LDS, 16x16x32 bf16 (or 16x16x128
 //                        E4M3) MFMA, causal block max in registers; writes
 //                        pooled scores.
-//   topk_rows_kernel     one wavefront per row: bitonic sorts of 64-bit keys
-//                        (score, inverted block id) across lanes plus
-//                        compaction of candidates above a threshold.
-//   sparse_decode_kernel one 8-wave workgroup per (sequence, group, split),
-//                        one 32-token chunk per wave; optionally ranks the
-//                        row's blocks itself; waves merge in LDS into a
-//                        partial per split; with arrival counters (msa_decode)
-//                        the last split of a (sequence, group) merges them all.
+//   topk_rows_kernel     one wavefront per row: a bitonic sort of the lanes'
+//                        best scores sets a threshold, the candidates above it
+//                        are compacted and one bitonic sort of 64-bit keys
+//                        (score, inverted block id) across lanes ranks them.
+//   sparse_decode_kernel one workgroup of 8 or 16 waves per (sequence, group,
+//                        split), one 32-token chunk per wave; optionally
+//                        ranks the row's blocks itself; waves merge in LDS
+//                        into a partial per split; with arrival counters
+//                        (msa_decode) the last split of a (sequence, group)
+//                        merges them all.
 //   combine_kernel       (msa_sparse_attn_decode) log-sum-exp merge of the
 //                        split partials.
 #include "msa_device.h"
@@ -220,7 +222,8 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(
     const int p = qs + t;
     uint64_t top = 0;
     if (p >= 0 && p < kv)
-        top = wave_topk_row(pooled + row * nb_max, p / S + 1, p / S + 1, K, lane, s_buf[wave]);
+        top = wave_topk_row_short(pooled + row * nb_max, p / S + 1, p / S + 1, K, lane,
+                                  s_buf[wave]);
     if (lane < K) {
         sel[row * K + lane] = top ? key_block(top) : -1;
         if (sel_scores) sel_scores[row * K + lane] = top ? key_score(top) : -INFINITY;
@@ -239,34 +242,39 @@ __device__ __forceinline__ float published(const float *p, float v) {
 }
 
 // Decode: the new token of sequence b sits at position kv - 1. Group g's
-// kept blocks give 4*nblk 32-token chunks; workgroup (b, g, split) has eight
-// waves and takes chunks [8*split, 8*split + 8), one per wave, so every load
-// of the split is in flight at once. With `pooled` non-null each workgroup
-// first ranks the row itself (wave 0, from the pooled block scores; split 0
-// also writes sel / sel_scores), otherwise it reads sel. The waves merge in
-// LDS into one unnormalised partial (O, m, l) per split, which
-// combine_kernel merges by log-sum-exp.
-constexpr int kDecWaves = 8;
-constexpr int kDecChunks = kDecWaves;  // chunks per split
+// kept blocks give 4*nblk 32-token chunks; workgroup (b, g, split) has NW
+// waves (16 when the grid fills the GPU, else 8; msa::decode_waves) and
+// takes chunks [NW*split, NW*split + NW), one per wave, so every load of the
+// split is in flight at once (with 16 waves one workgroup fills a CU's LDS:
+// the V staging takes 144 KiB). With `pooled` non-null each workgroup first
+// ranks the row itself (rows of up to kShortRow blocks by wave 0, longer
+// ones by all waves; split 0 also writes sel / sel_scores), otherwise it
+// reads sel. The waves merge in LDS into one unnormalised partial (O, m, l)
+// per split, which combine_kernel merges by log-sum-exp (or, in msa_decode,
+// the last split of (b, g) to finish).
+constexpr int kShortRow = 1024;
 
+template <int NW>
 struct DecodeLds {
-    // Ranking: [8][64] keys of the waves' lists, then [8][64] keys of their
-    // sorted top-K; then the V chunks; then [8][16][128] fp32 outputs.
-    __attribute__((aligned(16))) unsigned char vrows[kDecWaves * kVWave];
+    // Ranking: the waves' candidate lists and sorted runs (2 x NW x 64 keys);
+    // then the waves' V chunks; then [NW][16][128] fp32 outputs (the waves'
+    // merge).
+    __attribute__((aligned(16))) unsigned char vrows[NW * kVWave];
     int sel[KMAX];
     int blocks[KMAX];
     int nblk;
-    float m[kDecWaves * 16], l[kDecWaves * 16];
+    float m[NW * 16], l[NW * 16];
 };
 
-__global__ __launch_bounds__(512) void sparse_decode_kernel(
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sparse_decode_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache,
     const bf16_t *__restrict__ v_cache, const int32_t *__restrict__ kv_lens,
     const float *__restrict__ pooled, int64_t nb_max, int32_t *__restrict__ sel,
     float *__restrict__ sel_scores, int G, int R, int Nmax, int K, int nsplit, float scale_log2,
     float *__restrict__ part_o, float *__restrict__ part_ml, int32_t *__restrict__ counters,
     bf16_t *__restrict__ out, float *__restrict__ lse) {
-    __shared__ DecodeLds L;
+    __shared__ DecodeLds<NW> L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int split = (int)(blockIdx.x % nsplit);
     const int64_t unit = blockIdx.x / nsplit;  // (sequence, group)
@@ -279,13 +287,20 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     bf16x8 qf[4];
     load_query(qf, q + ((int64_t)b * H + (int64_t)g * R) * D, R, lane);
     if (pooled) {
-        // All eight waves rank a share of the row, wave 0 merges their lists.
+        // Every split ranks the row alike (a wave's ranking is shorter than
+        // publishing one split's to the others): wave 0 alone up to kShortRow
+        // blocks, else every wave a share and wave 0 merges their runs.
         // n_load = nb_max: the row's pooled scores are loaded while kv_lens is
         // still in flight.
         uint64_t *kbuf = reinterpret_cast<uint64_t *>(L.vrows);
-        const uint64_t top = block_topk_row<kDecWaves>(pooled + unit * nb_max,
-                                                       p >= 0 ? p / S + 1 : 0, (int)nb_max, K,
-                                                       lane, wave, kbuf, kbuf + kDecWaves * 64);
+        const float *row = pooled + unit * nb_max;
+        const int n = p >= 0 ? p / S + 1 : 0;
+        uint64_t top = 0;
+        if (nb_max <= kShortRow) {
+            if (wave == 0) top = wave_topk_row_short(row, n, (int)nb_max, K, lane, kbuf);
+        } else {
+            top = block_topk_row<NW>(row, n, (int)nb_max, K, lane, wave, kbuf, kbuf + NW * 64);
+        }
         if (wave == 0) {
             if (lane < K) {
                 const int blk = top ? key_block(top) : -1;
@@ -305,7 +320,7 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
         if (lane == 0) L.nblk = n;
     }
     __syncthreads();
-    const int c = split * kDecChunks + wave;  // this wave's chunk
+    const int c = split * NW + wave;  // this wave's chunk
     WaveAttn st;
     wave_attn_init(st);
     if (c < L.nblk * 4) {
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
                      v_cache + ((size_t)b * G + g) * Nmax * D, L.blocks[c >> 2] * S + (c & 3) * 32,
                      p, scale_log2, L.vrows + wave * kVWave, lane);
     }
-    // Merge the eight waves into this split's partial.
+    // Merge the NW waves into this split's partial.
     float *s_o = reinterpret_cast<float *>(L.vrows);
     const int col = lane & 15, kg = lane >> 4;
     if (lane < 16) {
@@ -328,21 +343,21 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
         if (h >= R) continue;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, L.m[w * 16 + h]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, L.m[w * 16 + h]);
         const float mw = L.m[wave * 16 + h];
         const float sc = mw == -INFINITY ? 0.f : exp2f(mw - M);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) s_o[(wave * 16 + h) * D + dt * 16 + col] = st.o[dt][r] * sc;
     }
     __syncthreads();
-    for (int idx = tid; idx < R * D; idx += kDecWaves * 64) {
+    for (int idx = tid; idx < R * D; idx += NW * 64) {
         const int h = idx / D, dd = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, L.m[w * 16 + h]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, L.m[w * 16 + h]);
         float Lsum = 0.f, acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < kDecWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             if (L.m[w * 16 + h] != -INFINITY) Lsum += exp2f(L.m[w * 16 + h] - M) * L.l[w * 16 + h];
             acc += s_o[(w * 16 + h) * D + dd];
         }
@@ -373,9 +388,8 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     // of the same call stored, and the merging workgroup reads each word until
     // it holds its split's value. Coherence of a single atomic location makes
     // that value the one the split stored; the arrival counter only chooses
-    // the merging workgroup. The stores have completed before the arrival is
-    // counted (vmcnt(0)), so the first read finds them.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // the merging workgroup, so it is counted while the partial stores are
+    // still on their way (the merging workgroup's reads wait for them).
     __syncthreads();
     if (tid == 0)
         L.nblk = __hip_atomic_fetch_add(&counters[unit], 1, __ATOMIC_RELAXED,
@@ -383,7 +397,7 @@ __global__ __launch_bounds__(512) void sparse_decode_kernel(
     __syncthreads();
     if (!L.nblk) return;
     // One round of loads per batch of eight splits, merged online.
-    for (int idx = tid; idx < R * D; idx += kDecWaves * 64) {
+    for (int idx = tid; idx < R * D; idx += NW * 64) {
         const int h = idx / D, dd = idx % D;
         const int64_t pu0 = unit * nsplit * R + h;
         float M = -INFINITY, Lsum = 0.f, acc = 0.f;
@@ -491,13 +505,19 @@ static msa_status launch_decode_attention(const msa_config *cfg, int32_t B, int3
                                           float *part_o, float *part_ml, hipStream_t st,
                                           int32_t *counters = nullptr) {
     const int G = cfg->num_kv_groups, R = cfg->heads_per_group, K = cfg->topk;
-    const int nsplit = msa::decode_splits(cfg);
+    const int nsplit = msa::decode_splits(cfg, B);
     const int64_t units = (int64_t)B * G;
-    sparse_decode_kernel<<<(unsigned)(units * nsplit), kDecWaves * 64, 0, st>>>(
-        static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k_cache),
-        static_cast<const bf16_t *>(v_cache), kv_lens, pooled, nb_max, sel, sel_scores, G, R, Nmax,
-        K, nsplit, scale_log2_of(cfg), part_o, part_ml, counters, static_cast<bf16_t *>(out),
-        lse);
+    auto launch = [&](auto kern, int waves) {
+        kern<<<(unsigned)(units * nsplit), waves * 64, 0, st>>>(
+            static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k_cache),
+            static_cast<const bf16_t *>(v_cache), kv_lens, pooled, nb_max, sel, sel_scores, G, R,
+            Nmax, K, nsplit, scale_log2_of(cfg), part_o, part_ml, counters,
+            static_cast<bf16_t *>(out), lse);
+    };
+    if (msa::decode_waves(cfg, B) == 16)
+        launch(sparse_decode_kernel<16>, 16);
+    else
+        launch(sparse_decode_kernel<8>, 8);
     msa_status s = launch_status("sparse decode kernel");
     if (s != MSA_OK || counters) return s;
     combine_kernel<<<(unsigned)(units * R), D, 0, st>>>(part_o, part_ml, G, R, nsplit,
@@ -621,7 +641,7 @@ msa_status decode_step(const msa_config *cfg, int32_t B, int32_t Nmax, const voi
     float *pooled = reinterpret_cast<float *>(base + w.pooled_off);
     int32_t *counters = reinterpret_cast<int32_t *>(base + w.counters_off);
     // The split partials, O then (m, l), are one contiguous run of words.
-    const int64_t n_part = (int64_t)B * cfg->num_kv_groups * msa::decode_splits(cfg) *
+    const int64_t n_part = (int64_t)B * cfg->num_kv_groups * msa::decode_splits(cfg, B) *
                            cfg->heads_per_group * (D + 2);
     s = msa::launch_pooled(cfg, B, 1, Nmax, q_idx, k_idx, kv_lens, nullptr, pooled, w.nb_max, st,
                            counters, reinterpret_cast<uint32_t *>(base + w.part_o_off), n_part);

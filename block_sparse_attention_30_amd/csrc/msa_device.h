@@ -137,10 +137,13 @@ __device__ __forceinline__ bf16_t to_bf16(float v) {
 // zero) in the high half and 0xFFFFFFFF - block in the low half, so a larger
 // key is a better block and equal scores rank the lower block first. Key 0 is
 // "no block".
-__device__ __forceinline__ uint64_t score_key(float s, int blk) {
+__device__ __forceinline__ uint32_t score_bits(float s) {
     const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
-    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)blk);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t score_key(float s, int blk) {
+    return ((uint64_t)score_bits(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)blk);
 }
 
 __device__ __forceinline__ float key_score(uint64_t k) {
@@ -373,6 +376,95 @@ __device__ __forceinline__ uint64_t wave_topk_row(const float *cand, int n, int 
     return top;
 }
 
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic_step_u32(uint32_t x, int lane) {
+    const uint32_t y = xor_lane32<J>(x, lane);
+    const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
+    return keep_max ? (x > y ? x : y) : (x < y ? x : y);
+}
+
+// Bitonic sort of one 32-bit value per lane, descending.
+__device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t x, int lane) {
+    x = bitonic_step_u32<2, 1>(x, lane);
+    x = bitonic_step_u32<4, 2>(x, lane);
+    x = bitonic_step_u32<4, 1>(x, lane);
+    x = bitonic_step_u32<8, 4>(x, lane);
+    x = bitonic_step_u32<8, 2>(x, lane);
+    x = bitonic_step_u32<8, 1>(x, lane);
+    x = bitonic_step_u32<16, 8>(x, lane);
+    x = bitonic_step_u32<16, 4>(x, lane);
+    x = bitonic_step_u32<16, 2>(x, lane);
+    x = bitonic_step_u32<16, 1>(x, lane);
+    x = bitonic_step_u32<32, 16>(x, lane);
+    x = bitonic_step_u32<32, 8>(x, lane);
+    x = bitonic_step_u32<32, 4>(x, lane);
+    x = bitonic_step_u32<32, 2>(x, lane);
+    x = bitonic_step_u32<32, 1>(x, lane);
+    x = bitonic_step_u32<64, 32>(x, lane);
+    x = bitonic_step_u32<64, 16>(x, lane);
+    x = bitonic_step_u32<64, 8>(x, lane);
+    x = bitonic_step_u32<64, 4>(x, lane);
+    x = bitonic_step_u32<64, 2>(x, lane);
+    return bitonic_step_u32<64, 1>(x, lane);
+}
+
+// Top-K (K <= 64) of one row of n pooled scores by one wavefront, the same
+// result as wave_topk_row with a shorter dependency chain for n <= 1024: the
+// first pass ranks only the score halves of the 64 lane maxima (a 32-bit
+// sort); the K-th of them is a score no top-K key lies below, since K lanes
+// hold a key at least that large. Every valid key whose score reaches it is a
+// candidate; when there are at most 64, they are compacted through `buf` (64
+// keys of this wave's LDS) and one 64-bit sort ranks them. Otherwise (n >
+// 1024, or ties that leave more than 64 candidates) wave_topk_row ranks the
+// row. n_load (>= n) entries of cand may be read; cand[i] is the score of
+// block blk0 + i.
+__device__ __forceinline__ uint64_t wave_topk_row_short(const float *cand, int n, int n_load,
+                                                        int K, int lane, uint64_t *buf,
+                                                        int blk0 = 0) {
+    constexpr int kBatch = 16;
+    if (n > 64 * kBatch) return wave_topk_row(cand, n, n_load, K, lane, buf, blk0);
+    float v[kBatch];
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) {
+        const int i = c * 64 + lane;
+        v[c] = i < n_load && i < 64 * kBatch ? cand[i] : 0.f;
+    }
+    uint32_t o[kBatch];
+    uint32_t lm = 0;
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) {
+        const int i = c * 64 + lane;
+        o[c] = i < n ? score_bits(v[c]) : 0u;
+        lm = o[c] > lm ? o[c] : lm;
+    }
+    const uint32_t thr = (uint32_t)__shfl((int)wave_sort_desc_u32(lm, lane), K - 1);
+    // Valid keys at or above the threshold: a per-lane count, then a wave
+    // prefix sum from five ballots of the count bits (count <= 16).
+    int my = 0;
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) my += (c * 64 + lane < n && o[c] >= thr) ? 1 : 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int excl = 0, total = 0;
+#pragma unroll
+    for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t bm = __ballot((my >> bit) & 1);
+        excl += __popcll(bm & below) << bit;
+        total += __popcll(bm) << bit;
+    }
+    if (total > 64) return wave_topk_row(cand, n, n_load, K, lane, buf, blk0);
+    int pos = excl;
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) {
+        const int i = c * 64 + lane;
+        if (i < n && o[c] >= thr) buf[pos++] = score_key(v[c], blk0 + i);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the list writes have landed
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t x = wave_sort_desc(lane < total ? buf[lane] : 0, lane);
+    __builtin_amdgcn_wave_barrier();
+    return lane < K ? x : 0;
+}
+
 // Bitonic stages 2*RUN .. 64 over one key per lane, for lanes that already
 // form runs of RUN keys with even runs descending and odd runs ascending (the
 // state after stage RUN); ends descending, lane 0 the largest. RUN = 1 is a
@@ -438,8 +530,9 @@ __device__ __forceinline__ uint64_t merge_runs(const uint64_t *runs, int nkeys, 
     return r[0];
 }
 
-// Top-K (K <= 64) of one row by the NW (<= 8) waves of a workgroup: wave w
-// ranks a contiguous share of the row's n pooled scores with wave_topk_row
+// Top-K (K <= 64) of one row by the NW (<= 16) waves of a workgroup: wave w
+// ranks a contiguous share of the row's n pooled scores with
+// wave_topk_row_short
 // and writes its K best keys, zero-padded to Kp (the next power of two), to
 // `runs` (LDS, NW * 64 keys); after a barrier wave 0 merges the NW sorted
 // runs. `bufs` is NW * 64 keys of LDS (wave_topk_row's lists). Every thread of
@@ -453,7 +546,7 @@ __device__ __forceinline__ uint64_t block_topk_row(const float *cand, int n, int
     const int chunk = (n_load + NW - 1) / NW;
     const int b0 = wave * chunk;
     const int nw = min(max(n - b0, 0), chunk), nlw = min(max(n_load - b0, 0), chunk);
-    const uint64_t mine = wave_topk_row(cand + b0, nw, nlw, K, lane, bufs + wave * 64, b0);
+    const uint64_t mine = wave_topk_row_short(cand + b0, nw, nlw, K, lane, bufs + wave * 64, b0);
     const int kp = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : K <= 16 ? 16 : K <= 32 ? 32 : 64;
     if (lane < kp) runs[wave * kp + lane] = mine;  // lanes K..kp-1 hold 0
     __syncthreads();

@@ -141,8 +141,14 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
     return w;
 }
 
-int32_t decode_splits(const msa_config *cfg) {
-    return (4 * cfg->topk + kDecodeChunksPerSplit - 1) / kDecodeChunksPerSplit;
+int32_t decode_waves(const msa_config *cfg, int32_t B) {
+    const int64_t splits16 = (4 * cfg->topk + 15) / 16;
+    return (int64_t)B * cfg->num_kv_groups * splits16 >= kDecodeFillWorkgroups ? 16 : 8;
+}
+
+int32_t decode_splits(const msa_config *cfg, int32_t B) {
+    const int32_t w = decode_waves(cfg, B);
+    return (4 * cfg->topk + w - 1) / w;
 }
 
 DecodeWs decode_ws(const msa_config *cfg, int32_t B, int32_t Nmax, bool with_index) {
@@ -154,7 +160,8 @@ DecodeWs decode_ws(const msa_config *cfg, int32_t B, int32_t Nmax, bool with_ind
     // prefill one above).
     const size_t pooled =
         with_index ? round_up((size_t)B * cfg->num_kv_groups * (size_t)w.nb_max * 4, kWsAlign) : 0;
-    const size_t units = (size_t)B * cfg->num_kv_groups * decode_splits(cfg) * cfg->heads_per_group;
+    const size_t units =
+        (size_t)B * cfg->num_kv_groups * decode_splits(cfg, B) * cfg->heads_per_group;
     w.part_o_off = pooled;
     // (m, l) directly after O (units * 512 bytes keep the alignment): the
     // decode kernels treat the partials as one run of units * (d + 2) words.
@@ -317,7 +324,7 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
     if (s != MSA_OK) return s;
     if ((s = check_dims(B, T, Nmax)) != MSA_OK) return s;
     if (B == 0 || T == 0) return MSA_OK;
-    if ((int64_t)B * T * cfg->num_kv_groups * decode_splits(cfg) > ((int64_t)1 << 31) - 1)
+    if ((int64_t)B * T * cfg->num_kv_groups * decode_splits(cfg, B) > ((int64_t)1 << 31) - 1)
         return fail(MSA_ERR_UNSUPPORTED, "too many (row, group) work items");
     if (which == MSA_WS_SPARSE_PREFILL) {
         const PrefillWs pw = prefill_ws(cfg, B, T, Nmax);

@@ -107,8 +107,13 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
 
 // Decode attention: split partials [B*G][nsplit][R] x (128 + 2) fp32, after
 // the pooled scores when the call also runs the index branch (msa_decode).
-constexpr int kDecodeChunksPerSplit = 8;
-int32_t decode_splits(const msa_config *cfg);
+// A split is one workgroup of decode_waves(cfg, B) waves, one 32-token chunk
+// each: 16 waves when the (sequence, group, split) grid of 16-wave
+// workgroups has at least kDecodeFillWorkgroups of them, else 8 (more, smaller
+// workgroups for few sequences).
+constexpr int64_t kDecodeFillWorkgroups = 256;
+int32_t decode_waves(const msa_config *cfg, int32_t B);
+int32_t decode_splits(const msa_config *cfg, int32_t B);
 // msa_decode also keeps one arrival counter per (sequence, group), zeroed by
 // the index kernel of the same call.
 struct DecodeWs {
