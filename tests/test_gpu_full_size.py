@@ -5,6 +5,8 @@ configuration the benchmark uses:
                                                  oracle);
   decode, 4 sequences x 1048576 tokens           every row, uniform lengths and
                                                  mixed {256k, 512k, 768k, 1M};
+  decode, 16 sequences of ragged lengths up to   every row (rows longer than
+  196608 tokens                                  1024 blocks, 16-wave form);
   both decode batches with E4M3 index data       every row (uniform lengths);
   prefill, 131072 tokens (4 groups x 8 heads)    a stratified sample of 2048 rows;
   chunked prefill, 1048576 tokens in 32768-row   all 32 chunks: the first, a
@@ -93,6 +95,18 @@ def test_decode_B4_N1M_all_rows(orc):
 
 def test_decode_B4_mixed_lengths_all_rows(orc):
     check_decode_workload(orc, wl.workload(4, mixed=True))
+
+
+def test_decode_B16_ragged_rows_past_1024_blocks(orc):
+    # Sixteen sequences of ragged lengths up to 196608 tokens: 1536 pooled
+    # blocks per row, so the attention kernel runs its 16-wave form (the grid
+    # fills the GPU) with every wave ranking a share of the row; the 1- and
+    # 2-token sequences leave most waves' shares empty. Seeds of the c2 decode.
+    lens = [196608, 150000, 140000, 131073, 131072, 100000, 70000, 1, 2, 129, 65536, 180000,
+            160001, 5000, 196607, 135000]
+    w = wl.Workload(2, "decode_B16_ragged_N196608", "decode", 16, 1, 196608, lens,
+                    [n - 1 for n in lens])
+    check_decode_workload(orc, w)
 
 
 def test_decode_B16_N131072_fp8_index_all_rows(orc):
