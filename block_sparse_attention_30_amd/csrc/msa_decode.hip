@@ -264,6 +264,8 @@ struct DecodeLds {
     int blocks[KMAX];
     int nblk;
     float m[NW * 16], l[NW * 16];
+    float sc[NW * 16];     // each wave's weight per head
+    float hm[16], hl[16];  // per head: max of the waves' m, weighted sum of l
 };
 
 template <int NW>
@@ -329,7 +331,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_decode_kernel(
                      v_cache + ((size_t)b * G + g) * Nmax * D, L.blocks[c >> 2] * S + (c & 3) * 32,
                      p, scale_log2, L.vrows + wave * kVWave, lane);
     }
-    // Merge the NW waves into this split's partial.
+    // Merge the NW waves into this split's partial: per head h the max M of
+    // the waves' m, each wave's weight exp2(m_w - M) and the weighted sum L of
+    // their l are computed once, by one thread per (wave, head); each wave then
+    // writes its O scaled by its weight, and every thread sums one (head, d)
+    // element over the waves.
     float *s_o = reinterpret_cast<float *>(L.vrows);
     const int col = lane & 15, kg = lane >> 4;
     if (lane < 16) {
@@ -337,30 +343,41 @@ __global__ __launch_bounds__(NW * 64) void sparse_decode_kernel(
         L.l[wave * 16 + lane] = st.l;
     }
     __syncthreads();
+    if (tid < NW * 16 && (tid & 15) < R) {
+        const int w0 = tid >> 4, h = tid & 15;
+        float mv[NW];
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            mv[w] = L.m[w * 16 + h];
+            M = fmaxf(M, mv[w]);
+        }
+        L.sc[tid] = mv[w0] == -INFINITY ? 0.f : exp2f(mv[w0] - M);
+        if (w0 == 0) {
+            float Lsum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                if (mv[w] != -INFINITY) Lsum += exp2f(mv[w] - M) * L.l[w * 16 + h];
+            L.hm[h] = M;
+            L.hl[h] = Lsum;
+        }
+    }
+    __syncthreads();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int h = 4 * kg + r;
         if (h >= R) continue;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, L.m[w * 16 + h]);
-        const float mw = L.m[wave * 16 + h];
-        const float sc = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        const float sc = L.sc[wave * 16 + h];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) s_o[(wave * 16 + h) * D + dt * 16 + col] = st.o[dt][r] * sc;
     }
     __syncthreads();
     for (int idx = tid; idx < R * D; idx += NW * 64) {
         const int h = idx / D, dd = idx % D;
-        float M = -INFINITY;
+        float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, L.m[w * 16 + h]);
-        float Lsum = 0.f, acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            if (L.m[w * 16 + h] != -INFINITY) Lsum += exp2f(L.m[w * 16 + h] - M) * L.l[w * 16 + h];
-            acc += s_o[(w * 16 + h) * D + dd];
-        }
+        for (int w = 0; w < NW; ++w) acc += s_o[(w * 16 + h) * D + dd];
+        const float M = L.hm[h], Lsum = L.hl[h];
         const int64_t pu = (unit * nsplit + split) * R + h;
         if (counters) {
             // Agent-scope stores (written through the XCD's L2): the merging
