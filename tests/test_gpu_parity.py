@@ -258,6 +258,35 @@ def test_decode_many_small_sequences(orc):
     compare_lse(lse.reshape(olse.shape), olse, "many sequences")
 
 
+@pytest.mark.parametrize("B,N,lens", [
+    # 16 sequences x 4 groups: the 16-wave attention kernel, rows of up to
+    # 128 blocks ranked by one wave
+    (16, 16384, [16384] * 8 + [9000, 129, 16383, 8192, 3000, 130, 12000, 16000]),
+    # rows of up to 2048 blocks: every wave ranks a share (8-wave kernel)
+    (2, 262144, [262144, 140000])])
+def test_decode_all_ties_take_the_general_ranking(orc, B, N, lens):
+    """Zero index queries tie every pooled score at 0 (-0.0 products in every
+    other sequence), so far more than 64 candidates reach the ranking's
+    threshold and it takes its general path; the K lowest blocks win, in
+    msa_decode and in msa_index_topk alike."""
+    G, R, K = 4, 8, 16
+    pr = random_problem(B, 1, N, G, R, seed=1300 + B)
+    pr["qi"][:] = 0
+    pr["qi"][1::2] = 0x8000
+    sel, sc, out, lse = run_fused_decode(pr, G, R, K, lens)
+    kv = np.array(lens, np.int32)
+    ocfg = oracle_cfg(G, R, K)
+    osel, _ = orc.index_topk(ocfg, pr["qi"], pr["ki"], kv, kv - 1)
+    assert np.array_equal(sel.reshape(osel.shape), osel)
+    full = kv >= K * 128
+    assert (sel.reshape(osel.shape)[full] == np.arange(K, dtype=np.int32)).all()
+    oout, olse = orc.sparse_attn(ocfg, pr["q"], pr["k"], pr["v"], kv, kv - 1, osel)
+    compare_out(out.reshape(oout.shape), oout, "ties, msa_decode")
+    compare_lse(lse.reshape(olse.shape), olse, "ties, msa_decode")
+    s2, _, _, _ = run_gpu(pr, G, R, K, lens, None, decode=True)
+    assert np.array_equal(s2, sel)
+
+
 @pytest.mark.parametrize("B,T,G,N,lens,qstart", [
     (3, 1, 4, 9000, [9000, 4100, 1], None),          # streaming kernel, one row per group
     (2, 4, 4, 3000, [3000, 130], None),               # streaming kernel, 16 rows
