@@ -38,7 +38,9 @@ Back-to-back steps re-read the same caches, so part of a working set that
 fits the 256 MB last-level cache may be served from it; each decode leg also
 reports a cold-cache time (a 1 GiB read between steps, per-step events). A
 streaming read of 512 MiB (best of plain and nontemporal loads), timed in the
-same run, gives the measured HBM read ceiling next to the published 8 TB/s.
+same run, gives the measured HBM read ceiling next to the published 8 TB/s,
+and a streaming copy of 512 MiB the ceiling of an even read/write mix (the
+token-level sparse prefill's kernels read and write about as much).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-chunked]
        [--decode-only] [--prefill-only] [--no-cpu-baseline] [--calibrate-copy]
@@ -102,6 +104,9 @@ def _probe_lib():
     lib.msa_probe_stream_read.restype = ctypes.c_int
     lib.msa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.msa_probe_stream_copy.restype = ctypes.c_int
+    lib.msa_probe_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
@@ -905,6 +910,39 @@ def read_ceiling(torch, mib=512, reps=20):
     return round(best, 1)
 
 
+def copy_ceiling(torch, mib=512, reps=20):
+    """The HBM bandwidth of an even mix of reads and writes, measured live: a
+    streaming copy of `mib` MiB between two device buffers (16-byte loads and
+    stores) from the probe library, best of plain and nontemporal stores and
+    of two workgroup counts; bytes counted = read + written."""
+    import ctypes
+    lib = _probe_lib()
+    nbytes = mib << 20
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = 0.0
+    for nt, wgs in ((0, 2048), (0, 16384), (1, 2048), (1, 16384)):
+        def launch():
+            rc = lib.msa_probe_stream_copy(ctypes.c_void_p(src.data_ptr()),
+                                           ctypes.c_void_p(dst.data_ptr()), nbytes, wgs, nt,
+                                           stream)
+            if rc != 0:
+                raise RuntimeError("stream-copy probe failed: %d" % rc)
+        for _ in range(3):
+            launch()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            launch()
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9)
+    del src, dst
+    return round(best, 1)
+
+
 def mfma_ceiling(torch, wgs=1024, reps=10):
     """The MFMA throughput measured live: the probe library's loop of
     independent 32x32x16 bf16 (or 32x32x64 E4M3) MFMAs with no memory
@@ -1028,6 +1066,11 @@ def main():
                             "what": "streaming read of 512 MiB (16-byte loads, best of plain and "
                                     "nontemporal loads and of 2048 and 16384 workgroups), "
                                     "measured in this run"}
+    line["copy_ceiling"] = {"value": copy_ceiling(torch), "unit": "GB/s",
+                            "what": "streaming copy of 512 MiB between two buffers (16-byte loads "
+                                    "and stores, best of plain and nontemporal stores and of 2048 "
+                                    "and 16384 workgroups), read + written bytes, measured in this "
+                                    "run: the ceiling of an even read/write mix"}
     line["mfma_ceiling"] = mfma_ceiling(torch)
     if args.calibrate_copy:
         line["copy_calibration"] = copy_calibration(torch)

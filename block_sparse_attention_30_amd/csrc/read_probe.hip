@@ -1,6 +1,8 @@
 // Ceiling probes for the benchmark, to set beside the published peaks:
 //   - a streaming read of a device buffer (plain or nontemporal loads), the
 //     HBM read bandwidth a kernel that only loads can reach on this GPU;
+//   - a streaming copy between two device buffers (plain or nontemporal
+//     stores), the bandwidth of an even mix of reads and writes;
 //   - a loop of independent MFMAs (32x32x16 bf16 or 32x32x64 OCP E4M3) with
 //     no memory traffic, the matrix throughput a kernel can sustain at the
 //     clock the chip holds under that load.
@@ -37,6 +39,33 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restric
     }
     const unsigned r = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
     if (r == 0x9E3779B9u) sink[blockIdx.x] = r;
+}
+
+// Workgroup w copies 16-byte words [w * per_wg, (w + 1) * per_wg) of src to
+// dst, eight loads per thread in flight, plain or nontemporal stores.
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4 *__restrict__ src,
+                                                          u32x4 *__restrict__ dst, size_t per_wg) {
+    constexpr int U = 8;
+    const size_t base = (size_t)blockIdx.x * per_wg;
+    for (size_t i = threadIdx.x; i < per_wg; i += 256 * U) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t j = i + (size_t)u * 256;
+            if (j < per_wg) v[u] = src[base + j];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t j = i + (size_t)u * 256;
+            if (j < per_wg) {
+                if (NT)
+                    __builtin_nontemporal_store(v[u], dst + base + j);
+                else
+                    dst[base + j] = v[u];
+            }
+        }
+    }
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -107,6 +136,23 @@ int msa_probe_mfma(int fp8, int wgs, int iters, void *sink, double *flops, void 
         mfma_loop_kernel<true><<<(unsigned)wgs, 256, 0, st>>>(iters, static_cast<unsigned *>(sink));
     else
         mfma_loop_kernel<false><<<(unsigned)wgs, 256, 0, st>>>(iters, static_cast<unsigned *>(sink));
+    return (int)hipGetLastError();
+}
+
+// Copies `bytes` (a multiple of 16 * wgs) from `src` to `dst` with `wgs`
+// workgroups on `stream`, with nontemporal stores if `nontemporal` is nonzero.
+// Returns 0, or -1 on bad arguments, or the HIP error code of the launch.
+int msa_probe_stream_copy(const void *src, void *dst, size_t bytes, int wgs, int nontemporal,
+                          void *stream) {
+    if (!src || !dst || wgs <= 0 || bytes == 0 || bytes % (16 * (size_t)wgs) != 0) return -1;
+    const size_t per_wg = bytes / 16 / (size_t)wgs;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (nontemporal)
+        stream_copy_kernel<true><<<(unsigned)wgs, 256, 0, st>>>(
+            static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), per_wg);
+    else
+        stream_copy_kernel<false><<<(unsigned)wgs, 256, 0, st>>>(
+            static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), per_wg);
     return (int)hipGetLastError();
 }
 
