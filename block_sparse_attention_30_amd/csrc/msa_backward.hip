@@ -172,9 +172,67 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_tile_kernel(
         if (kBwdCols < ncol) fetch(kBwdCols);
     }
     __syncthreads();
+    // This wave's K^T operands of the dq product (d tiles 2*(w>>1) + i, all
+    // 128 keys; keys 4*kg + 0..3 and 16 + 4*kg + 0..3 of each 32-key chunk),
+    // read transposed from LDS once per tile. The K staging area then holds
+    // the second dS buffer.
+    bf16x8 kT[S / 32][2];
+#pragma unroll
+    for (int cc = 0; cc < S / 32; ++cc)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const unsigned char *p =
+                k_s + (cc * 32 + 4 * kg + (col >> 2)) * kVRow + (2 * (wave >> 1) + i) * 32 + (col & 3) * 8;
+            const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 16 * kVRow);
+            kT[cc][i] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): k_s is read before it is reused
+    auto ds_buf = [&](int i) -> unsigned char * { return i ? k_s : ds_s; };
+    static_assert(S * kDsRow <= S * kVRow, "a dS buffer fits the K staging area");
+    // dq^T = K^T dS^T of the batch at column cbq (its dS in dsb), tau applied:
+    // wave w owns column tiles 2*(w&1) + j and d tiles 2*(w>>1) + i; dS^T is
+    // read transposed from LDS in the K^T operands' key order.
+    auto dq_batch = [&](int cbq, const unsigned char *dsb) {
+        f32x4 dqa[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dqa[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < S / 32; ++cc) {
+            const int krow = cc * 32 + 4 * kg + (col >> 2);
+            bf16x8 bq[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const unsigned char *p = dsb + krow * kDsRow + (2 * (wave & 1) + j) * 32 + (col & 3) * 8;
+                const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 16 * kDsRow);
+                bq[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) dqa[i][j] = mfma16(kT[cc][i], bq[j], dqa[i][j]);
+        }
+        // Lane holds column 16*ct + col, d = 16*dt + 4*kg + r.
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int tc = cbq + 16 * (2 * (wave & 1) + j) + col;
+            const int slot = s_slot[tc];
+            // A column without an entry stores into the trash area (no
+            // branch, so waits count the same stores on every path).
+            bf16_t *op = (slot >= 0 ? part_dq + ((int64_t)slot * R + tc % R) * D
+                                    : reinterpret_cast<bf16_t *>(trash) + (tc % R) * D) +
+                         4 * kg;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                *reinterpret_cast<u32x2 *>(op + (2 * (wave >> 1) + i) * 16) =
+                    u32x2{pack_bf16x2(tau * dqa[i][j][0], tau * dqa[i][j][1]),
+                          pack_bf16x2(tau * dqa[i][j][2], tau * dqa[i][j][3])};
+        }
+    };
     for (int cb = 0, cur = 0; cb < ncol; cb += kBwdCols, cur ^= 1) {
-        // The other buffer was last read in the previous batch, which ended
-        // with a barrier.
+        // The other q / dout buffer was last read in the previous batch,
+        // which ended with a barrier.
         if (cb + kBwdCols < ncol) {
             stage(cur ^ 1);
             if (cb + 2 * kBwdCols < ncol) fetch(cb + 2 * kBwdCols);
@@ -225,7 +283,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_tile_kernel(
                     }
                     pb[hf][kt2] = pack_bf16x4(pv[0], pv[1], pv[2], pv[3]);
                     dsb[hf][kt2] = pack_bf16x4(dsv[0], dsv[1], dsv[2], dsv[3]);
-                    *reinterpret_cast<v4i16 *>(ds_s + (16 * (KT * wave + kt2) + col) * kDsRow +
+                    *reinterpret_cast<v4i16 *>(ds_buf(cur) + (16 * (KT * wave + kt2) + col) * kDsRow +
                                                (16 * ct + 4 * kg) * 2) = dsb[hf][kt2];
                 }
             }
@@ -257,54 +315,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_tile_kernel(
                 }
             }
         }
-        __syncthreads();  // the batch's dS is in LDS
-        // dq^T = K^T dS^T for the batch, tau applied: wave w owns column
-        // tiles 2*(w&1) + j and d tiles 2*(w>>1) + i; K^T and dS^T are read
-        // transposed from LDS, keys 4*kg + 0..3 and 16 + 4*kg + 0..3 of each
-        // 32-key chunk in both operands.
-        {
-            f32x4 dqa[2][2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) dqa[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int cc = 0; cc < S / 32; ++cc) {
-                const int krow = cc * 32 + 4 * kg + (col >> 2);
-                bf16x8 bq[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const unsigned char *p = ds_s + krow * kDsRow + (2 * (wave & 1) + j) * 32 + (col & 3) * 8;
-                    const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 16 * kDsRow);
-                    bq[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const unsigned char *p = k_s + krow * kVRow + (2 * (wave >> 1) + i) * 32 + (col & 3) * 8;
-                    const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 16 * kVRow);
-                    const bf16x8 ka = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) dqa[i][j] = mfma16(ka, bq[j], dqa[i][j]);
-                }
-            }
-            // Lane holds column 16*ct + col, d = 16*dt + 4*kg + r.
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int tc = cb + 16 * (2 * (wave & 1) + j) + col;
-                const int slot = s_slot[tc];
-                // A column without an entry stores into the trash area (no
-                // branch, so waits count the same stores on every path).
-                bf16_t *op = (slot >= 0 ? part_dq + ((int64_t)slot * R + tc % R) * D
-                                        : reinterpret_cast<bf16_t *>(trash) + (tc % R) * D) +
-                             4 * kg;
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    *reinterpret_cast<u32x2 *>(op + (2 * (wave >> 1) + i) * 16) =
-                        u32x2{pack_bf16x2(tau * dqa[i][j][0], tau * dqa[i][j][1]),
-                              pack_bf16x2(tau * dqa[i][j][2], tau * dqa[i][j][3])};
-            }
-        }
-        __syncthreads();  // this batch's buffers are read, the next one is staged
+        // The previous batch's dq (its dS in the other buffer) overlaps this
+        // batch's products across the waves; then one barrier: this batch's
+        // dS is complete, the previous dS buffer and this q / dout buffer are
+        // free, and the next batch is staged.
+        if (cb > 0) dq_batch(cb - kBwdCols, ds_buf(cur ^ 1));
+        __syncthreads();
+    }
+    if (ncol > 0) {
+        const int last = (ncol - 1) / kBwdCols;
+        dq_batch(last * kBwdCols, ds_buf(last & 1));
     }
     // The tile's partial: [K rows 0..127][d] then [V rows][d], fp32 (tau not
     // yet applied to dK). Lane holds d = dt*16 + 4*kg + r of key col.
