@@ -98,7 +98,7 @@ def decode_bytes(w):
 
 
 def _probe_lib():
-    """The benchmark's streaming-read probe (libmsa_probe.so)."""
+    """The benchmark's ceiling probes (libmsa_probe.so)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_30_amd", "libmsa_probe.so"))
     lib.msa_probe_stream_read.restype = ctypes.c_int

@@ -1,6 +1,7 @@
 """Builds libmsa.so in-tree: the host validation unit with g++, the gfx950
 kernels with hipcc, linked into one shared library next to this file; and
-libmsa_probe.so, the benchmark's streaming-read probe."""
+libmsa_probe.so, the benchmark's ceiling probes (streaming read, streaming
+copy, MFMA loop)."""
 from __future__ import annotations
 
 import os
@@ -12,8 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libmsa.so")
-# The benchmark's streaming-read probe (measured HBM read ceiling), a
-# separate object: nothing in libmsa uses it.
+# The benchmark's ceiling probes (measured HBM read and copy ceilings, MFMA
+# loop), a separate object: nothing in libmsa uses it.
 PROBE_LIBRARY = os.path.join(PKG, "libmsa_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 # Kernel sources (each with its entry points), sharing msa_device.h.
