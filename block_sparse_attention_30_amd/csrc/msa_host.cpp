@@ -117,6 +117,15 @@ PrefillWs prefill_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax, 
     w.nb_max = ((int64_t)Nmax + kBlock - 1) / kBlock;
     w.nlists = (int64_t)B * groups * w.nb_max;
     w.nslots = (int64_t)B * rows * groups * K;
+    if (!backward) {
+        // A short prefill has few entries: fewer rounds per tile (down to one
+        // per wave), so that a pass still has about kPfFillTiles tiles to
+        // spread over the chip. (The backward keeps full tiles: its per-tile
+        // dk/dv partials are budgeted for them.)
+        const int32_t round = kPfWaves * kPfNq * (16 / (int32_t)R);
+        while (w.entries_per_tile > round && w.nslots / w.entries_per_tile < kPfFillTiles)
+            w.entries_per_tile /= 2;
+    }
     w.max_tiles = (w.nslots + w.entries_per_tile - 1) / w.entries_per_tile + w.nlists;
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };

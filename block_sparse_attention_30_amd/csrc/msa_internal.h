@@ -83,6 +83,7 @@ constexpr size_t kPfBitmapBudget = (size_t)1 << 30;
 constexpr int kPfWaves = 4;       // waves per attention workgroup
 constexpr int kPfNq = 2;          // 16-column query tiles per wave
 constexpr int kPfRounds = 16;     // passes of every wave over its tiles per workgroup
+constexpr int64_t kPfFillTiles = 1024;  // fewer rounds per tile below this many tiles a pass
 int32_t prefill_entries_per_tile(int32_t R);
 struct PrefillWs {
     bool kv_major;
