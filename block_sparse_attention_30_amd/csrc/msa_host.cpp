@@ -60,15 +60,17 @@ static msa_status check_dims(int32_t B, int32_t T, int32_t Nmax) {
     return MSA_OK;
 }
 
+bool index_uses_pooled(const msa_config *cfg, int32_t B, int32_t T) {
+    const int64_t rows = (int64_t)T * cfg->num_kv_groups;
+    if (rows <= kScanMaxRows || cfg->topk > kPrefillRegTopk) return true;
+    return (rows + kIdxTileRows - 1) / kIdxTileRows * B < kIdxRegMinWgs;
+}
+
 IndexWs index_ws(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax) {
     IndexWs w{};
     w.nb_max = ((int64_t)Nmax + kBlock - 1) / kBlock;
     w.pooled_off = 0;
-    // The streaming (decode) path and the prefill path with K above the
-    // register top-K keep pooled scores; the prefill kernel otherwise ranks
-    // rows in registers.
-    const bool scan = (int64_t)T * cfg->num_kv_groups <= kScanMaxRows;
-    const bool pooled = scan || cfg->topk > kPrefillRegTopk;
+    const bool pooled = index_uses_pooled(cfg, B, T);
     w.pooled_bytes =
         pooled ? (size_t)B * (size_t)T * (size_t)cfg->num_kv_groups * (size_t)w.nb_max * 4 : 0;
     w.total = round_up(w.pooled_bytes, kWsAlign);

@@ -20,6 +20,16 @@ constexpr int kMaxTopk = 64;
 constexpr int kPrefillRegTopk = 32;
 constexpr int kMaxHeadsPerGroup = 16;
 constexpr int kScanMaxRows = 16;  // T*G at or below this uses the streaming index kernel
+// The MFMA prefill index kernel takes kIdxTileRows (row, group) rows of one
+// sequence per workgroup. With fewer than kIdxRegMinWgs such workgroups (a
+// short prefill) msa_index_topk splits every tile's key blocks over several
+// workgroups instead, writing pooled scores, and ranks the rows afterwards.
+constexpr int kIdxTileRows = 256;
+constexpr int64_t kIdxRegMinWgs = 64;
+// msa_index_topk's path: pooled scores in the workspace, then a wavefront per
+// row ranks them (decode shapes, K above the register top-K, short
+// prefills); otherwise the prefill kernel ranks each row in registers.
+bool index_uses_pooled(const msa_config *cfg, int32_t B, int32_t T);
 constexpr size_t kWsAlign = 256;
 
 
@@ -60,10 +70,9 @@ msa_status check_sparse_args(const msa_config *cfg, int32_t B, int32_t T, int32_
                              const void *out, const float *lse, const void *workspace,
                              size_t ws_bytes, int32_t which);
 
-// Workspace layout: the streaming index path (T*G <= kScanMaxRows, and
-// msa_decode) and the prefill path with K > kPrefillRegTopk keep the pooled
-// block scores of every row, [B*T*G][ceil(Nmax/S)] fp32. The prefill index
-// path with K <= kPrefillRegTopk needs none.
+// Workspace layout: when index_uses_pooled (and in msa_decode) the index
+// branch keeps the pooled block scores of every row, [B*T*G][ceil(Nmax/S)]
+// fp32; the register top-K path needs none.
 struct IndexWs {
     size_t pooled_off, pooled_bytes, total;
     int64_t nb_max;  // ceil(Nmax / S)

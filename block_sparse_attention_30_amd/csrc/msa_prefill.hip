@@ -47,7 +47,7 @@ namespace {
 // over the four row tiles plus one exchange with lane l^32. bf16 keys use
 // 32x32x16 bf16 MFMAs (8 per row tile and column tile), OCP E4M3 keys
 // 32x32x64 f8f6f4 MFMAs with unit scales (2 per row tile and column tile).
-constexpr int kPfRows = 256;
+constexpr int kPfRows = msa::kIdxTileRows;
 
 // Physical 16-byte slot of logical piece `piece` of k_idx row `row` in the
 // staged tile: bf16 rows (16 pieces) swizzle by row & 15; E4M3 rows (8 pieces,
@@ -94,7 +94,8 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     const unsigned char *__restrict__ q_idx, const unsigned char *__restrict__ k_idx,
     const int32_t *__restrict__ kv_lens, const int32_t *__restrict__ q_start,
     float *__restrict__ pooled, int T, int G, int Nmax, int64_t nb_max, int K,
-    int32_t *__restrict__ sel, float *__restrict__ sel_scores, int nslots = 0) {
+    int32_t *__restrict__ sel, float *__restrict__ sel_scores, int nslots = 0,
+    int blk_split = 0) {
     constexpr int kRowBytes = DI * (F8 ? 1 : 2);
     constexpr int kRowPieces = kRowBytes / 16;
     constexpr int kRuns = S * kRowBytes / 1024 / 4;  // 1 KiB staging loads per wave per block
@@ -122,6 +123,11 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     }
     if (KC == 0 && p_hi < 0) return;
     const int nblk = (p_hi >= 0 && p_hi >= p_lo) ? p_hi / S + 1 : 0;
+    // Pooled scores only: workgroup z of a row tile takes key blocks
+    // [z * blk_split, (z + 1) * blk_split) (every block has one writer).
+    const int blo = KC == 0 && blk_split > 0 ? (int)blockIdx.z * blk_split : 0;
+    const int bhi = KC == 0 && blk_split > 0 ? min(nblk, blo + blk_split) : nblk;
+    if (KC == 0 && blo >= bhi) return;
 
     const int j = lane & 31, half = lane >> 5;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
         __builtin_amdgcn_s_barrier();
         if constexpr (QB)
             if (blk > 0) qb_offer(blk - 1);
-        if (blk + 1 < nblk) stage(blk + 1, lds_buf[(blk + 1) & 1]);
+        if (blk + 1 < bhi) stage(blk + 1, lds_buf[(blk + 1) & 1]);
         const unsigned char *lds = lds_buf[blk & 1];
         float cm0 = -INFINITY, cm1 = -INFINITY;
         // Two row tiles at a time: four independent accumulator chains.
@@ -287,9 +293,9 @@ __global__ __launch_bounds__(256, 2) void idx_prefill_kernel(
     };
     // Blocks [0, n_plain) end at or before the first row's position.
     const int n_plain = p_lo >= 0 ? min((p_lo + 1) / S, nblk) : 0;
-    if (nblk > 0) stage(0, lds_buf[0]);
-    for (int blk = 0; blk < n_plain; ++blk) do_block(BoolTag<false>{}, blk);
-    for (int blk = n_plain; blk < nblk; ++blk) do_block(BoolTag<true>{}, blk);
+    if (bhi > blo) stage(blo, lds_buf[blo & 1]);
+    for (int blk = blo; blk < min(n_plain, bhi); ++blk) do_block(BoolTag<false>{}, blk);
+    for (int blk = max(n_plain, blo); blk < bhi; ++blk) do_block(BoolTag<true>{}, blk);
     if constexpr (QB) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
@@ -1115,6 +1121,7 @@ void build_pass_lists(const PrefillWs &w, char *base, const int32_t *sel,
 
 // Pooled block scores of T*G > kScanMaxRows rows: the MFMA prefill index
 // kernel without the top-K epilogue.
+constexpr int64_t kIdxSplitWgs = 512;
 msa_status launch_prefill_pooled(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                                  const void *q_idx, const void *k_idx, const int32_t *kv_lens,
                                  const int32_t *q_start, float *pooled, int64_t nb_max,
@@ -1124,13 +1131,21 @@ msa_status launch_prefill_pooled(const msa_config *cfg, int32_t B, int32_t T, in
     const bool f8 = cfg->index_dtype == MSA_FP8_E4M3;
     const unsigned char *qi = static_cast<const unsigned char *>(q_idx);
     const unsigned char *ki = static_cast<const unsigned char *>(k_idx);
-    const dim3 grid((unsigned)((rows + kPfRows - 1) / kPfRows), (unsigned)B);
+    // A short prefill's few row tiles split their key blocks over up to
+    // kIdxSplitWgs workgroups in all.
+    const int64_t tiles = ((int64_t)rows + kPfRows - 1) / kPfRows * B;
+    const int64_t nz = tiles >= kIdxSplitWgs ? 1 : min(kIdxSplitWgs / tiles, nb_max);
+    const int bps = (int)((nb_max + nz - 1) / nz);
+    const int nzb = (int)((nb_max + bps - 1) / bps);
+    const dim3 grid((unsigned)((rows + kPfRows - 1) / kPfRows), (unsigned)B, (unsigned)nzb);
     if (f8)
         idx_prefill_kernel<true, 0><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
-                                                          Nmax, nb_max, 0, nullptr, nullptr);
+                                                          Nmax, nb_max, 0, nullptr, nullptr, 0,
+                                                          nzb > 1 ? bps : 0);
     else
         idx_prefill_kernel<false, 0><<<grid, 256, 0, st>>>(qi, ki, kv_lens, q_start, pooled, T, G,
-                                                           Nmax, nb_max, 0, nullptr, nullptr);
+                                                           Nmax, nb_max, 0, nullptr, nullptr, 0,
+                                                           nzb > 1 ? bps : 0);
     return launch_status("prefill index kernel");
 }
 
@@ -1149,7 +1164,7 @@ msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t N
     if (s != MSA_OK || B == 0 || T == 0) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int G = cfg->num_kv_groups, K = cfg->topk;
-    if (T * G > msa::kScanMaxRows && K <= msa::kPrefillRegTopk) {
+    if (!msa::index_uses_pooled(cfg, B, T)) {
         // Prefill: scores, block max and the row's top-K in one kernel.
         const bool f8 = cfg->index_dtype == MSA_FP8_E4M3;
         const unsigned char *qi = static_cast<const unsigned char *>(q_idx);
@@ -1166,7 +1181,7 @@ msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t N
 #undef MSA_IDX_PREFILL
         return launch_status("prefill index kernel");
     }
-    // Decode shapes, and prefill with K above the register top-K: pooled
+    // Decode shapes, K above the register top-K and short prefills: pooled
     // scores into the workspace, then a wavefront ranks each row.
     return msa::launch_scan_topk(cfg, B, T, Nmax, q_idx, k_idx, kv_lens, q_start, sel, sel_scores,
                                  workspace, st);

@@ -106,6 +106,35 @@ def test_shapes(orc, G, R, K, T, N):
     check_all_rows(orc, pr, G, R, K, [N, N - 37], None, what="G%d R%d K%d T%d" % (G, R, K, T))
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prefill_register_topk_K32_sampled_rows(orc, fp8):
+    """A prefill with enough row tiles (two 8192-token sequences x 4 groups:
+    256 workgroups) for the index kernel's fused register top-K, at K = 32
+    (its 32-slot variant), bf16 and E4M3: 640 seeded rows, bit for bit. (The
+    small prefills of the other tests split their key blocks and rank the
+    pooled scores instead.)"""
+    G, R, K, T = 4, 8, 32, 8192
+    lim = 16 if fp8 else 4
+    pr = random_problem(2, T, T, G, R, seed=1400 + fp8, fp8=fp8, idx_lo=-lim, idx_hi=lim)
+    cfg = lib_cfg(G, R, K, fp8)
+    assert msa.workspace_size(cfg, 2, T, T, msa.WS_INDEX_TOPK) == 0  # the register path
+    kv, qs = np.array([T, T - 300], np.int32), np.array([0, 0], np.int32)
+    say("register top-K prefill, fp8=%s" % fp8)
+    sel, sc = msa.index_topk(cfg, dev_index(pr["qi"]), dev_index(pr["ki"]), dev_i32(kv),
+                             dev_i32(qs), want_scores=True)
+    torch.cuda.synchronize()
+    sel, sc = sel.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(1401)
+    rb = rng.integers(0, 2, 640)
+    rows = np.stack([rb, rng.integers(0, kv[rb])], axis=1).astype(np.int32)
+    rows[:4] = [[0, 0], [0, T - 1], [1, 0], [1, T - 301]]
+    osel, osc = orc.index_topk(oracle_cfg(G, R, K, fp8), pr["qi"], pr["ki"], kv, qs, rows=rows)
+    gsel = sel[rows[:, 0], rows[:, 1]].reshape(osel.shape)
+    assert np.array_equal(gsel, osel)
+    assert np.array_equal(sc[rows[:, 0], rows[:, 1]].reshape(osc.shape), osc)
+    assert (sel[1, T - 300:] == -1).all()  # rows past the second sequence's cache
+
+
 def test_all_ties_select_lowest_blocks(orc):
     """Zero index queries make every pooled score 0 (including -0.0 products):
     the K lowest blocks win."""
