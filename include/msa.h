@@ -105,10 +105,13 @@ typedef struct {
  * for B*T*G rows. Writes sel (and sel_scores if non-NULL: the pooled score of
  * each kept block, -inf for padding). T small enough that T*G <= 16 uses a
  * streaming kernel (decode); larger T uses an MFMA kernel (prefill), which
- * ranks each row's blocks in registers for K <= 32 (no workspace) and for
- * K > 32 writes the pooled scores to the workspace and ranks them per row
- * (msa_workspace_size gives B*T*G*ceil(Nmax/S)*4 bytes then). Chunked
- * prefill is q_start[b] > 0 with the earlier keys already in k_idx.
+ * ranks each row's blocks in registers when K <= 32 and the call has at
+ * least 64 tiles of 256 (row, group) rows (ceil(T*G/256) * B >= 64; no
+ * workspace). Otherwise (K > 32, or a short prefill, whose key blocks are
+ * then split over more workgroups) it writes the pooled scores to the
+ * workspace and ranks them per row; msa_workspace_size gives
+ * B*T*G*ceil(Nmax/S)*4 bytes (rounded up) then. Chunked prefill is
+ * q_start[b] > 0 with the earlier keys already in k_idx.
  */
 msa_status msa_index_topk(const msa_config *cfg, int32_t B, int32_t T, int32_t Nmax,
                           const void *q_idx, const void *k_idx, const int32_t *kv_lens,
