@@ -41,10 +41,10 @@
  * nothing, keeps no state between calls and never synchronises: every call
  * enqueues its kernels on `stream` and returns. Scratch memory comes from the
  * caller's `workspace` (size from msa_workspace_size; a call whose size is 0,
- * such as msa_index_topk on prefill shapes, accepts NULL): plain scratch that
- * needs no initialisation and may be reused by any later call on the same
- * stream. Calls that may run at the same time (other streams) must not share
- * a workspace.
+ * such as msa_index_topk on a large prefill with K <= 32, accepts NULL): plain
+ * scratch that needs no initialisation and may be reused by any later call on
+ * the same stream. Calls that may run at the same time (other streams) must
+ * not share a workspace.
  *
  * Errors: shapes, pointers, alignment (16 bytes for tensors, 4 for int32 and
  * fp32 arrays, 256 for the workspace) and workspace size are checked on the
