@@ -414,3 +414,40 @@ def test_prefill_paths_more_shapes(orc, G, R, K, T, N, fp8):
     pr = random_problem(2, T, N, G, R, seed=1900 + G + R + K + T, fp8=fp8, idx_lo=-lim, idx_hi=lim)
     check_all_rows(orc, pr, G, R, K, [N, N - 300], None, fp8=fp8,
                    what="G%d R%d K%d T%d fp8=%d" % (G, R, K, T, fp8))
+
+
+def _sweep_cases(n=36, seed=2024):
+    """Seeded shapes for the sweep below: prefill, chunked prefill (query rows
+    after a cache prefix) and decode in turn, with the group, head, top-k and
+    index-type choices drawn from the supported ranges."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        mode = ("prefill", "chunked", "decode")[i % 3]
+        G = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        R = int(rng.choice([r for r in (1, 2, 3, 8, 16) if G * r <= 32]))
+        K = int(rng.choice([1, 2, 5, 16, 31, 32, 33, 48, 64]))
+        fp8 = bool(rng.integers(0, 2))
+        cases.append((i, mode, G, R, K, fp8))
+    return cases
+
+
+@pytest.mark.parametrize("i,mode,G,R,K,fp8", _sweep_cases())
+def test_seeded_shape_sweep(orc, i, mode, G, R, K, fp8):
+    """Every row of a seeded shape against the oracle: selections bit for bit,
+    outputs and lse within the tolerances (the short-prefill index split and
+    the small tiles of the sparse prefill, the 8-wave decode, K on both sides
+    of the register top-K)."""
+    rng = np.random.default_rng(3000 + i)
+    if mode == "decode":
+        lens = rng.integers(1, 6000, size=int(rng.integers(1, 21))).tolist()
+        test_decode_step_matches_oracle_and_two_calls(orc, G, R, K, lens, fp8)
+        return
+    B = int(rng.integers(1, 3))
+    T = int(rng.integers(17, 200))
+    qs = [0] * B if mode == "prefill" else rng.integers(1, 4000, size=B).tolist()
+    kv = [q + T + int(rng.integers(0, 300)) for q in qs]  # keys past the last row exist
+    lim = 16 if fp8 else 4
+    pr = random_problem(B, T, max(kv), G, R, seed=3100 + i, fp8=fp8, idx_lo=-lim, idx_hi=lim)
+    check_all_rows(orc, pr, G, R, K, kv, qs, fp8=fp8,
+                   what="sweep %d %s G%d R%d K%d fp8=%s" % (i, mode, G, R, K, fp8))
