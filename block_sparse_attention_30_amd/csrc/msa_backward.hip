@@ -242,13 +242,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_tile_kernel(
         const float *b_lse2 = s_lse2 + cb;
         const float *b_dl = s_dl + cb;
         const int *b_pc = s_pc + cb;
+        // P and dS of all four 16-column tiles first (their S and dP chains
+        // are independent), then per pair of tiles one 16x16x32 product per d
+        // tile whose k-slots 8*kg .. 8*kg+3 are columns 32*cp + 4*kg + 0..3
+        // and slots 8*kg+4 .. 8*kg+7 columns 32*cp + 16 + 4*kg + 0..3 (the
+        // same order in both operands).
+        v4i16 pbA[kBwdCols / 32][2][KT], dsbA[kBwdCols / 32][2][KT];
 #pragma unroll
         for (int cp = 0; cp < kBwdCols / 32; ++cp) {
-            // Two 16-column tiles per step: P and dS of both, then one
-            // 16x16x32 product per d tile whose k-slots 8*kg .. 8*kg+3 are
-            // columns 32*cp + 4*kg + 0..3 and slots 8*kg+4 .. 8*kg+7 columns
-            // 32*cp + 16 + 4*kg + 0..3 (the same order in both operands).
-            v4i16 pb[2][KT], dsb[2][KT];
+            auto &pb = pbA[cp];
+            auto &dsb = dsbA[cp];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int ct = 2 * cp + hf;
@@ -287,6 +290,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_tile_kernel(
                                                (16 * ct + 4 * kg) * 2) = dsb[hf][kt2];
                 }
             }
+        }
+#pragma unroll
+        for (int cp = 0; cp < kBwdCols / 32; ++cp) {
+            auto &pb = pbA[cp];
+            auto &dsb = dsbA[cp];
             // dv^T += dout^T P and dk^T += q^T dS over these 32 columns:
             // dout^T / q^T read transposed from LDS (column rows 4*kg + i of
             // each half).
