@@ -13,7 +13,10 @@
 //   idx_prefill_kernel   prefill index scores: 32x32x16 bf16 (or 32x32x64
 //                        E4M3) MFMA over a 256-row tile with the k_idx block
 //                        staged in LDS; block max-pool and a per-row running
-//                        top-K in registers in the epilogue.
+//                        top-K in registers in the epilogue, or (pooled
+//                        scores only: K above the register top-K, short
+//                        prefills) the block maxima written out, with a short
+//                        prefill's key blocks split over more workgroups.
 //   sparse_attn_kernel   (small prefill) one workgroup per (row, group):
 //                        gathers the kept 128-token K/V blocks, serves all R
 //                        heads of the group with 16x16x32 MFMA (QK^T and PV)
