@@ -16,9 +16,12 @@ namespace {
 //                     batch of 64 columns staged in LDS (two buffers), S = q
 //                     K^T, dP = dout V^T, dS, then dv^T += dout^T P and dk^T
 //                     += q^T dS (the columns as the reduction index); the
-//                     batch's dS goes to LDS, where dq^T = K^T dS^T over the
-//                     block's 128 keys gives tau * dq per (row, group, slot,
-//                     head), bf16; an fp32 [dk; dv] partial per tile;
+//                     batch's dS goes to LDS (two buffers, the second in the
+//                     K staging area once each wave holds its K^T operands
+//                     in registers), where dq^T = K^T dS^T over the block's
+//                     128 keys, run after the next batch's products, gives
+//                     tau * dq per (row, group, slot, head), bf16; one
+//                     barrier per batch; an fp32 [dk; dv] partial per tile;
 //   bwd_dkdv_reduce_kernel  per list: dk, dv = sum of its tiles' partials in
 //                     tile order (added to the earlier passes' values);
 //   bwd_dq_merge_kernel  dq of a (row, group) = fp32 sum of its kept slots'
