@@ -72,6 +72,16 @@ def test_project_ragged_rows():
     run(300, 256, 3, seed=501)
 
 
+def test_project_several_tiles_ragged_tail_two_k_steps():
+    # Nine 512-token tiles and a ragged tenth (the grid rounds tiles up to a
+    # multiple of eight), hidden size 64: two K steps, the fewest.
+    run(512 * 9 + 77, 64, 5, seed=506)
+
+
+def test_project_ragged_tail_six_k_steps_eight_groups():
+    run(1100, 192, 8, seed=507)
+
+
 def test_project_one_row_one_group_no_keys():
     run(1, 64, 1, seed=502, keys=False)
 
