@@ -1089,6 +1089,11 @@ def main():
     if not args.no_prefill:
         line["prefill"] = run_prefill(torch, msa, wl.workload(3),
                                       cpu_baseline=not args.no_cpu_baseline)
+        # The token-level sparse branch is bound by its schedule's traffic
+        # (half of it writes): its modelled bytes per second against the copy
+        # ceiling measured above.
+        line["prefill"]["sparse_schedule_frac_of_copy_ceiling"] = round(
+            line["prefill"]["sparse_schedule_gbs"] / line["copy_ceiling"]["value"], 4)
         line["prefill_qblock"] = run_prefill_qblock(torch, msa, wl.workload(3))
         line["index_projection"] = run_projection(torch, msa)
     if not args.no_prefill and not args.no_chunked:
