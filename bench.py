@@ -443,7 +443,7 @@ def cpu_baseline_prefill(w, host, n_rows=128, seed=0x4D534143):
     return res
 
 
-def run_prefill(torch, msa, w, steps=5, warmup=1, cpu_baseline=False):
+def run_prefill(torch, msa, w, steps=5, warmup=3, cpu_baseline=False):
     import numpy as np
     from msa_synth import workloads as wl
     t0 = time.time()
@@ -528,7 +528,7 @@ def run_prefill(torch, msa, w, steps=5, warmup=1, cpu_baseline=False):
     return res
 
 
-def run_projection(torch, msa, M=131072, h=6144, G=4, steps=5, warmup=1):
+def run_projection(torch, msa, M=131072, h=6144, G=4, steps=5, warmup=3):
     """Index projections (msa_index_project) for the 131072 tokens of the
     prefill: hidden [M, h] x w[(G+1)*dI, h]^T, bf16 in and out. The pages give
     no hidden size; 6144 is a stand-in."""
@@ -571,7 +571,7 @@ def qblock_rows(torch, sel_blk, q0, L):
     return sel_blk[:, slots]
 
 
-def run_prefill_qblock(torch, msa, w, steps=5, warmup=1):
+def run_prefill_qblock(torch, msa, w, steps=5, warmup=3):
     """The 131072-token prefill with query-block-shared selections (each
     128-row query block keeps one top-16): msa_index_topk_qblock +
     msa_sparse_attn_prefill_qblock, sparse flops counted exactly per row."""
