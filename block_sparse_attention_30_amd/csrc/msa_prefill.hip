@@ -24,8 +24,8 @@
 //   pf_*_kernel          (prefill) KV-major sparse attention: per-block entry
 //                        lists, one staged block per workgroup serving every
 //                        (row, head) that kept it, log-sum-exp merge.
-//   fill_i32_kernel      zeroes the list bitmaps (no memset, so the calls can
-//                        be captured in graphs).
+//   pf_clear_kernel      zeroes the list bitmaps (a kernel, not a memset, so
+//                        the calls can be captured in graphs).
 //   cache_append_kernel  (msa_cache_append) copies new K, V and index-key rows
 //                        into the caches, one wavefront per (sequence, row).
 //   idx_prefill_kernel<.., QB> and qb_attn_kernel  the query-block-shared
@@ -405,11 +405,6 @@ constexpr int kPfNq = msa::kPfNq;
 constexpr int kPfTileEntriesMax = msa::kPfRounds * msa::kPfWaves * msa::kPfNq * 16;
 
 
-__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = v;
-}
-
 // One wavefront per new (sequence, row): the row's G K rows and G V rows
 // (256 B each) and its index key (kib bytes) are copied 16 B per lane.
 __global__ __launch_bounds__(256) void cache_append_kernel(
@@ -440,6 +435,8 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 // List build of a pass: a counting sort of the kept (row, group, slot)
 // entries by block that keeps row order inside every list, so lists and tiles
 // come out the same on every run (the backward sums over them):
+//   pf_clear_kernel    zeroes the row bitmaps of the lists that can hold
+//                      entries;
 //   pf_mark_kernel     sets bit tl of the kept block's row bitmap (an atomic
 //                      OR, whose result does not depend on the order);
 //   pf_rank_kernel     per list: exclusive prefix popcounts of its bitmap
@@ -468,14 +465,48 @@ __global__ __launch_bounds__(256) void pf_mark_kernel(
     atomicOr(&bits[li * W + (tl >> 5)], 1u << (tl & 31));
 }
 
+// Key blocks of sequence b that exist (any row's kept blocks lie below):
+// lists (b, group, block) at or past it stay empty, so the list build
+// neither clears nor ranks their bitmaps (a chunk early in a long cache has
+// most of its lists past the keys written so far).
+__device__ __forceinline__ int pf_key_blocks(const int32_t *kv_lens, int b, int Nmax) {
+    const int kv = clamp_kv(kv_lens[b], Nmax);
+    return kv > 0 ? (kv - 1) / S + 1 : 0;
+}
+
+// Workgroup per (list, 1024 words of its bitmap): zero the words of the
+// lists that can hold entries (the list's coordinates are workgroup-uniform).
+__global__ __launch_bounds__(256) void pf_clear_kernel(uint32_t *__restrict__ bits,
+                                                       const int32_t *__restrict__ kv_lens,
+                                                       int W, int wchunks, int ng,
+                                                       int64_t nb_max, int Nmax) {
+    const int64_t li = blockIdx.x / (unsigned)wchunks;
+    const int w0 = (int)(blockIdx.x % (unsigned)wchunks) * 1024;
+    const int b = (int)(li / ((int64_t)ng * nb_max));
+    if (li % nb_max >= pf_key_blocks(kv_lens, b, Nmax)) return;
+    uint32_t *row = bits + li * W;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int w = w0 + u * 256 + (int)threadIdx.x;
+        if (w < W) row[w] = 0u;
+    }
+}
+
 // Wave per list.
 __global__ __launch_bounds__(256) void pf_rank_kernel(const uint32_t *__restrict__ bits,
                                                       int64_t nlists, int W,
+                                                      const int32_t *__restrict__ kv_lens,
+                                                      int ng, int64_t nb_max, int Nmax,
                                                       int32_t *__restrict__ wpre,
                                                       int32_t *__restrict__ counts) {
     const int64_t li = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (li >= nlists) return;
+    const int b = (int)(li / ((int64_t)ng * nb_max));
+    if (li % nb_max >= pf_key_blocks(kv_lens, b, Nmax)) {  // no entries; words never read
+        if (lane == 0) counts[li] = 0;
+        return;
+    }
     const uint32_t *bw = bits + li * W;
     int32_t *pw = wpre + li * W;
     int run = 0;
@@ -505,11 +536,19 @@ __global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict
     const int tid = threadIdx.x;
     const int64_t per = (n + 1023) / 1024;
     const int64_t a = min(n, (int64_t)tid * per), e = min(n, a + per);
+    // A thread's list sizes are read kBatch at a time (independent loads in
+    // flight together), in both walks over them.
+    constexpr int kBatch = 16;
     int32_t se = 0, st = 0;
-    for (int64_t i = a; i < e; ++i) {
-        const int32_t c = counts[i];
-        se += c;
-        st += (c + ch - 1) / ch;
+    for (int64_t i0 = a; i0 < e; i0 += kBatch) {
+        int32_t c[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) c[u] = i0 + u < e ? counts[i0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            se += c[u];
+            st += (c[u] + ch - 1) / ch;
+        }
     }
     s_e[tid] = se;
     s_t[tid] = st;
@@ -523,13 +562,21 @@ __global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict
         __syncthreads();
     }
     int32_t oe = s_e[tid] - se, ot = s_t[tid] - st;
-    for (int64_t i = a; i < e; ++i) {
-        const int32_t c = counts[i], nt = (c + ch - 1) / ch;
-        offsets[i] = oe;
-        tile_first[i] = ot;
-        for (int32_t j = 0; j < nt; ++j) tile_map[ot + j] = (int32_t)i;
-        oe += c;
-        ot += nt;
+    for (int64_t i0 = a; i0 < e; i0 += kBatch) {
+        int32_t c[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) c[u] = i0 + u < e ? counts[i0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t i = i0 + u;
+            if (i >= e) break;
+            const int32_t nt = (c[u] + ch - 1) / ch;
+            offsets[i] = oe;
+            tile_first[i] = ot;
+            for (int32_t j = 0; j < nt; ++j) tile_map[ot + j] = (int32_t)i;
+            oe += c[u];
+            ot += nt;
+        }
     }
     if (tid == 1023) {
         offsets[n] = s_e[1023];
@@ -1108,13 +1155,14 @@ void build_pass_lists(const PrefillWs &w, char *base, const int32_t *sel,
     int32_t *tile_first = reinterpret_cast<int32_t *>(base + w.tile_first_off);
     int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.tile_map_off);
     int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
-    const int64_t nwords = w.nlists * W;
     const unsigned slot_blocks = (unsigned)((w.nslots + 255) / 256);
-    fill_i32_kernel<<<(unsigned)((nwords + 255) / 256), 256, 0, st>>>(
-        reinterpret_cast<int32_t *>(bits), nwords, 0);
+    const int wchunks = (W + 1023) / 1024;
+    pf_clear_kernel<<<(unsigned)(w.nlists * wchunks), 256, 0, st>>>(bits, kv_lens, W, wchunks, ng,
+                                                                    w.nb_max, Nmax);
     pf_mark_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
                                                 w.rows, g0, ng, w.nb_max, W, bits);
-    pf_rank_kernel<<<(unsigned)((w.nlists + 3) / 4), 256, 0, st>>>(bits, w.nlists, W, wpre, counts);
+    pf_rank_kernel<<<(unsigned)((w.nlists + 3) / 4), 256, 0, st>>>(bits, w.nlists, W, kv_lens, ng,
+                                                                   w.nb_max, Nmax, wpre, counts);
     pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets, tile_first,
                                        tile_map);
     pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, bits, wpre, offsets, B,
