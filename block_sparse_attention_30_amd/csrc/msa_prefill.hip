@@ -437,8 +437,10 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 // come out the same on every run (the backward sums over them):
 //   pf_clear_kernel    zeroes the row bitmaps of the lists that can hold
 //                      entries;
-//   pf_mark_kernel     sets bit tl of the kept block's row bitmap (an atomic
-//                      OR, whose result does not depend on the order);
+//   pf_mark_lds_kernel (caches of up to kPfMarkLdsBlocks blocks) or
+//   pf_mark_kernel     sets bit tl of the kept block's row bitmap (an OR in
+//                      LDS per 32 rows, then a plain store per nonzero word;
+//                      or a global atomic OR; either result is order-free);
 //   pf_rank_kernel     per list: exclusive prefix popcounts of its bitmap
 //                      words and its entry count;
 //   pf_scan_kernel     list offsets and tiles;
@@ -472,6 +474,47 @@ __global__ __launch_bounds__(256) void pf_mark_kernel(
 __device__ __forceinline__ int pf_key_blocks(const int32_t *kv_lens, int b, int Nmax) {
     const int kv = clamp_kv(kv_lens[b], Nmax);
     return kv > 0 ? (kv - 1) / S + 1 : 0;
+}
+
+// Marking without global atomics, for caches of at most kPfMarkLdsBlocks key
+// blocks: workgroup per (sequence, 32 rows of the pass = one bitmap word,
+// group). Its rows' kept blocks set their bits in an LDS word per key block
+// (LDS OR), then every nonzero word goes to bits[list][word] with a plain
+// store: that word of every list belongs to this workgroup alone, and
+// pf_clear_kernel has zeroed the rest.
+constexpr int kPfMarkLdsBlocks = 16384;
+__global__ __launch_bounds__(256) void pf_mark_lds_kernel(
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, int T, int G, int Nmax, int K, int t0, int rows,
+    int g0, int ng, int64_t nb_max, int W, uint32_t *__restrict__ bits) {
+    // Dynamic LDS: nb_max words, then the 32 rows' selections (32 * K).
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];
+    uint32_t *s_word = s_dyn;
+    int32_t *s_sel = reinterpret_cast<int32_t *>(s_dyn + nb_max);
+    const int tid = threadIdx.x;
+    const int gl = (int)(blockIdx.x % (unsigned)ng);
+    const int bc = (int)(blockIdx.x / (unsigned)ng);  // (b, word c)
+    const int b = bc / W, c = bc % W;
+    const int nb = pf_key_blocks(kv_lens, b, Nmax);
+    const int r0 = 32 * c, nr = min(32, rows - r0);
+    for (int i = tid; i < nb; i += 256) s_word[i] = 0u;
+    for (int i = tid; i < nr * K; i += 256) {
+        const int t = t0 + r0 + i / K;  // a last pass may reach past the call's rows
+        s_sel[i] = t < T ? sel[(((int64_t)b * T + t) * G + g0 + gl) * K + i % K] : -1;
+    }
+    __syncthreads();
+    for (int i = tid; i < nr * K; i += 256) {
+        const int rl = i / K, k = i % K;
+        const int p = pf_row_pos(kv_lens, q_start, b, t0 + r0 + rl, T, Nmax);
+        if (p < 0 || !slot_kept(s_sel + rl * K, k, p / S + 1)) continue;
+        atomicOr(&s_word[s_sel[i]], 1u << rl);  // kept ids lie below p / S + 1 <= nb
+    }
+    __syncthreads();
+    uint32_t *col = bits + ((int64_t)b * ng + gl) * nb_max * W + c;
+    for (int i = tid; i < nb; i += 256) {
+        const uint32_t v = s_word[i];
+        if (v) col[(int64_t)i * W] = v;
+    }
 }
 
 // Workgroup per (list, 1024 words of its bitmap): zero the words of the
@@ -569,13 +612,14 @@ __global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int64_t i = i0 + u;
-            if (i >= e) break;
-            const int32_t nt = (c[u] + ch - 1) / ch;
-            offsets[i] = oe;
-            tile_first[i] = ot;
-            for (int32_t j = 0; j < nt; ++j) tile_map[ot + j] = (int32_t)i;
-            oe += c[u];
-            ot += nt;
+            if (i < e) {
+                const int32_t nt = (c[u] + ch - 1) / ch;
+                offsets[i] = oe;
+                tile_first[i] = ot;
+                for (int32_t j = 0; j < nt; ++j) tile_map[ot + j] = (int32_t)i;
+                oe += c[u];
+                ot += nt;
+            }
         }
     }
     if (tid == 1023) {
@@ -1159,8 +1203,13 @@ void build_pass_lists(const PrefillWs &w, char *base, const int32_t *sel,
     const int wchunks = (W + 1023) / 1024;
     pf_clear_kernel<<<(unsigned)(w.nlists * wchunks), 256, 0, st>>>(bits, kv_lens, W, wchunks, ng,
                                                                     w.nb_max, Nmax);
-    pf_mark_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
-                                                w.rows, g0, ng, w.nb_max, W, bits);
+    if (w.nb_max <= kPfMarkLdsBlocks)
+        pf_mark_lds_kernel<<<(unsigned)((int64_t)B * W * ng), 256,
+                             (size_t)(w.nb_max + 32 * K) * 4, st>>>(
+            sel, kv_lens, q_start, T, G, Nmax, K, t0, w.rows, g0, ng, w.nb_max, W, bits);
+    else
+        pf_mark_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
+                                                    w.rows, g0, ng, w.nb_max, W, bits);
     pf_rank_kernel<<<(unsigned)((w.nlists + 3) / 4), 256, 0, st>>>(bits, w.nlists, W, kv_lens, ng,
                                                                    w.nb_max, Nmax, wpre, counts);
     pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets, tile_first,
