@@ -569,62 +569,76 @@ __global__ __launch_bounds__(256) void pf_rank_kernel(const uint32_t *__restrict
 }
 
 // One workgroup of 1024 threads: exclusive scans of the list sizes and of
-// their tile counts, and the tile -> list map.
+// their tile counts, and the tile -> list map. The lists go by in segments
+// of 8192: the segment's sizes are read coalesced into LDS, every thread
+// takes eight consecutive ones, a workgroup scan places them after the
+// previous segments, and the offsets and tile starts are written back
+// coalesced from LDS (the tile map directly).
+constexpr int kScanSeg = 8;  // lists per thread per segment
 __global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict__ counts,
                                                        int64_t n, int ch,
                                                        int32_t *__restrict__ offsets,
                                                        int32_t *__restrict__ tile_first,
                                                        int32_t *__restrict__ tile_map) {
+    constexpr int kSeg = 1024 * kScanSeg;
+    __shared__ int32_t s_c[kSeg], s_f[kSeg];
     __shared__ int32_t s_e[1024], s_t[1024];
     const int tid = threadIdx.x;
-    const int64_t per = (n + 1023) / 1024;
-    const int64_t a = min(n, (int64_t)tid * per), e = min(n, a + per);
-    // A thread's list sizes are read kBatch at a time (independent loads in
-    // flight together), in both walks over them.
-    constexpr int kBatch = 16;
-    int32_t se = 0, st = 0;
-    for (int64_t i0 = a; i0 < e; i0 += kBatch) {
-        int32_t c[kBatch];
+    int32_t base_e = 0, base_t = 0;  // totals of the previous segments
+    for (int64_t s0 = 0; s0 < n; s0 += kSeg) {
+        const int m = (int)min((int64_t)kSeg, n - s0);
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) c[u] = i0 + u < e ? counts[i0 + u] : 0;
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            se += c[u];
-            st += (c[u] + ch - 1) / ch;
+        for (int v = 0; v < kScanSeg; ++v) {
+            const int i = v * 1024 + tid;
+            s_c[i] = i < m ? counts[s0 + i] : 0;
         }
-    }
-    s_e[tid] = se;
-    s_t[tid] = st;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t ve = tid >= off ? s_e[tid - off] : 0;
-        const int32_t vt = tid >= off ? s_t[tid - off] : 0;
         __syncthreads();
-        s_e[tid] += ve;
-        s_t[tid] += vt;
+        int32_t c[kScanSeg], nt[kScanSeg], se = 0, st = 0;
+#pragma unroll
+        for (int u = 0; u < kScanSeg; ++u) {
+            c[u] = s_c[tid * kScanSeg + u];
+            nt[u] = (c[u] + ch - 1) / ch;
+            se += c[u];
+            st += nt[u];
+        }
+        s_e[tid] = se;
+        s_t[tid] = st;
         __syncthreads();
-    }
-    int32_t oe = s_e[tid] - se, ot = s_t[tid] - st;
-    for (int64_t i0 = a; i0 < e; i0 += kBatch) {
-        int32_t c[kBatch];
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int32_t ve = tid >= off ? s_e[tid - off] : 0;
+            const int32_t vt = tid >= off ? s_t[tid - off] : 0;
+            __syncthreads();
+            s_e[tid] += ve;
+            s_t[tid] += vt;
+            __syncthreads();
+        }
+        int32_t oe = base_e + s_e[tid] - se, ot = base_t + s_t[tid] - st;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) c[u] = i0 + u < e ? counts[i0 + u] : 0;
+        for (int u = 0; u < kScanSeg; ++u) {
+            const int i = tid * kScanSeg + u;
+            s_c[i] = oe;  // this thread's own entries: no other thread reads them now
+            s_f[i] = ot;
+            if (i < m)
+                for (int32_t j = 0; j < nt[u]; ++j) tile_map[ot + j] = (int32_t)(s0 + i);
+            oe += c[u];
+            ot += nt[u];
+        }
+        base_e += s_e[1023];
+        base_t += s_t[1023];
+        __syncthreads();
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t i = i0 + u;
-            if (i < e) {
-                const int32_t nt = (c[u] + ch - 1) / ch;
-                offsets[i] = oe;
-                tile_first[i] = ot;
-                for (int32_t j = 0; j < nt; ++j) tile_map[ot + j] = (int32_t)i;
-                oe += c[u];
-                ot += nt;
+        for (int v = 0; v < kScanSeg; ++v) {
+            const int i = v * 1024 + tid;
+            if (i < m) {
+                offsets[s0 + i] = s_c[i];
+                tile_first[s0 + i] = s_f[i];
             }
         }
+        __syncthreads();  // s_c, s_e and s_t are refilled by the next segment
     }
-    if (tid == 1023) {
-        offsets[n] = s_e[1023];
-        tile_first[n] = s_t[1023];
+    if (tid == 0) {
+        offsets[n] = base_e;
+        tile_first[n] = base_t;
     }
 }
 
