@@ -444,8 +444,9 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 //   pf_rank_kernel     per list: exclusive prefix popcounts of its bitmap
 //                      words and its entry count;
 //   pf_scan_kernel     list offsets and tiles;
+//   pf_scatter_lds_kernel (with pf_mark_lds_kernel) or
 //   pf_scatter_kernel  an entry's rank is its word's prefix plus the popcount
-//                      of the lower bits of its word.
+//                      of the lower bits of its word (rebuilt in LDS, or read).
 // Thread per (sequence, row of the pass, group, slot).
 __global__ __launch_bounds__(256) void pf_mark_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
@@ -639,6 +640,50 @@ __global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict
     if (tid == 0) {
         offsets[n] = base_e;
         tile_first[n] = base_t;
+    }
+}
+
+// The scatter for caches of up to kPfMarkLdsBlocks key blocks, on the grid
+// of pf_mark_lds_kernel: the workgroup rebuilds its bitmap word of every list
+// in LDS (the same OR), so an entry's rank needs only its word's prefix.
+__global__ __launch_bounds__(256) void pf_scatter_lds_kernel(
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
+    const int32_t *__restrict__ q_start, const int32_t *__restrict__ wpre,
+    const int32_t *__restrict__ offsets, int T, int G, int Nmax, int K, int t0, int rows,
+    int g0, int ng, int64_t nb_max, int W, int32_t *__restrict__ list) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];
+    uint32_t *s_word = s_dyn;
+    int32_t *s_sel = reinterpret_cast<int32_t *>(s_dyn + nb_max);
+    const int tid = threadIdx.x;
+    const int gl = (int)(blockIdx.x % (unsigned)ng);
+    const int bc = (int)(blockIdx.x / (unsigned)ng);  // (b, word c)
+    const int b = bc / W, c = bc % W;
+    const int nb = pf_key_blocks(kv_lens, b, Nmax);
+    const int r0 = 32 * c, nr = min(32, rows - r0);
+    for (int i = tid; i < nb; i += 256) s_word[i] = 0u;
+    for (int i = tid; i < nr * K; i += 256) {
+        const int t = t0 + r0 + i / K;
+        s_sel[i] = t < T ? sel[(((int64_t)b * T + t) * G + g0 + gl) * K + i % K] : -1;
+    }
+    __syncthreads();
+    // Kept entries: this thread's, as a bit mask over its (at most eight) indices.
+    uint32_t mine = 0u;
+    for (int i = tid, n = 0; i < nr * K; i += 256, ++n) {
+        const int rl = i / K, k = i % K;
+        const int p = pf_row_pos(kv_lens, q_start, b, t0 + r0 + rl, T, Nmax);
+        if (p < 0 || !slot_kept(s_sel + rl * K, k, p / S + 1)) continue;
+        mine |= 1u << n;
+        atomicOr(&s_word[s_sel[i]], 1u << rl);
+    }
+    __syncthreads();
+    const int64_t l0 = ((int64_t)b * ng + gl) * nb_max;
+    for (int i = tid, n = 0; i < nr * K; i += 256, ++n) {
+        if (!((mine >> n) & 1u)) continue;
+        const int rl = i / K, k = i % K;
+        const int blk = s_sel[i];
+        const int64_t li = l0 + blk;
+        const int r = wpre[li * W + c] + __popc(s_word[blk] & ((1u << rl) - 1u));
+        list[offsets[li] + r] = ((r0 + rl) << kEntShift) | k;
     }
 }
 
@@ -1228,9 +1273,15 @@ void build_pass_lists(const PrefillWs &w, char *base, const int32_t *sel,
                                                                    w.nb_max, Nmax, wpre, counts);
     pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets, tile_first,
                                        tile_map);
-    pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, bits, wpre, offsets, B,
-                                                   T, G, Nmax, K, t0, w.rows, g0, ng, w.nb_max, W,
-                                                   list);
+    if (w.nb_max <= kPfMarkLdsBlocks)
+        pf_scatter_lds_kernel<<<(unsigned)((int64_t)B * W * ng), 256,
+                                (size_t)(w.nb_max + 32 * K) * 4, st>>>(
+            sel, kv_lens, q_start, wpre, offsets, T, G, Nmax, K, t0, w.rows, g0, ng, w.nb_max, W,
+            list);
+    else
+        pf_scatter_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, bits, wpre, offsets,
+                                                       B, T, G, Nmax, K, t0, w.rows, g0, ng,
+                                                       w.nb_max, W, list);
 }
 
 // Pooled block scores of T*G > kScanMaxRows rows: the MFMA prefill index
