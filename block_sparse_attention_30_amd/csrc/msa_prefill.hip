@@ -643,6 +643,67 @@ __global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict
     }
 }
 
+// The same scan for at most kScanSmall lists: every thread walks a run of
+// consecutive lists (for a few dozen lists, as in short prefills, this is
+// several times faster than the segmented form).
+constexpr int64_t kScanSmall = 8192;
+__global__ __launch_bounds__(1024) void pf_scan_small_kernel(const int32_t *__restrict__ counts,
+                                                       int64_t n, int ch,
+                                                       int32_t *__restrict__ offsets,
+                                                       int32_t *__restrict__ tile_first,
+                                                       int32_t *__restrict__ tile_map) {
+    __shared__ int32_t s_e[1024], s_t[1024];
+    const int tid = threadIdx.x;
+    const int64_t per = (n + 1023) / 1024;
+    const int64_t a = min(n, (int64_t)tid * per), e = min(n, a + per);
+    // A thread's list sizes are read kBatch at a time, in both walks.
+    constexpr int kBatch = 16;
+    int32_t se = 0, st = 0;
+    for (int64_t i0 = a; i0 < e; i0 += kBatch) {
+        int32_t c[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) c[u] = i0 + u < e ? counts[i0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            se += c[u];
+            st += (c[u] + ch - 1) / ch;
+        }
+    }
+    s_e[tid] = se;
+    s_t[tid] = st;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t ve = tid >= off ? s_e[tid - off] : 0;
+        const int32_t vt = tid >= off ? s_t[tid - off] : 0;
+        __syncthreads();
+        s_e[tid] += ve;
+        s_t[tid] += vt;
+        __syncthreads();
+    }
+    int32_t oe = s_e[tid] - se, ot = s_t[tid] - st;
+    for (int64_t i0 = a; i0 < e; i0 += kBatch) {
+        int32_t c[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) c[u] = i0 + u < e ? counts[i0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t i = i0 + u;
+            if (i < e) {
+                const int32_t nt = (c[u] + ch - 1) / ch;
+                offsets[i] = oe;
+                tile_first[i] = ot;
+                for (int32_t j = 0; j < nt; ++j) tile_map[ot + j] = (int32_t)i;
+                oe += c[u];
+                ot += nt;
+            }
+        }
+    }
+    if (tid == 1023) {
+        offsets[n] = s_e[1023];
+        tile_first[n] = s_t[1023];
+    }
+}
+
 // The scatter for caches of up to kPfMarkLdsBlocks key blocks, on the grid
 // of pf_mark_lds_kernel: the workgroup rebuilds its bitmap word of every list
 // in LDS (the same OR), so an entry's rank needs only its word's prefix.
@@ -1271,8 +1332,12 @@ void build_pass_lists(const PrefillWs &w, char *base, const int32_t *sel,
                                                     w.rows, g0, ng, w.nb_max, W, bits);
     pf_rank_kernel<<<(unsigned)((w.nlists + 3) / 4), 256, 0, st>>>(bits, w.nlists, W, kv_lens, ng,
                                                                    w.nb_max, Nmax, wpre, counts);
-    pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets, tile_first,
-                                       tile_map);
+    if (w.nlists <= kScanSmall)
+        pf_scan_small_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets,
+                                                 tile_first, tile_map);
+    else
+        pf_scan_kernel<<<1, 1024, 0, st>>>(counts, w.nlists, w.entries_per_tile, offsets,
+                                           tile_first, tile_map);
     if (w.nb_max <= kPfMarkLdsBlocks)
         pf_scatter_lds_kernel<<<(unsigned)((int64_t)B * W * ng), 256,
                                 (size_t)(w.nb_max + 32 * K) * 4, st>>>(
