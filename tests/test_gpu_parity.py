@@ -451,3 +451,49 @@ def test_seeded_shape_sweep(orc, i, mode, G, R, K, fp8):
     pr = random_problem(B, T, max(kv), G, R, seed=3100 + i, fp8=fp8, idx_lo=-lim, idx_hi=lim)
     check_all_rows(orc, pr, G, R, K, kv, qs, fp8=fp8,
                    what="sweep %d %s G%d R%d K%d fp8=%s" % (i, mode, G, R, K, fp8))
+
+
+def test_list_build_paths_for_caches_past_16384_blocks(orc):
+    """A cache capacity above 16384 key blocks takes the list build's global
+    atomic marking and plain scatter instead of the LDS forms: the same rows
+    and keys with a small and a large capacity give bit-identical forward
+    outputs and gradients, and the forward matches the oracle."""
+    G, R, K, T = 1, 4, 8, 300
+    kv, qs = [600], [300]
+    N_small, N_big = 1024, 16386 * 128  # 8 and 16386 key blocks
+    pr = random_problem(1, T, N_small, G, R, seed=2300)
+    cfg = lib_cfg(G, R, K)
+
+    def caches(N):
+        k = np.zeros((1, G, N, 128), np.uint16)
+        v = np.zeros((1, G, N, 128), np.uint16)
+        ki = np.zeros((1, N, 128), np.uint16)
+        k[:, :, :N_small], v[:, :, :N_small], ki[:, :N_small] = pr["k"], pr["v"], pr["ki"]
+        return dev_bf16(k), dev_bf16(v), dev_bf16(ki)
+
+    q, qi = dev_bf16(pr["q"]), dev_bf16(pr["qi"])
+    kvd, qsd = dev_i32(kv), dev_i32(qs)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(23)
+    dout = torch.randn((1, T, G * R, 128), generator=g, device="cuda").to(torch.bfloat16)
+    res = {}
+    for N in (N_small, N_big):
+        k, v, ki = caches(N)
+        say("list build paths: Nmax=%d" % N)
+        sel = msa.index_topk(cfg, qi, ki, kvd, qsd)
+        out, lse = msa.sparse_attn_prefill(cfg, q, k, v, kvd, sel, q_start=qsd, want_lse=True)
+        dq, dk, dv = msa.sparse_attn_backward(cfg, q, k, v, kvd, sel, out, lse, dout, q_start=qsd)
+        torch.cuda.synchronize()
+        assert not dk[:, :, N_small:].any() and not dv[:, :, N_small:].any()
+        res[N] = (sel.cpu(), out.cpu(), lse.cpu(), dq.cpu(), dk[:, :, :N_small].cpu(),
+                  dv[:, :, :N_small].cpu())
+        del k, v, ki, dk, dv
+        torch.cuda.empty_cache()
+    for a, b in zip(res[N_small], res[N_big]):
+        assert torch.equal(a, b)
+    sel, lse = res[N_small][0].numpy(), res[N_small][2].numpy()
+    osel, _ = orc.index_topk(oracle_cfg(G, R, K), pr["qi"], pr["ki"], kv, qs)
+    assert np.array_equal(sel.reshape(osel.shape), osel)
+    oout, olse = orc.sparse_attn(oracle_cfg(G, R, K), pr["q"], pr["k"], pr["v"], kv, qs, osel)
+    compare_out(bf16_out_to_f64(res[N_small][1]).reshape(oout.shape), oout, "list paths")
+    compare_lse(lse.astype(np.float64).reshape(olse.shape), olse, "list paths")
