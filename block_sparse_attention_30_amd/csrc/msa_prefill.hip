@@ -443,6 +443,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 //                      or a global atomic OR; either result is order-free);
 //   pf_rank_kernel     per list: exclusive prefix popcounts of its bitmap
 //                      words and its entry count;
+//   pf_scan_small_kernel (up to kScanSmall lists) or
 //   pf_scan_kernel     list offsets and tiles;
 //   pf_scatter_lds_kernel (with pf_mark_lds_kernel) or
 //   pf_scatter_kernel  an entry's rank is its word's prefix plus the popcount
