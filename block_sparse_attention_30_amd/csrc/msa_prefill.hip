@@ -483,12 +483,15 @@ __device__ __forceinline__ int pf_key_blocks(const int32_t *kv_lens, int b, int 
 // group). Its rows' kept blocks set their bits in an LDS word per key block
 // (LDS OR), then every nonzero word goes to bits[list][word] with a plain
 // store: that word of every list belongs to this workgroup alone, and
-// pf_clear_kernel has zeroed the rest.
+// pf_clear_kernel has zeroed the rest. With write_all (caches of at most
+// kPfMarkAllBlocks blocks, where the scattered zero stores are few) every
+// word below the key blocks is stored and no clear runs.
 constexpr int kPfMarkLdsBlocks = 16384;
+constexpr int kPfMarkAllBlocks = 64;
 __global__ __launch_bounds__(256) void pf_mark_lds_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, int T, int G, int Nmax, int K, int t0, int rows,
-    int g0, int ng, int64_t nb_max, int W, uint32_t *__restrict__ bits) {
+    int g0, int ng, int64_t nb_max, int W, int write_all, uint32_t *__restrict__ bits) {
     // Dynamic LDS: nb_max words, then the 32 rows' selections (32 * K).
     extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];
     uint32_t *s_word = s_dyn;
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(256) void pf_mark_lds_kernel(
     uint32_t *col = bits + ((int64_t)b * ng + gl) * nb_max * W + c;
     for (int i = tid; i < nb; i += 256) {
         const uint32_t v = s_word[i];
-        if (v) col[(int64_t)i * W] = v;
+        if (v || write_all) col[(int64_t)i * W] = v;
     }
 }
 
@@ -1322,12 +1325,15 @@ void build_pass_lists(const PrefillWs &w, char *base, const int32_t *sel,
     int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
     const unsigned slot_blocks = (unsigned)((w.nslots + 255) / 256);
     const int wchunks = (W + 1023) / 1024;
-    pf_clear_kernel<<<(unsigned)(w.nlists * wchunks), 256, 0, st>>>(bits, kv_lens, W, wchunks, ng,
-                                                                    w.nb_max, Nmax);
+    const int write_all = w.nb_max <= kPfMarkAllBlocks;
+    if (!write_all)
+        pf_clear_kernel<<<(unsigned)(w.nlists * wchunks), 256, 0, st>>>(bits, kv_lens, W, wchunks,
+                                                                        ng, w.nb_max, Nmax);
     if (w.nb_max <= kPfMarkLdsBlocks)
         pf_mark_lds_kernel<<<(unsigned)((int64_t)B * W * ng), 256,
                              (size_t)(w.nb_max + 32 * K) * 4, st>>>(
-            sel, kv_lens, q_start, T, G, Nmax, K, t0, w.rows, g0, ng, w.nb_max, W, bits);
+            sel, kv_lens, q_start, T, G, Nmax, K, t0, w.rows, g0, ng, w.nb_max, W, write_all,
+            bits);
     else
         pf_mark_kernel<<<slot_blocks, 256, 0, st>>>(sel, kv_lens, q_start, B, T, G, Nmax, K, t0,
                                                     w.rows, g0, ng, w.nb_max, W, bits);
