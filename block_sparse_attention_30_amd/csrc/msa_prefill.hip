@@ -33,6 +33,7 @@
 //                        msa_sparse_attn_prefill_qblock): one top-K per
 //                        128-row query block; attention query-major with an
 //                        online softmax over the block's kept blocks.
+#include <algorithm>
 #include "msa_device.h"
 
 namespace {
@@ -1248,7 +1249,9 @@ __global__ __launch_bounds__(512, 1) void qb_attn_kernel(
 
 // One workgroup per (sequence, row of the pass, group): the kept slots are
 // listed once, their (m, l) staged in LDS, then every thread merges four
-// d-values of one head over the kept slots.
+// d-values of one head over the kept slots. The workgroup is sized to the
+// R * D / 4 threads that merge (64 for two heads), so small groups leave no
+// idle waves holding the compute units' wave slots.
 __global__ __launch_bounds__(256) void pf_merge_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const bf16_t *__restrict__ part_o,
@@ -1258,7 +1261,7 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
     __shared__ int32_t s_kept[KMAX];
     __shared__ int32_t s_n;
     __shared__ float2 s_ml[KMAX * msa::kMaxHeadsPerGroup];
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, nthr = blockDim.x;
     const int64_t unit = blockIdx.x;  // (b, tl, gl), group g0 + gl
     const int g = g0 + (int)(unit % ng);
     const int64_t btl = unit / ng;
@@ -1268,7 +1271,7 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
     const int p = pf_row_pos(kv_lens, q_start, b, t, T, Nmax);
     if (tid < K) s_sel[tid] = p >= 0 ? sel[(((int64_t)b * T + t) * G + g) * K + tid] : -1;
     __syncthreads();
-    if (tid < 64) {
+    if (tid < 64) {  // K <= KMAX = 64: one wave lists the kept slots
         const bool keep = lane < K && p >= 0 && slot_kept(s_sel, lane, p / S + 1);
         const uint64_t m = __ballot(keep);
         if (keep) s_kept[__popcll(m & ((1ull << lane) - 1ull))] = lane;
@@ -1277,10 +1280,10 @@ __global__ __launch_bounds__(256) void pf_merge_kernel(
     __syncthreads();
     const int n = s_n;
     const int64_t slot0 = unit * K;
-    for (int i = tid; i < n * R; i += 256) s_ml[i] = part_ml[(slot0 + s_kept[i / R]) * R + i % R];
+    for (int i = tid; i < n * R; i += nthr) s_ml[i] = part_ml[(slot0 + s_kept[i / R]) * R + i % R];
     __syncthreads();
     const int H = G * R;
-    for (int idx = tid; idx < R * (D / 4); idx += 256) {
+    for (int idx = tid; idx < R * (D / 4); idx += nthr) {
         const int r = idx / (D / 4), d0 = (idx % (D / 4)) * 4;
         float M = -INFINITY;
         for (int i = 0; i < n; ++i) M = fmaxf(M, s_ml[i * R + r].x);
@@ -1466,6 +1469,9 @@ msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, 
     int32_t *list = reinterpret_cast<int32_t *>(base + w.list_off);
     bf16_t *part_o = reinterpret_cast<bf16_t *>(base + w.part_o_off);
     float2 *part_ml = reinterpret_cast<float2 *>(base + w.part_ml_off);
+    // Merge threads: R * D / 4 rounded up to whole waves, at most 256 (K <= 64
+    // needs one wave, which every size here has).
+    const unsigned merge_threads = (unsigned)std::min(256, (R * (D / 4) + 63) / 64 * 64);
     for (int32_t g0 = 0; g0 < G; g0 += w.groups)
       for (int32_t t0 = 0; t0 < T; t0 += w.rows) {
         const int ng = w.groups;
@@ -1474,7 +1480,7 @@ msa_status msa_sparse_attn_prefill(const msa_config *cfg, int32_t B, int32_t T, 
             qp, kp, vp, kv_lens, q_start, offsets, tile_first, tile_map, list, w.nlists, T, G, R,
             Nmax, K, t0, w.rows, g0, ng, w.nb_max, w.entries_per_tile, sl2, part_o, part_ml,
             reinterpret_cast<unsigned char *>(base + w.trash_off));
-        pf_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), 256, 0, st>>>(
+        pf_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), merge_threads, 0, st>>>(
             sel, kv_lens, q_start, part_o, part_ml, T, G, R, Nmax, K, t0, w.rows, g0, ng, op, lse);
         s = launch_status("sparse prefill kernels");
         if (s != MSA_OK) return s;
