@@ -1,5 +1,6 @@
 // libmsa backward of the sparse branch for gfx950 (MI355X, CDNA4) and its
 // entry point, msa_sparse_attn_backward.
+#include <algorithm>
 #include "msa_device.h"
 
 namespace {
@@ -383,7 +384,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(
 }
 
 // dq of one (sequence, row of the pass, group): the kept slots' partials
-// summed in slot order; zero for a row outside the cache.
+// summed in slot order; zero for a row outside the cache. The workgroup
+// holds the R * D / 4 threads that sum, rounded up to whole waves.
 __global__ __launch_bounds__(256) void bwd_dq_merge_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ kv_lens,
     const int32_t *__restrict__ q_start, const bf16_t *__restrict__ part_dq, int T, int G, int R,
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(256) void bwd_dq_merge_kernel(
     __shared__ int32_t s_sel[KMAX];
     __shared__ int32_t s_kept[KMAX];
     __shared__ int32_t s_n;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, nthr = blockDim.x;
     const int64_t unit = blockIdx.x;
     const int g = g0 + (int)(unit % ng);
     const int64_t btl = unit / ng;
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(256) void bwd_dq_merge_kernel(
     const int p = pf_row_pos(kv_lens, q_start, b, t, T, Nmax);
     if (tid < K) s_sel[tid] = p >= 0 ? sel[(((int64_t)b * T + t) * G + g) * K + tid] : -1;
     __syncthreads();
-    if (tid < 64) {
+    if (tid < 64) {  // K <= KMAX = 64: one wave lists the kept slots
         const bool keep = lane < K && p >= 0 && slot_kept(s_sel, lane, p / S + 1);
         const uint64_t m = __ballot(keep);
         if (keep) s_kept[__popcll(m & ((1ull << lane) - 1ull))] = lane;
@@ -410,7 +412,7 @@ __global__ __launch_bounds__(256) void bwd_dq_merge_kernel(
     __syncthreads();
     const int n = s_n;
     const int H = G * R;
-    for (int idx = tid; idx < R * (D / 4); idx += 256) {
+    for (int idx = tid; idx < R * (D / 4); idx += nthr) {
         const int r = idx / (D / 4), d0 = (idx % (D / 4)) * 4;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < n; ++i) {
@@ -460,6 +462,8 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
     const int64_t nrows = (int64_t)B * T * G * R;
     bwd_delta_kernel<<<(unsigned)((nrows * 16 + 255) / 256), 256, 0, st>>>(
         static_cast<const bf16_t *>(out), dop, nrows, delta);
+    // dq merge threads: R * D / 4 rounded up to whole waves, at most 256.
+    const unsigned merge_threads = (unsigned)std::min(256, (R * (D / 4) + 63) / 64 * 64);
     for (int32_t g0 = 0; g0 < G; g0 += w.groups)
       for (int32_t t0 = 0; t0 < T; t0 += w.rows) {
         const int ng = w.groups;
@@ -470,7 +474,7 @@ msa_status msa_sparse_attn_backward(const msa_config *cfg, int32_t B, int32_t T,
             tau, part_dq, part_kv, reinterpret_cast<unsigned char *>(base + w.trash_off));
         bwd_dkdv_reduce_kernel<<<(unsigned)w.nlists, 256, 0, st>>>(
             tile_first, part_kv, G, Nmax, g0, ng, w.nb_max, tau, t0 > 0 ? 1 : 0, dk, dv);
-        bwd_dq_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), 256, 0, st>>>(
+        bwd_dq_merge_kernel<<<(unsigned)((int64_t)B * w.rows * ng), merge_threads, 0, st>>>(
             sel, kv_lens, q_start, part_dq, T, G, R, Nmax, K, t0, w.rows, g0, ng, dq);
         s = launch_status("sparse backward kernels");
         if (s != MSA_OK) return s;

@@ -83,6 +83,12 @@ def test_backward_short_context_odd_heads(orc):
     run(orc, 1, 257, 257, 3, 5, 16, [257], [0], seed=830)
 
 
+@pytest.mark.parametrize("G,R", [(1, 2), (3, 1)])
+def test_backward_one_and_two_heads_per_group(orc, G, R):
+    # one-wave dq merge workgroups (R * D / 4 <= 64 threads)
+    run(orc, 1, 700, 700, G, R, 16, [700], [0], seed=840 + R)
+
+
 def test_backward_bitwise_repeatable():
     # 4096 rows over 32 blocks: most lists span several tiles, so dk and dv
     # are sums over many tiles; two calls must agree bit for bit (the lists
