@@ -437,7 +437,9 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 // entries by block that keeps row order inside every list, so lists and tiles
 // come out the same on every run (the backward sums over them):
 //   pf_clear_kernel    zeroes the row bitmaps of the lists that can hold
-//                      entries;
+//                      entries (not launched for caches of at most
+//                      kPfMarkAllBlocks blocks, whose marking stores every
+//                      word);
 //   pf_mark_lds_kernel (caches of up to kPfMarkLdsBlocks blocks) or
 //   pf_mark_kernel     sets bit tl of the kept block's row bitmap (an OR in
 //                      LDS per 32 rows, then a plain store per nonzero word;
