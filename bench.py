@@ -784,7 +784,8 @@ def run_small_prefill(torch, msa, steps=20, warmup=3):
     """The 4096-token prefill with one group of two heads: latency of
     msa_index_topk, msa_sparse_attn_prefill and the pair, and of the
     last-token decode step (msa_decode with the 4096-token cache), each call
-    between its own events; min and median over `steps`."""
+    between its own events; then the pair replayed from a HIP graph; min and
+    median over `steps`."""
     from msa_synth import workloads as wl
     w = wl.workload(1)
     kh, vh, kih = wl.gen_caches(w)
@@ -821,6 +822,26 @@ def run_small_prefill(torch, msa, steps=20, warmup=3):
             t_att.append(ev[1].elapsed_time(ev[2]) * 1e3)
             t_pair.append(ev[0].elapsed_time(ev[2]) * 1e3)
             t_dec.append(ev[3].elapsed_time(ev[4]) * 1e3)
+    # The same pair replayed from a HIP graph, as a fixed-shape serving loop
+    # replays it: the device-side latency without the host's marshalling and
+    # launch costs (the eager figures above start on an idle GPU, so they
+    # hold both). The replays must reproduce the eager selection and output.
+    eager_sel, eager_out = sel.clone(), out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        msa.index_topk(cfg, qi, ki, kv, qs, sel=sel, workspace=ws_i)
+        msa.sparse_attn_prefill(cfg, q, k, v, kv, sel, q_start=qs, out=out, workspace=ws_p)
+    torch.cuda.synchronize()
+    t_graph = []
+    for s in range(warmup + steps):
+        ev[0].record()
+        graph.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        if s >= warmup:
+            t_graph.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    graph_equal = bool(torch.equal(sel, eager_sel) and torch.equal(out, eager_out))
+    del graph
     med = lambda xs: sorted(xs)[len(xs) // 2]
     L = w.T
     f_idx = 2.0 * 128 * w.G * L * (L + 1) / 2
@@ -832,6 +853,9 @@ def run_small_prefill(torch, msa, steps=20, warmup=3):
            "sparse_attn_us_median": round(med(t_att), 2),
            "last_token_decode_us_min": round(min(t_dec), 2),
            "last_token_decode_us_median": round(med(t_dec), 2),
+           "graph_prefill_us_min": round(min(t_graph), 2),
+           "graph_prefill_us_median": round(med(t_graph), 2),
+           "graph_matches_eager": graph_equal,
            "index_flops": f_idx, "sparse_flops": f_att,
            "note": "latency figures (32 query tiles; the work is too small to fill the chip)"}
     del k, v, ki, q, qi, sel, out, dsel, dout, ws_i, ws_p, ws_d
