@@ -1021,6 +1021,9 @@ def main():
                     help="skip the 1M-token chunked prefill with E4M3 index data")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling its kernels)")
+    ap.add_argument("--short-prefill-only", action="store_true",
+                    help="run only the 4096-token prefill latency leg (for profiling its "
+                         "kernels)")
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the 16 x 131072 decode legs (bf16 and E4M3 index data), "
                          "for profiling their kernels")
@@ -1038,6 +1041,10 @@ def main():
         sys.exit(1)
     msa.load()
 
+    if args.short_prefill_only:
+        print(json.dumps({"prefill_L4096_G1": run_small_prefill(
+            torch, msa, steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
     if args.prefill_only:
         res = {"prefill": run_prefill(torch, msa, wl.workload(3), steps=args.steps,
                                       warmup=args.warmup),

@@ -652,15 +652,17 @@ __global__ __launch_bounds__(1024) void pf_scan_kernel(const int32_t *__restrict
 
 // The same scan for at most kScanSmall lists: every thread walks a run of
 // consecutive lists (for a few dozen lists, as in short prefills, this is
-// several times faster than the segmented form).
+// several times faster than the segmented form). The runs' sums are scanned
+// within each wave by lane shuffles, then the sixteen wave totals by wave 0:
+// two barriers.
 constexpr int64_t kScanSmall = 8192;
 __global__ __launch_bounds__(1024) void pf_scan_small_kernel(const int32_t *__restrict__ counts,
                                                        int64_t n, int ch,
                                                        int32_t *__restrict__ offsets,
                                                        int32_t *__restrict__ tile_first,
                                                        int32_t *__restrict__ tile_map) {
-    __shared__ int32_t s_e[1024], s_t[1024];
-    const int tid = threadIdx.x;
+    __shared__ int32_t s_we[16], s_wt[16], s_tot[2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t per = (n + 1023) / 1024;
     const int64_t a = min(n, (int64_t)tid * per), e = min(n, a + per);
     // A thread's list sizes are read kBatch at a time, in both walks.
@@ -676,18 +678,42 @@ __global__ __launch_bounds__(1024) void pf_scan_small_kernel(const int32_t *__re
             st += (c[u] + ch - 1) / ch;
         }
     }
-    s_e[tid] = se;
-    s_t[tid] = st;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t ve = tid >= off ? s_e[tid - off] : 0;
-        const int32_t vt = tid >= off ? s_t[tid - off] : 0;
-        __syncthreads();
-        s_e[tid] += ve;
-        s_t[tid] += vt;
-        __syncthreads();
+    int32_t xe = se, xt = st;  // inclusive scans over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t ye = __shfl_up(xe, off), yt = __shfl_up(xt, off);
+        if (lane >= off) {
+            xe += ye;
+            xt += yt;
+        }
     }
-    int32_t oe = s_e[tid] - se, ot = s_t[tid] - st;
+    if (lane == 63) {
+        s_we[wave] = xe;
+        s_wt[wave] = xt;
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive prefixes of the wave totals, and the totals
+        const int32_t we = lane < 16 ? s_we[lane] : 0, wt = lane < 16 ? s_wt[lane] : 0;
+        int32_t ve = we, vt = wt;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int32_t ye = __shfl_up(ve, off), yt = __shfl_up(vt, off);
+            if (lane >= off) {
+                ve += ye;
+                vt += yt;
+            }
+        }
+        if (lane < 16) {
+            s_we[lane] = ve - we;
+            s_wt[lane] = vt - wt;
+        }
+        if (lane == 15) {
+            s_tot[0] = ve;
+            s_tot[1] = vt;
+        }
+    }
+    __syncthreads();
+    int32_t oe = s_we[wave] + xe - se, ot = s_wt[wave] + xt - st;
     for (int64_t i0 = a; i0 < e; i0 += kBatch) {
         int32_t c[kBatch];
 #pragma unroll
@@ -705,9 +731,9 @@ __global__ __launch_bounds__(1024) void pf_scan_small_kernel(const int32_t *__re
             }
         }
     }
-    if (tid == 1023) {
-        offsets[n] = s_e[1023];
-        tile_first[n] = s_t[1023];
+    if (tid == 0) {
+        offsets[n] = s_tot[0];
+        tile_first[n] = s_tot[1];
     }
 }
 
