@@ -1029,7 +1029,7 @@ def main():
                          "for profiling their kernels")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this MSA build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
